@@ -1,0 +1,351 @@
+"""Plain fp64 CPU oracle for fused scaled-dot-product attention with the
+additive bias and mask used by vision transformers.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+What is computed, and the passage each step follows (page title, section):
+
+* Attention itself -- queries and keys, through a softmax, give the attention
+  map, whose values weight the value tensor; heads are independent copies
+  ["Training and inference acceleration for large vision models" (Swin
+  Transformer talk), section 1 "Swin Transformer introduction"].  The scaled
+  form is the ``scaled_dot_product_attention`` function of
+  ["Accelerated Diffusers with PyTorch 2.0", section "Accelerating
+  transformer blocks"]; its default scale 1/sqrt(d) is used throughout.
+  Bias and mask are added to the scaled logits, before the softmax.
+* Self- and cross-attention: same computation, key/value length may differ
+  from the query length [Swin talk, section 1].
+* Window attention, the window shift and the relative-position bias table
+  [Swin talk, section 1; the window partition/shift/merge operations are pure
+  index mappings, section 2 "Swin Transformer training optimisation"].
+* Decomposed relative position (SAM): per-query coordinates index the
+  relative-position tables [“Accelerating Generative AI with PyTorch:
+  Segment Anything, Fast”, section "Bfloat16 half precision (plus GPU syncs
+  and batching)"]; the bias is q·Rh[qh-kh+gh-1] + q·Rw[qw-kw+gw-1].
+
+Readings taken where the pages are silent (all are listed with reasons in the
+design notes of the repository):
+
+* token t of a gh x gw grid sits at row t // gw, column t % gw;
+* windows are numbered row-major inside an image and images are outermost
+  (batch item = image * n_windows + window);
+* table row for offset (dh, dw) = query - key is (dh+gh-1)*(2gw-1) + (dw+gw-1),
+  the table is [(2gh-1)(2gw-1), H] (column = head);
+* the relative-position tables Rh [2gh-1, d], Rw [2gw-1, d] are shared by all
+  heads and are dotted with the raw (unscaled) query;
+* the shifted window attention rolls the image content by (-sh, -sw) before
+  partitioning (shifted[y] = x[(y + sh) mod img_h]) and rolls back after;
+  the region of a shifted-image pixel is 3*ry + rx, where ry is 0, 1, 2 for
+  rows in [0, img_h-win_h), [img_h-win_h, img_h-sh), [img_h-sh, img_h) (same
+  for columns); query/key pairs from different regions get an additive
+  ``value`` (default -100);
+* an additive bias of shape [nB, Nq, Nk] applies to batch item b as b % nB,
+  an additive mask [nW, Nq, Nk] as b % nW.
+
+Everything is numpy float64.  The inputs are the exact values the device
+receives (already rounded to the device dtype), upcast to float64.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+@dataclass
+class Bias:
+    """Additive bias description (mirrors the bias kinds of the attention call).
+
+    kind: "none" | "table" | "relpos" | "additive"
+    grid: (gh, gw) token grid of one batch item (table, relpos)
+    table: [(2gh-1)(2gw-1), H]
+    rh, rw: [2gh-1, d], [2gw-1, d]
+    add: [nB, Nq, Nk], batch item b uses add[b % nB]
+    """
+
+    kind: str = "none"
+    grid: Optional[tuple] = None
+    table: Optional[np.ndarray] = None
+    rh: Optional[np.ndarray] = None
+    rw: Optional[np.ndarray] = None
+    add: Optional[np.ndarray] = None
+
+
+@dataclass
+class Mask:
+    """Additive mask description.
+
+    kind: "none" | "additive" | "shift"
+    add: [nW, Nq, Nk], batch item b uses add[b % nW]
+    window: (img_h, img_w, win_h, win_w, shift_h, shift_w)
+    value: added to pairs from different shifted regions
+    """
+
+    kind: str = "none"
+    add: Optional[np.ndarray] = None
+    window: Optional[tuple] = None
+    value: float = -100.0
+
+
+# ---------------------------------------------------------------------------
+# Index structure of windows and grids
+# ---------------------------------------------------------------------------
+
+def token_coords(gh: int, gw: int):
+    """(row, col) of every token of a gh x gw grid, tokens in row-major order."""
+    t = np.arange(gh * gw)
+    return t // gw, t % gw
+
+
+def table_relative_index(gh: int, gw: int) -> np.ndarray:
+    """[N, N] row of the relative-position table used by query i and key j.
+
+    Swin talk, section 1 (relative position bias); the offset is query minus
+    key, shifted to be non-negative and flattened row-major over the
+    (2gh-1) x (2gw-1) offsets.
+    """
+    r, c = token_coords(gh, gw)
+    dh = r[:, None] - r[None, :]
+    dw = c[:, None] - c[None, :]
+    return (dh + gh - 1) * (2 * gw - 1) + (dw + gw - 1)
+
+
+def table_bias(table: np.ndarray, gh: int, gw: int) -> np.ndarray:
+    """[H, N, N] bias gathered from a [(2gh-1)(2gw-1), H] table."""
+    table = np.asarray(table, dtype=np.float64)
+    assert table.shape[0] == (2 * gh - 1) * (2 * gw - 1)
+    idx = table_relative_index(gh, gw)
+    return np.transpose(table[idx], (2, 0, 1))
+
+
+def relpos_bias(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
+                rw: np.ndarray, gh: int, gw: int) -> np.ndarray:
+    """Decomposed relative-position bias for selected query rows -> [R, N].
+
+    SAM blog, section "Bfloat16 half precision": per-query coordinates index
+    the relative-position tables.  rel_h[i, kh] = q_i . Rh[qh_i - kh + gh - 1]
+    and rel_w[i, kw] = q_i . Rw[qw_i - kw + gw - 1]; the bias of key
+    j = (kh, kw) is rel_h[i, kh] + rel_w[i, kw].  q is the raw query row.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    rh = np.asarray(rh, dtype=np.float64)
+    rw = np.asarray(rw, dtype=np.float64)
+    assert rh.shape[0] == 2 * gh - 1 and rw.shape[0] == 2 * gw - 1
+    qh, qw = np.asarray(rows) // gw, np.asarray(rows) % gw
+    kh = np.arange(gh)
+    kw = np.arange(gw)
+    rh_sel = rh[qh[:, None] - kh[None, :] + gh - 1]          # [R, gh, d]
+    rw_sel = rw[qw[:, None] - kw[None, :] + gw - 1]          # [R, gw, d]
+    rel_h = np.einsum("rc,rkc->rk", q_rows, rh_sel)          # [R, gh]
+    rel_w = np.einsum("rc,rkc->rk", q_rows, rw_sel)          # [R, gw]
+    return (rel_h[:, :, None] + rel_w[:, None, :]).reshape(len(rows), gh * gw)
+
+
+def relpos_bias_gather(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
+                       rw: np.ndarray, gh: int, gw: int) -> np.ndarray:
+    """Same bias through the literal per-pair gather (small grids only).
+
+    For every (query i, key j) pair the two table rows are gathered first,
+    [R, N, d], and then dotted with q_i: q_i . Rh[dh] + q_i . Rw[dw].
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    rh = np.asarray(rh, dtype=np.float64)
+    rw = np.asarray(rw, dtype=np.float64)
+    qr, qc = np.asarray(rows) // gw, np.asarray(rows) % gw
+    kr, kc = token_coords(gh, gw)
+    gath_h = rh[qr[:, None] - kr[None, :] + gh - 1]          # [R, N, d]
+    gath_w = rw[qc[:, None] - kc[None, :] + gw - 1]          # [R, N, d]
+    return (np.einsum("rc,rjc->rj", q_rows, gath_h)
+            + np.einsum("rc,rjc->rj", q_rows, gath_w))
+
+
+# ---------------------------------------------------------------------------
+# Windows, the cyclic shift and the shifted-region mask
+# ---------------------------------------------------------------------------
+
+def shift_region_labels(img_h: int, img_w: int, win_h: int, win_w: int,
+                        shift_h: int, shift_w: int) -> np.ndarray:
+    """[img_h, img_w] region id of every pixel of the shifted image.
+
+    Swin talk, section 1: the window shift brings pixels from different parts
+    of the image into one window; pairs from different parts are kept apart.
+    Each axis splits into the three ranges [0, n-win), [n-win, n-shift),
+    [n-shift, n); regions are numbered row range major.
+    """
+    labels = np.zeros((img_h, img_w), dtype=np.int64)
+    hs = [(0, img_h - win_h), (img_h - win_h, img_h - shift_h), (img_h - shift_h, img_h)]
+    ws = [(0, img_w - win_w), (img_w - win_w, img_w - shift_w), (img_w - shift_w, img_w)]
+    cnt = 0
+    for (h0, h1) in hs:
+        for (w0, w1) in ws:
+            labels[h0:h1, w0:w1] = cnt
+            cnt += 1
+    return labels
+
+
+def window_partition(x: np.ndarray, win_h: int, win_w: int) -> np.ndarray:
+    """[B, H, img_h, img_w, d] -> [B * nW, H, win_h*win_w, d].
+
+    Windows row-major inside an image, images outermost, tokens row-major
+    inside a window (Swin talk, section 1: the image is split into windows and
+    attention runs inside each window only).
+    """
+    B, H, ih, iw, d = x.shape
+    nwy, nwx = ih // win_h, iw // win_w
+    assert nwy * win_h == ih and nwx * win_w == iw
+    y = x.reshape(B, H, nwy, win_h, nwx, win_w, d)
+    y = y.transpose(0, 2, 4, 1, 3, 5, 6)                      # B, wy, wx, H, th, tw, d
+    return y.reshape(B * nwy * nwx, H, win_h * win_w, d)
+
+
+def window_reverse(w: np.ndarray, img_h: int, img_w: int, win_h: int,
+                   win_w: int) -> np.ndarray:
+    """Inverse of :func:`window_partition`."""
+    nwy, nwx = img_h // win_h, img_w // win_w
+    BnW, H, N, d = w.shape
+    B = BnW // (nwy * nwx)
+    y = w.reshape(B, nwy, nwx, H, win_h, win_w, d)
+    y = y.transpose(0, 3, 1, 4, 2, 5, 6)                      # B, H, wy, th, wx, tw, d
+    return y.reshape(B, H, img_h, img_w, d)
+
+
+def shift_mask(img_h: int, img_w: int, win_h: int, win_w: int, shift_h: int,
+               shift_w: int, value: float = -100.0) -> np.ndarray:
+    """[nW, N, N] additive mask: ``value`` where query and key regions differ."""
+    labels = shift_region_labels(img_h, img_w, win_h, win_w, shift_h, shift_w)
+    lw = window_partition(labels[None, None, :, :, None].astype(np.float64),
+                          win_h, win_w)[:, 0, :, 0]           # [nW, N]
+    diff = lw[:, :, None] != lw[:, None, :]
+    return np.where(diff, float(value), 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _additive_rows(b: int, h: int, rows: np.ndarray, q_rows: np.ndarray,
+                   Nk: int, bias: Bias, mask: Mask, cache: dict) -> np.ndarray:
+    """bias + mask for query rows ``rows`` of batch item b, head h -> [R, Nk]."""
+    add = np.zeros((len(rows), Nk), dtype=np.float64)
+    if bias is not None and bias.kind != "none":
+        if bias.kind == "table":
+            gh, gw = bias.grid
+            key = ("table", h)
+            if key not in cache:
+                cache[key] = table_bias(bias.table, gh, gw)[h]
+            add += cache[key][rows]
+        elif bias.kind == "relpos":
+            gh, gw = bias.grid
+            add += relpos_bias(q_rows, rows, bias.rh, bias.rw, gh, gw)
+        elif bias.kind == "additive":
+            a = np.asarray(bias.add, dtype=np.float64)
+            add += a[b % a.shape[0]][rows]
+        else:
+            raise ValueError(f"unknown bias kind {bias.kind!r}")
+    if mask is not None and mask.kind != "none":
+        if mask.kind == "shift":
+            if "shift" not in cache:
+                cache["shift"] = shift_mask(*mask.window, value=mask.value)
+            m = cache["shift"]
+            add += m[b % m.shape[0]][rows]
+        elif mask.kind == "additive":
+            a = np.asarray(mask.add, dtype=np.float64)
+            add += a[b % a.shape[0]][rows]
+        else:
+            raise ValueError(f"unknown mask kind {mask.kind!r}")
+    return add
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax exp(s - max) / sum, in float64."""
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_probs(q, k, bias: Optional[Bias] = None,
+                    mask: Optional[Mask] = None) -> np.ndarray:
+    """Attention map P = softmax(scale*QK^T + bias + mask), [B, H, Nq, Nk]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = 1.0 / np.sqrt(d)
+    cache: dict = {}
+    out = np.empty((B, H, Nq, Nk))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            s = s + _additive_rows(b, h, rows, q[b, h], Nk, bias, mask, cache)
+            out[b, h] = _softmax_rows(s)
+    return out
+
+
+def attention(q, k, v, bias: Optional[Bias] = None, mask: Optional[Mask] = None,
+              select: Optional[Sequence] = None, row_block: int = 512):
+    """O = softmax(scale*QK^T + bias + mask) V in float64.
+
+    q: [B, H, Nq, d]; k, v: [B, H, Nk, d] (batched layout: windows are extra
+    batch items).  With ``select`` = [(b, h, rows), ...] only those output
+    rows are computed and a list of [len(rows), d] arrays is returned;
+    otherwise the full [B, H, Nq, d] output.  Query rows are processed in
+    blocks of ``row_block``; each row's softmax is independent, so this is
+    still the plain definition.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    assert k.shape == (B, H, Nk, d) and v.shape == (B, H, Nk, v.shape[3])
+    scale = 1.0 / np.sqrt(d)
+    cache: dict = {}
+
+    def rows_out(b, h, rows):
+        rows = np.asarray(rows)
+        res = np.empty((len(rows), v.shape[3]))
+        for s0 in range(0, len(rows), row_block):
+            r = rows[s0:s0 + row_block]
+            s = scale * (q[b, h, r] @ k[b, h].T)
+            s = s + _additive_rows(b, h, r, q[b, h, r], Nk, bias, mask, cache)
+            res[s0:s0 + row_block] = _softmax_rows(s) @ v[b, h]
+        return res
+
+    if select is not None:
+        return [rows_out(b, h, rows) for (b, h, rows) in select]
+    out = np.empty((B, H, Nq, v.shape[3]))
+    all_rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = rows_out(b, h, all_rows)
+    return out
+
+
+def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
+                    mask: Optional[Mask] = None) -> np.ndarray:
+    """Shifted-window attention on image-layout tensors [B, H, img_h*img_w, d].
+
+    Swin talk, section 2: shift, partition, attention, reverse partition and
+    reverse shift.  The content is rolled by (-sh, -sw), partitioned into
+    windows, attended with the window bias and mask, merged back and rolled by
+    (+sh, +sw).
+    """
+    img_h, img_w, win_h, win_w, sh, sw = window
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    assert N == img_h * img_w
+
+    def to_windows(x):
+        x = x.reshape(B, H, img_h, img_w, x.shape[-1])
+        x = np.roll(x, shift=(-sh, -sw), axis=(2, 3))
+        return window_partition(x, win_h, win_w)
+
+    ow = attention(to_windows(q), to_windows(k), to_windows(v), bias, mask)
+    o = window_reverse(ow, img_h, img_w, win_h, win_w)
+    o = np.roll(o, shift=(sh, sw), axis=(2, 3))
+    return o.reshape(B, H, N, v.shape[-1])

@@ -1,0 +1,158 @@
+"""Seeded synthetic workloads (shapes and random inputs only).
+
+This module draws the random inputs that both the HIP path and the oracle
+consume.  It contains none of the attention arithmetic: it only knows tensor
+shapes, dtypes and how to draw numbers.
+
+The shapes stand in for the workloads on the pages (no trained weights or
+images are available): Swin window attention ["Training and inference
+acceleration for large vision models", section 1], SAM image-encoder
+attention with decomposed relative position ["Accelerating Generative AI with
+PyTorch: Segment Anything, Fast", sections "Bfloat16" and "SDPA"], and the
+Stable Diffusion v1.5 UNet self/cross attention ["Accelerated Diffusers with
+PyTorch 2.0", section "Stable Diffusion benchmark"].
+
+Recipe: every tensor is drawn with ``numpy.random.Generator(PCG64(
+SeedSequence([16, cfg_id, tensor_id])))`` as float32 standard normals
+(tensor_id q=0, k=1, v=2, table/Rh=3, Rw=4); Q, K, V ~ N(0, 1); table, Rh, Rw
+~ N(0, 0.02^2).  Values are then rounded to the device dtype with torch on
+the CPU (round to nearest even).  An optional ``seed`` offsets the sequence so
+tests can draw independent cases.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+F32, F16, BF16 = "f32", "f16", "bf16"
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    name: str
+    cfg_id: int
+    dtype: str
+    B: int                       # batch items as the kernel sees them (windows included)
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    bias: str = "none"           # none | table | relpos | additive
+    grid: Optional[tuple] = None
+    mask: str = "none"           # none | shift | additive
+    layout: str = "batched"      # batched | image
+    images: Optional[int] = None
+    window: Optional[tuple] = None   # (img_h, img_w, win_h, win_w, shift_h, shift_w)
+    note: str = ""
+
+    @property
+    def q_shape(self):
+        if self.layout == "image":
+            ih, iw = self.window[0], self.window[1]
+            return (self.images, self.H, ih * iw, self.d)
+        return (self.B, self.H, self.Nq, self.d)
+
+    @property
+    def kv_shape(self):
+        if self.layout == "image":
+            return self.q_shape
+        return (self.B, self.H, self.Nk, self.d)
+
+    @property
+    def flops(self) -> int:
+        """4*B*H*Nq*Nk*d (two contractions of 2*Nq*Nk*d each)."""
+        return 4 * self.B * self.H * self.Nq * self.Nk * self.d
+
+    def bytes_per_elem(self) -> int:
+        return {F32: 4, F16: 2, BF16: 2}[self.dtype]
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q + K + V read once, O written once, plus the bias tables."""
+        e = self.bytes_per_elem()
+        qo = 2 * int(np.prod(self.q_shape))
+        kv = 2 * int(np.prod(self.kv_shape))
+        tables = 0
+        if self.bias == "table":
+            gh, gw = self.grid
+            tables = (2 * gh - 1) * (2 * gw - 1) * self.H
+        elif self.bias == "relpos":
+            gh, gw = self.grid
+            tables = (2 * gh - 1 + 2 * gw - 1) * self.d
+        return (qo + kv + tables) * e
+
+
+WORKLOADS = {
+    "C1": Workload("C1", "swin_window_tiny_f32", 1, F32, B=4, H=3, Nq=49, Nk=49, d=32,
+                   bias="table", grid=(7, 7),
+                   note="4 windows of 7x7 tokens, 3 heads, d=32, table bias"),
+    "C2": Workload("C2", "swin_t_stage1_shifted_f16", 2, F16, B=8 * 64, H=3, Nq=49, Nk=49,
+                   d=32, bias="table", grid=(7, 7), mask="shift", layout="image",
+                   images=8, window=(56, 56, 7, 7, 3, 3),
+                   note="8 images of 56x56 tokens, 7x7 windows, cyclic shift 3"),
+    "C3": Workload("C3", "sam_b_windowed_bf16", 3, BF16, B=8 * 25, H=12, Nq=196, Nk=196,
+                   d=64, bias="relpos", grid=(14, 14),
+                   note="SAM ViT-B windowed: 64x64 grid padded to 70x70, 25 windows of 14x14"),
+    "C4": Workload("C4", "sam_b_global_bf16", 4, BF16, B=8, H=12, Nq=4096, Nk=4096, d=64,
+                   bias="relpos", grid=(64, 64), note="SAM ViT-B global attention, 64x64 grid"),
+    "C4h": Workload("C4h", "sam_h_global_bf16", 44, BF16, B=8, H=16, Nq=4096, Nk=4096, d=80,
+                    bias="relpos", grid=(64, 64), note="SAM ViT-H global attention"),
+    "C5s": Workload("C5s", "sd15_unet_self_f16", 5, F16, B=16, H=8, Nq=4096, Nk=4096, d=40,
+                    note="SD 1.5 UNet self-attention at 64x64 latent, CFG batch 16"),
+    "C5x": Workload("C5x", "sd15_unet_cross_f16", 55, F16, B=16, H=8, Nq=4096, Nk=77, d=40,
+                    note="SD 1.5 UNet cross-attention, 77 context tokens"),
+}
+
+
+def _rng(cfg_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
+    parts = [16, cfg_id, tensor_id] + ([seed] if seed else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(parts)))
+
+
+def normal(shape, cfg_id: int, tensor_id: int, std: float = 1.0, seed: int = 0) -> np.ndarray:
+    """float32 N(0, std^2) draws of the given shape."""
+    x = _rng(cfg_id, tensor_id, seed).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def to_dtype(x: np.ndarray, dtype: str):
+    """Round float32 values to the device dtype (torch CPU, round to nearest even)."""
+    import torch
+
+    tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dtype]
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt)
+
+
+def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0) -> dict:
+    """Draw the inputs of workload ``w`` as torch CPU tensors in its dtype.
+
+    Returns q, k, v and, depending on the bias kind, table or rh/rw.
+    """
+    out = {
+        "q": to_dtype(normal(w.q_shape, w.cfg_id, 0, std_qkv, seed), w.dtype),
+        "k": to_dtype(normal(w.kv_shape, w.cfg_id, 1, std_qkv, seed), w.dtype),
+        "v": to_dtype(normal(w.kv_shape, w.cfg_id, 2, std_qkv, seed), w.dtype),
+    }
+    if w.bias == "table":
+        gh, gw = w.grid
+        out["table"] = to_dtype(normal(((2 * gh - 1) * (2 * gw - 1), w.H), w.cfg_id, 3,
+                                       0.02, seed), w.dtype)
+    elif w.bias == "relpos":
+        gh, gw = w.grid
+        out["rh"] = to_dtype(normal((2 * gh - 1, w.d), w.cfg_id, 3, 0.02, seed), w.dtype)
+        out["rw"] = to_dtype(normal((2 * gw - 1, w.d), w.cfg_id, 4, 0.02, seed), w.dtype)
+    return out
+
+
+def custom(dtype: str, B: int, H: int, Nq: int, Nk: int, d: int, bias: str = "none",
+           grid=None, mask: str = "none", layout: str = "batched", images=None,
+           window=None, cfg_id: int = 900, key: str = "custom") -> Workload:
+    """A workload of arbitrary shape for tests (same drawing recipe)."""
+    return Workload(key, key, cfg_id, dtype, B=B, H=H, Nq=Nq, Nk=Nk, d=d, bias=bias,
+                    grid=grid, mask=mask, layout=layout, images=images, window=window)
