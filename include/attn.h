@@ -1,0 +1,186 @@
+/*
+ * attn.h -- C ABI of libattn: fused scaled-dot-product attention forward for
+ * AMD Instinct MI355X (gfx950), with the additive biases and masks of vision
+ * transformers.
+ *
+ *   O = softmax(scale * Q K^T + bias + mask) V,   scale = 1/sqrt(d)
+ *
+ * The operation: queries and keys, through a softmax, give the attention map
+ * whose values weight V; multi-head attention repeats it per head; diffusion
+ * models use both self- and cross-attention ("Training and inference
+ * acceleration for large vision models", Swin Transformer talk, section 1).
+ * The scaled form and its 1/sqrt(d) default are PyTorch's
+ * scaled_dot_product_attention ("Accelerated Diffusers with PyTorch 2.0",
+ * section "Accelerating transformer blocks").  The biases:
+ *   - TABLE: Swin's relative-position bias table (Swin talk, section 1);
+ *   - RELPOS: SAM's decomposed relative position, per-query coordinates
+ *     indexing Rh/Rw ("Accelerating Generative AI with PyTorch: Segment
+ *     Anything, Fast", section "Bfloat16 half precision");
+ *   - ADDITIVE: a dense additive tensor.
+ * The masks: Swin's shifted-window region mask (Swin talk, section 1) or a
+ * dense additive tensor.  Window partition, cyclic shift and their reverses
+ * are pure index mappings (Swin talk, section 2) and are folded into the
+ * kernel's addressing by ATTN_LAYOUT_IMAGE.
+ *
+ * Conventions
+ *  - All tensor pointers are DEVICE pointers owned by the caller; they must
+ *    stay valid until the work queued on `stream` has finished.  The library
+ *    allocates nothing, keeps no pointer after returning, holds no mutable
+ *    global state, and is safe to call from several host threads.
+ *  - attn_fwd never synchronises the device and never copies host memory to
+ *    the device: every index computation (bias gathers, window and shift
+ *    maps, region labels) happens inside the kernel from by-value integers.
+ *    (The pages trace a hidden host sync to indexing with host tensors, SAM
+ *    blog, sections "Baseline" and "Bfloat16"; this ABI has none.)
+ *  - Descriptors themselves are HOST structs read during the call only.
+ *  - Results are deterministic: identical inputs give bitwise-identical
+ *    outputs (no atomics, fixed reduction order).
+ *  - Errors are returned as status codes; nothing is thrown or aborted
+ *    across the ABI.  NaN/Inf in the inputs are not checked; they propagate
+ *    to the affected output rows.  A row whose logits are all -inf (only
+ *    possible through an ADDITIVE mask/bias) produces NaN, as the plain
+ *    definition does.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_API __attribute__((visibility("default")))
+
+/* Status codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = 1,        /* a required pointer is NULL                        */
+  ATTN_E_SHAPE = 2,       /* inconsistent B/H/N/d, grid or window geometry     */
+  ATTN_E_LAYOUT = 3,      /* bad strides or alignment                          */
+  ATTN_E_UNSUPPORTED = 4, /* head_dim, dtype or size outside what is built     */
+  ATTN_E_ALIAS = 5,       /* out overlaps q, k or v                            */
+  ATTN_E_LAUNCH = 6,      /* the HIP launch reported an error                  */
+  ATTN_E_INVALID = 7      /* an enum value or field is out of range            */
+};
+
+/* Element type of q, k, v, out, the bias tables and dense bias/mask tensors. */
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
+
+/* Token layout of a tensor.
+ *  BATCHED: dims = {B_eff, H, N, d}; windows are extra batch items.
+ *  IMAGE:   dims = {B_img, H, img_h*img_w, d}, tokens in image row-major
+ *           order.  The kernel partitions the image into win_h x win_w
+ *           windows (after a cyclic shift by (shift_h, shift_w) when they are
+ *           non-zero) and writes `out` back in image order, i.e. reverse
+ *           partition and reverse shift.  The window geometry is taken from
+ *           mask_desc->win.  Batch item b_eff = img * nW + window, windows
+ *           row-major.  q, k, v and out must all use IMAGE together.        */
+typedef enum { ATTN_LAYOUT_BATCHED = 0, ATTN_LAYOUT_IMAGE = 1 } attn_layout_t;
+
+/* A strided 4-D tensor [B, H, N, d]; the d stride is 1.
+ * strides[] are in ELEMENTS for the B, H and N axes.  `data` must be 16-byte
+ * aligned and every row (N stride * element size) a multiple of 16 bytes for
+ * the half-precision types (4 bytes for f32).                               */
+typedef struct {
+  void* data;
+  int64_t dims[4];
+  int64_t strides[3];
+  int32_t layout; /* attn_layout_t */
+} attn_tensor_t;
+
+typedef enum {
+  ATTN_BIAS_NONE = 0,
+  ATTN_BIAS_TABLE = 1,    /* bias[i,j] = table[(qh-kh+gh-1)*(2gw-1) + (qw-kw+gw-1), head] */
+  ATTN_BIAS_RELPOS = 2,   /* bias[i,j] = q_i.Rh[qh-kh+gh-1] + q_i.Rw[qw-kw+gw-1]          */
+  ATTN_BIAS_ADDITIVE = 3  /* bias[i,j] = add[b % add_batch, i, j]                          */
+} attn_bias_kind_t;
+
+/* Bias descriptor.
+ *  grid_h, grid_w: token grid of one batch item (window or image); required
+ *    for TABLE and RELPOS, where Nq = Nk = grid_h * grid_w and token t sits
+ *    at (t / grid_w, t % grid_w).
+ *  table: [(2gh-1)(2gw-1), H] contiguous, element [r, head] at r*H + head.
+ *  rh: [2gh-1, d], rw: [2gw-1, d] contiguous, shared by all heads; they are
+ *    dotted with the raw (unscaled) query row; the bias is not scaled.
+ *  add: [add_batch, Nq, Nk] with element strides add_strides[0..1] for the
+ *    first two axes, last stride 1; batch item b uses add[b % add_batch].
+ *  All bias data uses the call's dtype.                                     */
+typedef struct {
+  int32_t kind; /* attn_bias_kind_t */
+  int32_t grid_h, grid_w;
+  const void* table;
+  const void* rh;
+  const void* rw;
+  const void* add;
+  int64_t add_batch;
+  int64_t add_strides[2];
+} attn_bias_desc_t;
+
+typedef enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_ADDITIVE = 1,      /* mask[i,j] = add[b % n_win, i, j]                       */
+  ATTN_MASK_SHIFT_REGIONS = 2  /* mask[i,j] = value if region(i) != region(j), else 0     */
+} attn_mask_kind_t;
+
+/* Window geometry (Swin).  img_h, img_w: token image; win_h, win_w: window;
+ * shift_h, shift_w: cyclic shift, 0 <= shift < win.  Region of a pixel of the
+ * shifted image at (y, x): 3*ry + rx, with ry = 0 for y < img_h-win_h, 1 for
+ * y < img_h-shift_h, 2 otherwise (same for x).  Used by SHIFT_REGIONS and by
+ * ATTN_LAYOUT_IMAGE.                                                         */
+typedef struct {
+  int32_t img_h, img_w, win_h, win_w, shift_h, shift_w;
+} attn_window_t;
+
+/* Mask descriptor.
+ *  add: [n_win, Nq, Nk], element strides add_strides[0..1], last stride 1,
+ *    batch item b uses add[b % n_win].
+ *  win: window geometry (SHIFT_REGIONS and IMAGE layout).  In BATCHED layout
+ *    SHIFT_REGIONS labels batch item b as window b % nW of an image, where
+ *    nW = (img_h/win_h)*(img_w/win_w).
+ *  value: the additive value for pairs from different regions (Swin uses
+ *    -100).                                                                  */
+typedef struct {
+  int32_t kind; /* attn_mask_kind_t */
+  const void* add;
+  int64_t n_win;
+  int64_t add_strides[2];
+  attn_window_t win;
+  float value;
+} attn_mask_desc_t;
+
+/* attn_fwd: queue O = softmax(QK^T/sqrt(d) + bias + mask) V on `stream`.
+ *
+ *  q: [B, H, Nq, d]; k, v: [B, H, Nk, d]; out: [B, H, Nq, d] (written).
+ *  bias_desc, mask_desc: may be NULL, meaning NONE.
+ *  dtype: element type of every tensor and table.
+ *  stream: a hipStream_t (NULL = the default stream), passed as void*.
+ *
+ *  Supported: d in {32, 40, 64, 80} for F16/BF16; d <= 128, d % 4 == 0 for
+ *  F32.  Nq, Nk >= 1.  TABLE/RELPOS/SHIFT_REGIONS need Nq == Nk ==
+ *  grid_h*grid_w (SHIFT_REGIONS: == win_h*win_w).
+ *  Returns ATTN_OK after queueing the kernel, or an error code (nothing is
+ *  queued on error).  Asynchronous: kernel faults surface at the caller's
+ *  next synchronisation.                                                     */
+ATTN_API int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+             const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+             const attn_tensor_t* out, int32_t dtype, void* stream);
+
+/* attn_check: the validation attn_fwd performs, without touching the GPU.
+ * Same arguments minus the stream; returns the status attn_fwd would return
+ * for an argument error (ATTN_OK if the call is valid).                      */
+ATTN_API int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+               const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+               const attn_tensor_t* out, int32_t dtype);
+
+/* attn_strerror: static text for a status code (never NULL).                */
+ATTN_API const char* attn_strerror(int status);
+
+/* attn_version: library ABI version, (major << 16) | minor.                 */
+ATTN_API int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

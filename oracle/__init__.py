@@ -26,4 +26,5 @@ from .attention import (  # noqa: F401
     attention_probs,
     attention,
     attention_image,
+    run_workload,
 )

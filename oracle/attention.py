@@ -349,3 +349,29 @@ def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
     o = window_reverse(ow, img_h, img_w, win_h, win_w)
     o = np.roll(o, shift=(sh, sw), axis=(2, 3))
     return o.reshape(B, H, N, v.shape[-1])
+
+
+def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
+    """Oracle output for a workload description.
+
+    ``w`` is any object with the attributes bias, grid, mask, layout, window
+    (a workload record); ``arrays`` maps q, k, v and the bias tables
+    (table / rh, rw / bias_add, mask_add) to float64 numpy arrays holding the
+    exact device values.  ``select`` as in :func:`attention` (batched layout).
+    """
+    bias = Bias("none")
+    if w.bias == "table":
+        bias = Bias("table", grid=w.grid, table=arrays["table"])
+    elif w.bias == "relpos":
+        bias = Bias("relpos", grid=w.grid, rh=arrays["rh"], rw=arrays["rw"])
+    elif w.bias == "additive":
+        bias = Bias("additive", add=arrays["bias_add"])
+    mask = Mask("none")
+    if w.mask == "shift":
+        mask = Mask("shift", window=tuple(w.window))
+    elif w.mask == "additive":
+        mask = Mask("additive", add=arrays["mask_add"])
+    if w.layout == "image":
+        assert select is None, "image layout is evaluated whole"
+        return attention_image(arrays["q"], arrays["k"], arrays["v"], tuple(w.window), bias, mask)
+    return attention(arrays["q"], arrays["k"], arrays["v"], bias, mask, select=select)

@@ -1,0 +1,266 @@
+"""ctypes binding of libattn (argument marshalling only).
+
+Every step of the attention runs in the HIP library; this module turns torch
+tensors into the C descriptors of ``include/attn.h`` and passes torch's
+current stream.  PyTorch is used for device memory and streams only.  If the
+library is not built, the first call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+# Enumerations of include/attn.h.
+ATTN_OK = 0
+STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_LAYOUT", 4: "E_UNSUPPORTED", 5: "E_ALIAS",
+          6: "E_LAUNCH", 7: "E_INVALID"}
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+LAYOUT_BATCHED, LAYOUT_IMAGE = 0, 1
+BIAS_NONE, BIAS_TABLE, BIAS_RELPOS, BIAS_ADDITIVE = 0, 1, 2, 3
+MASK_NONE, MASK_ADDITIVE, MASK_SHIFT_REGIONS = 0, 1, 2
+
+
+class AttnTensorC(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dims", ctypes.c_int64 * 4),
+                ("strides", ctypes.c_int64 * 3), ("layout", ctypes.c_int32)]
+
+
+class BiasDescC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("table", ctypes.c_void_p), ("rh", ctypes.c_void_p), ("rw", ctypes.c_void_p),
+                ("add", ctypes.c_void_p), ("add_batch", ctypes.c_int64),
+                ("add_strides", ctypes.c_int64 * 2)]
+
+
+class WindowC(ctypes.Structure):
+    _fields_ = [("img_h", ctypes.c_int32), ("img_w", ctypes.c_int32), ("win_h", ctypes.c_int32),
+                ("win_w", ctypes.c_int32), ("shift_h", ctypes.c_int32), ("shift_w", ctypes.c_int32)]
+
+
+class MaskDescC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("add", ctypes.c_void_p), ("n_win", ctypes.c_int64),
+                ("add_strides", ctypes.c_int64 * 2), ("win", WindowC), ("value", ctypes.c_float)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m scaled_dot_product_16_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        h.attn_fwd.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
+                               P(MaskDescC), P(AttnTensorC), ctypes.c_int32, ctypes.c_void_p]
+        h.attn_fwd.restype = ctypes.c_int
+        h.attn_check.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
+                                 P(MaskDescC), P(AttnTensorC), ctypes.c_int32]
+        h.attn_check.restype = ctypes.c_int
+        h.attn_strerror.argtypes = [ctypes.c_int]
+        h.attn_strerror.restype = ctypes.c_char_p
+        h.attn_version.argtypes = []
+        h.attn_version.restype = ctypes.c_int
+        _lib_handle = h
+    return _lib_handle
+
+
+# ---------------------------------------------------------------------------
+# Python-side descriptions of bias and mask
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Window:
+    img_h: int
+    img_w: int
+    win_h: int
+    win_w: int
+    shift_h: int = 0
+    shift_w: int = 0
+
+    def c(self) -> WindowC:
+        return WindowC(self.img_h, self.img_w, self.win_h, self.win_w, self.shift_h, self.shift_w)
+
+
+@dataclass
+class TableBias:
+    """Swin relative-position bias table [(2gh-1)(2gw-1), H]."""
+    table: torch.Tensor
+    grid: tuple
+
+
+@dataclass
+class RelposBias:
+    """SAM decomposed relative position: Rh [2gh-1, d], Rw [2gw-1, d]."""
+    rh: torch.Tensor
+    rw: torch.Tensor
+    grid: tuple
+
+
+@dataclass
+class AdditiveBias:
+    """Dense additive bias [nB, Nq, Nk]; batch item b uses add[b % nB]."""
+    add: torch.Tensor
+
+
+@dataclass
+class ShiftMask:
+    """Swin shifted-window region mask (value where regions differ)."""
+    window: Window
+    value: float = -100.0
+
+
+@dataclass
+class AdditiveMask:
+    """Dense additive mask [nW, Nq, Nk]; batch item b uses add[b % nW]."""
+    add: torch.Tensor
+
+
+def _tensor_c(t: torch.Tensor, layout: int) -> AttnTensorC:
+    if t.dim() != 4:
+        raise ValueError("q, k, v and out must be 4-D [B, H, N, d]")
+    if t.stride(3) != 1:
+        raise ValueError("the head_dim stride must be 1")
+    return AttnTensorC(t.data_ptr(), (ctypes.c_int64 * 4)(*t.shape),
+                       (ctypes.c_int64 * 3)(*t.stride()[:3]), layout)
+
+
+def _descs(bias, mask, layout: int, window: Optional[Window], keep: list):
+    bd = BiasDescC()
+    if bias is None:
+        bd.kind = BIAS_NONE
+    elif isinstance(bias, TableBias):
+        keep.append(bias.table.contiguous())
+        bd.kind, (bd.grid_h, bd.grid_w), bd.table = BIAS_TABLE, bias.grid, keep[-1].data_ptr()
+    elif isinstance(bias, RelposBias):
+        keep += [bias.rh.contiguous(), bias.rw.contiguous()]
+        bd.kind, (bd.grid_h, bd.grid_w) = BIAS_RELPOS, bias.grid
+        bd.rh, bd.rw = keep[-2].data_ptr(), keep[-1].data_ptr()
+    elif isinstance(bias, AdditiveBias):
+        a = bias.add if bias.add.dim() == 3 else bias.add.reshape(-1, *bias.add.shape[-2:])
+        if a.stride(2) != 1:
+            a = a.contiguous()
+        keep.append(a)
+        bd.kind, bd.add, bd.add_batch = BIAS_ADDITIVE, a.data_ptr(), a.shape[0]
+        bd.add_strides[0], bd.add_strides[1] = a.stride(0), a.stride(1)
+    else:
+        raise TypeError(f"unknown bias {type(bias).__name__}")
+
+    md = MaskDescC()
+    md.value = -100.0
+    if mask is None:
+        md.kind = MASK_NONE
+    elif isinstance(mask, ShiftMask):
+        md.kind, md.value = MASK_SHIFT_REGIONS, mask.value
+        window = window or mask.window
+    elif isinstance(mask, AdditiveMask):
+        a = mask.add if mask.add.dim() == 3 else mask.add.reshape(-1, *mask.add.shape[-2:])
+        if a.stride(2) != 1:
+            a = a.contiguous()
+        keep.append(a)
+        md.kind, md.add, md.n_win = MASK_ADDITIVE, a.data_ptr(), a.shape[0]
+        md.add_strides[0], md.add_strides[1] = a.stride(0), a.stride(1)
+    else:
+        raise TypeError(f"unknown mask {type(mask).__name__}")
+    if window is not None:
+        md.win = window.c()
+    return bd, md
+
+
+def _check_extents(q, k, bias, mask, lay, window):
+    """Shapes of the tables and dense tensors the kernel will index."""
+    H, D = q.shape[1], q.shape[3]
+    win = window or (mask.window if isinstance(mask, ShiftMask) else None)
+    if lay == LAYOUT_IMAGE:
+        if win is None:
+            raise ValueError("image layout needs a window geometry")
+        nq = nk = win.win_h * win.win_w
+    else:
+        nq, nk = q.shape[2], k.shape[2]
+    if isinstance(bias, TableBias):
+        gh, gw = bias.grid
+        if tuple(bias.table.shape) != ((2 * gh - 1) * (2 * gw - 1), H):
+            raise ValueError(f"table must be [{(2 * gh - 1) * (2 * gw - 1)}, {H}]")
+    elif isinstance(bias, RelposBias):
+        gh, gw = bias.grid
+        if tuple(bias.rh.shape) != (2 * gh - 1, D) or tuple(bias.rw.shape) != (2 * gw - 1, D):
+            raise ValueError(f"rh, rw must be [{2 * gh - 1}, {D}], [{2 * gw - 1}, {D}]")
+    elif isinstance(bias, AdditiveBias):
+        if tuple(bias.add.shape[-2:]) != (nq, nk):
+            raise ValueError(f"additive bias must end in [{nq}, {nk}]")
+    if isinstance(mask, AdditiveMask) and tuple(mask.add.shape[-2:]) != (nq, nk):
+        raise ValueError(f"additive mask must end in [{nq}, {nk}]")
+
+
+def _marshal(q, k, v, out, bias, mask, layout, window):
+    lay = {"batched": LAYOUT_BATCHED, "image": LAYOUT_IMAGE}[layout]
+    if q.dtype not in DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    keep: list = []
+    bd, md = _descs(bias, mask, lay, window, keep)
+    for t in keep:
+        if t.dtype != q.dtype:
+            raise TypeError("bias/mask tensors must have the dtype of q")
+        if t.device != q.device:
+            raise ValueError("bias/mask tensors must be on the device of q")
+    _check_extents(q, k, bias, mask, lay, window)
+    return (_tensor_c(q, lay), _tensor_c(k, lay), _tensor_c(v, lay), bd, md,
+            _tensor_c(out, lay), DTYPES[q.dtype], keep)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
+        out: Optional[torch.Tensor] = None, layout: str = "batched",
+        window: Optional[Window] = None, stream=None) -> torch.Tensor:
+    """O = softmax(QK^T/sqrt(d) + bias + mask) V on the GPU via libattn.
+
+    q: [B, H, Nq, d], k, v: [B, H, Nk, d] CUDA (HIP) tensors, last stride 1.
+    layout "image": tensors are [B_img, H, img_h*img_w, d] and ``window`` (or
+    the ShiftMask's window) gives the window geometry.  ``out`` may be given;
+    otherwise it is allocated with torch.  Queued on ``stream`` (default:
+    torch's current stream); no synchronisation.
+    """
+    h = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = h.attn_fwd(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                    ctypes.byref(md), ctypes.byref(oc), dt, ctypes.c_void_p(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, h.attn_strerror(st).decode())
+    del keep
+    return out
+
+
+def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
+          window: Optional[Window] = None) -> int:
+    """Status attn_fwd would return for these arguments (no GPU needed)."""
+    h = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
+    return h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                        ctypes.byref(md), ctypes.byref(oc), dt)

@@ -1,0 +1,224 @@
+// Host side of the C ABI: argument validation (no HIP dependency, so it can be
+// exercised on a machine without a GPU through attn_check) and the exported
+// entry points.  The launch itself lives in attn_kernels.hip.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+int elem_size(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool head_dim_supported(int32_t dtype, int64_t d) {
+  if (dtype == ATTN_F32) return d >= 4 && d <= 128 && d % 4 == 0;
+  return d == 32 || d == 40 || d == 64 || d == 80;
+}
+
+// Byte range [lo, hi) touched by a strided 4-D tensor.
+void extent(const attn_tensor_t* t, int es, uintptr_t* lo, uintptr_t* hi) {
+  int64_t last = 0;
+  for (int i = 0; i < 3; ++i) last += (t->dims[i] - 1) * t->strides[i];
+  last += t->dims[3] - 1;
+  *lo = (uintptr_t)t->data;
+  *hi = (uintptr_t)t->data + (uintptr_t)((last + 1) * es);
+}
+
+bool overlaps(const attn_tensor_t* a, const attn_tensor_t* b, int es) {
+  uintptr_t alo, ahi, blo, bhi;
+  extent(a, es, &alo, &ahi);
+  extent(b, es, &blo, &bhi);
+  return alo < bhi && blo < ahi;
+}
+
+int check_tensor(const attn_tensor_t* t, int es) {
+  if (!t->data) return ATTN_E_NULL;
+  for (int i = 0; i < 4; ++i)
+    if (t->dims[i] < 1 || t->dims[i] > (int64_t(1) << 30)) return ATTN_E_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (t->strides[i] < 0) return ATTN_E_LAYOUT;
+  // Vector loads move 16 bytes: base and every row start must be 16-byte aligned.
+  const int64_t vec = 16 / es;
+  if ((uintptr_t)t->data % 16) return ATTN_E_LAYOUT;
+  for (int i = 0; i < 3; ++i)
+    if (t->strides[i] % vec) return ATTN_E_LAYOUT;
+  if (t->layout != ATTN_LAYOUT_BATCHED && t->layout != ATTN_LAYOUT_IMAGE) return ATTN_E_INVALID;
+  return ATTN_OK;
+}
+
+bool window_valid(const attn_window_t& w) {
+  if (w.img_h < 1 || w.img_w < 1 || w.win_h < 1 || w.win_w < 1) return false;
+  if (w.img_h % w.win_h || w.img_w % w.win_w) return false;
+  if (w.shift_h < 0 || w.shift_w < 0 || w.shift_h >= w.win_h || w.shift_w >= w.win_w) return false;
+  if (w.img_h > kMaxGridSide * 16 || w.img_w > kMaxGridSide * 16) return false;
+  if (w.win_h > kMaxGridSide || w.win_w > kMaxGridSide) return false;
+  return true;
+}
+
+}  // namespace
+
+int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
+             const void* maskv, const void* outv, int32_t dtype, AttnArgs* a) {
+  const attn_tensor_t* q = (const attn_tensor_t*)qv;
+  const attn_tensor_t* k = (const attn_tensor_t*)kv;
+  const attn_tensor_t* v = (const attn_tensor_t*)vv;
+  const attn_tensor_t* o = (const attn_tensor_t*)outv;
+  const attn_bias_desc_t* bias = (const attn_bias_desc_t*)biasv;
+  const attn_mask_desc_t* mask = (const attn_mask_desc_t*)maskv;
+  if (!q || !k || !v || !o || !a) return ATTN_E_NULL;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  const int es = elem_size(dtype);
+  int st;
+  if ((st = check_tensor(q, es)) || (st = check_tensor(k, es)) || (st = check_tensor(v, es)) ||
+      (st = check_tensor(o, es)))
+    return st;
+
+  // Shapes: [B, H, N, d] with shared B, H, d; k and v share N; out matches q.
+  const int64_t B = q->dims[0], H = q->dims[1], Nq = q->dims[2], D = q->dims[3];
+  const int64_t Nk = k->dims[2];
+  if (k->dims[0] != B || v->dims[0] != B || o->dims[0] != B) return ATTN_E_SHAPE;
+  if (k->dims[1] != H || v->dims[1] != H || o->dims[1] != H) return ATTN_E_SHAPE;
+  if (k->dims[3] != D || v->dims[3] != D || o->dims[3] != D) return ATTN_E_SHAPE;
+  if (v->dims[2] != Nk || o->dims[2] != Nq) return ATTN_E_SHAPE;
+  if (!head_dim_supported(dtype, D)) return ATTN_E_UNSUPPORTED;
+
+  const int32_t layout = q->layout;
+  if (k->layout != layout || v->layout != layout || o->layout != layout) return ATTN_E_LAYOUT;
+
+  const int32_t bias_kind = bias ? bias->kind : ATTN_BIAS_NONE;
+  const int32_t mask_kind = mask ? mask->kind : ATTN_MASK_NONE;
+  if (bias_kind < ATTN_BIAS_NONE || bias_kind > ATTN_BIAS_ADDITIVE) return ATTN_E_INVALID;
+  if (mask_kind < ATTN_MASK_NONE || mask_kind > ATTN_MASK_SHIFT_REGIONS) return ATTN_E_INVALID;
+
+  memset(a, 0, sizeof(*a));
+  a->q = q->data;
+  a->k = k->data;
+  a->v = v->data;
+  a->o = o->data;
+  a->q_sb = q->strides[0]; a->q_sh = q->strides[1]; a->q_sn = q->strides[2];
+  a->k_sb = k->strides[0]; a->k_sh = k->strides[1]; a->k_sn = k->strides[2];
+  a->v_sb = v->strides[0]; a->v_sh = v->strides[1]; a->v_sn = v->strides[2];
+  a->o_sb = o->strides[0]; a->o_sh = o->strides[1]; a->o_sn = o->strides[2];
+  a->dtype = dtype;
+  a->H = (int32_t)H;
+  a->D = (int32_t)D;
+  a->scale = (float)(1.0 / sqrt((double)D));
+
+  // Window geometry: needed by IMAGE layout and by SHIFT_REGIONS.
+  const bool need_win = layout == ATTN_LAYOUT_IMAGE || mask_kind == ATTN_MASK_SHIFT_REGIONS;
+  int64_t Beff = B, nq_eff = Nq, nk_eff = Nk;
+  if (need_win) {
+    if (!mask) return ATTN_E_NULL;
+    const attn_window_t& w = mask->win;
+    if (!window_valid(w)) return ATTN_E_SHAPE;
+    a->img_h = w.img_h; a->img_w = w.img_w; a->win_h = w.win_h; a->win_w = w.win_w;
+    a->shift_h = w.shift_h; a->shift_w = w.shift_w;
+    a->nwx = w.img_w / w.win_w;
+    a->nw = (w.img_h / w.win_h) * a->nwx;
+    const int64_t wt = (int64_t)w.win_h * w.win_w;
+    if (layout == ATTN_LAYOUT_IMAGE) {
+      if (Nq != (int64_t)w.img_h * w.img_w || Nk != Nq) return ATTN_E_SHAPE;
+      a->image = 1;
+      Beff = B * a->nw;
+      nq_eff = nk_eff = wt;
+    } else if (Nq != wt || Nk != wt) {
+      return ATTN_E_SHAPE;
+    }
+  }
+  if (Beff > (int64_t(1) << 30)) return ATTN_E_UNSUPPORTED;
+  a->B = (int32_t)Beff;
+  a->Nq = (int32_t)nq_eff;
+  a->Nk = (int32_t)nk_eff;
+
+  // Bias.
+  a->bias_kind = bias_kind;
+  if (bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS) {
+    if (bias->grid_h < 1 || bias->grid_w < 1) return ATTN_E_SHAPE;
+    if (bias->grid_h > kMaxGridSide || bias->grid_w > kMaxGridSide) return ATTN_E_UNSUPPORTED;
+    const int64_t g = (int64_t)bias->grid_h * bias->grid_w;
+    if (nq_eff != g || nk_eff != g) return ATTN_E_SHAPE;
+    if (g > kMaxIndexedTokens) return ATTN_E_UNSUPPORTED;
+    a->gh = bias->grid_h;
+    a->gw = bias->grid_w;
+    if (bias_kind == ATTN_BIAS_TABLE) {
+      if (!bias->table) return ATTN_E_NULL;
+      if ((int64_t)(2 * a->gh - 1) * (2 * a->gw - 1) > 16384) return ATTN_E_UNSUPPORTED;
+      a->table = bias->table;
+    } else {
+      if (!bias->rh || !bias->rw) return ATTN_E_NULL;
+      if ((uintptr_t)bias->rh % 16 || (uintptr_t)bias->rw % 16) return ATTN_E_LAYOUT;
+      if (a->gh + a->gw > 256) return ATTN_E_UNSUPPORTED;
+      a->rh = bias->rh;
+      a->rw = bias->rw;
+    }
+  } else if (bias_kind == ATTN_BIAS_ADDITIVE) {
+    if (!bias->add) return ATTN_E_NULL;
+    if (bias->add_batch < 1 || bias->add_strides[0] < 0 || bias->add_strides[1] < 0)
+      return ATTN_E_SHAPE;
+    a->badd = bias->add;
+    a->badd_n = bias->add_batch;
+    a->badd_s0 = bias->add_strides[0];
+    a->badd_s1 = bias->add_strides[1];
+  }
+
+  // Mask.
+  a->mask_kind = mask_kind;
+  if (mask_kind == ATTN_MASK_SHIFT_REGIONS) {
+    if (nq_eff > kMaxIndexedTokens) return ATTN_E_UNSUPPORTED;
+    if (!isfinite(mask->value)) return ATTN_E_INVALID;
+    a->mask_value = mask->value;
+  } else if (mask_kind == ATTN_MASK_ADDITIVE) {
+    if (!mask->add) return ATTN_E_NULL;
+    if (mask->n_win < 1 || mask->add_strides[0] < 0 || mask->add_strides[1] < 0)
+      return ATTN_E_SHAPE;
+    a->madd = mask->add;
+    a->madd_n = mask->n_win;
+    a->madd_s0 = mask->add_strides[0];
+    a->madd_s1 = mask->add_strides[1];
+  }
+
+  // out must not overlap the inputs it is computed from.
+  if (overlaps(o, q, es) || overlaps(o, k, es) || overlaps(o, v, es)) return ATTN_E_ALIAS;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+               const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+               const attn_tensor_t* out, int32_t dtype) {
+  attn::AttnArgs a;
+  return attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, &a);
+}
+
+int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+             const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+             const attn_tensor_t* out, int32_t dtype, void* stream) {
+  attn::AttnArgs a;
+  int st = attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, &a);
+  if (st != ATTN_OK) return st;
+  return attn::launch(a, stream);
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "inconsistent shapes, grid or window geometry";
+    case ATTN_E_LAYOUT: return "unsupported strides, layout or alignment";
+    case ATTN_E_UNSUPPORTED: return "head dim, dtype or size not supported";
+    case ATTN_E_ALIAS: return "out overlaps q, k or v";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_INVALID: return "invalid enum value or field";
+    default: return "unknown status";
+  }
+}
+
+int attn_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

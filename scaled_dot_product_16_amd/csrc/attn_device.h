@@ -1,0 +1,577 @@
+// Fused scaled-dot-product attention forward for gfx950 (CDNA4).
+//
+//   O = softmax(scale * Q K^T + bias + mask) V
+//
+// The attention map is never written to memory: a workgroup owns a tile of
+// queries of one (batch item, head), streams key/value tiles through LDS and
+// keeps the running row maximum, row sum and output accumulator in registers
+// (online softmax).  Operator fusion keeps intermediate results in registers
+// and shared memory instead of global memory ("Training and inference
+// acceleration for large vision models", section 2); the window
+// partition/shift/reverse of Swin are index mappings (same section) and are
+// folded into the load/store addresses here.
+//
+// Half-precision path: both contractions run on v_mfma_f32_16x16x32_{bf16,f16}.
+// The score tile is computed transposed, S^T = K Q^T, so that in the MFMA
+// accumulator layout each lane holds scores of ONE query (column lane%16) for
+// 4 keys per 16x16 block: row statistics need only two cross-lane steps, the
+// softmax rescale of the output accumulator is one scalar per lane, and the
+// probabilities are already in the B-operand layout of O^T += V^T P^T (the
+// key order inside a 32-key chunk is permuted, and V^T is stored in LDS with
+// the same permutation).
+#ifndef ATTN_DEVICE_H_
+#define ATTN_DEVICE_H_
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+struct BF16 {
+  static __device__ __forceinline__ float to_f(uint16_t x) {
+    return __uint_as_float((uint32_t)x << 16);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ float to_f(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};  // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <class E>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  return E::to_f(((const uint16_t*)p)[i]);
+}
+struct F32E {};
+template <>
+__device__ __forceinline__ float load_elem<F32E>(const void* p, int64_t i) {
+  return ((const float*)p)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Token addressing: batched layout, or image layout with the window partition
+// and the cyclic shift folded in (window w of image img, token t of the
+// window reads shifted-image pixel (wy*win_h+ty, wx*win_w+tx), which holds
+// original pixel ((y+shift_h) mod img_h, (x+shift_w) mod img_w)).  Stores use
+// the same map, which is the reverse partition and reverse shift.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_t sh, int64_t sn,
+                                           int b, int h, int t) {
+  if (!a.image) return (int64_t)b * sb + (int64_t)h * sh + (int64_t)t * sn;
+  const int img = b / a.nw;
+  const int w = b - img * a.nw;
+  const int wy = w / a.nwx, wx = w - wy * a.nwx;
+  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  int y = wy * a.win_h + ty + a.shift_h;
+  if (y >= a.img_h) y -= a.img_h;
+  int x = wx * a.win_w + tx + a.shift_w;
+  if (x >= a.img_w) x -= a.img_w;
+  return (int64_t)img * sb + (int64_t)h * sh + (int64_t)(y * a.img_w + x) * sn;
+}
+
+// Region (0..8) of token t of window w in the shifted image (SHIFT_REGIONS).
+__device__ __forceinline__ int region_of(const AttnArgs& a, int w, int t) {
+  const int wy = w / a.nwx, wx = w - wy * a.nwx;
+  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  const int y = wy * a.win_h + ty, x = wx * a.win_w + tx;
+  const int ry = y < a.img_h - a.win_h ? 0 : (y < a.img_h - a.shift_h ? 1 : 2);
+  const int rx = x < a.img_w - a.win_w ? 0 : (x < a.img_w - a.shift_w ? 1 : 2);
+  return 3 * ry + rx;
+}
+
+// ---------------------------------------------------------------------------
+// Bias and mask, evaluated per (query, key) from on-chip index data.
+//
+// LDS layout (dynamic):  kinfo[Nk] (when any index-based term is present),
+// then either the head's table column [(2gh-1)(2gw-1)] or relh[gh][BM],
+// relw[gw][BM] (relative-position terms of this workgroup's queries).  All
+// stored values are pre-multiplied by log2(e): the softmax runs in base 2.
+// kinfo[j] = kh | kw << 11 | region << 22.
+// ---------------------------------------------------------------------------
+struct BiasCtx {
+  const int* kinfo;
+  const float* tbl;   // TABLE
+  const float* relh;  // RELPOS [gh][BM]
+  const float* relw;  // RELPOS [gw][BM]
+};
+
+__host__ __device__ constexpr bool needs_kinfo(int bias_kind, bool mask) {
+  return bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS || mask;
+}
+
+inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
+  const bool kinfo = a.bias_kind == ATTN_BIAS_TABLE || a.bias_kind == ATTN_BIAS_RELPOS ||
+                     a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
+  size_t n = kinfo ? ((size_t)a.Nk * 4 + 15) / 16 * 16 : 0;
+  if (a.bias_kind == ATTN_BIAS_TABLE) n += (size_t)(2 * a.gh - 1) * (2 * a.gw - 1) * 4;
+  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)(a.gh + a.gw) * bm * 4;
+  return n;
+}
+
+// Fill kinfo and the table / relative-position terms.  `E` is the element
+// type of the tables and of q (relative-position terms use the raw query).
+template <class E, int BIAS, bool MASK, int BM, int NT>
+__device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, BiasCtx& bc) {
+  const int tid = threadIdx.x;
+  char* p = dyn;
+  bc.kinfo = nullptr;
+  bc.tbl = bc.relh = bc.relw = nullptr;
+  if (needs_kinfo(BIAS, MASK)) {
+    int* kinfo = (int*)p;
+    const int w = a.nw ? b % a.nw : 0;
+    for (int j = tid; j < a.Nk; j += NT) {
+      int v = 0;
+      if (BIAS == ATTN_BIAS_TABLE || BIAS == ATTN_BIAS_RELPOS) {
+        const int kh = j / a.gw;
+        v = kh | ((j - kh * a.gw) << 11);
+      }
+      if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) v |= region_of(a, w, j) << 22;
+      kinfo[j] = v;
+    }
+    bc.kinfo = kinfo;
+    p += ((size_t)a.Nk * 4 + 15) / 16 * 16;
+  }
+  if (BIAS == ATTN_BIAS_TABLE) {
+    float* tbl = (float*)p;
+    const int n = (2 * a.gh - 1) * (2 * a.gw - 1);
+    for (int r = tid; r < n; r += NT) tbl[r] = load_elem<E>(a.table, (int64_t)r * a.H + h) * kLog2e;
+    bc.tbl = tbl;
+  }
+  if (BIAS == ATTN_BIAS_RELPOS) {
+    // relh[kh][i] = q_i . Rh[qh_i - kh + gh - 1], relw[kw][i] = q_i . Rw[qw_i - kw + gw - 1]
+    float* relh = (float*)p;
+    float* relw = relh + a.gh * BM;
+    const int nk = a.gh + a.gw;
+    for (int e = tid; e < BM * nk; e += NT) {
+      const int il = e % BM, kk = e / BM;
+      const int qi = min(q0 + il, a.Nq - 1);
+      const int qh = qi / a.gw, qw = qi - qh * a.gw;
+      const int64_t qo = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+      const int64_t to = kk < a.gh ? (int64_t)(qh - kk + a.gh - 1) * a.D
+                                   : (int64_t)(qw - (kk - a.gh) + a.gw - 1) * a.D;
+      const void* tb = kk < a.gh ? a.rh : a.rw;
+      float acc = 0.f;
+      for (int c = 0; c < a.D; ++c) acc += load_elem<E>(a.q, qo + c) * load_elem<E>(tb, to + c);
+      (kk < a.gh ? relh + kk * BM : relw + (kk - a.gh) * BM)[il] = acc * kLog2e;
+    }
+    bc.relh = relh;
+    bc.relw = relw;
+  }
+}
+
+// Per-query constants for the bias of one query row.
+struct QInfo {
+  int il;      // row inside the workgroup's query tile
+  int qi;      // query index, clamped to Nq-1
+  int tab;     // TABLE: (qh+gh-1)*(2gw-1) + qw+gw-1
+  int region;  // SHIFT_REGIONS
+};
+
+template <int BIAS, bool MASK>
+__device__ __forceinline__ QInfo make_qinfo(const AttnArgs& a, int b, int qi, int il) {
+  QInfo qinf;
+  qinf.il = il;
+  qinf.qi = qi;
+  qinf.tab = 0;
+  qinf.region = 0;
+  if (BIAS == ATTN_BIAS_TABLE) {
+    const int qh = qi / a.gw, qw = qi - qh * a.gw;
+    qinf.tab = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
+  }
+  if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) qinf.region = region_of(a, b % a.nw, qi);
+  return qinf;
+}
+
+// (bias + mask) * log2(e) for query `qinf` and key kj (kj < Nk).
+template <class E, int BIAS, bool MASK, int BM>
+__device__ __forceinline__ float bias_log2(const AttnArgs& a, const BiasCtx& bc, const QInfo& qinf,
+                                           int b, int kj) {
+  float r = 0.f;
+  int ki = 0;
+  if (needs_kinfo(BIAS, MASK)) ki = bc.kinfo[kj];
+  if (BIAS == ATTN_BIAS_TABLE) {
+    const int kh = ki & 2047, kw = (ki >> 11) & 2047;
+    r += bc.tbl[qinf.tab - (kh * (2 * a.gw - 1) + kw)];
+  } else if (BIAS == ATTN_BIAS_RELPOS) {
+    const int kh = ki & 2047, kw = (ki >> 11) & 2047;
+    r += bc.relh[kh * BM + qinf.il] + bc.relw[kw * BM + qinf.il];
+  } else if (BIAS == ATTN_BIAS_ADDITIVE) {
+    const int64_t off = (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)qinf.qi * a.badd_s1 + kj;
+    r += load_elem<E>(a.badd, off) * kLog2e;
+  }
+  if (MASK) {
+    if (a.mask_kind == ATTN_MASK_SHIFT_REGIONS) {
+      if ((ki >> 22) != qinf.region) r += a.mask_value * kLog2e;
+    } else {
+      const int64_t off = (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)qinf.qi * a.madd_s1 + kj;
+      r += load_elem<E>(a.madd, off) * kLog2e;
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Half-precision MFMA kernel.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;  // keys per tile
+
+// Position of key kl (0..31) of a 32-key chunk in the MFMA contraction order:
+// lane group g = (kl%16)/4 of the score accumulator holds keys g*4+r (first
+// 16-key block) and 16+g*4+r (second block), which become B-operand elements
+// g*8 + r and g*8 + 4 + r.
+__device__ __forceinline__ int kperm(int kl) {
+  return ((kl & 15) >> 2) * 8 + (kl >> 4) * 4 + (kl & 3);
+}
+
+template <class E, int D, int NQB, int BIAS, bool MASK>
+__global__ __launch_bounds__(kThreads) void attn_fwd_mfma(AttnArgs a) {
+  constexpr int BM = kWaves * NQB * 16;
+  constexpr int KCH = (D + 31) / 32;   // 32-wide contraction chunks of QK^T
+  constexpr int DK = KCH * 32;
+  constexpr int CB = (D + 15) / 16;    // 16-row blocks of O^T
+  constexpr int DV = CB * 16;
+  constexpr int KROW = DK + 8;         // LDS row strides (elements), padded
+  constexpr int VROW = kBN + 8;
+  constexpr int RCH = D / 8;           // 16-byte chunks per row
+  constexpr int NCH = kBN * RCH;
+  constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DV * VROW];
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  int bid = blockIdx.x;
+  const int qt = bid % a.n_qtiles;
+  bid /= a.n_qtiles;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int q0 = qt * BM;
+
+  // The contraction padding columns [D, DK) of K are never loaded: zero them.
+  if (DK > D) {
+    for (int i = tid; i < 2 * kBN * (DK - D); i += kThreads) {
+      const int st = i / (kBN * (DK - D)), r = i % (kBN * (DK - D));
+      Ks[st][(r / (DK - D)) * KROW + D + r % (DK - D)] = 0;
+    }
+  }
+
+  BiasCtx bc;
+  setup_bias<E, BIAS, MASK, BM, kThreads>(a, dyn_lds, b, h, q0, bc);
+
+  // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
+  u32x4 qf[NQB][KCH];
+  QInfo qinf[NQB];
+  const uint16_t* qbase = (const uint16_t*)a.q;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int il = wave * NQB * 16 + qb * 16 + l16;
+    const int qi = min(q0 + il, a.Nq - 1);
+    const int64_t off = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      qf[qb][dc] = d0 < D ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
+    }
+    qinf[qb] = make_qinfo<BIAS, MASK>(a, b, qi, il);
+  }
+
+  // Tile loader: each thread moves CPT 16-byte chunks of K and of V.
+  const uint16_t* kbase = (const uint16_t*)a.k;
+  const uint16_t* vbase = (const uint16_t*)a.v;
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kThreads;
+      kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
+      if (ch < NCH) {
+        const int row = ch / RCH, col = (ch % RCH) * 8;
+        const int key = t * kBN + row;
+        if (key < a.Nk) {
+          kreg[c] = *(const u32x4*)(kbase + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + col);
+          vreg[c] = *(const u32x4*)(vbase + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + col);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kThreads;
+      if (ch < NCH) {
+        const int row = ch / RCH, col = (ch % RCH) * 8;
+        *(u32x4*)&Ks[st][row * KROW + col] = kreg[c];
+        const int pos = (row & ~31) + kperm(row & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Vt[st][(col + 2 * i) * VROW + pos] = (uint16_t)(vreg[c][i] & 0xffffu);
+          Vt[st][(col + 2 * i + 1) * VROW + pos] = (uint16_t)(vreg[c][i] >> 16);
+        }
+      }
+    }
+  };
+
+  f32x4 o[CB][NQB];
+  float m[NQB], l[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale * kLog2e;
+  const int ntiles = (a.Nk + kBN - 1) / kBN;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+
+    // S^T = K Q^T for 4 key blocks x NQB query blocks.
+    f32x4 s[4][NQB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 kf = *(const u32x4*)&Ks[st][(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
+      }
+    }
+
+    // Online softmax (base 2) per query block; lane owns one query.
+    const int k0 = t * kBN;
+    const bool tail = k0 + kBN > a.Nk;
+    u32x4 pf[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float x[16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = k0 + kb * 16 + g * 4 + r;
+          float v = s[kb][qb][r] * sl2;
+          if (BIAS != ATTN_BIAS_NONE || MASK)
+            v += bias_log2<E, BIAS, MASK, BM>(a, bc, qinf[qb], b, min(kj, a.Nk - 1));
+          if (tail && kj >= a.Nk) v = -INFINITY;
+          x[kb * 4 + r] = v;
+        }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[qb], mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mref);
+      m[qb] = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+        ps += x[i];
+      }
+      l[qb] = l[qb] * alpha + ps;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        pf[qb][kc] = u32x4{E::pack2(x[kc * 8 + 0], x[kc * 8 + 1]), E::pack2(x[kc * 8 + 2], x[kc * 8 + 3]),
+                           E::pack2(x[kc * 8 + 4], x[kc * 8 + 5]), E::pack2(x[kc * 8 + 6], x[kc * 8 + 7])};
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const u32x4 vf = *(const u32x4*)&Vt[st][(cb * 16 + l16) * VROW + kc * 32 + g * 8];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
+      }
+
+    if (t + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise and store O (lane holds O[q][cb*16 + g*4 .. +3]).
+  uint16_t* obase = (uint16_t*)a.o;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float lt = l[qb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.f / lt;
+    const int qi = q0 + wave * NQB * 16 + qb * 16 + l16;
+    if (qi < a.Nq) {
+      const int64_t off = tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, qi);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 v = o[cb][qb] * inv;
+          *(u32x2*)(obase + off + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: one thread per query, key/value tiles broadcast from LDS.
+// ---------------------------------------------------------------------------
+constexpr int kF32Threads = 64;
+constexpr int kF32BN = 32;
+
+template <int DMAX, int BIAS, bool MASK>
+__global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
+  constexpr int BM = kF32Threads;
+  __shared__ __attribute__((aligned(16))) float Ks[kF32BN][DMAX];
+  __shared__ __attribute__((aligned(16))) float Vs[kF32BN][DMAX];
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+
+  const int tid = threadIdx.x;
+  int bid = blockIdx.x;
+  const int qt = bid % a.n_qtiles;
+  bid /= a.n_qtiles;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int q0 = qt * BM;
+  const int D = a.D;
+
+  BiasCtx bc;
+  setup_bias<F32E, BIAS, MASK, BM, kF32Threads>(a, dyn_lds, b, h, q0, bc);
+
+  const int qi = min(q0 + tid, a.Nq - 1);
+  const QInfo qinf = make_qinfo<BIAS, MASK>(a, b, qi, tid);
+  float qv[DMAX], acc[DMAX];
+  {
+    const float* qp = (const float*)a.q + tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+#pragma unroll
+    for (int c = 0; c < DMAX; c += 4) {
+      const f32x4 v = c < D ? *(const f32x4*)(qp + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      qv[c] = v[0]; qv[c + 1] = v[1]; qv[c + 2] = v[2]; qv[c + 3] = v[3];
+      acc[c] = acc[c + 1] = acc[c + 2] = acc[c + 3] = 0.f;
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  const int ntiles = (a.Nk + kF32BN - 1) / kF32BN;
+  const int rch = D / 4;
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    for (int ch = tid; ch < kF32BN * rch; ch += kF32Threads) {
+      const int row = ch / rch, col = (ch % rch) * 4;
+      const int key = t * kF32BN + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < a.Nk) {
+        kv = *(const f32x4*)((const float*)a.k + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + col);
+        vv = *(const f32x4*)((const float*)a.v + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + col);
+      }
+      *(f32x4*)&Ks[row][col] = kv;
+      *(f32x4*)&Vs[row][col] = vv;
+    }
+    __syncthreads();
+    float s[kF32BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      const int kj = t * kF32BN + j;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < DMAX; c += 4) {
+        if (c < D) {
+          const f32x4 kv = *(const f32x4*)&Ks[j][c];
+          dot = fmaf(qv[c], kv[0], dot);
+          dot = fmaf(qv[c + 1], kv[1], dot);
+          dot = fmaf(qv[c + 2], kv[2], dot);
+          dot = fmaf(qv[c + 3], kv[3], dot);
+        }
+      }
+      float v = dot * sl2;
+      if (BIAS != ATTN_BIAS_NONE || MASK)
+        v += bias_log2<F32E, BIAS, MASK, BM>(a, bc, qinf, b, min(kj, a.Nk - 1));
+      if (kj >= a.Nk) v = -INFINITY;
+      s[j] = v;
+      mx = fmaxf(mx, v);
+    }
+    const float mnew = fmaxf(m, mx);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(m - mref);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < DMAX; ++c) acc[c] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      const float p = exp2f(s[j] - mref);
+      l += p;
+#pragma unroll
+      for (int c = 0; c < DMAX; c += 4) {
+        if (c < D) {
+          const f32x4 vv = *(const f32x4*)&Vs[j][c];
+          acc[c] = fmaf(p, vv[0], acc[c]);
+          acc[c + 1] = fmaf(p, vv[1], acc[c + 1]);
+          acc[c + 2] = fmaf(p, vv[2], acc[c + 2]);
+          acc[c + 3] = fmaf(p, vv[3], acc[c + 3]);
+        }
+      }
+    }
+  }
+  if (q0 + tid < a.Nq) {
+    const float inv = 1.f / l;
+    float* op = (float*)a.o + tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, q0 + tid);
+#pragma unroll
+    for (int c = 0; c < DMAX; c += 4)
+      if (c < D) *(f32x4*)(op + c) = f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+  }
+}
+
+}  // namespace attn
+
+#endif  // ATTN_DEVICE_H_

@@ -1,0 +1,77 @@
+// One compiled instance of the attention kernels, selected by INST_DT (an
+// attn_dtype_t value) and INST_D (head dim, or the fp32 register bucket).
+#include "attn_device.h"
+#include "attn_launch.h"
+
+#ifndef INST_DT
+#error "INST_DT must be defined"
+#endif
+#ifndef INST_D
+#error "INST_D must be defined"
+#endif
+
+namespace attn {
+namespace {
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <typename K>
+int launch_kernel(K kernel, int threads, int bm, size_t static_lds, AttnArgs a, hipStream_t s) {
+  a.n_qtiles = (a.Nq + bm - 1) / bm;
+  const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
+  if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
+  const size_t dyn = dyn_lds_bytes(a, bm);
+  if (dyn + static_lds > kMaxLds) return ATTN_E_UNSUPPORTED;
+  if (dyn > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
+          hipSuccess)
+    return ATTN_E_LAUNCH;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), dyn, s, a);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+// Preprocessor conditions use the enum's numeric values (0 f32, 1 f16, 2 bf16).
+#if INST_DT == 0
+template <int BIAS, bool MASK>
+int launch_one(const AttnArgs& a, hipStream_t s) {
+  return launch_kernel(attn_fwd_f32<INST_D, BIAS, MASK>, kF32Threads, kF32Threads,
+                       2 * (size_t)kF32BN * INST_D * 4, a, s);
+}
+#else
+#if INST_DT == 2
+using Elem = BF16;
+#else
+using Elem = F16;
+#endif
+template <int BIAS, bool MASK>
+int launch_one(const AttnArgs& a, hipStream_t s) {
+  constexpr int D = INST_D;
+  constexpr int NQB = 2;
+  constexpr int BM = kWaves * NQB * 16;
+  constexpr int KROW = (D + 31) / 32 * 32 + 8;
+  constexpr int DV = (D + 15) / 16 * 16;
+  constexpr size_t st = 2 * (size_t)kBN * KROW * 2 + 2 * (size_t)DV * (kBN + 8) * 2;
+  return launch_kernel(attn_fwd_mfma<Elem, D, NQB, BIAS, MASK>, kThreads, BM, st, a, s);
+}
+#endif
+
+}  // namespace
+
+template <>
+int launch_inst<INST_DT, INST_D>(const AttnArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const bool mask = a.mask_kind != ATTN_MASK_NONE;
+  switch (a.bias_kind) {
+    case ATTN_BIAS_NONE:
+      return mask ? launch_one<ATTN_BIAS_NONE, true>(a, s) : launch_one<ATTN_BIAS_NONE, false>(a, s);
+    case ATTN_BIAS_TABLE:
+      return mask ? launch_one<ATTN_BIAS_TABLE, true>(a, s) : launch_one<ATTN_BIAS_TABLE, false>(a, s);
+    case ATTN_BIAS_RELPOS:
+      return mask ? launch_one<ATTN_BIAS_RELPOS, true>(a, s) : launch_one<ATTN_BIAS_RELPOS, false>(a, s);
+    default:
+      return mask ? launch_one<ATTN_BIAS_ADDITIVE, true>(a, s)
+                  : launch_one<ATTN_BIAS_ADDITIVE, false>(a, s);
+  }
+}
+
+}  // namespace attn

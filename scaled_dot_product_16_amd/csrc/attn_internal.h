@@ -1,0 +1,64 @@
+// Internal interface between the host validation layer (attn_api.cpp, no HIP
+// dependency) and the kernel launcher (attn_kernels.hip).
+#ifndef ATTN_INTERNAL_H_
+#define ATTN_INTERNAL_H_
+
+#include <stdint.h>
+
+namespace attn {
+
+// A validated call, flattened into plain integers and pointers.  Passed by
+// value to every kernel, so it must stay trivially copyable.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int32_t dtype;
+  int32_t B;     // batch items as attention sees them (images * windows for IMAGE)
+  int32_t H;
+  int32_t Nq;    // tokens per batch item (window tokens for IMAGE)
+  int32_t Nk;
+  int32_t D;
+  // Window geometry (IMAGE layout address folding and SHIFT_REGIONS labels).
+  int32_t image;
+  int32_t img_h, img_w, win_h, win_w, shift_h, shift_w;
+  int32_t nwx, nw;
+  // Bias.
+  int32_t bias_kind;
+  int32_t gh, gw;
+  const void* table;
+  const void* rh;
+  const void* rw;
+  const void* badd;
+  int64_t badd_n, badd_s0, badd_s1;
+  // Mask.
+  int32_t mask_kind;
+  const void* madd;
+  int64_t madd_n, madd_s0, madd_s1;
+  float mask_value;
+  float scale;
+  // Filled by the launcher.
+  int32_t n_qtiles;
+};
+
+// Host-side validation shared by attn_check and attn_fwd.  Returns an ATTN_*
+// status and fills *a on success.
+int validate(const void* q, const void* k, const void* v, const void* bias_desc,
+             const void* mask_desc, const void* out, int32_t dtype, AttnArgs* a);
+
+// Queue the kernel for a validated call on `stream` (a hipStream_t).
+int launch(const AttnArgs& a, void* stream);
+
+// Largest grid side accepted for TABLE/RELPOS/SHIFT_REGIONS and the largest
+// token count of a batch item for which per-key index data fits on chip.
+constexpr int kMaxGridSide = 1024;
+constexpr int kMaxIndexedTokens = 16384;
+
+}  // namespace attn
+
+#endif  // ATTN_INTERNAL_H_

@@ -156,3 +156,28 @@ def custom(dtype: str, B: int, H: int, Nq: int, Nk: int, d: int, bias: str = "no
     """A workload of arbitrary shape for tests (same drawing recipe)."""
     return Workload(key, key, cfg_id, dtype, B=B, H=H, Nq=Nq, Nk=Nk, d=d, bias=bias,
                     grid=grid, mask=mask, layout=layout, images=images, window=window)
+
+
+def device_args(w: Workload, t: dict) -> dict:
+    """Keyword arguments of ``binding.fwd`` for workload ``w``.
+
+    ``t`` holds the workload's tensors already on the device (see
+    :func:`make_inputs`).  Only descriptors are built here.
+    """
+    from . import binding as B
+
+    kw: dict = {"layout": w.layout}
+    if w.bias == "table":
+        kw["bias"] = B.TableBias(t["table"], w.grid)
+    elif w.bias == "relpos":
+        kw["bias"] = B.RelposBias(t["rh"], t["rw"], w.grid)
+    elif w.bias == "additive":
+        kw["bias"] = B.AdditiveBias(t["bias_add"])
+    win = B.Window(*w.window) if w.window is not None else None
+    if w.mask == "shift":
+        kw["mask"] = B.ShiftMask(win)
+    elif w.mask == "additive":
+        kw["mask"] = B.AdditiveMask(t["mask_add"])
+    if w.layout == "image":
+        kw["window"] = win
+    return kw

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Full-size workloads are compared element by element where the oracle is fast
+(Swin windows, SAM windowed) and on sampled rows otherwise (SAM global, SD);
+reduced sizes sweep head dims, dtypes, ragged tiles, every bias and mask kind
+and both layouts.  Max-abs tolerances: f32 1e-5, f16 5e-3, bf16 2e-2.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_16_amd import workloads as W
+from tests.helpers import (TOL, check_full, check_sampled, oracle_arrays, run_gpu, sample_select,
+                           to_device, with_dense_terms)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from scaled_dot_product_16_amd import binding
+    binding.lib()  # fails loudly if the library is missing
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["C1", "C2", "C3"])
+def test_workload_full(key):
+    w = W.WORKLOADS[key]
+    say(f"[parity full] {key} {w.name}")
+    inp = W.make_inputs(w)
+    out = run_gpu(w, to_device(inp))
+    err = check_full(w, inp, out)
+    say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
+
+
+@pytest.mark.parametrize("key", ["C4", "C4h", "C5s", "C5x"])
+def test_workload_sampled(key):
+    w = W.WORKLOADS[key]
+    say(f"[parity sampled] {key} {w.name}")
+    inp = W.make_inputs(w)
+    out = run_gpu(w, to_device(inp))
+    assert torch.isfinite(out).all().item()
+    err = check_sampled(w, inp, out, sample_select(w))
+    say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
+
+
+# ---------------------------------------------------------------------------
+# Reduced-size sweeps (several tiles and ragged tails)
+# ---------------------------------------------------------------------------
+
+SHAPES = [(1, 1), (7, 300), (300, 77), (129, 64), (200, 200), (64, 1)]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("d", [32, 40, 64, 80])
+@pytest.mark.parametrize("nq,nk", SHAPES)
+def test_plain_shapes(dtype, d, nq, nk):
+    w = W.custom(dtype, B=2, H=3, Nq=nq, Nk=nk, d=d, cfg_id=100 + d)
+    say(f"[sweep] {dtype} d={d} Nq={nq} Nk={nk}")
+    inp = W.make_inputs(w, seed=nq * 1000 + nk)
+    check_full(w, inp, run_gpu(w, to_device(inp)))
+
+
+BIAS_CASES = [
+    # (bias, grid, mask, window)
+    ("table", (7, 7), "none", None),
+    ("table", (5, 9), "none", None),
+    ("relpos", (6, 10), "none", None),
+    ("relpos", (14, 14), "none", None),
+    ("relpos", (3, 50), "none", None),
+    ("additive", None, "none", None),
+    ("none", None, "additive", None),
+    ("additive", None, "additive", None),
+    ("table", (7, 7), "shift", (28, 21, 7, 7, 3, 2)),
+    ("none", None, "shift", (16, 16, 4, 8, 2, 5)),
+    ("relpos", (4, 8), "shift", (16, 16, 4, 8, 1, 3)),
+]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("case", range(len(BIAS_CASES)))
+def test_bias_and_mask_kinds(dtype, case):
+    bias, grid, mask, window = BIAS_CASES[case]
+    if mask == "shift":
+        ih, iw, wh, ww = window[:4]
+        n = wh * ww
+        B = 2 * (ih // wh) * (iw // ww)
+    else:
+        n = grid[0] * grid[1] if grid else 150
+        B = 3
+    d = 64 if dtype != W.F32 else 32
+    w = W.custom(dtype, B=B, H=2, Nq=n, Nk=n, d=d, bias=bias, grid=grid, mask=mask,
+                 window=window, cfg_id=200 + case)
+    say(f"[bias/mask] {dtype} {bias} {grid} {mask} {window} B={B} N={n}")
+    inp = with_dense_terms(w, W.make_inputs(w, seed=case), n_bias=2, n_mask=3)
+    check_full(w, inp, run_gpu(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("geom", [(14, 14, 7, 7, 3, 3), (16, 32, 4, 8, 2, 5), (12, 12, 6, 6, 0, 0)])
+def test_image_layout(dtype, geom):
+    ih, iw, wh, ww, sh, sw = geom
+    nW = (ih // wh) * (iw // ww)
+    mask = "shift" if sh or sw else "none"
+    d = 32
+    w = W.custom(dtype, B=2 * nW, H=3, Nq=wh * ww, Nk=wh * ww, d=d, bias="table", grid=(wh, ww),
+                 mask=mask, layout="image", images=2, window=geom, cfg_id=300)
+    say(f"[image] {dtype} {geom}")
+    inp = W.make_inputs(w, seed=sum(geom))
+    dev = to_device(inp)
+    out = run_gpu(w, dev)
+    check_full(w, inp, out)
+
+    # Same result, bit for bit, from explicitly shifted and partitioned inputs
+    # in the batched layout.
+    def part(x):
+        x = x.reshape(2, 3, ih, iw, d)
+        x = torch.roll(x, shifts=(-sh, -sw), dims=(2, 3))
+        x = x.reshape(2, 3, ih // wh, wh, iw // ww, ww, d).permute(0, 2, 4, 1, 3, 5, 6)
+        return x.reshape(2 * nW, 3, wh * ww, d).contiguous()
+
+    wb = W.custom(dtype, B=2 * nW, H=3, Nq=wh * ww, Nk=wh * ww, d=d, bias="table", grid=(wh, ww),
+                  mask=mask, layout="batched", window=geom, cfg_id=300)
+    devb = dict(dev, q=part(dev["q"]), k=part(dev["k"]), v=part(dev["v"]))
+    outb = run_gpu(wb, devb)
+    assert torch.equal(part(out), outb)
+
+
+# ---------------------------------------------------------------------------
+# Invariants and special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+def test_single_key_returns_v0(dtype):
+    w = W.custom(dtype, B=2, H=2, Nq=100, Nk=1, d=64 if dtype != W.F32 else 32, cfg_id=400)
+    inp = W.make_inputs(w)
+    out = run_gpu(w, to_device(inp))
+    assert torch.equal(out.cpu(), inp["v"].expand_as(out))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_constant_v_gives_constant_output(dtype):
+    w = W.custom(dtype, B=1, H=2, Nq=130, Nk=333, d=40, cfg_id=401)
+    inp = W.make_inputs(w)
+    inp["v"] = torch.ones_like(inp["v"])
+    out = run_gpu(w, to_device(inp)).float()
+    assert (out - 1).abs().max().item() <= TOL[dtype]
+
+
+def test_deterministic_and_strided_inputs():
+    w = W.WORKLOADS["C5x"]
+    inp = W.make_inputs(w)
+    dev = to_device(inp)
+    a = run_gpu(w, dev)
+    b = run_gpu(w, dev)
+    assert torch.equal(a, b)
+    # [B, N, H, d] storage viewed as [B, H, N, d] (projection output layout).
+    devs = {k: v.transpose(1, 2).contiguous().transpose(1, 2) for k, v in dev.items()}
+    outs = torch.empty(w.B, w.Nq, w.H, w.d, dtype=a.dtype, device=a.device).transpose(1, 2)
+    c = run_gpu(w, devs, out=outs)
+    assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_large_logits_stay_finite(dtype):
+    w = W.custom(dtype, B=2, H=2, Nq=200, Nk=300, d=64, cfg_id=402)
+    inp = W.make_inputs(w, std_qkv=1.0)
+    inp["q"] = (inp["q"].float() * 12).to(inp["q"].dtype)
+    inp["k"] = (inp["k"].float() * 12).to(inp["k"].dtype)
+    out = run_gpu(w, to_device(inp))
+    assert torch.isfinite(out).all().item()
+    check_full(w, inp, out)
+
+
+def test_error_status_from_fwd():
+    from scaled_dot_product_16_amd import binding
+    q = torch.zeros(1, 1, 8, 48, dtype=torch.float16, device="cuda")
+    with pytest.raises(binding.AttnError) as e:
+        binding.fwd(q, q.clone(), q.clone())
+    assert e.value.status == 4  # head dim 48 is not built
