@@ -26,6 +26,11 @@ HIP_FLAGS = [
     # Packed fp32 VALU forms are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # Min/max need no NaN-quieting canonicalisation (no signalling NaNs are
+    # produced or tested for); MFMA accumulators stay in VGPRs so the softmax
+    # reads them without accvgpr moves.
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
 ]
 
 

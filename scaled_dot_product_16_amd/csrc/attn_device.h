@@ -80,6 +80,23 @@ __device__ __forceinline__ float load_elem<F32E>(const void* p, int64_t i) {
   return ((const float*)p)[i];
 }
 
+// Dot product of 4 consecutive elements of two arrays (8-byte / 16-byte loads).
+template <class E>
+__device__ __forceinline__ float dot4(const void* x, int64_t i, const void* y, int64_t j) {
+  const u32x2 a = *(const u32x2*)((const uint16_t*)x + i);
+  const u32x2 b = *(const u32x2*)((const uint16_t*)y + j);
+  float r = E::to_f(a[0] & 0xffff) * E::to_f(b[0] & 0xffff);
+  r = fmaf(E::to_f(a[0] >> 16), E::to_f(b[0] >> 16), r);
+  r = fmaf(E::to_f(a[1] & 0xffff), E::to_f(b[1] & 0xffff), r);
+  return fmaf(E::to_f(a[1] >> 16), E::to_f(b[1] >> 16), r);
+}
+template <>
+__device__ __forceinline__ float dot4<F32E>(const void* x, int64_t i, const void* y, int64_t j) {
+  const f32x4 a = *(const f32x4*)((const float*)x + i);
+  const f32x4 b = *(const f32x4*)((const float*)y + j);
+  return fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], a[0] * b[0])));
+}
+
 // ---------------------------------------------------------------------------
 // Token addressing: batched layout, or image layout with the window partition
 // and the cyclic shift folded in (window w of image img, token t of the
@@ -183,7 +200,7 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
                                    : (int64_t)(qw - (kk - a.gh) + a.gw - 1) * a.D;
       const void* tb = kk < a.gh ? a.rh : a.rw;
       float acc = 0.f;
-      for (int c = 0; c < a.D; ++c) acc += load_elem<E>(a.q, qo + c) * load_elem<E>(tb, to + c);
+      for (int c = 0; c < a.D; c += 4) acc += dot4<E>(a.q, qo + c, tb, to + c);
       (kk < a.gh ? relh + kk * BM : relw + (kk - a.gh) * BM)[il] = acc * kLog2e;
     }
     bc.relh = relh;
@@ -240,226 +257,6 @@ __device__ __forceinline__ float bias_log2(const AttnArgs& a, const BiasCtx& bc,
     }
   }
   return r;
-}
-
-// ---------------------------------------------------------------------------
-// Half-precision MFMA kernel.
-// ---------------------------------------------------------------------------
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBN = 64;  // keys per tile
-
-// Position of key kl (0..31) of a 32-key chunk in the MFMA contraction order:
-// lane group g = (kl%16)/4 of the score accumulator holds keys g*4+r (first
-// 16-key block) and 16+g*4+r (second block), which become B-operand elements
-// g*8 + r and g*8 + 4 + r.
-__device__ __forceinline__ int kperm(int kl) {
-  return ((kl & 15) >> 2) * 8 + (kl >> 4) * 4 + (kl & 3);
-}
-
-template <class E, int D, int NQB, int BIAS, bool MASK>
-__global__ __launch_bounds__(kThreads) void attn_fwd_mfma(AttnArgs a) {
-  constexpr int BM = kWaves * NQB * 16;
-  constexpr int KCH = (D + 31) / 32;   // 32-wide contraction chunks of QK^T
-  constexpr int DK = KCH * 32;
-  constexpr int CB = (D + 15) / 16;    // 16-row blocks of O^T
-  constexpr int DV = CB * 16;
-  constexpr int KROW = DK + 8;         // LDS row strides (elements), padded
-  constexpr int VROW = kBN + 8;
-  constexpr int RCH = D / 8;           // 16-byte chunks per row
-  constexpr int NCH = kBN * RCH;
-  constexpr int CPT = (NCH + kThreads - 1) / kThreads;
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DV * VROW];
-  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  int bid = blockIdx.x;
-  const int qt = bid % a.n_qtiles;
-  bid /= a.n_qtiles;
-  const int h = bid % a.H;
-  const int b = bid / a.H;
-  const int q0 = qt * BM;
-
-  // The contraction padding columns [D, DK) of K are never loaded: zero them.
-  if (DK > D) {
-    for (int i = tid; i < 2 * kBN * (DK - D); i += kThreads) {
-      const int st = i / (kBN * (DK - D)), r = i % (kBN * (DK - D));
-      Ks[st][(r / (DK - D)) * KROW + D + r % (DK - D)] = 0;
-    }
-  }
-
-  BiasCtx bc;
-  setup_bias<E, BIAS, MASK, BM, kThreads>(a, dyn_lds, b, h, q0, bc);
-
-  // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
-  u32x4 qf[NQB][KCH];
-  QInfo qinf[NQB];
-  const uint16_t* qbase = (const uint16_t*)a.q;
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int il = wave * NQB * 16 + qb * 16 + l16;
-    const int qi = min(q0 + il, a.Nq - 1);
-    const int64_t off = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
-#pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
-      const int d0 = dc * 32 + g * 8;
-      qf[qb][dc] = d0 < D ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
-    }
-    qinf[qb] = make_qinfo<BIAS, MASK>(a, b, qi, il);
-  }
-
-  // Tile loader: each thread moves CPT 16-byte chunks of K and of V.
-  const uint16_t* kbase = (const uint16_t*)a.k;
-  const uint16_t* vbase = (const uint16_t*)a.v;
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * kThreads;
-      kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
-      if (ch < NCH) {
-        const int row = ch / RCH, col = (ch % RCH) * 8;
-        const int key = t * kBN + row;
-        if (key < a.Nk) {
-          kreg[c] = *(const u32x4*)(kbase + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + col);
-          vreg[c] = *(const u32x4*)(vbase + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + col);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * kThreads;
-      if (ch < NCH) {
-        const int row = ch / RCH, col = (ch % RCH) * 8;
-        *(u32x4*)&Ks[st][row * KROW + col] = kreg[c];
-        const int pos = (row & ~31) + kperm(row & 31);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Vt[st][(col + 2 * i) * VROW + pos] = (uint16_t)(vreg[c][i] & 0xffffu);
-          Vt[st][(col + 2 * i + 1) * VROW + pos] = (uint16_t)(vreg[c][i] >> 16);
-        }
-      }
-    }
-  };
-
-  f32x4 o[CB][NQB];
-  float m[NQB], l[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float sl2 = a.scale * kLog2e;
-  const int ntiles = (a.Nk + kBN - 1) / kBN;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // S^T = K Q^T for 4 key blocks x NQB query blocks.
-    f32x4 s[4][NQB];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 kf = *(const u32x4*)&Ks[st][(kb * 16 + l16) * KROW + dc * 32 + g * 8];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
-      }
-    }
-
-    // Online softmax (base 2) per query block; lane owns one query.
-    const int k0 = t * kBN;
-    const bool tail = k0 + kBN > a.Nk;
-    u32x4 pf[NQB][2];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float x[16];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kj = k0 + kb * 16 + g * 4 + r;
-          float v = s[kb][qb][r] * sl2;
-          if (BIAS != ATTN_BIAS_NONE || MASK)
-            v += bias_log2<E, BIAS, MASK, BM>(a, bc, qinf[qb], b, min(kj, a.Nk - 1));
-          if (tail && kj >= a.Nk) v = -INFINITY;
-          x[kb * 4 + r] = v;
-        }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mref);
-      m[qb] = mnew;
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(x[i] - mref);
-        ps += x[i];
-      }
-      l[qb] = l[qb] * alpha + ps;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        pf[qb][kc] = u32x4{E::pack2(x[kc * 8 + 0], x[kc * 8 + 1]), E::pack2(x[kc * 8 + 2], x[kc * 8 + 3]),
-                           E::pack2(x[kc * 8 + 4], x[kc * 8 + 5]), E::pack2(x[kc * 8 + 6], x[kc * 8 + 7])};
-    }
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const u32x4 vf = *(const u32x4*)&Vt[st][(cb * 16 + l16) * VROW + kc * 32 + g * 8];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
-      }
-
-    if (t + 1 < ntiles) store_tile(st ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: normalise and store O (lane holds O[q][cb*16 + g*4 .. +3]).
-  uint16_t* obase = (uint16_t*)a.o;
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.f / lt;
-    const int qi = q0 + wave * NQB * 16 + qb * 16 + l16;
-    if (qi < a.Nq) {
-      const int64_t off = tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, qi);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c0 = cb * 16 + g * 4;
-        if (c0 < D) {
-          const f32x4 v = o[cb][qb] * inv;
-          *(u32x2*)(obase + off + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------

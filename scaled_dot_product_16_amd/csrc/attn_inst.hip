@@ -1,6 +1,7 @@
 // One compiled instance of the attention kernels, selected by INST_DT (an
 // attn_dtype_t value) and INST_D (head dim, or the fp32 register bucket).
 #include "attn_device.h"
+#include "attn_mfma.h"
 #include "attn_launch.h"
 
 #ifndef INST_DT
@@ -16,13 +17,12 @@ namespace {
 constexpr size_t kMaxLds = 160 * 1024;
 
 template <typename K>
-int launch_kernel(K kernel, int threads, int bm, size_t static_lds, AttnArgs a, hipStream_t s) {
+int launch_kernel(K kernel, int threads, int bm, size_t dyn, AttnArgs a, hipStream_t s) {
   a.n_qtiles = (a.Nq + bm - 1) / bm;
   const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
   if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
-  const size_t dyn = dyn_lds_bytes(a, bm);
-  if (dyn + static_lds > kMaxLds) return ATTN_E_UNSUPPORTED;
-  if (dyn > 64 * 1024 &&
+  if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
+  if (dyn > 32 * 1024 &&
       hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
           hipSuccess)
     return ATTN_E_LAUNCH;
@@ -30,12 +30,13 @@ int launch_kernel(K kernel, int threads, int bm, size_t static_lds, AttnArgs a, 
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
-// Preprocessor conditions use the enum's numeric values (0 f32, 1 f16, 2 bf16).
 #if INST_DT == 0
 template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
+  constexpr size_t st = 2 * (size_t)kF32BN * INST_D * 4;
+  if (dyn_lds_bytes(a, kF32Threads) + st > kMaxLds) return ATTN_E_UNSUPPORTED;
   return launch_kernel(attn_fwd_f32<INST_D, BIAS, MASK>, kF32Threads, kF32Threads,
-                       2 * (size_t)kF32BN * INST_D * 4, a, s);
+                       dyn_lds_bytes(a, kF32Threads), a, s);
 }
 #else
 #if INST_DT == 2
@@ -43,15 +44,21 @@ using Elem = BF16;
 #else
 using Elem = F16;
 #endif
+constexpr int kNW = 4;
+constexpr int kNQB = 2;
+
 template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int D = INST_D;
-  constexpr int NQB = 2;
-  constexpr int BM = kWaves * NQB * 16;
-  constexpr int KROW = (D + 31) / 32 * 32 + 8;
-  constexpr int DV = (D + 15) / 16 * 16;
-  constexpr size_t st = 2 * (size_t)kBN * KROW * 2 + 2 * (size_t)DV * (kBN + 8) * 2;
-  return launch_kernel(attn_fwd_mfma<Elem, D, NQB, BIAS, MASK>, kThreads, BM, st, a, s);
+  using C = MfmaCfg<D, kNW, kNQB>;
+  // 64-wide relative-position grids take the register-resident form.
+  if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
+    if (a.gw == 64)
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, true>, C::NT, C::BM,
+                           mfma_lds_bytes<D, kNW, kNQB>(a, true), a, s);
+  }
+  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, false>, C::NT, C::BM,
+                       mfma_lds_bytes<D, kNW, kNQB>(a, false), a, s);
 }
 #endif
 

@@ -1,0 +1,399 @@
+// Half-precision attention kernel on gfx950 matrix cores.
+//
+// One workgroup = NW waves = a tile of BM = NW*NQB*16 queries of one
+// (batch item, head).  Each wave owns NQB blocks of 16 queries and streams
+// key/value tiles of 64 tokens through LDS (double buffered, 16-byte loads
+// and stores, rows padded against bank conflicts).
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32:
+//   A = K rows from LDS (lane l: key l%16, 8 head-dim elements (l/16)*8..),
+//   B = Q^T kept in registers for the whole key loop,
+//   C: lane l holds the scores of query l%16 for keys (l/16)*4 + r, r < 4.
+// So every lane owns one query: the row max / row sum need only two
+// cross-lane steps (v_permlane16_swap, v_permlane32_swap), the output
+// rescale is one scalar per lane, and the probabilities are already laid out
+// as the B operand of O^T += V^T P^T.  The A operand V^T is read straight
+// from the row-major V tile with ds_read_b64_tr_b16 (16-lane transposing
+// reads), with the key order of each 32-key chunk matching the score layout.
+//
+// The softmax runs in base 2 (exp2 of log2(e)-scaled logits) with a lazily
+// updated row reference: the output is rescaled only when some row's
+// maximum grew by more than 2^8, which keeps every probability <= 256 and
+// skips almost every rescale after the first tiles.  This is the same
+// softmax: any reference value gives the same normalised result.
+//
+// Relative position (SAM), fast form for 64-wide token grids: a key tile is
+// exactly one grid row, so q.Rw[qw-kw+63] depends only on the key's place in
+// the tile and is used as the initial accumulator of the QK^T MFMA chain
+// (zero extra instructions per score), while q.Rh[qh-kh+63] is one scalar per
+// query and tile, folded into the row offset.  Both come from small MFMA
+// products of the query block with Rw / Rh in the prologue.
+#ifndef ATTN_MFMA_H_
+#define ATTN_MFMA_H_
+
+#include "attn_device.h"
+
+namespace attn {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int NW, int NQB>
+struct MfmaCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = NW * NQB * 16;
+  static constexpr int BN = 64;
+  static constexpr int KCH = (D + 31) / 32;  // 32-wide contraction chunks of QK^T
+  static constexpr int DK = KCH * 32;
+  static constexpr int CB = (D + 15) / 16;   // 16-row blocks of O^T
+  static constexpr int DV = CB * 16;
+  static constexpr int KROW = DK + 8;        // LDS row strides (elements)
+  static constexpr int VROW = DV + 8;
+  static constexpr int RCH = D / 8;          // 16-byte chunks per token row
+  static constexpr int NCH = BN * RCH;
+  static constexpr int CPT = (NCH + NT - 1) / NT;
+  static constexpr int K_ELEMS = BN * KROW;  // per stage
+  static constexpr int V_ELEMS = BN * VROW;
+  static constexpr size_t KV_BYTES = 2 * (size_t)(K_ELEMS + V_ELEMS) * 2;
+  static constexpr int GROW = 132;           // relpos prologue scratch row (floats)
+  static constexpr size_t SCRATCH_BYTES = (size_t)NW * 16 * GROW * 4;
+  static constexpr size_t BASE_BYTES =
+      ((KV_BYTES > SCRATCH_BYTES ? KV_BYTES : SCRATCH_BYTES) + 15) / 16 * 16;
+};
+
+// Dynamic LDS bytes of one workgroup.
+template <int D, int NW, int NQB>
+inline size_t mfma_lds_bytes(const AttnArgs& a, bool rfast) {
+  using C = MfmaCfg<D, NW, NQB>;
+  if (rfast) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
+  return C::KV_BYTES + dyn_lds_bytes(a, C::BM);
+}
+
+__device__ __forceinline__ float max_across_groups(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_across_groups(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-lane transposing LDS read: lane j of a 16-lane group receives element
+// j%4 of the 4-element chunks addressed by lanes j/4, j/4+4, j/4+8, j/4+12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <class E, int D, int NW, int NQB, int BIAS, bool MASK, bool RFAST>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
+  using C = MfmaCfg<D, NW, NQB>;
+  constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, DK = C::DK, CB = C::CB,
+                DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH, NCH = C::NCH,
+                CPT = C::CPT;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  uint16_t* Ks = (uint16_t*)lds;          // [2][BN][KROW]
+  uint16_t* Vs = Ks + 2 * C::K_ELEMS;     // [2][BN][VROW]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  int bid = blockIdx.x;
+  const int qt = bid % a.n_qtiles;
+  bid /= a.n_qtiles;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int q0 = qt * BM;
+  const int wq0 = wave * NQB * 16;  // first query row of this wave inside the tile
+
+  // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
+  u32x4 qf[NQB][KCH];
+  const uint16_t* qbase = (const uint16_t*)a.q;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
+    const int64_t off = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      qf[qb][dc] = d0 < D ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  BiasCtx bc;
+  QInfo qinf[NQB];
+  f32x4 sinit[4][NQB];
+  const float* relh_lds = nullptr;
+  if constexpr (RFAST) {
+    // Relative position for a 64-wide grid (tile t = grid row t).
+    float* relh_tab = (float*)(lds + C::BASE_BYTES);  // [gh][BM], log2 units
+    float* gscr = (float*)lds + wave * 16 * C::GROW;   // per-wave scratch, overlays K/V
+    const uint16_t* rh = (const uint16_t*)a.rh;
+    const uint16_t* rw = (const uint16_t*)a.rw;
+    const float inv_scale = 1.f / a.scale;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int il0 = wq0 + qb * 16;
+      const int qblk = min(q0 + il0, a.Nq - 1);
+      const int qh = qblk >> 6;  // shared by the 16 queries of the block
+      // relh[i][kh] = Rh[qh + gh - 1 - kh] . q_i, as C[kh][i] of an MFMA product.
+      for (int mb = 0; mb * 16 < a.gh; ++mb) {
+        const int kh_row = mb * 16 + l16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) {
+          const int d0 = dc * 32 + g * 8;
+          u32x4 af = {0, 0, 0, 0};
+          if (kh_row < a.gh && d0 < D)
+            af = *(const u32x4*)(rh + (int64_t)(qh + a.gh - 1 - kh_row) * D + d0);
+          acc = E::mfma(af, qf[qb][dc], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kh = mb * 16 + g * 4 + r;
+          if (kh < a.gh) relh_tab[kh * BM + il0 + l16] = acc[r] * kLog2e;
+        }
+      }
+      // G[m][i] = Rw[m] . q_i for every table row m, then the per-lane gather
+      // relw[i][kw] = G[qw_i + 63 - kw][i] for this lane's 16 keys.
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const int m_row = mb * 16 + l16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) {
+          const int d0 = dc * 32 + g * 8;
+          u32x4 af = {0, 0, 0, 0};
+          if (m_row < 127 && d0 < D) af = *(const u32x4*)(rw + (int64_t)m_row * D + d0);
+          acc = E::mfma(af, qf[qb][dc], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gscr[l16 * C::GROW + mb * 16 + g * 4 + r] = acc[r];
+      }
+      __syncthreads();
+      const int qw = min(q0 + il0 + l16, a.Nq - 1) & 63;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sinit[kb][qb][r] = gscr[l16 * C::GROW + qw + 63 - (kb * 16 + g * 4 + r)] * inv_scale;
+      __syncthreads();
+    }
+    relh_lds = relh_tab;
+  } else {
+    setup_bias<E, BIAS, MASK, BM, NT>(a, lds + C::KV_BYTES, b, h, q0, bc);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int il = wq0 + qb * 16 + l16;
+      qinf[qb] = make_qinfo<BIAS, MASK>(a, b, min(q0 + il, a.Nq - 1), il);
+    }
+  }
+
+  // Padding columns of the K and V tiles are never loaded: zero them once.
+  if constexpr (DK > D) {
+    for (int i = tid; i < 2 * BN * (DK - D); i += NT) {
+      const int row = i / (DK - D), col = D + i % (DK - D);
+      Ks[row * KROW + col] = 0;
+    }
+  }
+  if constexpr (DV > D) {
+    for (int i = tid; i < 2 * BN * (DV - D); i += NT) {
+      const int row = i / (DV - D), col = D + i % (DV - D);
+      Vs[row * VROW + col] = 0;
+    }
+  }
+
+  // Tile loader: CPT 16-byte chunks of K and of V per thread.  The chunk's
+  // row/column inside a tile are fixed; in the batched layout its global
+  // offset advances by 64 token rows per tile.
+  const uint16_t* kbase = (const uint16_t*)a.k;
+  const uint16_t* vbase = (const uint16_t*)a.v;
+  u32x4 kreg[CPT], vreg[CPT];
+  int crow[CPT], ccol[CPT], kls[CPT], vls[CPT];
+  int64_t koff[CPT], voff[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * NT;
+    crow[c] = ch < NCH ? ch / RCH : (1 << 29);
+    ccol[c] = ch < NCH ? (ch % RCH) * 8 : 0;
+    kls[c] = crow[c] * KROW + ccol[c];
+    vls[c] = crow[c] * VROW + ccol[c];
+    koff[c] = (int64_t)b * a.k_sb + (int64_t)h * a.k_sh + (int64_t)crow[c] * a.k_sn + ccol[c];
+    voff[c] = (int64_t)b * a.v_sb + (int64_t)h * a.v_sh + (int64_t)crow[c] * a.v_sn + ccol[c];
+  }
+  auto load_tile = [&](int t) {
+    const int64_t ks = (int64_t)t * BN * a.k_sn, vs = (int64_t)t * BN * a.v_sn;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
+      const int key = t * BN + crow[c];
+      if (key < a.Nk) {
+        if (a.image) {
+          kreg[c] = *(const u32x4*)(kbase + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + ccol[c]);
+          vreg[c] = *(const u32x4*)(vbase + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + ccol[c]);
+        } else {
+          kreg[c] = *(const u32x4*)(kbase + koff[c] + ks);
+          vreg[c] = *(const u32x4*)(vbase + voff[c] + vs);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (crow[c] < BN) {
+        *(u32x4*)&Ks[st * C::K_ELEMS + kls[c]] = kreg[c];
+        *(u32x4*)&Vs[st * C::V_ELEMS + vls[c]] = vreg[c];
+      }
+    }
+  };
+
+  f32x4 o[CB][NQB];
+  float m[NQB], l[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = a.scale * kLog2e;  // logits in log2 units = c2 * (q.k)
+  const int ntiles = (a.Nk + BN - 1) / BN;
+  // Transposing V reads: this lane addresses key row (l16 / 4) of its group's
+  // 4-key slice and channel block 4 * (l16 % 4).
+  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  // Keys past Nk exist only in the last tile; their scores start from -inf
+  // (the K rows are zero), which removes them from max, exp and sum.
+  f32x4 tinit[4];
+  {
+    const int kl = (ntiles - 1) * BN;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        tinit[kb][r] = kl + kb * 16 + g * 4 + r < a.Nk ? 0.f : -INFINITY;
+  }
+
+  load_tile(0);
+  __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const uint16_t* Kt = Ks + st * C::K_ELEMS;
+    const uint16_t* Vt = Vs + st * C::V_ELEMS;
+    if (t + 1 < ntiles) load_tile(t + 1);
+
+    // S^T = K Q^T (optionally starting from the relative-position init).
+    f32x4 s[4][NQB];
+    const bool last = t + 1 == ntiles;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if constexpr (RFAST) s[kb][qb] = sinit[kb][qb];
+        else s[kb][qb] = last ? tinit[kb] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
+      }
+    }
+
+    // Online softmax (base 2).  y * cy + hh is the logit in log2 units.
+    const int k0 = t * BN;
+    u32x4 pf[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float y[16];
+      float cy = c2, hh = 0.f;
+      if constexpr (RFAST) hh = relh_lds[t * BM + wq0 + qb * 16 + l16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = s[kb][qb][r];
+          if constexpr (!RFAST && (BIAS != ATTN_BIAS_NONE || MASK)) {
+            const int kj = k0 + kb * 16 + g * 4 + r;
+            v = fmaf(v, c2, bias_log2<E, BIAS, MASK, BM>(a, bc, qinf[qb], b, min(kj, a.Nk - 1)));
+          }
+          y[kb * 4 + r] = v;
+        }
+      if constexpr (!RFAST && (BIAS != ATTN_BIAS_NONE || MASK)) cy = 1.f;
+      float mx = fmaxf(fmaxf(y[0], y[1]), y[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[i]), y[i + 1]);
+      mx = fmaxf(mx, y[15]);
+      mx = max_across_groups(mx);
+      const float mt = fmaf(mx, cy, hh);  // tile row maximum, log2 units
+      if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
+        const float mn = fmaxf(m[qb], mt);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
+      }
+      const float nb = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        y[i] = __builtin_amdgcn_exp2f(fmaf(y[i], cy, nb));
+        ps += y[i];
+      }
+      l[qb] += ps;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        pf[qb][kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
+                           E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
+    }
+
+    // O^T += V^T P^T; V^T fragments come from transposing reads of the V tile.
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
+      }
+
+    if (t + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise and store O (lane holds O[q][cb*16 + g*4 .. +3]).
+  uint16_t* obase = (uint16_t*)a.o;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float inv = 1.f / sum_across_groups(l[qb]);
+    const int qi = q0 + wq0 + qb * 16 + l16;
+    if (qi < a.Nq) {
+      const int64_t off = tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, qi);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 v = o[cb][qb] * inv;
+          *(u32x2*)(obase + off + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+}  // namespace attn
+
+#endif  // ATTN_MFMA_H_
