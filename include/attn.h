@@ -157,7 +157,8 @@ typedef struct {
  *  stream: a hipStream_t (NULL = the default stream), passed as void*.
  *
  *  Supported: d in {32, 40, 64, 80} for F16/BF16; d <= 128, d % 4 == 0 for
- *  F32.  Nq, Nk >= 1.  TABLE/RELPOS/SHIFT_REGIONS need Nq == Nk ==
+ *  F32.  Nq, Nk >= 1.  Within one (batch item, head) slice every element
+ *  offset, (N-1)*N-stride + d, must be below 2^31 (else ATTN_E_UNSUPPORTED).  TABLE/RELPOS/SHIFT_REGIONS need Nq == Nk ==
  *  grid_h*grid_w (SHIFT_REGIONS: == win_h*win_w).
  *  Returns ATTN_OK after queueing the kernel, or an error code (nothing is
  *  queued on error).  Asynchronous: kernel faults surface at the caller's

@@ -180,6 +180,11 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
     a->madd_s1 = mask->add_strides[1];
   }
 
+  // Offsets inside one (batch item, head) slice are 32-bit in the kernels.
+  const attn_tensor_t* ts[4] = {q, k, v, o};
+  for (const attn_tensor_t* t : ts)
+    if ((t->dims[2] - 1) * t->strides[2] + t->dims[3] >= (int64_t(1) << 31)) return ATTN_E_UNSUPPORTED;
+
   // out must not overlap the inputs it is computed from.
   if (overlaps(o, q, es) || overlaps(o, k, es) || overlaps(o, v, es)) return ATTN_E_ALIAS;
   return ATTN_OK;

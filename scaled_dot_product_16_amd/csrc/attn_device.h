@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/attn.h"
 #include "attn_internal.h"
 
@@ -43,6 +45,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Element types
 // ---------------------------------------------------------------------------
 struct BF16 {
+  static __device__ __forceinline__ uint16_t one_bits() { return 0x3f80; }
   static __device__ __forceinline__ float to_f(uint16_t x) {
     return __uint_as_float((uint32_t)x << 16);
   }
@@ -57,6 +60,7 @@ struct BF16 {
 };
 
 struct F16 {
+  static __device__ __forceinline__ uint16_t one_bits() { return 0x3c00; }
   static __device__ __forceinline__ float to_f(uint16_t x) {
     return (float)__builtin_bit_cast(_Float16, x);
   }
@@ -116,6 +120,25 @@ __device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_
   int x = wx * a.win_w + tx + a.shift_w;
   if (x >= a.img_w) x -= a.img_w;
   return (int64_t)img * sb + (int64_t)h * sh + (int64_t)(y * a.img_w + x) * sn;
+}
+
+// The same map split into a per-(batch item, head) base (uniform across a
+// workgroup) and a 32-bit per-token offset; the host guarantees every
+// in-slice offset fits in 31 bits.
+__device__ __forceinline__ int64_t tok_base(const AttnArgs& a, int64_t sb, int64_t sh, int b, int h) {
+  const int img = a.image ? b / a.nw : b;
+  return (int64_t)img * sb + (int64_t)h * sh;
+}
+__device__ __forceinline__ uint32_t tok_row(const AttnArgs& a, int64_t sn, int b, int t) {
+  if (!a.image) return (uint32_t)t * (uint32_t)sn;
+  const int w = b % a.nw;
+  const int wy = w / a.nwx, wx = w - wy * a.nwx;
+  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  int y = wy * a.win_h + ty + a.shift_h;
+  if (y >= a.img_h) y -= a.img_h;
+  int x = wx * a.win_w + tx + a.shift_w;
+  if (x >= a.img_w) x -= a.img_w;
+  return (uint32_t)(y * a.img_w + x) * (uint32_t)sn;
 }
 
 // Region (0..8) of token t of window w in the shifted image (SHIFT_REGIONS).

@@ -51,13 +51,18 @@ template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int D = INST_D;
   using C = MfmaCfg<D, kNW, kNQB>;
+  // Waves per SIMD the register allocation targets: the most that still
+  // fit the tile state without spilling (checked per head dim).
+  constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);
+  constexpr int kWpeRelpos = D <= 40 ? 3 : 2;
   // 64-wide relative-position grids take the register-resident form.
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
     if (a.gw == 64)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, true>, C::NT, C::BM,
-                           mfma_lds_bytes<D, kNW, kNQB>(a, true), a, s);
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, true, kWpeRelpos>, C::NT,
+                           C::BM, mfma_lds_bytes<D, kNW, kNQB>(a, true), a, s);
   }
-  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, false>, C::NT, C::BM,
+  constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
+  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, false, wpe>, C::NT, C::BM,
                        mfma_lds_bytes<D, kNW, kNQB>(a, false), a, s);
 }
 #endif

@@ -37,6 +37,23 @@ namespace attn {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// Build-time variants of the main loop (defaults are the measured best).
+#ifndef ATTN_PIPE
+#define ATTN_PIPE 0   // K tiles one tile ahead of V, QK^T(t+1) issued with softmax(t)
+#endif
+#ifndef ATTN_ONES
+#define ATTN_ONES 1   // row sums from a ones row of V on the matrix cores
+#endif
+#ifndef ATTN_TAIL_BRANCH
+#define ATTN_TAIL_BRANCH 0  // separate code for the last key tile (else a select)
+#endif
+#ifndef ATTN_VPAD
+#define ATTN_VPAD 8   // V tile row padding (elements)
+#endif
+#ifndef ATTN_KPAD
+#define ATTN_KPAD 8   // K tile row padding (elements)
+#endif
+
 template <int D, int NW, int NQB>
 struct MfmaCfg {
   static constexpr int NT = NW * 64;
@@ -44,10 +61,13 @@ struct MfmaCfg {
   static constexpr int BN = 64;
   static constexpr int KCH = (D + 31) / 32;  // 32-wide contraction chunks of QK^T
   static constexpr int DK = KCH * 32;
-  static constexpr int CB = (D + 15) / 16;   // 16-row blocks of O^T
+  // The ones row needs an extra 16-row block when D is a multiple of 16; at
+  // D = 80 that block does not fit the two-waves-per-SIMD register budget.
+  static constexpr bool ONES = ATTN_ONES && (D % 16 != 0 || D <= 64);
+  static constexpr int CB = ONES ? D / 16 + 1 : (D + 15) / 16;  // 16-row blocks of O^T
   static constexpr int DV = CB * 16;
-  static constexpr int KROW = DK + 8;        // LDS row strides (elements)
-  static constexpr int VROW = DV + 8;
+  static constexpr int KROW = DK + ATTN_KPAD;  // LDS row strides (elements)
+  static constexpr int VROW = DV + ATTN_VPAD;
   static constexpr int RCH = D / 8;          // 16-byte chunks per token row
   static constexpr int NCH = BN * RCH;
   static constexpr int CPT = (NCH + NT - 1) / NT;
@@ -90,8 +110,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <class E, int D, int NW, int NQB, int BIAS, bool MASK, bool RFAST>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
+// WPE: waves per SIMD the register allocation targets (2 lets the softmax of
+// one wave overlap the matrix products of another).
+#ifndef ATTN_WPE_ATTR
+#define ATTN_WPE_ATTR 1
+#endif
+#if ATTN_WPE_ATTR
+#define ATTN_WAVES_PER_EU(n) __attribute__((amdgpu_waves_per_eu(n, n)))
+#else
+#define ATTN_WAVES_PER_EU(n)
+#endif
+template <class E, int D, int NW, int NQB, int BIAS, bool MASK, bool RFAST, int WPE>
+__global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
   using C = MfmaCfg<D, NW, NQB>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, DK = C::DK, CB = C::CB,
                 DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH, NCH = C::NCH,
@@ -112,11 +142,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
 
   // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
   u32x4 qf[NQB][KCH];
-  const uint16_t* qbase = (const uint16_t*)a.q;
+  const uint16_t* qbase = (const uint16_t*)a.q + tok_base(a, a.q_sb, a.q_sh, b, h);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
-    const int64_t off = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+    const uint32_t off = tok_row(a, a.q_sn, b, qi);
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
@@ -194,6 +224,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
   }
 
   // Padding columns of the K and V tiles are never loaded: zero them once.
+  // Column D of V is set to 1, so row D of O^T accumulates the row sum of
+  // the (rounded) probabilities on the matrix cores.
   if constexpr (DK > D) {
     for (int i = tid; i < 2 * BN * (DK - D); i += NT) {
       const int row = i / (DK - D), col = D + i % (DK - D);
@@ -203,64 +235,39 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
   if constexpr (DV > D) {
     for (int i = tid; i < 2 * BN * (DV - D); i += NT) {
       const int row = i / (DV - D), col = D + i % (DV - D);
-      Vs[row * VROW + col] = 0;
+      Vs[row * VROW + col] = (C::ONES && col == D) ? E::one_bits() : 0;
     }
   }
 
-  // Tile loader: CPT 16-byte chunks of K and of V per thread.  The chunk's
-  // row/column inside a tile are fixed; in the batched layout its global
-  // offset advances by 64 token rows per tile.
-  const uint16_t* kbase = (const uint16_t*)a.k;
-  const uint16_t* vbase = (const uint16_t*)a.v;
+  // Tile loaders: CPT 16-byte chunks of K and of V per thread.  A chunk's
+  // row/column inside the tile are fixed; its global address is the
+  // (uniform) base of this batch item and head plus key * row stride.
+  const uint16_t* kbase = (const uint16_t*)a.k + tok_base(a, a.k_sb, a.k_sh, b, h);
+  const uint16_t* vbase = (const uint16_t*)a.v + tok_base(a, a.v_sb, a.v_sh, b, h);
   u32x4 kreg[CPT], vreg[CPT];
-  int crow[CPT], ccol[CPT], kls[CPT], vls[CPT];
-  int64_t koff[CPT], voff[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * NT;
-    crow[c] = ch < NCH ? ch / RCH : (1 << 29);
-    ccol[c] = ch < NCH ? (ch % RCH) * 8 : 0;
-    kls[c] = crow[c] * KROW + ccol[c];
-    vls[c] = crow[c] * VROW + ccol[c];
-    koff[c] = (int64_t)b * a.k_sb + (int64_t)h * a.k_sh + (int64_t)crow[c] * a.k_sn + ccol[c];
-    voff[c] = (int64_t)b * a.v_sb + (int64_t)h * a.v_sh + (int64_t)crow[c] * a.v_sn + ccol[c];
-  }
-  auto load_tile = [&](int t) {
-    const int64_t ks = (int64_t)t * BN * a.k_sn, vs = (int64_t)t * BN * a.v_sn;
+  auto crow = [&](int c) { const int ch = tid + c * NT; return ch < NCH ? ch / RCH : (1 << 29); };
+  auto ccol = [&](int c) { return ((tid + c * NT) % RCH) * 8; };
+  auto load_rows = [&](const uint16_t* base, int64_t sn, int t, u32x4* reg) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
-      const int key = t * BN + crow[c];
-      if (key < a.Nk) {
-        if (a.image) {
-          kreg[c] = *(const u32x4*)(kbase + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + ccol[c]);
-          vreg[c] = *(const u32x4*)(vbase + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + ccol[c]);
-        } else {
-          kreg[c] = *(const u32x4*)(kbase + koff[c] + ks);
-          vreg[c] = *(const u32x4*)(vbase + voff[c] + vs);
-        }
-      }
+      reg[c] = u32x4{0, 0, 0, 0};
+      const int key = t * BN + crow(c);
+      if (key < a.Nk) reg[c] = *(const u32x4*)(base + (tok_row(a, sn, b, key) + (uint32_t)ccol(c)));
     }
   };
-  auto store_tile = [&](int st) {
+  auto load_k = [&](int t) { load_rows(kbase, a.k_sn, t, kreg); };
+  auto load_v = [&](int t) { load_rows(vbase, a.v_sn, t, vreg); };
+  auto store_k = [&](int st) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      if (crow[c] < BN) {
-        *(u32x4*)&Ks[st * C::K_ELEMS + kls[c]] = kreg[c];
-        *(u32x4*)&Vs[st * C::V_ELEMS + vls[c]] = vreg[c];
-      }
-    }
+    for (int c = 0; c < CPT; ++c)
+      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = kreg[c];
+  };
+  auto store_v = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = vreg[c];
   };
 
-  f32x4 o[CB][NQB];
-  float m[NQB], l[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const float c2 = a.scale * kLog2e;  // logits in log2 units = c2 * (q.k)
   const int ntiles = (a.Nk + BN - 1) / BN;
   // Transposing V reads: this lane addresses key row (l16 / 4) of its group's
@@ -278,26 +285,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
         tinit[kb][r] = kl + kb * 16 + g * 4 + r < a.Nk ? 0.f : -INFINITY;
   }
 
-  load_tile(0);
-  __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    const uint16_t* Kt = Ks + st * C::K_ELEMS;
-    const uint16_t* Vt = Vs + st * C::V_ELEMS;
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // S^T = K Q^T (optionally starting from the relative-position init).
-    f32x4 s[4][NQB];
-    const bool last = t + 1 == ntiles;
+  // S^T = K Q^T for one key tile.
+  auto qk = [&](auto last, const uint16_t* Kt, f32x4 (&s)[4][NQB]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         if constexpr (RFAST) s[kb][qb] = sinit[kb][qb];
-        else s[kb][qb] = last ? tinit[kb] : f32x4{0.f, 0.f, 0.f, 0.f};
+        else if constexpr (decltype(last)::value) s[kb][qb] = tinit[kb];
+        else s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
@@ -308,56 +304,123 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
         for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
       }
     }
+  };
+  auto qk_tile = [&](int t, f32x4 (&s)[4][NQB]) {
+    const uint16_t* Kt = Ks + (t & 1) * C::K_ELEMS;
+#if ATTN_TAIL_BRANCH
+    if (t + 1 == ntiles) qk(std::true_type{}, Kt, s);
+    else qk(std::false_type{}, Kt, s);
+#else
+    // Keys past Nk (last tile only) start from -inf.
+    f32x4 init[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) init[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!RFAST && t + 1 == ntiles) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t * BN + kb * 16 + g * 4 + r >= a.Nk) init[kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if constexpr (RFAST) s[kb][qb] = sinit[kb][qb];
+        else s[kb][qb] = init[kb];
+      }
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
+      }
+    }
+#endif
+  };
 
-    // Online softmax (base 2).  y * cy + hh is the logit in log2 units.
+  f32x4 o[CB][NQB];
+  float m[NQB], l[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One key tile t: (1) row maxima and the lazy rescale of the output
+  // (branches), then (2) one branch-free region holding the exponentials and
+  // O^T += V^T P^T of tile t together with the QK^T products of tile t+1, so
+  // the scheduler can issue matrix instructions between the softmax ALU work.
+  f32x4 s_cur[4][NQB], s_nxt[4][NQB];
+  auto tile = [&](int t, auto has_next, auto next_last) {
     const int k0 = t * BN;
+    constexpr bool kGenericBias = !RFAST && (BIAS != ATTN_BIAS_NONE || MASK);
+    const float cy = kGenericBias ? 1.f : c2;
+    float y[NQB][16];
+    float nb[NQB];
     u32x4 pf[NQB][2];
+    // p = 2^(y*cy + nb), rounded to the element type as the B operand of PV.
+    auto exp_pack = [&](int qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[qb][i] = __builtin_amdgcn_exp2f(fmaf(y[qb][i], cy, nb[qb]));
+      if constexpr (!C::ONES) {
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps += y[qb][i];
+        l[qb] += ps;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        pf[qb][kc] = u32x4{E::pack2(y[qb][kc * 8 + 0], y[qb][kc * 8 + 1]),
+                           E::pack2(y[qb][kc * 8 + 2], y[qb][kc * 8 + 3]),
+                           E::pack2(y[qb][kc * 8 + 4], y[qb][kc * 8 + 5]),
+                           E::pack2(y[qb][kc * 8 + 6], y[qb][kc * 8 + 7])};
+    };
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      float y[16];
-      float cy = c2, hh = 0.f;
+      float hh = 0.f;
       if constexpr (RFAST) hh = relh_lds[t * BM + wq0 + qb * 16 + l16];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = s[kb][qb][r];
-          if constexpr (!RFAST && (BIAS != ATTN_BIAS_NONE || MASK)) {
+          float v = s_cur[kb][qb][r];
+          if constexpr (kGenericBias) {
             const int kj = k0 + kb * 16 + g * 4 + r;
             v = fmaf(v, c2, bias_log2<E, BIAS, MASK, BM>(a, bc, qinf[qb], b, min(kj, a.Nk - 1)));
           }
-          y[kb * 4 + r] = v;
+          y[qb][kb * 4 + r] = v;
         }
-      if constexpr (!RFAST && (BIAS != ATTN_BIAS_NONE || MASK)) cy = 1.f;
-      float mx = fmaxf(fmaxf(y[0], y[1]), y[2]);
+      float mx = fmaxf(fmaxf(y[qb][0], y[qb][1]), y[qb][2]);
 #pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[i]), y[i + 1]);
-      mx = fmaxf(mx, y[15]);
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[qb][i]), y[qb][i + 1]);
+      mx = fmaxf(mx, y[qb][15]);
       mx = max_across_groups(mx);
       const float mt = fmaf(mx, cy, hh);  // tile row maximum, log2 units
       if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
         const float mn = fmaxf(m[qb], mt);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qb] - mn);
         m[qb] = mn;
-        l[qb] *= alpha;
+        if constexpr (!C::ONES) l[qb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
       }
-      const float nb = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        y[i] = __builtin_amdgcn_exp2f(fmaf(y[i], cy, nb));
-        ps += y[i];
-      }
-      l[qb] += ps;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        pf[qb][kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
-                           E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
+      nb[qb] = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
+      if constexpr (!ATTN_PIPE) exp_pack(qb);
     }
 
+    // ---- branch-free region ----
+    if constexpr (decltype(has_next)::value) qk(next_last, Ks + ((t + 1) & 1) * C::K_ELEMS, s_nxt);
+    if constexpr (ATTN_PIPE) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) exp_pack(qb);
+    }
     // O^T += V^T P^T; V^T fragments come from transposing reads of the V tile.
+    const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -369,19 +432,86 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
       }
+    // Interleave: one matrix instruction, then a few ALU instructions.
+    constexpr int kMfma = (decltype(has_next)::value ? 4 * KCH * NQB : 0) + 2 * CB * NQB;
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    }
+  };
 
-    if (t + 1 < ntiles) store_tile(st ^ 1);
+  // Pipeline: K tiles run one tile ahead of V tiles, so the QK^T products of
+  // tile t+1 are issued next to the softmax of tile t.  Buffers: K(t) in
+  // K-stage t&1, V(t) in V-stage t&1; global loads of K(t+3) and V(t+2) fly
+  // during iteration t+1.
+  auto after_tile = [&](int t) {
+    if (t + 1 < ntiles) store_v((t + 1) & 1);
+    if (t + 2 < ntiles) store_k(t & 1);
+    __syncthreads();
+    if (t + 2 < ntiles) load_v(t + 2);
+    if (t + 3 < ntiles) load_k(t + 3);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s_cur[kb][qb] = s_nxt[kb][qb];
+  };
+  load_k(0);
+  load_v(0);
+  __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
+  store_k(0);
+  store_v(0);
+#if ATTN_PIPE
+  if (ntiles > 1) {
+    load_k(1);
+    store_k(1);
+  }
+  __syncthreads();
+  qk_tile(0, s_cur);
+  if (ntiles > 1) load_v(1);
+  if (ntiles > 2) load_k(2);
+  int t = 0;
+  for (; t + 2 < ntiles; ++t) {
+    tile(t, std::true_type{}, std::false_type{});
+    after_tile(t);
+  }
+  if (t + 1 < ntiles) {
+    tile(t, std::true_type{}, std::true_type{});
+    after_tile(t);
+    ++t;
+  }
+  tile(t, std::false_type{}, std::false_type{});
+#else
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      load_k(t + 1);
+      load_v(t + 1);
+    }
+    qk_tile(t, s_cur);
+    tile(t, std::false_type{}, std::false_type{});
+    if (t + 1 < ntiles) {
+      store_k((t + 1) & 1);
+      store_v((t + 1) & 1);
+    }
     __syncthreads();
   }
+#endif
 
-  // Epilogue: normalise and store O (lane holds O[q][cb*16 + g*4 .. +3]).
-  uint16_t* obase = (uint16_t*)a.o;
+  // Epilogue: normalise by the row sum (row D of O^T, held by lane group
+  // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).
+  uint16_t* obase = (uint16_t*)a.o + tok_base(a, a.o_sb, a.o_sh, b, h);
+  constexpr int LB = D / 16, LG = (D % 16) / 4, LR = D % 4;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float inv = 1.f / sum_across_groups(l[qb]);
+    float lsum;
+    if constexpr (C::ONES) lsum = __shfl(o[LB < CB ? LB : 0][qb][LR], LG * 16 + l16);
+    else lsum = sum_across_groups(l[qb]);
+    const float inv = 1.f / lsum;
     const int qi = q0 + wq0 + qb * 16 + l16;
     if (qi < a.Nq) {
-      const int64_t off = tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, qi);
+      const uint32_t off = tok_row(a, a.o_sn, b, qi);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int c0 = cb * 16 + g * 4;
