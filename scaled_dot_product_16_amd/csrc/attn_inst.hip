@@ -2,6 +2,7 @@
 // attn_dtype_t value) and INST_D (head dim, or the fp32 register bucket).
 #include "attn_device.h"
 #include "attn_mfma.h"
+#include "attn_win.h"
 #include "attn_launch.h"
 
 #ifndef INST_DT
@@ -51,6 +52,26 @@ template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int D = INST_D;
   using C = MfmaCfg<D, kNW, kNQB>;
+  // Windows of at most 64 tokens: one wave per (window, head) unit.
+  if constexpr (BIAS != ATTN_BIAS_RELPOS) {
+    if (a.Nq <= 64 && a.Nk <= 64) {
+      AttnArgs w = a;
+      w.n_qtiles = 1;
+      const int64_t blocks = (int64_t)a.B * a.H;
+      if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
+      const size_t dyn = win_lds_bytes(a, WinCfg<D>::KV_BYTES);
+      if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
+      auto kern = !MASK ? attn_fwd_win<Elem, D, BIAS, ATTN_MASK_NONE>
+                  : a.mask_kind == ATTN_MASK_ADDITIVE ? attn_fwd_win<Elem, D, BIAS, ATTN_MASK_ADDITIVE>
+                                                      : attn_fwd_win<Elem, D, BIAS, ATTN_MASK_SHIFT_REGIONS>;
+      if (dyn > 32 * 1024 &&
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
+              hipSuccess)
+        return ATTN_E_LAUNCH;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWinWaves * 64), dyn, s, w);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+    }
+  }
   // Waves per SIMD the register allocation targets: the most that still
   // fit the tile state without spilling (checked per head dim).
   constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);

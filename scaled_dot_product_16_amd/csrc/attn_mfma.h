@@ -130,7 +130,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   uint16_t* Ks = (uint16_t*)lds;          // [2][BN][KROW]
   uint16_t* Vs = Ks + 2 * C::K_ELEMS;     // [2][BN][VROW]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g = lane >> 4;
   int bid = blockIdx.x;
   const int qt = bid % a.n_qtiles;
