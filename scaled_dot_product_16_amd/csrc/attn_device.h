@@ -171,7 +171,7 @@ __host__ __device__ constexpr bool needs_kinfo(int bias_kind, bool mask) {
   return bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS || mask;
 }
 
-inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
+__host__ __device__ inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
   const bool kinfo = a.bias_kind == ATTN_BIAS_TABLE || a.bias_kind == ATTN_BIAS_RELPOS ||
                      a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
   size_t n = kinfo ? ((size_t)a.Nk * 4 + 15) / 16 * 16 : 0;
@@ -182,7 +182,9 @@ inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
 
 // Fill kinfo and the table / relative-position terms.  `E` is the element
 // type of the tables and of q (relative-position terms use the raw query).
-template <class E, int BIAS, bool MASK, int BM, int NT>
+// RELPOS_VALU: compute the relative-position tables here with plain dot
+// products (the fp32 kernel); the MFMA kernel fills them itself.
+template <class E, int BIAS, bool MASK, int BM, int NT, bool RELPOS_VALU = true>
 __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, BiasCtx& bc) {
   const int tid = threadIdx.x;
   char* p = dyn;
@@ -214,7 +216,7 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
     float* relh = (float*)p;
     float* relw = relh + a.gh * BM;
     const int nk = a.gh + a.gw;
-    for (int e = tid; e < BM * nk; e += NT) {
+    for (int e = tid; RELPOS_VALU && e < BM * nk; e += NT) {
       const int il = e % BM, kk = e / BM;
       const int qi = min(q0 + il, a.Nq - 1);
       const int qh = qi / a.gw, qw = qi - qh * a.gw;

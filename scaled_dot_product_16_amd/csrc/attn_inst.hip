@@ -76,15 +76,19 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   // fit the tile state without spilling (checked per head dim).
   constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);
   constexpr int kWpeRelpos = D <= 40 ? 3 : 2;
-  // 64-wide relative-position grids take the register-resident form.
+  // Relative position: 64-wide grids take the row form, grids with
+  // gh + gw <= 32 fold the bias into the QK^T contraction.
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
     if (a.gw == 64)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, true, kWpeRelpos>, C::NT,
-                           C::BM, mfma_lds_bytes<D, kNW, kNQB>(a, true), a, s);
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelRow64, kWpeRelpos>, C::NT,
+                           C::BM, mfma_lds_bytes<D, kNW, kNQB, kRelRow64>(a), a, s);
+    if (a.gh + a.gw <= 32)
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, 2>, C::NT, C::BM,
+                           mfma_lds_bytes<D, kNW, kNQB, kRelAug>(a), a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
-  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, false, wpe>, C::NT, C::BM,
-                       mfma_lds_bytes<D, kNW, kNQB>(a, false), a, s);
+  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kRelTables, wpe>, C::NT, C::BM,
+                       mfma_lds_bytes<D, kNW, kNQB>(a), a, s);
 }
 #endif
 

@@ -54,13 +54,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define ATTN_KPAD 8   // K tile row padding (elements)
 #endif
 
-template <int D, int NW, int NQB>
+// Relative-position modes of the kernel.
+constexpr int kRelTables = 0;  // per-score lookups in LDS tables (also non-relpos biases)
+constexpr int kRelRow64 = 1;   // 64-wide grids: Rw term seeds the accumulator, Rh term per row
+constexpr int kRelAug = 2;     // gh + gw <= 32: bias folded into the QK^T contraction
+
+template <int D, int NW, int NQB, bool AUG = false>
 struct MfmaCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BM = NW * NQB * 16;
   static constexpr int BN = 64;
-  static constexpr int KCH = (D + 31) / 32;  // 32-wide contraction chunks of QK^T
-  static constexpr int DK = KCH * 32;
+  static constexpr int KCH = (D + 31) / 32;  // 32-wide contraction chunks of the head dim
+  static constexpr int KCHT = KCH + (AUG ? 1 : 0);  // plus one chunk of bias one-hots
+  static constexpr int DK = KCHT * 32;
   // The ones row needs an extra 16-row block when D is a multiple of 16; at
   // D = 80 that block does not fit the two-waves-per-SIMD register budget.
   static constexpr bool ONES = ATTN_ONES && (D % 16 != 0 || D <= 64);
@@ -80,12 +86,22 @@ struct MfmaCfg {
       ((KV_BYTES > SCRATCH_BYTES ? KV_BYTES : SCRATCH_BYTES) + 15) / 16 * 16;
 };
 
+// Row length (floats) of the relative-position prologue scratch.
+inline __host__ __device__ int relpos_grow(const AttnArgs& a) {
+  const int m = 2 * (a.gh > a.gw ? a.gh : a.gw) - 1;
+  return (m + 15) / 16 * 16 + 4;
+}
+
 // Dynamic LDS bytes of one workgroup.
-template <int D, int NW, int NQB>
-inline size_t mfma_lds_bytes(const AttnArgs& a, bool rfast) {
-  using C = MfmaCfg<D, NW, NQB>;
-  if (rfast) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
-  return C::KV_BYTES + dyn_lds_bytes(a, C::BM);
+template <int D, int NW, int NQB, int RMODE = kRelTables>
+__host__ __device__ inline size_t mfma_lds_bytes(const AttnArgs& a) {
+  using C = MfmaCfg<D, NW, NQB, RMODE == kRelAug>;
+  if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
+  if (RMODE == kRelAug) return C::KV_BYTES + (size_t)NW * 16 * relpos_grow(a) * 4;
+  size_t n = C::KV_BYTES + dyn_lds_bytes(a, C::BM);
+  // Relative-position prologue scratch: G[16 queries][2g-1 rows] per wave.
+  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)NW * 16 * relpos_grow(a) * 4;
+  return n;
 }
 
 __device__ __forceinline__ float max_across_groups(float v) {
@@ -120,12 +136,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #else
 #define ATTN_WAVES_PER_EU(n)
 #endif
-template <class E, int D, int NW, int NQB, int BIAS, bool MASK, bool RFAST, int WPE>
+template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int WPE>
 __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
-  using C = MfmaCfg<D, NW, NQB>;
-  constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, DK = C::DK, CB = C::CB,
-                DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH, NCH = C::NCH,
-                CPT = C::CPT;
+  constexpr bool RFAST = RMODE == kRelRow64;
+  constexpr bool RAUG = RMODE == kRelAug;
+  using C = MfmaCfg<D, NW, NQB, RAUG>;
+  constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, KCHT = C::KCHT, DK = C::DK,
+                CB = C::CB, DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH,
+                NCH = C::NCH, CPT = C::CPT;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   uint16_t* Ks = (uint16_t*)lds;          // [2][BN][KROW]
   uint16_t* Vs = Ks + 2 * C::K_ELEMS;     // [2][BN][VROW]
@@ -142,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   const int wq0 = wave * NQB * 16;  // first query row of this wave inside the tile
 
   // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
-  u32x4 qf[NQB][KCH];
+  u32x4 qf[NQB][KCHT];
   const uint16_t* qbase = (const uint16_t*)a.q + tok_base(a, a.q_sb, a.q_sh, b, h);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -215,21 +233,115 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       __syncthreads();
     }
     relh_lds = relh_tab;
+  } else if constexpr (RAUG) {
+    // Relative position folded into the contraction: the extra Q chunk holds
+    // relh[i][0..gh) and relw[i][0..gw) divided by the scale (the K tile's
+    // extra chunk holds one-hots at kh and gh + kw), so QK^T directly gives
+    // q.k + (relh + relw) / scale.  G = R Q^T comes from the matrix cores and
+    // is gathered per lane through this wave's scratch rows.
+    const int grow = relpos_grow(a);
+    float* gscr = (float*)(lds + C::KV_BYTES) + wave * 16 * grow;
+    const float inv_scale = 1.f / a.scale;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
+      const int qh = qi / a.gw, qw = qi - qh * a.gw;
+      float ext[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ext[e] = 0.f;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const int gg = part == 0 ? a.gh : a.gw;
+        const uint16_t* tab = (const uint16_t*)(part == 0 ? a.rh : a.rw);
+        for (int mb = 0; mb * 16 < 2 * gg - 1; ++mb) {
+          const int m_row = mb * 16 + l16;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < KCH; ++dc) {
+            const int d0 = dc * 32 + g * 8;
+            u32x4 af = {0, 0, 0, 0};
+            if (m_row < 2 * gg - 1 && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
+            acc = E::mfma(af, qf[qb][dc], acc);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gscr[l16 * grow + mb * 16 + g * 4 + r] = acc[r];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Extension column k = g*8 + e: relh[kh = k] or relw[kw = k - gh].
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = g * 8 + e;
+          const int kk = part == 0 ? k : k - a.gh;
+          const int qc = part == 0 ? qh : qw;
+          if (kk >= 0 && kk < gg) ext[e] = gscr[l16 * grow + qc - kk + gg - 1] * inv_scale;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      qf[qb][KCH] = u32x4{E::pack2(ext[0], ext[1]), E::pack2(ext[2], ext[3]), E::pack2(ext[4], ext[5]),
+                          E::pack2(ext[6], ext[7])};
+    }
   } else {
-    setup_bias<E, BIAS, MASK, BM, NT>(a, lds + C::KV_BYTES, b, h, q0, bc);
+    setup_bias<E, BIAS, MASK, BM, NT, false>(a, lds + C::KV_BYTES, b, h, q0, bc);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int il = wq0 + qb * 16 + l16;
       qinf[qb] = make_qinfo<BIAS, MASK>(a, b, min(q0 + il, a.Nq - 1), il);
+    }
+    if constexpr (BIAS == ATTN_BIAS_RELPOS && !RAUG) {
+      // relh[kh][i] = q_i . Rh[qh_i - kh + gh - 1] and relw[kw][i] likewise:
+      // G = R Q^T on the matrix cores for every table row, then a per-lane
+      // gather through this wave's scratch rows.
+      const int grow = relpos_grow(a);
+      float* gscr = (float*)(lds + mfma_lds_bytes<D, NW, NQB>(a)) - (NW - wave) * 16 * grow;
+      float* relh = (float*)bc.relh;
+      float* relw = (float*)bc.relw;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int il = wq0 + qb * 16 + l16;
+        const int qi = min(q0 + il, a.Nq - 1);
+        const int qh = qi / a.gw, qw = qi - qh * a.gw;
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int gg = part == 0 ? a.gh : a.gw;
+          const uint16_t* tab = (const uint16_t*)(part == 0 ? a.rh : a.rw);
+          for (int mb = 0; mb * 16 < 2 * gg - 1; ++mb) {
+            const int m_row = mb * 16 + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < KCH; ++dc) {
+              const int d0 = dc * 32 + g * 8;
+              u32x4 af = {0, 0, 0, 0};
+              if (m_row < 2 * gg - 1 && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
+              acc = E::mfma(af, qf[qb][dc], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gscr[l16 * grow + mb * 16 + g * 4 + r] = acc[r];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int qc = part == 0 ? qh : qw;
+          float* dst = part == 0 ? relh : relw;
+          for (int kk = g; kk < gg; kk += 4) dst[kk * BM + il] = gscr[l16 * grow + qc - kk + gg - 1] * kLog2e;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+      }
     }
   }
 
   // Padding columns of the K and V tiles are never loaded: zero them once.
   // Column D of V is set to 1, so row D of O^T accumulates the row sum of
   // the (rounded) probabilities on the matrix cores.
-  if constexpr (DK > D) {
-    for (int i = tid; i < 2 * BN * (DK - D); i += NT) {
-      const int row = i / (DK - D), col = D + i % (DK - D);
+  if constexpr (KCH * 32 > D) {
+    constexpr int P = KCH * 32 - D;
+    for (int i = tid; i < 2 * BN * P; i += NT) {
+      const int row = i / P, col = D + i % P;
       Ks[row * KROW + col] = 0;
     }
   }
@@ -258,10 +370,28 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   };
   auto load_k = [&](int t) { load_rows(kbase, a.k_sn, t, kreg); };
   auto load_v = [&](int t) { load_rows(vbase, a.v_sn, t, vreg); };
-  auto store_k = [&](int st) {
+  auto store_k = [&](int st, int t) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
       if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = kreg[c];
+    if constexpr (RAUG) {
+      // One-hot chunk of key row `row`: ones at columns kh and gh + kw.
+      for (int i = tid; i < BN * 4; i += NT) {
+        const int row = i >> 2, cq = (i & 3) * 8;
+        const int j = t * BN + row;
+        // (j + 0.5) / gw is within 0.004 of j / gw and gw <= 31, so the
+        // truncation is exact for j < 16384.
+        const int kh = (int)(((float)j + 0.5f) / (float)a.gw), kw = j - kh * a.gw;
+        uint32_t w4[4] = {0, 0, 0, 0};
+        const uint32_t one = E::one_bits();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int col = cq + e;
+          if (j < a.Nk && (col == kh || col == a.gh + kw)) w4[e >> 1] |= one << ((e & 1) * 16);
+        }
+        *(u32x4*)&Ks[st * C::K_ELEMS + row * KROW + KCH * 32 + cq] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
   };
   auto store_v = [&](int st) {
 #pragma unroll
@@ -297,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         else s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
+    for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
@@ -331,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         else s[kb][qb] = init[kb];
       }
 #pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
+    for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
@@ -359,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   f32x4 s_cur[4][NQB], s_nxt[4][NQB];
   auto tile = [&](int t, auto has_next, auto next_last) {
     const int k0 = t * BN;
-    constexpr bool kGenericBias = !RFAST && (BIAS != ATTN_BIAS_NONE || MASK);
+    constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
     float y[NQB][16];
     float nb[NQB];
@@ -449,7 +579,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // during iteration t+1.
   auto after_tile = [&](int t) {
     if (t + 1 < ntiles) store_v((t + 1) & 1);
-    if (t + 2 < ntiles) store_k(t & 1);
+    if (t + 2 < ntiles) store_k(t & 1, t + 2);
     __syncthreads();
     if (t + 2 < ntiles) load_v(t + 2);
     if (t + 3 < ntiles) load_k(t + 3);
@@ -461,12 +591,12 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   load_k(0);
   load_v(0);
   __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
-  store_k(0);
+  store_k(0, 0);
   store_v(0);
 #if ATTN_PIPE
   if (ntiles > 1) {
     load_k(1);
-    store_k(1);
+    store_k(1, 1);
   }
   __syncthreads();
   qk_tile(0, s_cur);
@@ -493,7 +623,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     qk_tile(t, s_cur);
     tile(t, std::false_type{}, std::false_type{});
     if (t + 1 < ntiles) {
-      store_k((t + 1) & 1);
+      store_k((t + 1) & 1, t + 1);
       store_v((t + 1) & 1);
     }
     __syncthreads();
