@@ -83,7 +83,7 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
       return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelRow64, kWpeRelpos>, C::NT,
                            C::BM, mfma_lds_bytes<D, kNW, kNQB, kRelRow64>(a), a, s);
     if (a.gh + a.gw <= 32)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, 2>, C::NT, C::BM,
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, (D <= 32 ? 3 : 2)>, C::NT, C::BM,
                            mfma_lds_bytes<D, kNW, kNQB, kRelAug>(a), a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;

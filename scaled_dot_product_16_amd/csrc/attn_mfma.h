@@ -69,7 +69,7 @@ struct MfmaCfg {
   static constexpr int DK = KCHT * 32;
   // The ones row needs an extra 16-row block when D is a multiple of 16; at
   // D = 80 that block does not fit the two-waves-per-SIMD register budget.
-  static constexpr bool ONES = ATTN_ONES && (D % 16 != 0 || D <= 64);
+  static constexpr bool ONES = ATTN_ONES && !AUG && (D % 16 != 0 || D <= 64);
   static constexpr int CB = ONES ? D / 16 + 1 : (D + 15) / 16;  // 16-row blocks of O^T
   static constexpr int DV = CB * 16;
   static constexpr int KROW = DK + ATTN_KPAD;  // LDS row strides (elements)
@@ -97,7 +97,10 @@ template <int D, int NW, int NQB, int RMODE = kRelTables>
 __host__ __device__ inline size_t mfma_lds_bytes(const AttnArgs& a) {
   using C = MfmaCfg<D, NW, NQB, RMODE == kRelAug>;
   if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
-  if (RMODE == kRelAug) return C::KV_BYTES + (size_t)NW * 16 * relpos_grow(a) * 4;
+  if (RMODE == kRelAug) {
+    const size_t scr = (size_t)NW * 16 * relpos_grow(a) * 4;  // overlays the K/V tiles
+    return C::KV_BYTES > scr ? C::KV_BYTES : scr;
+  }
   size_t n = C::KV_BYTES + dyn_lds_bytes(a, C::BM);
   // Relative-position prologue scratch: G[16 queries][2g-1 rows] per wave.
   if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)NW * 16 * relpos_grow(a) * 4;
@@ -173,6 +176,57 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     }
   }
 
+  // Tile loaders: CPT 16-byte chunks of K and of V per thread.  A chunk's
+  // row/column inside the tile are fixed; its global address is the
+  // (uniform) base of this batch item and head plus key * row stride.
+  const uint16_t* kbase = (const uint16_t*)a.k + tok_base(a, a.k_sb, a.k_sh, b, h);
+  const uint16_t* vbase = (const uint16_t*)a.v + tok_base(a, a.v_sb, a.v_sh, b, h);
+  u32x4 kreg[CPT], vreg[CPT];
+  auto crow = [&](int c) { const int ch = tid + c * NT; return ch < NCH ? ch / RCH : (1 << 29); };
+  auto ccol = [&](int c) { return ((tid + c * NT) % RCH) * 8; };
+  auto load_rows = [&](const uint16_t* base, int64_t sn, int t, u32x4* reg) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      reg[c] = u32x4{0, 0, 0, 0};
+      const int key = t * BN + crow(c);
+      if (key < a.Nk) reg[c] = *(const u32x4*)(base + (tok_row(a, sn, b, key) + (uint32_t)ccol(c)));
+    }
+  };
+  auto load_k = [&](int t) { load_rows(kbase, a.k_sn, t, kreg); };
+  auto load_v = [&](int t) { load_rows(vbase, a.v_sn, t, vreg); };
+  auto store_k = [&](int st, int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = kreg[c];
+    if constexpr (RAUG) {
+      // One-hot chunk of key row `row`: ones at columns kh and gh + kw.
+      for (int i = tid; i < BN * 4; i += NT) {
+        const int row = i >> 2, cq = (i & 3) * 8;
+        const int j = t * BN + row;
+        // (j + 0.5) / gw is within 0.004 of j / gw and gw <= 31, so the
+        // truncation is exact for j < 16384.
+        const int kh = (int)(((float)j + 0.5f) / (float)a.gw), kw = j - kh * a.gw;
+        uint32_t w4[4] = {0, 0, 0, 0};
+        const uint32_t one = E::one_bits();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int col = cq + e;
+          if (j < a.Nk && (col == kh || col == a.gh + kw)) w4[e >> 1] |= one << ((e & 1) * 16);
+        }
+        *(u32x4*)&Ks[st * C::K_ELEMS + row * KROW + KCH * 32 + cq] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+  };
+  auto store_v = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = vreg[c];
+  };
+
+  // The first K/V tile is in flight while the bias prologue runs.
+  load_k(0);
+  load_v(0);
+
   BiasCtx bc;
   QInfo qinf[NQB];
   f32x4 sinit[4][NQB];
@@ -240,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     // q.k + (relh + relw) / scale.  G = R Q^T comes from the matrix cores and
     // is gathered per lane through this wave's scratch rows.
     const int grow = relpos_grow(a);
-    float* gscr = (float*)(lds + C::KV_BYTES) + wave * 16 * grow;
+    float* gscr = (float*)lds + wave * 16 * grow;  // overlays the K/V tiles
     const float inv_scale = 1.f / a.scale;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -334,70 +388,6 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       }
     }
   }
-
-  // Padding columns of the K and V tiles are never loaded: zero them once.
-  // Column D of V is set to 1, so row D of O^T accumulates the row sum of
-  // the (rounded) probabilities on the matrix cores.
-  if constexpr (KCH * 32 > D) {
-    constexpr int P = KCH * 32 - D;
-    for (int i = tid; i < 2 * BN * P; i += NT) {
-      const int row = i / P, col = D + i % P;
-      Ks[row * KROW + col] = 0;
-    }
-  }
-  if constexpr (DV > D) {
-    for (int i = tid; i < 2 * BN * (DV - D); i += NT) {
-      const int row = i / (DV - D), col = D + i % (DV - D);
-      Vs[row * VROW + col] = (C::ONES && col == D) ? E::one_bits() : 0;
-    }
-  }
-
-  // Tile loaders: CPT 16-byte chunks of K and of V per thread.  A chunk's
-  // row/column inside the tile are fixed; its global address is the
-  // (uniform) base of this batch item and head plus key * row stride.
-  const uint16_t* kbase = (const uint16_t*)a.k + tok_base(a, a.k_sb, a.k_sh, b, h);
-  const uint16_t* vbase = (const uint16_t*)a.v + tok_base(a, a.v_sb, a.v_sh, b, h);
-  u32x4 kreg[CPT], vreg[CPT];
-  auto crow = [&](int c) { const int ch = tid + c * NT; return ch < NCH ? ch / RCH : (1 << 29); };
-  auto ccol = [&](int c) { return ((tid + c * NT) % RCH) * 8; };
-  auto load_rows = [&](const uint16_t* base, int64_t sn, int t, u32x4* reg) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      reg[c] = u32x4{0, 0, 0, 0};
-      const int key = t * BN + crow(c);
-      if (key < a.Nk) reg[c] = *(const u32x4*)(base + (tok_row(a, sn, b, key) + (uint32_t)ccol(c)));
-    }
-  };
-  auto load_k = [&](int t) { load_rows(kbase, a.k_sn, t, kreg); };
-  auto load_v = [&](int t) { load_rows(vbase, a.v_sn, t, vreg); };
-  auto store_k = [&](int st, int t) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = kreg[c];
-    if constexpr (RAUG) {
-      // One-hot chunk of key row `row`: ones at columns kh and gh + kw.
-      for (int i = tid; i < BN * 4; i += NT) {
-        const int row = i >> 2, cq = (i & 3) * 8;
-        const int j = t * BN + row;
-        // (j + 0.5) / gw is within 0.004 of j / gw and gw <= 31, so the
-        // truncation is exact for j < 16384.
-        const int kh = (int)(((float)j + 0.5f) / (float)a.gw), kw = j - kh * a.gw;
-        uint32_t w4[4] = {0, 0, 0, 0};
-        const uint32_t one = E::one_bits();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int col = cq + e;
-          if (j < a.Nk && (col == kh || col == a.gh + kw)) w4[e >> 1] |= one << ((e & 1) * 16);
-        }
-        *(u32x4*)&Ks[st * C::K_ELEMS + row * KROW + KCH * 32 + cq] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-      }
-    }
-  };
-  auto store_v = [&](int st) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = vreg[c];
-  };
 
   const float c2 = a.scale * kLog2e;  // logits in log2 units = c2 * (q.k)
   const int ntiles = (a.Nk + BN - 1) / BN;
@@ -588,9 +578,24 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) s_cur[kb][qb] = s_nxt[kb][qb];
   };
-  load_k(0);
-  load_v(0);
   __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
+  // Padding columns of the K and V tiles are never loaded: zero them once.
+  // Column D of V is set to 1, so row D of O^T accumulates the row sum of
+  // the (rounded) probabilities on the matrix cores.
+  if constexpr (KCH * 32 > D) {
+    constexpr int P = KCH * 32 - D;
+    for (int i = tid; i < 2 * BN * P; i += NT) {
+      const int row = i / P, col = D + i % P;
+      Ks[row * KROW + col] = 0;
+    }
+  }
+  if constexpr (DV > D) {
+    for (int i = tid; i < 2 * BN * (DV - D); i += NT) {
+      const int row = i / (DV - D), col = D + i % (DV - D);
+      Vs[row * VROW + col] = (C::ONES && col == D) ? E::one_bits() : 0;
+    }
+  }
+
   store_k(0, 0);
   store_v(0);
 #if ATTN_PIPE
