@@ -38,11 +38,18 @@ RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a stored counter record stays valid across comment-only edits."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_16_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -100,6 +107,21 @@ def cpu_baseline(w, budget_s: float = 10.0):
             "sample": f"{sample} {reps}x, {t_total:.1f} s, numpy float64"}
 
 
+def copy_calibration(torch, mib: int):
+    """Plain device-to-device copies of a known size.  Under a counter run the
+    per-dispatch FETCH_SIZE / WRITE_SIZE of these copies, divided by the bytes
+    they must move (mib MiB each way), give the scale applied to the attention
+    kernel's counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").normal_()
+    dst = [torch.empty_like(src) for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(5):
+        dst[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +132,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches with per-launch events instead of a graph replay")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (reference dispatches "
+                         "for scaling the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -117,6 +142,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
 
     from scaled_dot_product_16_amd import binding
     from scaled_dot_product_16_amd import workloads as W

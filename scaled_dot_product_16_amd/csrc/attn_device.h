@@ -102,6 +102,22 @@ __device__ __forceinline__ float dot4<F32E>(const void* x, int64_t i, const void
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup renumbering for the 8 XCDs of MI355X.  The dispatcher hands
+// workgroup i to XCD i % 8, and each XCD has its own L2.  The logical id
+// returned here gives every XCD one contiguous range of ids, so tiles that
+// read the same data (the query tiles of one (batch item, head), which all
+// stream the same K/V; neighbouring windows, which share cache lines of an
+// image row) are processed by one XCD at about the same time and fetch the
+// shared lines from HBM once.  A bijection on [0, n) for any n.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_logical_id(int i, int n) {
+  constexpr int kXcds = 8;
+  const int per = n / kXcds, extra = n % kXcds;
+  const int x = i % kXcds, local = i / kXcds;
+  return x * per + (x < extra ? x : extra) + local;
+}
+
+// ---------------------------------------------------------------------------
 // Token addressing: batched layout, or image layout with the window partition
 // and the cyclic shift folded in (window w of image img, token t of the
 // window reads shifted-image pixel (wy*win_h+ty, wx*win_w+tx), which holds
@@ -186,7 +202,7 @@ __host__ __device__ inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
 // products (the fp32 kernel); the MFMA kernel fills them itself.
 template <class E, int BIAS, bool MASK, int BM, int NT, bool RELPOS_VALU = true>
 __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, BiasCtx& bc) {
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   char* p = dyn;
   bc.kinfo = nullptr;
   bc.tbl = bc.relh = bc.relw = nullptr;
@@ -297,8 +313,8 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Vs[kF32BN][DMAX];
   extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
 
-  const int tid = threadIdx.x;
-  int bid = blockIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
   const int qt = bid % a.n_qtiles;
   bid /= a.n_qtiles;
   const int h = bid % a.H;

@@ -23,6 +23,7 @@ int launch_kernel(K kernel, int threads, int bm, size_t dyn, AttnArgs a, hipStre
   const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
   if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
   if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
+  a.n_blocks = (int)blocks;
   if (dyn > 32 * 1024 &&
       hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
           hipSuccess)
@@ -59,6 +60,7 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
       w.n_qtiles = 1;
       const int64_t blocks = (int64_t)a.B * a.H;
       if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
+      w.n_blocks = (int)blocks;
       const size_t dyn = win_lds_bytes(a, WinCfg<D>::KV_BYTES);
       if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
       auto kern = !MASK ? attn_fwd_win<Elem, D, BIAS, ATTN_MASK_NONE>

@@ -1,5 +1,5 @@
 // Internal interface between the host validation layer (attn_api.cpp, no HIP
-// dependency) and the kernel launcher (attn_kernels.hip).
+// dependency) and the kernel launcher (attn_dispatch.cpp, attn_inst.hip).
 #ifndef ATTN_INTERNAL_H_
 #define ATTN_INTERNAL_H_
 
@@ -44,6 +44,7 @@ struct AttnArgs {
   float scale;
   // Filled by the launcher.
   int32_t n_qtiles;
+  int32_t n_blocks;  // workgroups in the grid
 };
 
 // Host-side validation shared by attn_check and attn_fwd.  Returns an ATTN_*

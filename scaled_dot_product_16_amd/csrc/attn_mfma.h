@@ -38,14 +38,8 @@ namespace attn {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Build-time variants of the main loop (defaults are the measured best).
-#ifndef ATTN_PIPE
-#define ATTN_PIPE 0   // K tiles one tile ahead of V, QK^T(t+1) issued with softmax(t)
-#endif
 #ifndef ATTN_ONES
 #define ATTN_ONES 1   // row sums from a ones row of V on the matrix cores
-#endif
-#ifndef ATTN_TAIL_BRANCH
-#define ATTN_TAIL_BRANCH 0  // separate code for the last key tile (else a select)
 #endif
 #ifndef ATTN_VPAD
 #define ATTN_VPAD 8   // V tile row padding (elements)
@@ -53,6 +47,22 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #ifndef ATTN_KPAD
 #define ATTN_KPAD 8   // K tile row padding (elements)
 #endif
+
+// Word 3 of a buffer resource on gfx9-family chips: 32-bit data format,
+// no swizzle.  With stride 0 the resource is "raw": an access at byte offset
+// >= num_records returns zero and touches no memory.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Raw buffer resource over [p, p + nrec bytes).  p and nrec must be the same
+// in every lane of the wave (they are taken from the first active lane, so
+// the resource lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t nrec) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0,
+                                           (int)__builtin_amdgcn_readfirstlane(nrec), kBufferWord3);
+}
 
 // Relative-position modes of the kernel.
 constexpr int kRelTables = 0;  // per-score lookups in LDS tables (also non-relpos biases)
@@ -151,10 +161,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   uint16_t* Ks = (uint16_t*)lds;          // [2][BN][KROW]
   uint16_t* Vs = Ks + 2 * C::K_ELEMS;     // [2][BN][VROW]
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g = lane >> 4;
-  int bid = blockIdx.x;
+  int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
   const int qt = bid % a.n_qtiles;
   bid /= a.n_qtiles;
   const int h = bid % a.H;
@@ -176,24 +186,44 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     }
   }
 
-  // Tile loaders: CPT 16-byte chunks of K and of V per thread.  A chunk's
-  // row/column inside the tile are fixed; its global address is the
-  // (uniform) base of this batch item and head plus key * row stride.
+  // Tile loaders: CPT 16-byte chunks of K and of V per thread, through
+  // buffer resources.  Batched layout: the resource of tile t starts at key
+  // t*BN and ends with the last byte of key Nk-1, so a chunk's byte offset is
+  // the same in every tile and chunks of keys past Nk read as zero without a
+  // memory access.  Image layout: per-key offsets through the window map,
+  // with keys past Nk clamped to Nk-1.  Either way those keys' scores are
+  // set to -inf before the softmax.
   const uint16_t* kbase = (const uint16_t*)a.k + tok_base(a, a.k_sb, a.k_sh, b, h);
   const uint16_t* vbase = (const uint16_t*)a.v + tok_base(a, a.v_sb, a.v_sh, b, h);
   u32x4 kreg[CPT], vreg[CPT];
   auto crow = [&](int c) { const int ch = tid + c * NT; return ch < NCH ? ch / RCH : (1 << 29); };
   auto ccol = [&](int c) { return ((tid + c * NT) % RCH) * 8; };
-  auto load_rows = [&](const uint16_t* base, int64_t sn, int t, u32x4* reg) {
+  uint32_t koff[CPT], voff[CPT];  // batched layout: chunk byte offsets inside a tile
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      reg[c] = u32x4{0, 0, 0, 0};
-      const int key = t * BN + crow(c);
-      if (key < a.Nk) reg[c] = *(const u32x4*)(base + (tok_row(a, sn, b, key) + (uint32_t)ccol(c)));
+  for (int c = 0; c < CPT; ++c) {
+    const int r = crow(c);
+    const int64_t ko = (int64_t)r * a.k_sn + ccol(c), vo = (int64_t)r * a.v_sn + ccol(c);
+    koff[c] = r < BN && 2 * ko < 0xFFFFFFF0ll ? (uint32_t)(2 * ko) : 0xFFFFFFF0u;
+    voff[c] = r < BN && 2 * vo < 0xFFFFFFF0ll ? (uint32_t)(2 * vo) : 0xFFFFFFF0u;
+  }
+  auto load_rows = [&](const uint16_t* base, int64_t sn, const uint32_t* off, int t, u32x4* reg) {
+    if (!a.image) {
+      const int64_t k0 = (int64_t)t * BN;
+      const uint32_t nrec = (uint32_t)(2 * ((a.Nk - 1 - k0) * sn + D));
+      const auto rs = buffer_rsrc(base + k0 * sn, nrec);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], 0, 0);
+    } else {
+      const auto rs = buffer_rsrc(base, 0xFFFFFFFFu);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int key = min(t * BN + min(crow(c), BN - 1), a.Nk - 1);
+        reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * (tok_row(a, sn, b, key) + (uint32_t)ccol(c)), 0, 0);
+      }
     }
   };
-  auto load_k = [&](int t) { load_rows(kbase, a.k_sn, t, kreg); };
-  auto load_v = [&](int t) { load_rows(vbase, a.v_sn, t, vreg); };
+  auto load_k = [&](int t) { load_rows(kbase, a.k_sn, koff, t, kreg); };
+  auto load_v = [&](int t) { load_rows(vbase, a.v_sn, voff, t, vreg); };
   auto store_k = [&](int st, int t) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
@@ -394,72 +424,25 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // Transposing V reads: this lane addresses key row (l16 / 4) of its group's
   // 4-key slice and channel block 4 * (l16 % 4).
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
-  // Keys past Nk exist only in the last tile; their scores start from -inf
-  // (the K rows are zero), which removes them from max, exp and sum.
-  f32x4 tinit[4];
-  {
-    const int kl = (ntiles - 1) * BN;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tinit[kb][r] = kl + kb * 16 + g * 4 + r < a.Nk ? 0.f : -INFINITY;
-  }
-
-  // S^T = K Q^T for one key tile.
-  auto qk = [&](auto last, const uint16_t* Kt, f32x4 (&s)[4][NQB]) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        if constexpr (RFAST) s[kb][qb] = sinit[kb][qb];
-        else if constexpr (decltype(last)::value) s[kb][qb] = tinit[kb];
-        else s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+  // S^T = K Q^T for one key tile.  The first product of each chain takes
+  // its addend directly: zero, or the row-form relative-position term.
+  auto qk = [&](const uint16_t* Kt, f32x4 (&s)[4][NQB]) {
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
+        for (int qb = 0; qb < NQB; ++qb) {
+          f32x4 c = s[kb][qb];
+          if (dc == 0) {
+            if constexpr (RFAST) c = sinit[kb][qb];
+            else c = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          s[kb][qb] = E::mfma(kf, qf[qb][dc], c);
+        }
       }
     }
-  };
-  auto qk_tile = [&](int t, f32x4 (&s)[4][NQB]) {
-    const uint16_t* Kt = Ks + (t & 1) * C::K_ELEMS;
-#if ATTN_TAIL_BRANCH
-    if (t + 1 == ntiles) qk(std::true_type{}, Kt, s);
-    else qk(std::false_type{}, Kt, s);
-#else
-    // Keys past Nk (last tile only) start from -inf.
-    f32x4 init[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) init[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!RFAST && t + 1 == ntiles) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t * BN + kb * 16 + g * 4 + r >= a.Nk) init[kb][r] = -INFINITY;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        if constexpr (RFAST) s[kb][qb] = sinit[kb][qb];
-        else s[kb][qb] = init[kb];
-      }
-#pragma unroll
-    for (int dc = 0; dc < KCHT; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][dc], s[kb][qb]);
-      }
-    }
-#endif
   };
 
   f32x4 o[CB][NQB];
@@ -472,12 +455,11 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One key tile t: (1) row maxima and the lazy rescale of the output
-  // (branches), then (2) one branch-free region holding the exponentials and
-  // O^T += V^T P^T of tile t together with the QK^T products of tile t+1, so
-  // the scheduler can issue matrix instructions between the softmax ALU work.
-  f32x4 s_cur[4][NQB], s_nxt[4][NQB];
-  auto tile = [&](int t, auto has_next, auto next_last) {
+  // One key tile t: row maxima and the lazy rescale of the output, then the
+  // exponentials and O^T += V^T P^T.
+  f32x4 s_cur[4][NQB];
+  const bool ragged = (a.Nk % BN) != 0;
+  auto tile = [&](int t) {
     const int k0 = t * BN;
     constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
@@ -516,6 +498,15 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           }
           y[qb][kb * 4 + r] = v;
         }
+      if (ragged && t + 1 == ntiles) {
+        // Keys past Nk (last tile only) leave the softmax.
+        const int lim = a.Nk - k0 - g * 4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * 16 + r >= lim) y[qb][kb * 4 + r] = -INFINITY;
+      }
       float mx = fmaxf(fmaxf(y[qb][0], y[qb][1]), y[qb][2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[qb][i]), y[qb][i + 1]);
@@ -531,14 +522,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
       }
       nb[qb] = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
-      if constexpr (!ATTN_PIPE) exp_pack(qb);
-    }
-
-    // ---- branch-free region ----
-    if constexpr (decltype(has_next)::value) qk(next_last, Ks + ((t + 1) & 1) * C::K_ELEMS, s_nxt);
-    if constexpr (ATTN_PIPE) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) exp_pack(qb);
+      exp_pack(qb);
     }
     // O^T += V^T P^T; V^T fragments come from transposing reads of the V tile.
     const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
@@ -554,7 +538,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
       }
     // Interleave: one matrix instruction, then a few ALU instructions.
-    constexpr int kMfma = (decltype(has_next)::value ? 4 * KCH * NQB : 0) + 2 * CB * NQB;
+    constexpr int kMfma = 2 * CB * NQB;
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
@@ -563,21 +547,6 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     }
   };
 
-  // Pipeline: K tiles run one tile ahead of V tiles, so the QK^T products of
-  // tile t+1 are issued next to the softmax of tile t.  Buffers: K(t) in
-  // K-stage t&1, V(t) in V-stage t&1; global loads of K(t+3) and V(t+2) fly
-  // during iteration t+1.
-  auto after_tile = [&](int t) {
-    if (t + 1 < ntiles) store_v((t + 1) & 1);
-    if (t + 2 < ntiles) store_k(t & 1, t + 2);
-    __syncthreads();
-    if (t + 2 < ntiles) load_v(t + 2);
-    if (t + 3 < ntiles) load_k(t + 3);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s_cur[kb][qb] = s_nxt[kb][qb];
-  };
   __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
   // Padding columns of the K and V tiles are never loaded: zero them once.
   // Column D of V is set to 1, so row D of O^T accumulates the row sum of
@@ -598,42 +567,20 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 
   store_k(0, 0);
   store_v(0);
-#if ATTN_PIPE
-  if (ntiles > 1) {
-    load_k(1);
-    store_k(1, 1);
-  }
-  __syncthreads();
-  qk_tile(0, s_cur);
-  if (ntiles > 1) load_v(1);
-  if (ntiles > 2) load_k(2);
-  int t = 0;
-  for (; t + 2 < ntiles; ++t) {
-    tile(t, std::true_type{}, std::false_type{});
-    after_tile(t);
-  }
-  if (t + 1 < ntiles) {
-    tile(t, std::true_type{}, std::true_type{});
-    after_tile(t);
-    ++t;
-  }
-  tile(t, std::false_type{}, std::false_type{});
-#else
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) {
       load_k(t + 1);
       load_v(t + 1);
     }
-    qk_tile(t, s_cur);
-    tile(t, std::false_type{}, std::false_type{});
+    qk(Ks + (t & 1) * C::K_ELEMS, s_cur);
+    tile(t);
     if (t + 1 < ntiles) {
       store_k((t + 1) & 1, t + 1);
       store_v((t + 1) & 1);
     }
     __syncthreads();
   }
-#endif
 
   // Epilogue: normalise by the row sum (row D of O^T, held by lane group
   // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).

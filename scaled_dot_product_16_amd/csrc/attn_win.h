@@ -1,15 +1,15 @@
 // Short-sequence attention (windows of up to 64 tokens) on gfx950.
 //
 // Swin-style window attention has many small, independent (window, head)
-// units: 49 tokens each for 7x7 windows.  One wave owns one unit and keeps
-// all of it on chip: Q and K are loaded straight from memory into MFMA
-// operand registers, V is staged in a per-wave LDS slice for the
-// transposing read, the 64x64 score tile (keys past N start from -inf) lives
-// in registers, and the softmax needs no running rescale because the whole
-// key range is one tile.  Table bias indices, region labels and the image
-// addressing of the window partition and cyclic shift (Swin talk, sections 1
-// and 2) are computed from per-lane token coordinates that are the same for
-// every unit.
+// units: 49 tokens each for 7x7 windows.  One workgroup of four waves owns
+// one unit and keeps all of it on chip: wave w holds queries 16w..16w+15 as
+// MFMA operands in registers, K and V of the whole unit are staged once in
+// LDS (V read back transposed), the 64-key score tile (keys past N start
+// from -inf) lives in registers, and the softmax needs no running rescale
+// because the whole key range is one tile.  Table bias indices, region
+// labels and the image addressing of the window partition and cyclic shift
+// (Swin talk, sections 1 and 2) are computed from per-lane token
+// coordinates.
 #ifndef ATTN_WIN_H_
 #define ATTN_WIN_H_
 
@@ -34,9 +34,21 @@ struct WinCfg {
   static constexpr size_t KV_BYTES = (size_t)64 * (KROW + VROW) * 2;
 };
 
+// Entries of the bias table of a window unit: the relative-position table
+// (TABLE bias), or a single zero entry when only the region mask is present.
+inline __host__ __device__ int win_tab_entries(const AttnArgs& a) {
+  return a.bias_kind == ATTN_BIAS_TABLE ? (2 * a.gh - 1) * (2 * a.gw - 1) : 1;
+}
+
+// Bias and region mask come from one LDS table lookup per score when the
+// bias is a table and/or the mask is the shifted-window region mask.
+inline __host__ __device__ bool win_uses_table(const AttnArgs& a) {
+  return a.bias_kind == ATTN_BIAS_TABLE || a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
+}
+
 inline size_t win_lds_bytes(const AttnArgs& a, size_t kv_bytes) {
   size_t n = kv_bytes + 64 * 4;  // per-key index data
-  if (a.bias_kind == ATTN_BIAS_TABLE) n += (size_t)(2 * a.gh - 1) * (2 * a.gw - 1) * 4;
+  if (win_uses_table(a)) n += (size_t)9 * win_tab_entries(a) * 4;
   return n;
 }
 
@@ -78,29 +90,42 @@ __device__ __forceinline__ int win_region(const AttnArgs& a, const WinPos& p, in
 // One workgroup = one (batch item, head) unit of at most 64 tokens; wave w
 // owns queries 16w .. 16w+15.  MASKK: ATTN_MASK_NONE / _ADDITIVE /
 // _SHIFT_REGIONS.
+//
+// Table bias and region mask share one LDS lookup per score.  The table of
+// n entries is stored 9 times: copy c = 3*(dy+1) + (dx+1) holds the table
+// plus the mask value, except copy 4 (dy = dx = 0), where dy and dx are the
+// differences of the query's and the key's region labels along each axis
+// (in a window they differ by at most one).  The lookup address splits into
+// a per-query part and a per-key part:
+//   idx(q) - idx(k) + n * c  =  [idx(q) + n*(3*ry_q + rx_q)]
+//                              + [4n - idx(k) - n*(3*ry_k + rx_k)],
+// with idx(q) = (qh+gh-1)(2gw-1) + qw+gw-1 and idx(k) = kh(2gw-1) + kw, so
+// each score costs one add and one LDS read.
 template <class E, int D, int BIAS, int MASKK>
 __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   using C = WinCfg<D>;
-  constexpr int NT = C::NT, KCH = C::KCH, DK = C::DK, CB = C::CB, DV = C::DV, KROW = C::KROW,
-                VROW = C::VROW, RCH = C::RCH, NCH = C::NCH, CPT = C::CPT;
+  constexpr int NT = C::NT, KCH = C::KCH, CB = C::CB, KROW = C::KROW, VROW = C::VROW,
+                RCH = C::RCH, NCH = C::NCH, CPT = C::CPT, DK = C::DK, DV = C::DV;
+  constexpr bool kTab = BIAS == ATTN_BIAS_TABLE || MASKK == ATTN_MASK_SHIFT_REGIONS;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   uint16_t* Ks = (uint16_t*)lds;        // [64][KROW]
   uint16_t* Vs = Ks + 64 * KROW;        // [64][VROW]
-  int* kinfo = (int*)(lds + C::KV_BYTES);            // per key: table offset | region << 24
-  float* tbl = (float*)(lds + C::KV_BYTES + 64 * 4);  // this head's table column, log2 units
+  int* kinfo = (int*)(lds + C::KV_BYTES);              // per key: byte offset of its table part
+  constexpr int kTabByte = (int)C::KV_BYTES + 64 * 4;  // 9 table copies, log2 units
+  float* tbl = (float*)(lds + kTabByte);
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int H = a.H, N = a.Nq, Nk = a.Nk;
-  const int unit = blockIdx.x;
+  const int unit = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
   const int b = unit / H, h = unit - (unit / H) * H;
 
   // Token t < 64 of a window -> (row, column) for a row length n <= 1024: the
   // float quotient (t + 0.5) / n is within 2e-5 of the exact value and at
   // least 0.5 / n away from an integer, so truncation is exact.
-  const float inv_ww = 1.f / (float)(a.win_w > 0 ? a.win_w : 1);
-  const float inv_gw = 1.f / (float)(a.gw > 0 ? a.gw : 1);
+  const float inv_ww = __builtin_amdgcn_rcpf((float)(a.win_w > 0 ? a.win_w : 1));
+  const float inv_gw = __builtin_amdgcn_rcpf((float)(a.gw > 0 ? a.gw : 1));
   auto div_small = [](int t, float inv) { return (int)(((float)t + 0.5f) * inv); };
   auto split = [&](int t, int& ty, int& tx) {
     ty = div_small(t, inv_ww);
@@ -108,11 +133,13 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   };
   const WinPos pos = win_pos(a, b);
   const int bimg = a.image ? pos.img : b;
-  auto row_off = [&](int t, int64_t sn) -> uint32_t {
-    if (!a.image) return (uint32_t)t * (uint32_t)sn;
+  // Token t -> its row in the (image, head) slice: t itself (batched
+  // layout) or the shifted-image pixel of window token t (image layout).
+  auto tok_pix = [&](int t) -> uint32_t {
+    if (!a.image) return (uint32_t)t;
     int ty, tx;
     split(t, ty, tx);
-    return win_tok_off(a, pos, ty, tx, sn);
+    return win_tok_off(a, pos, ty, tx, 1);
   };
   const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh);
   const uint16_t* kp = (const uint16_t*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh);
@@ -126,38 +153,51 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = min(tid + c * NT, NCH - 1);
-    const int key = min(ch / RCH, Nk - 1);
+    const uint32_t pix = tok_pix(min(ch / RCH, Nk - 1));
     const uint32_t col = (uint32_t)((ch % RCH) * 8);
-    kreg[c] = *(const u32x4*)(kp + (row_off(key, a.k_sn) + col));
-    vreg[c] = *(const u32x4*)(vp + (row_off(key, a.v_sn) + col));
+    kreg[c] = *(const u32x4*)(kp + (pix * (uint32_t)a.k_sn + col));
+    vreg[c] = *(const u32x4*)(vp + (pix * (uint32_t)a.v_sn + col));
   }
   const int q_tok = min(wave * 16 + l16, N - 1);
-  const uint32_t q_off = row_off(q_tok, a.q_sn);
+  const uint32_t q_pix = tok_pix(q_tok);
+  const uint32_t q_off = q_pix * (uint32_t)a.q_sn;
   u32x4 qf[KCH];
 #pragma unroll
   for (int dc = 0; dc < KCH; ++dc) {
     const int d0 = dc * 32 + g * 8;
     qf[dc] = d0 < D ? *(const u32x4*)(qp + (q_off + (uint32_t)d0)) : u32x4{0, 0, 0, 0};
   }
-  if constexpr (BIAS == ATTN_BIAS_TABLE) {
-    const int n = (2 * a.gh - 1) * (2 * a.gw - 1);
-    for (int r = tid; r < n; r += NT) tbl[r] = load_elem<E>(a.table, (int64_t)r * H + h) * kLog2e;
-  }
+
+  // Only windows on the last window row or column of the shifted image hold
+  // more than one region.
   const bool regions = MASKK == ATTN_MASK_SHIFT_REGIONS &&
                        (pos.y0 + a.win_h > a.img_h - a.win_h || pos.x0 + a.win_w > a.img_w - a.win_w);
-  if (tid < 64) {
-    const int j = min(tid, Nk - 1);
-    int info = 0;
-    if constexpr (BIAS == ATTN_BIAS_TABLE) {
-      const int kh = div_small(j, inv_gw), kw = j - kh * a.gw;
-      info = kh * (2 * a.gw - 1) + kw;
+  const int n_tab = win_tab_entries(a);
+  if constexpr (kTab) {
+    const float mv = a.mask_value * kLog2e;
+    for (int r = tid; r < n_tab; r += NT) {
+      const float t = BIAS == ATTN_BIAS_TABLE ? load_elem<E>(a.table, (int64_t)r * H + h) * kLog2e : 0.f;
+      tbl[4 * n_tab + r] = t;
+      if (regions) {
+#pragma unroll
+        for (int c = 0; c < 9; ++c)
+          if (c != 4) tbl[c * n_tab + r] = t + mv;
+      }
     }
-    if (regions) {
-      int ty, tx;
-      split(j, ty, tx);
-      info |= win_region(a, pos, ty, tx) << 24;
+    if (tid < 64) {
+      const int j = min(tid, Nk - 1);
+      int part = 4 * n_tab;
+      if constexpr (BIAS == ATTN_BIAS_TABLE) {
+        const int kh = div_small(j, inv_gw), kw = j - kh * a.gw;
+        part -= kh * (2 * a.gw - 1) + kw;
+      }
+      if (regions) {
+        int ty, tx;
+        split(j, ty, tx);
+        part -= n_tab * win_region(a, pos, ty, tx);
+      }
+      kinfo[tid] = part * 4;
     }
-    kinfo[tid] = info;
   }
   // Padding columns of the tiles are never loaded: zero them.
   if constexpr (DK > D) {
@@ -177,12 +217,17 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   __syncthreads();
   if (wave * 16 >= N) return;  // no barrier below this point
 
-  // S^T = K Q^T for the 4 key blocks; keys past Nk start from -inf.
+  // S^T = K Q^T for the 4 key blocks; keys past Nk (only in a block that
+  // reaches past Nk) start from -inf.
   f32x4 s[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb * 16 + 16 > Nk) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[kb][r] = kb * 16 + g * 4 + r < Nk ? 0.f : -INFINITY;
+      for (int r = 0; r < 4; ++r)
+        if (kb * 16 + g * 4 + r >= Nk) s[kb][r] = -INFINITY;
+    }
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const u32x4 kf = *(const u32x4*)&Ks[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
@@ -190,48 +235,41 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     }
   }
 
-  // Bias and mask (log2 units).  The region test is needed only when this
-  // window straddles a shifted-region boundary.
+  // Bias and mask (log2 units).
   const float c2 = a.scale * kLog2e;
-  const float mval = a.mask_value * kLog2e;
-  int qtab = 0, qreg = 0;
-  if constexpr (BIAS == ATTN_BIAS_TABLE) {
-    const int qh = div_small(q_tok, inv_gw), qw = q_tok - qh * a.gw;
-    qtab = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
-  }
-  if (regions) {
-    int ty, tx;
-    split(q_tok, ty, tx);
-    qreg = win_region(a, pos, ty, tx);
-  }
-  // This lane's keys are kb*16 + g*4 + r: four consecutive kinfo entries.
-  int ki[16];
-  if (BIAS == ATTN_BIAS_TABLE || regions) {
+  float y[16];
+  if constexpr (kTab) {
+    int qpart = 0;
+    if constexpr (BIAS == ATTN_BIAS_TABLE) {
+      const int qh = div_small(q_tok, inv_gw), qw = q_tok - qh * a.gw;
+      qpart = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
+    }
+    if (regions) {
+      int ty, tx;
+      split(q_tok, ty, tx);
+      qpart += n_tab * win_region(a, pos, ty, tx);
+    }
+    const char* qbase = lds + kTabByte + qpart * 4;
+    // This lane's keys are kb*16 + g*4 + r: four consecutive kinfo entries.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const u32x4 v = *(const u32x4*)&kinfo[kb * 16 + g * 4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ki[kb * 4 + r] = (int)v[r];
+      for (int r = 0; r < 4; ++r) y[kb * 4 + r] = fmaf(s[kb][r], c2, *(const float*)(qbase + (int)v[r]));
     }
-  }
-  float y[16];
+  } else {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = min(kb * 16 + g * 4 + r, Nk - 1);
-      float bias = 0.f;
-      if constexpr (BIAS == ATTN_BIAS_TABLE) bias = tbl[qtab - (ki[kb * 4 + r] & 0xffffff)];
-      if constexpr (BIAS == ATTN_BIAS_ADDITIVE)
-        bias = load_elem<E>(a.badd, (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)q_tok * a.badd_s1 + j) * kLog2e;
-      if constexpr (MASKK == ATTN_MASK_ADDITIVE)
-        bias += load_elem<E>(a.madd, (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)q_tok * a.madd_s1 + j) * kLog2e;
-      y[kb * 4 + r] = fmaf(s[kb][r], c2, bias);
-    }
-  if (regions) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if ((ki[e] >> 24) != qreg) y[e] += mval;
+      for (int r = 0; r < 4; ++r) {
+        const int j = min(kb * 16 + g * 4 + r, Nk - 1);
+        float bias = 0.f;
+        if constexpr (BIAS == ATTN_BIAS_ADDITIVE)
+          bias = load_elem<E>(a.badd, (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)q_tok * a.badd_s1 + j) * kLog2e;
+        if constexpr (MASKK == ATTN_MASK_ADDITIVE)
+          bias += load_elem<E>(a.madd, (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)q_tok * a.madd_s1 + j) * kLog2e;
+        y[kb * 4 + r] = fmaf(s[kb][r], c2, bias);
+      }
   }
 
   // Softmax over the single key tile.
@@ -267,9 +305,9 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     }
 
   const float inv = __builtin_amdgcn_rcpf(sum_across_groups(ps));
-  const int qi = wave * 16 + l16;
-  if (qi < N) {
-    const uint32_t off = row_off(qi, a.o_sn);
+  if (wave * 16 + l16 < N) {
+    // Query row wave*16 + l16 is q_tok here, so its pixel is q_pix.
+    const uint32_t off = q_pix * (uint32_t)a.o_sn;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int c0 = cb * 16 + g * 4;
