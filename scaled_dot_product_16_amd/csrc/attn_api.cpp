@@ -180,6 +180,12 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
     a->madd_s1 = mask->add_strides[1];
   }
 
+  a->fd_h = make_fastdiv(a->H);
+  a->fd_nw = make_fastdiv(a->nw);
+  a->fd_nwx = make_fastdiv(a->nwx);
+  a->fd_win_w = make_fastdiv(a->win_w);
+  a->fd_gw = make_fastdiv(a->gw);
+
   // Offsets inside one (batch item, head) slice are 32-bit in the kernels.
   const attn_tensor_t* ts[4] = {q, k, v, o};
   for (const attn_tensor_t* t : ts)

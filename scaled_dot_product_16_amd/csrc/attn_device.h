@@ -101,6 +101,13 @@ __device__ __forceinline__ float dot4<F32E>(const void* x, int64_t i, const void
   return fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], a[0] * b[0])));
 }
 
+// n / d for 0 <= n < 2^31 with host-computed constants (multiply-high, add,
+// shift; scalar instructions when n is uniform).
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)n * f.mul) >> 32);
+  return (int)((hi + (uint32_t)n) >> f.shift);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup renumbering for the 8 XCDs of MI355X.  The dispatcher hands
 // workgroup i to XCD i % 8, and each XCD has its own L2.  The logical id
@@ -127,10 +134,10 @@ __device__ __forceinline__ int xcd_logical_id(int i, int n) {
 __device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_t sh, int64_t sn,
                                            int b, int h, int t) {
   if (!a.image) return (int64_t)b * sb + (int64_t)h * sh + (int64_t)t * sn;
-  const int img = b / a.nw;
+  const int img = fdiv(b, a.fd_nw);
   const int w = b - img * a.nw;
-  const int wy = w / a.nwx, wx = w - wy * a.nwx;
-  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
+  const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
   int y = wy * a.win_h + ty + a.shift_h;
   if (y >= a.img_h) y -= a.img_h;
   int x = wx * a.win_w + tx + a.shift_w;
@@ -142,14 +149,14 @@ __device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_
 // workgroup) and a 32-bit per-token offset; the host guarantees every
 // in-slice offset fits in 31 bits.
 __device__ __forceinline__ int64_t tok_base(const AttnArgs& a, int64_t sb, int64_t sh, int b, int h) {
-  const int img = a.image ? b / a.nw : b;
+  const int img = a.image ? fdiv(b, a.fd_nw) : b;
   return (int64_t)img * sb + (int64_t)h * sh;
 }
 __device__ __forceinline__ uint32_t tok_row(const AttnArgs& a, int64_t sn, int b, int t) {
   if (!a.image) return (uint32_t)t * (uint32_t)sn;
-  const int w = b % a.nw;
-  const int wy = w / a.nwx, wx = w - wy * a.nwx;
-  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  const int w = b - fdiv(b, a.fd_nw) * a.nw;
+  const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
+  const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
   int y = wy * a.win_h + ty + a.shift_h;
   if (y >= a.img_h) y -= a.img_h;
   int x = wx * a.win_w + tx + a.shift_w;
@@ -159,8 +166,8 @@ __device__ __forceinline__ uint32_t tok_row(const AttnArgs& a, int64_t sn, int b
 
 // Region (0..8) of token t of window w in the shifted image (SHIFT_REGIONS).
 __device__ __forceinline__ int region_of(const AttnArgs& a, int w, int t) {
-  const int wy = w / a.nwx, wx = w - wy * a.nwx;
-  const int ty = t / a.win_w, tx = t - ty * a.win_w;
+  const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
+  const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
   const int y = wy * a.win_h + ty, x = wx * a.win_w + tx;
   const int ry = y < a.img_h - a.win_h ? 0 : (y < a.img_h - a.shift_h ? 1 : 2);
   const int rx = x < a.img_w - a.win_w ? 0 : (x < a.img_w - a.shift_w ? 1 : 2);
@@ -208,11 +215,11 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
   bc.tbl = bc.relh = bc.relw = nullptr;
   if (needs_kinfo(BIAS, MASK)) {
     int* kinfo = (int*)p;
-    const int w = a.nw ? b % a.nw : 0;
+    const int w = a.nw ? b - fdiv(b, a.fd_nw) * a.nw : 0;
     for (int j = tid; j < a.Nk; j += NT) {
       int v = 0;
       if (BIAS == ATTN_BIAS_TABLE || BIAS == ATTN_BIAS_RELPOS) {
-        const int kh = j / a.gw;
+        const int kh = fdiv(j, a.fd_gw);
         v = kh | ((j - kh * a.gw) << 11);
       }
       if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) v |= region_of(a, w, j) << 22;
@@ -235,7 +242,7 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
     for (int e = tid; RELPOS_VALU && e < BM * nk; e += NT) {
       const int il = e % BM, kk = e / BM;
       const int qi = min(q0 + il, a.Nq - 1);
-      const int qh = qi / a.gw, qw = qi - qh * a.gw;
+      const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
       const int64_t qo = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
       const int64_t to = kk < a.gh ? (int64_t)(qh - kk + a.gh - 1) * a.D
                                    : (int64_t)(qw - (kk - a.gh) + a.gw - 1) * a.D;
@@ -265,10 +272,10 @@ __device__ __forceinline__ QInfo make_qinfo(const AttnArgs& a, int b, int qi, in
   qinf.tab = 0;
   qinf.region = 0;
   if (BIAS == ATTN_BIAS_TABLE) {
-    const int qh = qi / a.gw, qw = qi - qh * a.gw;
+    const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
     qinf.tab = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
   }
-  if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) qinf.region = region_of(a, b % a.nw, qi);
+  if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) qinf.region = region_of(a, b - fdiv(b, a.fd_nw) * a.nw, qi);
   return qinf;
 }
 
@@ -315,10 +322,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
-  const int qt = bid % a.n_qtiles;
-  bid /= a.n_qtiles;
-  const int h = bid % a.H;
-  const int b = bid / a.H;
+  const int qt_div = fdiv(bid, a.fd_qt);
+  const int qt = bid - qt_div * a.n_qtiles;
+  const int b = fdiv(qt_div, a.fd_h);
+  const int h = qt_div - b * a.H;
   const int q0 = qt * BM;
   const int D = a.D;
 

@@ -20,6 +20,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 template <typename K>
 int launch_kernel(K kernel, int threads, int bm, size_t dyn, AttnArgs a, hipStream_t s) {
   a.n_qtiles = (a.Nq + bm - 1) / bm;
+  a.fd_qt = make_fastdiv(a.n_qtiles);
   const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
   if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
   if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
@@ -58,6 +59,7 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
     if (a.Nq <= 64 && a.Nk <= 64) {
       AttnArgs w = a;
       w.n_qtiles = 1;
+      w.fd_qt = make_fastdiv(1);
       const int64_t blocks = (int64_t)a.B * a.H;
       if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
       w.n_blocks = (int)blocks;

@@ -7,6 +7,22 @@
 
 namespace attn {
 
+// Division by a runtime constant d >= 1 as a multiply-high, an add and a
+// shift: n / d == (mulhi(n, mul) + n) >> shift for 0 <= n < 2^31, with
+// shift = ceil(log2 d) and mul = floor(2^(32+shift) / d) + 1 - 2^32.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(int64_t d) {
+  if (d < 1) d = 1;
+  uint32_t s = 0;
+  while ((int64_t(1) << s) < d) ++s;
+  const unsigned __int128 m = ((unsigned __int128)1 << (32 + s)) / (uint64_t)d + 1;
+  return FastDiv{(uint32_t)(uint64_t)(m - ((unsigned __int128)1 << 32)), s};
+}
+
 // A validated call, flattened into plain integers and pointers.  Passed by
 // value to every kernel, so it must stay trivially copyable.
 struct AttnArgs {
@@ -42,6 +58,8 @@ struct AttnArgs {
   int64_t madd_n, madd_s0, madd_s1;
   float mask_value;
   float scale;
+  // Divisors used in index arithmetic.
+  FastDiv fd_h, fd_nw, fd_nwx, fd_win_w, fd_gw, fd_qt;
   // Filled by the launcher.
   int32_t n_qtiles;
   int32_t n_blocks;  // workgroups in the grid

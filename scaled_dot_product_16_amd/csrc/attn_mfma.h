@@ -165,10 +165,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g = lane >> 4;
   int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
-  const int qt = bid % a.n_qtiles;
-  bid /= a.n_qtiles;
-  const int h = bid % a.H;
-  const int b = bid / a.H;
+  const int qt_div = fdiv(bid, a.fd_qt);
+  const int qt = bid - qt_div * a.n_qtiles;
+  const int b = fdiv(qt_div, a.fd_h);
+  const int h = qt_div - b * a.H;
   const int q0 = qt * BM;
   const int wq0 = wave * NQB * 16;  // first query row of this wave inside the tile
 
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
-      const int qh = qi / a.gw, qw = qi - qh * a.gw;
+      const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
       float ext[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) ext[e] = 0.f;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       for (int qb = 0; qb < NQB; ++qb) {
         const int il = wq0 + qb * 16 + l16;
         const int qi = min(q0 + il, a.Nq - 1);
-        const int qh = qi / a.gw, qw = qi - qh * a.gw;
+        const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
           const int gg = part == 0 ? a.gh : a.gw;

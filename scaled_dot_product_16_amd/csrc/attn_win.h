@@ -60,10 +60,11 @@ struct WinPos {
 
 __device__ __forceinline__ WinPos win_pos(const AttnArgs& a, int b) {
   WinPos p;
-  const int nw = a.nw ? a.nw : 1;
-  p.img = b / nw;
-  const int w = b - p.img * nw;
-  const int wy = a.nwx ? w / a.nwx : 0;
+  // Without window geometry nw = nwx = 0 and both divisors are 1: the
+  // origin below is then (0, 0).
+  p.img = fdiv(b, a.fd_nw);
+  const int w = b - p.img * a.nw;
+  const int wy = fdiv(w, a.fd_nwx);
   const int wx = w - wy * a.nwx;
   p.y0 = wy * a.win_h;
   p.x0 = wx * a.win_w;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const int H = a.H, N = a.Nq, Nk = a.Nk;
   const int unit = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
-  const int b = unit / H, h = unit - (unit / H) * H;
+  const int b = fdiv(unit, a.fd_h), h = unit - b * H;
 
   // Token t < 64 of a window -> (row, column) for a row length n <= 1024: the
   // float quotient (t + 0.5) / n is within 2e-5 of the exact value and at
