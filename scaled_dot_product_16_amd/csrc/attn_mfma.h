@@ -424,14 +424,19 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // Transposing V reads: this lane addresses key row (l16 / 4) of its group's
   // 4-key slice and channel block 4 * (l16 % 4).
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
-  // S^T = K Q^T for one key tile.  The first product of each chain takes
-  // its addend directly: zero, or the row-form relative-position term.
+  // S^T = K Q^T for one key tile.  All K fragments are read first, so the
+  // LDS latency is paid once per tile.  The first product of each chain
+  // takes its addend directly: zero, or the row-form relative-position term.
   auto qk = [&](const uint16_t* Kt, f32x4 (&s)[4][NQB]) {
+    u32x4 kf[KCHT][4];
+#pragma unroll
+    for (int dc = 0; dc < KCHT; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kf[dc][kb] = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 kf = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           f32x4 c = s[kb][qb];
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
             if constexpr (RFAST) c = sinit[kb][qb];
             else c = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          s[kb][qb] = E::mfma(kf, qf[qb][dc], c);
+          s[kb][qb] = E::mfma(kf[dc][kb], qf[qb][dc], c);
         }
       }
     }
@@ -456,11 +461,25 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   }
 
   // One key tile t: row maxima and the lazy rescale of the output, then the
-  // exponentials and O^T += V^T P^T.
+  // exponentials and O^T += V^T P^T.  The V^T fragments are read from LDS
+  // before the softmax so their latency hides behind it.  Keys past Nk can
+  // only occur in the last tile (never with the 64-wide row form).
   f32x4 s_cur[4][NQB];
   const bool ragged = (a.Nk % BN) != 0;
-  auto tile = [&](int t) {
+  auto tile = [&](int t, auto last) {
+    constexpr bool LAST = decltype(last)::value && !RFAST;
     const int k0 = t * BN;
+    const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
+    u32x4 vf[2][CB];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
+        vf[kc][cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
     constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
     float y[NQB][16];
@@ -498,8 +517,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           }
           y[qb][kb * 4 + r] = v;
         }
-      if (ragged && t + 1 == ntiles) {
-        // Keys past Nk (last tile only) leave the softmax.
+      if (LAST && ragged) {
+        // Keys past Nk leave the softmax.
         const int lim = a.Nk - k0 - g * 4;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -524,27 +543,13 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       nb[qb] = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
       exp_pack(qb);
     }
-    // O^T += V^T P^T; V^T fragments come from transposing reads of the V tile.
-    const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
+    // O^T += V^T P^T.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
-        const u32x2 lo = lds_read_tr16(vp);
-        const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
-        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf, pf[qb][kc], o[cb][qb]);
-      }
-    // Interleave: one matrix instruction, then a few ALU instructions.
-    constexpr int kMfma = 2 * CB * NQB;
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    }
+        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf[kc][cb], pf[qb][kc], o[cb][qb]);
   };
 
   __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
@@ -568,19 +573,20 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   store_k(0, 0);
   store_v(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
-      load_k(t + 1);
-      load_v(t + 1);
-    }
+  // Tile t+1 streams from HBM into registers while tile t is computed, and
+  // is stored into the other LDS stage afterwards.  The last tile is peeled
+  // (it alone may hold keys past Nk).
+  for (int t = 0; t + 1 < ntiles; ++t) {
+    load_k(t + 1);
+    load_v(t + 1);
     qk(Ks + (t & 1) * C::K_ELEMS, s_cur);
-    tile(t);
-    if (t + 1 < ntiles) {
-      store_k((t + 1) & 1, t + 1);
-      store_v((t + 1) & 1);
-    }
+    tile(t, std::false_type{});
+    store_k((t + 1) & 1, t + 1);
+    store_v((t + 1) & 1);
     __syncthreads();
   }
+  qk(Ks + ((ntiles - 1) & 1) * C::K_ELEMS, s_cur);
+  tile(ntiles - 1, std::true_type{});
 
   // Epilogue: normalise by the row sum (row D of O^T, held by lane group
   // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).
