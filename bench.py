@@ -53,17 +53,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(w, launches_per_record: int = 1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+def traffic_record(w):
+    """HBM bytes per launch from the committed rocprofv3 counter record of this
+    workload, if it was taken on the current kernel sources (else None)."""
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}_traffic.json"))):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("workload") == w.name and rec.get("kernel_source_hash") == kernel_source_hash():
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, budget_s: float = 10.0):

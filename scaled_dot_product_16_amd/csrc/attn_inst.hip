@@ -48,7 +48,10 @@ using Elem = BF16;
 using Elem = F16;
 #endif
 constexpr int kNW = 4;
-constexpr int kNQB = 2;
+#ifndef ATTN_NQB
+#define ATTN_NQB 2  // 16-query blocks per wave
+#endif
+constexpr int kNQB = ATTN_NQB;
 
 template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
@@ -78,8 +81,29 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   }
   // Waves per SIMD the register allocation targets: the most that still
   // fit the tile state without spilling (checked per head dim).
+#ifdef ATTN_WPE  // one occupancy target for every path (tuning builds)
+  constexpr int kWpeNone = ATTN_WPE, kWpeRelpos = ATTN_WPE, kWpeAug = ATTN_WPE;
+#else
   constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);
   constexpr int kWpeRelpos = D <= 40 ? 3 : 2;
+  constexpr int kWpeAug = D <= 32 ? 3 : 2;
+#endif
+#ifndef ATTN_PP
+#define ATTN_PP 1
+#endif
+#ifndef ATTN_PP_MIN_KEYS
+#define ATTN_PP_MIN_KEYS 1024
+#endif
+  // Long key ranges with the 64-wide relative-position row form: eight-wave
+  // workgroups whose two wave groups alternate matrix and softmax phases
+  // (measured faster there; without a bias the four-wave kernel is faster).
+  if constexpr (ATTN_PP && !MASK && BIAS == ATTN_BIAS_RELPOS) {
+    if (a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256) {
+      using P = MfmaCfg<D, 8, kNQB>;
+      return launch_kernel(attn_fwd_mfma<Elem, D, 8, kNQB, BIAS, false, kRelRow64, 2>, P::NT, P::BM,
+                           mfma_lds_bytes<D, 8, kNQB, kRelRow64>(a), a, s);
+    }
+  }
   // Relative position: 64-wide grids take the row form, grids with
   // gh + gw <= 32 fold the bias into the QK^T contraction.
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
@@ -87,7 +111,7 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
       return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelRow64, kWpeRelpos>, C::NT,
                            C::BM, mfma_lds_bytes<D, kNW, kNQB, kRelRow64>(a), a, s);
     if (a.gh + a.gw <= 32)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, (D <= 32 ? 3 : 2)>, C::NT, C::BM,
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, kWpeAug>, C::NT, C::BM,
                            mfma_lds_bytes<D, kNW, kNQB, kRelAug>(a), a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;

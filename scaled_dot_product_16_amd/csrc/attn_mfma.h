@@ -41,9 +41,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #ifndef ATTN_ONES
 #define ATTN_ONES 1   // row sums from a ones row of V on the matrix cores
 #endif
-#ifndef ATTN_VPAD
-#define ATTN_VPAD 8   // V tile row padding (elements)
-#endif
+// V tile rows are padded to 16 elements past a multiple of 32 (row stride
+// of 8 or 24 dwords modulo 32): the transposing reads then fetch the 4 rows
+// x 4 column slices of each 16-lane group from distinct banks (also for 64
+// banks with 32 lanes per pass).
+__host__ __device__ constexpr int v_row_pad(int dv) { return ((16 - dv % 32) + 32) % 32; }
 #ifndef ATTN_KPAD
 #define ATTN_KPAD 8   // K tile row padding (elements)
 #endif
@@ -83,7 +85,7 @@ struct MfmaCfg {
   static constexpr int CB = ONES ? D / 16 + 1 : (D + 15) / 16;  // 16-row blocks of O^T
   static constexpr int DV = CB * 16;
   static constexpr int KROW = DK + ATTN_KPAD;  // LDS row strides (elements)
-  static constexpr int VROW = DV + ATTN_VPAD;
+  static constexpr int VROW = DV + v_row_pad(DV);
   static constexpr int RCH = D / 8;          // 16-byte chunks per token row
   static constexpr int NCH = BN * RCH;
   static constexpr int CPT = (NCH + NT - 1) / NT;
@@ -153,6 +155,8 @@ template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int W
 __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
   constexpr bool RFAST = RMODE == kRelRow64;
   constexpr bool RAUG = RMODE == kRelAug;
+  constexpr bool PP = NW == 8;  // ping-pong schedule of two wave groups
+  static_assert(!PP || !RAUG, "the ping-pong schedule is not built for the augmented contraction");
   using C = MfmaCfg<D, NW, NQB, RAUG>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, KCHT = C::KCHT, DK = C::DK,
                 CB = C::CB, DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH,
@@ -552,6 +556,85 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf[kc][cb], pf[qb][kc], o[cb][qb]);
   };
 
+  // Ping-pong schedule (8-wave workgroups): the softmax of tile t producing
+  // the packed probabilities, and the matrix phase PV(t-1) + QK(t).
+  u32x4 pp_p[NQB][2];
+  auto softmax_pp = [&](int t, auto last) {
+    constexpr bool LAST = decltype(last)::value && !RFAST;
+    const int k0 = t * BN;
+    constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
+    const float cy = kGenericBias ? 1.f : c2;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float y[16];
+      float hh = 0.f;
+      if constexpr (RFAST) hh = relh_lds[t * BM + wq0 + qb * 16 + l16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = s_cur[kb][qb][r];
+          if constexpr (kGenericBias) {
+            const int kj = k0 + kb * 16 + g * 4 + r;
+            v = fmaf(v, c2, bias_log2<E, BIAS, MASK, BM>(a, bc, qinf[qb], b, min(kj, a.Nk - 1)));
+          }
+          y[kb * 4 + r] = v;
+        }
+      if (LAST && ragged) {
+        const int lim = a.Nk - k0 - g * 4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * 16 + r >= lim) y[kb * 4 + r] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(y[0], y[1]), y[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[i]), y[i + 1]);
+      mx = max_across_groups(fmaxf(mx, y[15]));
+      const float mt = fmaf(mx, cy, hh);
+      if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
+        const float mn = fmaxf(m[qb], mt);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+        if constexpr (!C::ONES) l[qb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= alpha;
+      }
+      const float nb = hh - (m[qb] == -INFINITY ? 0.f : m[qb]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = __builtin_amdgcn_exp2f(fmaf(y[i], cy, nb));
+      if constexpr (!C::ONES) {
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps += y[i];
+        l[qb] += ps;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        pp_p[qb][kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
+                             E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
+    }
+  };
+  auto pv_pp = [&](int t) {
+    const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      u32x4 vf[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
+        vf[cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf[cb], pp_p[qb][kc], o[cb][qb]);
+    }
+  };
+
   __syncthreads();  // prologue scratch (overlaying the K/V tiles) is free now
   // Padding columns of the K and V tiles are never loaded: zero them once.
   // Column D of V is set to 1, so row D of O^T accumulates the row sum of
@@ -570,6 +653,43 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     }
   }
 
+  if constexpr (PP) {
+    // Two groups of four waves (one wave of each per SIMD) alternate between
+    // a matrix phase, PV(t-1) + QK(t), and a softmax phase, separated by
+    // workgroup barriers; group B runs one phase behind group A, so while
+    // one wave of a SIMD keeps the matrix cores busy the other one runs its
+    // exponentials.  Tile t's K and tile t-1's V are read during phases 2t
+    // and 2t+1; K(t+1) and V(t) are written into the other stages during
+    // phase 2t+1 (by group A after its softmax, by group B after its matrix
+    // phase), which is the last use of those stages' previous contents.
+    const bool grp_b = wave >= NW / 2;
+    // V(0) stays in registers (loaded before the prologue) until phase 1.
+    store_k(0, 0);
+    if (ntiles > 1) load_k(1);
+    auto store_next = [&](int t) {
+      if (t + 1 < ntiles) store_k((t + 1) & 1, t + 1);
+      store_v(t & 1);
+      if (t + 2 < ntiles) load_k(t + 2);
+      if (t + 1 < ntiles) load_v(t + 1);
+    };
+    __syncthreads();
+    if (grp_b) __syncthreads();
+    auto iter = [&](int t, auto last) {
+      __builtin_amdgcn_s_setprio(1);
+      if (t > 0) pv_pp(t - 1);
+      qk(Ks + (t & 1) * C::K_ELEMS, s_cur);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp_b) store_next(t);
+      __syncthreads();
+      softmax_pp(t, last);
+      if (!grp_b) store_next(t);
+      __syncthreads();
+    };
+    for (int t = 0; t + 1 < ntiles; ++t) iter(t, std::false_type{});
+    iter(ntiles - 1, std::true_type{});
+    pv_pp(ntiles - 1);
+    if (!grp_b) __syncthreads();
+  } else {
   store_k(0, 0);
   store_v(0);
   __syncthreads();
@@ -587,6 +707,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   }
   qk(Ks + ((ntiles - 1) & 1) * C::K_ELEMS, s_cur);
   tile(ntiles - 1, std::true_type{});
+  }
 
   // Epilogue: normalise by the row sum (row D of O^T, held by lane group
   // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).

@@ -27,7 +27,7 @@ struct WinCfg {
   static constexpr int CB = (D + 15) / 16;
   static constexpr int DV = CB * 16;
   static constexpr int KROW = DK + 8;
-  static constexpr int VROW = DV + 8;
+  static constexpr int VROW = DV + v_row_pad(DV);
   static constexpr int RCH = D / 8;
   static constexpr int NCH = 64 * RCH;               // 16-byte chunks of a 64-token tile
   static constexpr int CPT = (NCH + NT - 1) / NT;    // per thread

@@ -60,7 +60,9 @@ def test_workload_sampled(key):
 # Reduced-size sweeps (several tiles and ragged tails)
 # ---------------------------------------------------------------------------
 
-SHAPES = [(1, 1), (7, 300), (300, 77), (129, 64), (200, 200), (64, 1)]
+# (300, 1100): long key range with a ragged last key tile and a partial
+# query tile.
+SHAPES = [(1, 1), (7, 300), (300, 77), (129, 64), (200, 200), (64, 1), (300, 1100)]
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
@@ -80,6 +82,7 @@ BIAS_CASES = [
     ("relpos", (6, 10), "none", None),
     ("relpos", (14, 14), "none", None),
     ("relpos", (3, 50), "none", None),
+    ("relpos", (17, 64), "none", None),  # 64-wide grid, long key range (two-group schedule)
     ("additive", None, "none", None),
     ("none", None, "additive", None),
     ("additive", None, "additive", None),
