@@ -348,6 +348,13 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
   const float sl2 = a.scale * kLog2e;
   const int ntiles = (a.Nk + kF32BN - 1) / kF32BN;
   const int rch = D / 4;
+  // Columns D..DMAX of the tiles are never loaded: zero them once, so the
+  // dot products below run over DMAX columns without per-column branches.
+  for (int i = tid; i < kF32BN * (DMAX - D); i += kF32Threads) {
+    const int row = i / (DMAX - D), col = D + i % (DMAX - D);
+    Ks[row][col] = 0.f;
+    Vs[row][col] = 0.f;
+  }
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     for (int ch = tid; ch < kF32BN * rch; ch += kF32Threads) {
@@ -370,13 +377,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < DMAX; c += 4) {
-        if (c < D) {
-          const f32x4 kv = *(const f32x4*)&Ks[j][c];
-          dot = fmaf(qv[c], kv[0], dot);
-          dot = fmaf(qv[c + 1], kv[1], dot);
-          dot = fmaf(qv[c + 2], kv[2], dot);
-          dot = fmaf(qv[c + 3], kv[3], dot);
-        }
+        const f32x4 kv = *(const f32x4*)&Ks[j][c];
+        dot = fmaf(qv[c], kv[0], dot);
+        dot = fmaf(qv[c + 1], kv[1], dot);
+        dot = fmaf(qv[c + 2], kv[2], dot);
+        dot = fmaf(qv[c + 3], kv[3], dot);
       }
       float v = dot * sl2;
       if (BIAS != ATTN_BIAS_NONE || MASK)
@@ -387,24 +392,22 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
     }
     const float mnew = fmaxf(m, mx);
     const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f(m - mref);
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     m = mnew;
     l *= alpha;
 #pragma unroll
     for (int c = 0; c < DMAX; ++c) acc[c] *= alpha;
 #pragma unroll
     for (int j = 0; j < kF32BN; ++j) {
-      const float p = exp2f(s[j] - mref);
+      const float p = __builtin_amdgcn_exp2f(s[j] - mref);
       l += p;
 #pragma unroll
       for (int c = 0; c < DMAX; c += 4) {
-        if (c < D) {
-          const f32x4 vv = *(const f32x4*)&Vs[j][c];
-          acc[c] = fmaf(p, vv[0], acc[c]);
-          acc[c + 1] = fmaf(p, vv[1], acc[c + 1]);
-          acc[c + 2] = fmaf(p, vv[2], acc[c + 2]);
-          acc[c + 3] = fmaf(p, vv[3], acc[c + 3]);
-        }
+        const f32x4 vv = *(const f32x4*)&Vs[j][c];
+        acc[c] = fmaf(p, vv[0], acc[c]);
+        acc[c + 1] = fmaf(p, vv[1], acc[c + 1]);
+        acc[c + 2] = fmaf(p, vv[2], acc[c + 2]);
+        acc[c + 3] = fmaf(p, vv[3], acc[c + 3]);
       }
     }
   }
