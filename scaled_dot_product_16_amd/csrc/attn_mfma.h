@@ -431,16 +431,20 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // S^T = K Q^T for one key tile.  All K fragments are read first, so the
   // LDS latency is paid once per tile.  The first product of each chain
   // takes its addend directly: zero, or the row-form relative-position term.
-  auto qk = [&](const uint16_t* Kt, f32x4 (&s)[4][NQB]) {
+  // nkb: key blocks of 16 holding keys below Nk (4 except in a ragged last
+  // tile, whose empty blocks are skipped: their scores are masked anyway).
+  auto qk = [&](const uint16_t* Kt, f32x4 (&s)[4][NQB], int nkb = 4) {
     u32x4 kf[KCHT][4];
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kf[dc][kb] = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+      for (int kb = 0; kb < 4; ++kb)
+        if (kb < nkb) kf[dc][kb] = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        if (kb >= nkb) continue;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           f32x4 c = s[kb][qb];
@@ -473,12 +477,15 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   auto tile = [&](int t, auto last) {
     constexpr bool LAST = decltype(last)::value && !RFAST;
     const int k0 = t * BN;
+    // Keys 32..63 of a ragged last tile may all lie past Nk.
+    const int nkc = LAST && k0 + 32 >= a.Nk ? 1 : 2;
     const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
     u32x4 vf[2][CB];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
+        if (kc >= nkc) continue;
         const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
         const u32x2 lo = lds_read_tr16(vp);
         const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
@@ -551,9 +558,11 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb) {
+        if (kc >= nkc) continue;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) o[cb][qb] = E::mfma(vf[kc][cb], pf[qb][kc], o[cb][qb]);
+      }
   };
 
   // Ping-pong schedule (8-wave workgroups): the softmax of tile t producing
@@ -696,17 +705,24 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // Tile t+1 streams from HBM into registers while tile t is computed, and
   // is stored into the other LDS stage afterwards.  The last tile is peeled
   // (it alone may hold keys past Nk).
+  // A wave whose queries all lie past Nq only helps with the tile loads.
+  const bool active = q0 + wq0 < a.Nq;
   for (int t = 0; t + 1 < ntiles; ++t) {
     load_k(t + 1);
     load_v(t + 1);
-    qk(Ks + (t & 1) * C::K_ELEMS, s_cur);
-    tile(t, std::false_type{});
+    if (active) {
+      qk(Ks + (t & 1) * C::K_ELEMS, s_cur);
+      tile(t, std::false_type{});
+    }
     store_k((t + 1) & 1, t + 1);
     store_v((t + 1) & 1);
     __syncthreads();
   }
-  qk(Ks + ((ntiles - 1) & 1) * C::K_ELEMS, s_cur);
-  tile(ntiles - 1, std::true_type{});
+  if (active) {
+    const int klast = (ntiles - 1) * BN;
+    qk(Ks + ((ntiles - 1) & 1) * C::K_ELEMS, s_cur, RFAST ? 4 : min(4, (a.Nk - klast + 15) / 16));
+    tile(ntiles - 1, std::true_type{});
+  }
   }
 
   // Epilogue: normalise by the row sum (row D of O^T, held by lane group
