@@ -248,6 +248,12 @@ def main():
     if w.grid:
         cfg["grid"] = list(w.grid)
 
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "hip": torch.version.hip, "torch": torch.__version__,
+              "peaks": {"hbm_GBs": PEAK_HBM_GBS, "bf16_fp16_mfma_TFLOPs": PEAK_MFMA_TFLOPS,
+                        "fp32_TFLOPs": PEAK_F32_TFLOPS}}
     line = {
         "metric": METRIC,
         "value": round(tflops, 4),
@@ -266,6 +272,7 @@ def main():
         "flops_per_step": flops,
         "algorithmic_bytes_per_step": nbytes,
         "rotating_input_sets": n_sets,
+        "device": device,
         "roofline": {
             "bound": bound,
             "achieved": round(achieved, 3),
