@@ -36,6 +36,29 @@ int launch_kernel(K kernel, int threads, int bm, size_t dyn, AttnArgs a, hipStre
 #if INST_DT == 0
 template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
+  // Windows of at most 64 tokens: one workgroup per (window, head) unit on
+  // the fp32 matrix instructions.
+  if constexpr (BIAS != ATTN_BIAS_RELPOS) {
+    if (a.Nq <= 64 && a.Nk <= 64) {
+      AttnArgs w = a;
+      w.n_qtiles = 1;
+      w.fd_qt = make_fastdiv(1);
+      const int64_t blocks = (int64_t)a.B * a.H;
+      if (blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
+      w.n_blocks = (int)blocks;
+      const size_t dyn = win_lds_bytes(a, WinCfgF32<INST_D>::KV_BYTES);
+      if (dyn > kMaxLds) return ATTN_E_UNSUPPORTED;
+      auto kern = !MASK ? attn_fwd_win<F32E, INST_D, BIAS, ATTN_MASK_NONE>
+                  : a.mask_kind == ATTN_MASK_ADDITIVE ? attn_fwd_win<F32E, INST_D, BIAS, ATTN_MASK_ADDITIVE>
+                                                      : attn_fwd_win<F32E, INST_D, BIAS, ATTN_MASK_SHIFT_REGIONS>;
+      if (dyn > 32 * 1024 &&
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
+              hipSuccess)
+        return ATTN_E_LAUNCH;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWinWaves * 64), dyn, s, w);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+    }
+  }
   constexpr size_t st = 2 * (size_t)kF32BN * INST_D * 4;
   if (dyn_lds_bytes(a, kF32Threads) + st > kMaxLds) return ATTN_E_UNSUPPORTED;
   return launch_kernel(attn_fwd_f32<INST_D, BIAS, MASK>, kF32Threads, kF32Threads,

@@ -13,6 +13,8 @@
 #ifndef ATTN_WIN_H_
 #define ATTN_WIN_H_
 
+#include <type_traits>
+
 #include "attn_mfma.h"
 
 namespace attn {
@@ -32,6 +34,20 @@ struct WinCfg {
   static constexpr int NCH = 64 * RCH;               // 16-byte chunks of a 64-token tile
   static constexpr int CPT = (NCH + NT - 1) / NT;    // per thread
   static constexpr size_t KV_BYTES = (size_t)64 * (KROW + VROW) * 2;
+};
+
+// fp32 units on v_mfma_f32_16x16x4_f32: D is the head-dim bucket DMAX (the
+// call's head dim is at most DMAX; missing columns are zero).  K is stored
+// row-major, V transposed (d rows of 64 keys) so that one 16-byte LDS read
+// yields the A operands of four consecutive K-steps.
+template <int DMAX>
+struct WinCfgF32 {
+  static constexpr int NT = kWinWaves * 64;
+  static constexpr int QC = DMAX / 4;        // K-steps of QK^T; Q floats per lane
+  static constexpr int CB = DMAX / 16;       // 16-row blocks of O^T
+  static constexpr int KROW = DMAX + 4;      // floats
+  static constexpr int VTROW = 64 + 4;       // floats (keys)
+  static constexpr size_t KV_BYTES = ((size_t)64 * KROW + (size_t)DMAX * VTROW) * 4;
 };
 
 // Entries of the bias table of a window unit: the relative-position table
@@ -102,17 +118,25 @@ __device__ __forceinline__ int win_region(const AttnArgs& a, const WinPos& p, in
 //                              + [4n - idx(k) - n*(3*ry_k + rx_k)],
 // with idx(q) = (qh+gh-1)(2gw-1) + qw+gw-1 and idx(k) = kh(2gw-1) + kw, so
 // each score costs one add and one LDS read.
+//
+// E = F32E selects the fp32 form (WinCfgF32): same structure, with
+// v_mfma_f32_16x16x4_f32 products and fp32 tiles.
 template <class E, int D, int BIAS, int MASKK>
 __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
-  using C = WinCfg<D>;
-  constexpr int NT = C::NT, KCH = C::KCH, CB = C::CB, KROW = C::KROW, VROW = C::VROW,
+  constexpr bool F32 = std::is_same<E, F32E>::value;
+  using C = WinCfg<F32 ? 32 : D>;
+  using CF = WinCfgF32<F32 ? D : 32>;
+  constexpr int NT = C::NT, KCH = C::KCH, CB = F32 ? CF::CB : C::CB, KROW = C::KROW, VROW = C::VROW,
                 RCH = C::RCH, NCH = C::NCH, CPT = C::CPT, DK = C::DK, DV = C::DV;
+  constexpr size_t kKvBytes = F32 ? CF::KV_BYTES : C::KV_BYTES;
   constexpr bool kTab = BIAS == ATTN_BIAS_TABLE || MASKK == ATTN_MASK_SHIFT_REGIONS;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   uint16_t* Ks = (uint16_t*)lds;        // [64][KROW]
   uint16_t* Vs = Ks + 64 * KROW;        // [64][VROW]
-  int* kinfo = (int*)(lds + C::KV_BYTES);              // per key: byte offset of its table part
-  constexpr int kTabByte = (int)C::KV_BYTES + 64 * 4;  // 9 table copies, log2 units
+  float* Kf = (float*)lds;              // fp32: [64][CF::KROW]
+  float* Vtf = Kf + 64 * CF::KROW;      // fp32: [DMAX][CF::VTROW], V transposed
+  int* kinfo = (int*)(lds + kKvBytes);               // per key: byte offset of its table part
+  constexpr int kTabByte = (int)kKvBytes + 64 * 4;   // 9 table copies, log2 units
   float* tbl = (float*)(lds + kTabByte);
 
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
@@ -142,31 +166,56 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     split(t, ty, tx);
     return win_tok_off(a, pos, ty, tx, 1);
   };
-  const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh);
-  const uint16_t* kp = (const uint16_t*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh);
-  const uint16_t* vp = (const uint16_t*)a.v + ((int64_t)bimg * a.v_sb + (int64_t)h * a.v_sh);
-  uint16_t* op = (uint16_t*)a.o + ((int64_t)bimg * a.o_sb + (int64_t)h * a.o_sh);
+  constexpr int ES = F32 ? 4 : 2;  // element bytes
+  const char* qp = (const char*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh) * ES;
+  const char* kp = (const char*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh) * ES;
+  const char* vp = (const char*)a.v + ((int64_t)bimg * a.v_sb + (int64_t)h * a.v_sh) * ES;
+  char* op = (char*)a.o + ((int64_t)bimg * a.o_sb + (int64_t)h * a.o_sh) * ES;
 
   // Global loads first.  Token rows past N are clamped to the last token, so
   // every load is unconditional; those keys start from -inf below, so their
   // probabilities are exactly zero and their finite values never reach O.
-  u32x4 kreg[CPT], vreg[CPT];
+  constexpr int FCH = F32 ? 64 * CF::QC : 1;          // fp32: 16-byte chunks of a tile (QC per row)
+  constexpr int FCPT = (FCH + NT - 1) / NT;
+  u32x4 kreg[F32 ? FCPT : CPT], vreg[F32 ? FCPT : CPT];
+  if constexpr (F32) {
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = min(tid + c * NT, NCH - 1);
-    const uint32_t pix = tok_pix(min(ch / RCH, Nk - 1));
-    const uint32_t col = (uint32_t)((ch % RCH) * 8);
-    kreg[c] = *(const u32x4*)(kp + (pix * (uint32_t)a.k_sn + col));
-    vreg[c] = *(const u32x4*)(vp + (pix * (uint32_t)a.v_sn + col));
+    for (int c = 0; c < FCPT; ++c) {
+      const int ch = min(tid + c * NT, FCH - 1);
+      const int c4 = (ch % CF::QC) * 4;
+      const uint32_t pix = tok_pix(min(ch / CF::QC, Nk - 1));
+      const int col = c4 < a.D ? c4 : 0;
+      kreg[c] = *(const u32x4*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * 4);
+      vreg[c] = *(const u32x4*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * 4);
+      if (c4 >= a.D) kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = min(tid + c * NT, NCH - 1);
+      const uint32_t pix = tok_pix(min(ch / RCH, Nk - 1));
+      const uint32_t col = (uint32_t)((ch % RCH) * 8);
+      kreg[c] = *(const u32x4*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * 2);
+      vreg[c] = *(const u32x4*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * 2);
+    }
   }
   const int q_tok = min(wave * 16 + l16, N - 1);
   const uint32_t q_pix = tok_pix(q_tok);
   const uint32_t q_off = q_pix * (uint32_t)a.q_sn;
-  u32x4 qf[KCH];
+  u32x4 qf[F32 ? CF::QC / 4 : KCH];
+  if constexpr (F32) {
+    // K-step dc of this lane's group g covers column g*QC + dc.
 #pragma unroll
-  for (int dc = 0; dc < KCH; ++dc) {
-    const int d0 = dc * 32 + g * 8;
-    qf[dc] = d0 < D ? *(const u32x4*)(qp + (q_off + (uint32_t)d0)) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < CF::QC / 4; ++j) {
+      const int d0 = g * CF::QC + 4 * j;
+      qf[j] = d0 < a.D ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 4) : u32x4{0, 0, 0, 0};
+    }
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      qf[dc] = d0 < D ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 2) : u32x4{0, 0, 0, 0};
+    }
   }
 
   // Only windows on the last window row or column of the shifted image hold
@@ -200,19 +249,32 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
       kinfo[tid] = part * 4;
     }
   }
-  // Padding columns of the tiles are never loaded: zero them.
-  if constexpr (DK > D) {
-    for (int i = tid; i < 64 * (DK - D); i += NT) Ks[(i / (DK - D)) * KROW + D + i % (DK - D)] = 0;
-  }
-  if constexpr (DV > D) {
-    for (int i = tid; i < 64 * (DV - D); i += NT) Vs[(i / (DV - D)) * VROW + D + i % (DV - D)] = 0;
-  }
+  if constexpr (F32) {
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * NT;
-    if (ch < NCH) {
-      *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = kreg[c];
-      *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = vreg[c];
+    for (int c = 0; c < FCPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < FCH) {
+        const int row = ch / CF::QC, c4 = (ch % CF::QC) * 4;
+        *(u32x4*)&Kf[row * CF::KROW + c4] = kreg[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Vtf[(c4 + e) * CF::VTROW + row] = __uint_as_float(vreg[c][e]);
+      }
+    }
+  } else {
+    // Padding columns of the tiles are never loaded: zero them.
+    if constexpr (DK > D) {
+      for (int i = tid; i < 64 * (DK - D); i += NT) Ks[(i / (DK - D)) * KROW + D + i % (DK - D)] = 0;
+    }
+    if constexpr (DV > D) {
+      for (int i = tid; i < 64 * (DV - D); i += NT) Vs[(i / (DV - D)) * VROW + D + i % (DV - D)] = 0;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < NCH) {
+        *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = kreg[c];
+        *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = vreg[c];
+      }
     }
   }
   __syncthreads();
@@ -229,10 +291,20 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
       for (int r = 0; r < 4; ++r)
         if (kb * 16 + g * 4 + r >= Nk) s[kb][r] = -INFINITY;
     }
+    if constexpr (F32) {
 #pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
-      const u32x4 kf = *(const u32x4*)&Ks[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
-      s[kb] = E::mfma(kf, qf[dc], s[kb]);
+      for (int j = 0; j < CF::QC / 4; ++j) {
+        const f32x4 kv = *(const f32x4*)&Kf[(kb * 16 + l16) * CF::KROW + g * CF::QC + 4 * j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], __uint_as_float(qf[j][e]), s[kb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        const u32x4 kf = *(const u32x4*)&Ks[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+        s[kb] = E::mfma(kf, qf[dc], s[kb]);
+      }
     }
   }
 
@@ -284,37 +356,50 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     y[i] = __builtin_amdgcn_exp2f(y[i] - mx);
     ps += y[i];
   }
-  u32x4 pf[2];
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
-    pf[kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
-                   E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
-
-  // O^T += V^T P^T with transposing reads of the V tile.
   f32x4 o[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  if constexpr (F32) {
+    // O^T += V^T P^T over K-steps of 4 keys {kb*16 + 4k + r : k = 0..3}:
+    // this lane's own probability of key kb*16 + 4g + r is the B operand.
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const uint16_t* vptr = Vs + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
-      const u32x2 lo = lds_read_tr16(vptr);
-      const u32x2 hi = lds_read_tr16(vptr + 16 * VROW);
-      o[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kc], o[cb]);
-    }
+      for (int cb = 0; cb < CB; ++cb) {
+        const f32x4 vt = *(const f32x4*)&Vtf[(cb * 16 + l16) * CF::VTROW + kb * 16 + g * 4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[r], y[kb * 4 + r], o[cb], 0, 0, 0);
+      }
+  } else {
+    u32x4 pf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+      pf[kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
+                     E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
+    // O^T += V^T P^T with transposing reads of the V tile.
+    const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t* vptr = Vs + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+        const u32x2 lo = lds_read_tr16(vptr);
+        const u32x2 hi = lds_read_tr16(vptr + 16 * VROW);
+        o[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kc], o[cb]);
+      }
+  }
 
-  const float inv = __builtin_amdgcn_rcpf(sum_across_groups(ps));
+  const float inv = F32 ? 1.f / sum_across_groups(ps) : __builtin_amdgcn_rcpf(sum_across_groups(ps));
   if (wave * 16 + l16 < N) {
     // Query row wave*16 + l16 is q_tok here, so its pixel is q_pix.
     const uint32_t off = q_pix * (uint32_t)a.o_sn;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int c0 = cb * 16 + g * 4;
-      if (c0 < D) {
+      if (c0 < (F32 ? a.D : D)) {
         const f32x4 v = o[cb] * inv;
-        *(u32x2*)(op + (off + (uint32_t)c0)) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+        if constexpr (F32) *(f32x4*)(op + (size_t)(off + c0) * 4) = v;
+        else *(u32x2*)(op + (size_t)(off + c0) * 2) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
       }
     }
   }
