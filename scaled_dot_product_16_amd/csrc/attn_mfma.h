@@ -98,6 +98,10 @@ struct MfmaCfg {
       ((KV_BYTES > SCRATCH_BYTES ? KV_BYTES : SCRATCH_BYTES) + 15) / 16 * 16;
 };
 
+// Scratch row (floats) of the augmented prologue: the <= 62 rows of the
+// stacked table [Rh; Rw] for one query, padded to keep 16-byte stores aligned.
+constexpr int kAugGrow = 68;
+
 // Row length (floats) of the relative-position prologue scratch.
 inline __host__ __device__ int relpos_grow(const AttnArgs& a) {
   const int m = 2 * (a.gh > a.gw ? a.gh : a.gw) - 1;
@@ -110,7 +114,7 @@ __host__ __device__ inline size_t mfma_lds_bytes(const AttnArgs& a) {
   using C = MfmaCfg<D, NW, NQB, RMODE == kRelAug>;
   if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
   if (RMODE == kRelAug) {
-    const size_t scr = (size_t)NW * 16 * relpos_grow(a) * 4;  // overlays the K/V tiles
+    const size_t scr = (size_t)NW * 16 * kAugGrow * 4;  // overlays the K/V tiles
     return C::KV_BYTES > scr ? C::KV_BYTES : scr;
   }
   size_t n = C::KV_BYTES + dyn_lds_bytes(a, C::BM);
@@ -257,6 +261,26 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = vreg[c];
   };
 
+  // Augmented relative position: A fragments of the stacked table [Rh; Rw]
+  // ((2gh-1) + (2gw-1) <= 62 rows, so four 16-row blocks), issued before the
+  // K/V tile loads so that the prologue waits for these and Q only.
+  constexpr int RFB = RAUG ? 4 : 1;
+  u32x4 rfrag[RFB][RAUG ? KCH : 1];
+  if constexpr (RAUG) {
+    const int nh = 2 * a.gh - 1, nrows = nh + 2 * a.gw - 1;
+#pragma unroll
+    for (int mb = 0; mb < RFB; ++mb) {
+      const int m = mb * 16 + l16;
+      const uint16_t* row = m < nh ? (const uint16_t*)a.rh + (int64_t)m * D
+                                   : (const uint16_t*)a.rw + (int64_t)(m < nrows ? m - nh : 0) * D;
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        rfrag[mb][dc] = m < nrows && d0 < D ? *(const u32x4*)(row + d0) : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
   // The first K/V tile is in flight while the bias prologue runs.
   load_k(0);
   load_v(0);
@@ -325,50 +349,40 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     // Relative position folded into the contraction: the extra Q chunk holds
     // relh[i][0..gh) and relw[i][0..gw) divided by the scale (the K tile's
     // extra chunk holds one-hots at kh and gh + kw), so QK^T directly gives
-    // q.k + (relh + relw) / scale.  G = R Q^T comes from the matrix cores and
-    // is gathered per lane through this wave's scratch rows.
-    const int grow = relpos_grow(a);
-    float* gscr = (float*)lds + wave * 16 * grow;  // overlays the K/V tiles
+    // q.k + (relh + relw) / scale.  G = [Rh; Rw] Q^T comes from the matrix
+    // cores and is gathered per lane through this wave's scratch rows.
+    float* gscr = (float*)lds + wave * 16 * kAugGrow;  // overlays the K/V tiles
+    const int nh = 2 * a.gh - 1, nrows = nh + 2 * a.gw - 1;
     const float inv_scale = 1.f / a.scale;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
       const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
+#pragma unroll
+      for (int mb = 0; mb < RFB; ++mb) {
+        if (mb * 16 >= nrows) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) acc = E::mfma(rfrag[mb][dc], qf[qb][dc], acc);
+        *(f32x4*)&gscr[l16 * kAugGrow + mb * 16 + g * 4] = acc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Extension column k = g*8 + e: relh[kh = k] (stacked row qh - kh + gh - 1)
+      // or relw[kw = k - gh] (stacked row nh + qw - kw + gw - 1).
       float ext[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ext[e] = 0.f;
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const int gg = part == 0 ? a.gh : a.gw;
-        const uint16_t* tab = (const uint16_t*)(part == 0 ? a.rh : a.rw);
-        for (int mb = 0; mb * 16 < 2 * gg - 1; ++mb) {
-          const int m_row = mb * 16 + l16;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int dc = 0; dc < KCH; ++dc) {
-            const int d0 = dc * 32 + g * 8;
-            u32x4 af = {0, 0, 0, 0};
-            if (m_row < 2 * gg - 1 && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
-            acc = E::mfma(af, qf[qb][dc], acc);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) gscr[l16 * grow + mb * 16 + g * 4 + r] = acc[r];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Extension column k = g*8 + e: relh[kh = k] or relw[kw = k - gh].
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = g * 8 + e;
-          const int kk = part == 0 ? k : k - a.gh;
-          const int qc = part == 0 ? qh : qw;
-          if (kk >= 0 && kk < gg) ext[e] = gscr[l16 * grow + qc - kk + gg - 1] * inv_scale;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int e = 0; e < 8; ++e) {
+        const int k = g * 8 + e, kw = k - a.gh;
+        const bool in = k < a.gh + a.gw;
+        const int m = !in ? 0 : k < a.gh ? qh - k + a.gh - 1 : nh + qw - kw + a.gw - 1;
+        const float gv = gscr[l16 * kAugGrow + m] * inv_scale;
+        ext[e] = in ? gv : 0.f;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       qf[qb][KCH] = u32x4{E::pack2(ext[0], ext[1]), E::pack2(ext[2], ext[3]), E::pack2(ext[4], ext[5]),
                           E::pack2(ext[6], ext[7])};
     }
