@@ -281,6 +281,39 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     }
   }
 
+  // Row form (64-wide grids): A fragments of all 127 Rw rows and of the
+  // first 64 Rh rows this wave needs.  A wave's 32 queries start at a
+  // multiple of 32 and Nq = 64 gh, so they lie in one grid row qh_w (clamped
+  // queries past Nq fall in the last row, as does Nq - 1) and share Rh rows.
+  constexpr int RWB = RFAST ? 8 : 1, RHB = RFAST ? 4 : 1, RKC = RFAST ? KCH : 1;
+  u32x4 wfrag[RWB][RKC], hfrag[RHB][RKC];
+  const int qh_w = min(q0 + wq0, a.Nq - 1) >> 6;
+  auto load_hfrag = [&](int mb0) {
+#pragma unroll
+    for (int mb = 0; mb < RHB; ++mb) {
+      const int kh_row = (mb0 + mb) * 16 + l16;
+      const uint16_t* row = (const uint16_t*)a.rh + (int64_t)(kh_row < a.gh ? qh_w + a.gh - 1 - kh_row : 0) * D;
+#pragma unroll
+      for (int dc = 0; dc < RKC; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        hfrag[mb][dc] = kh_row < a.gh && d0 < D ? *(const u32x4*)(row + d0) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  if constexpr (RFAST) {
+#pragma unroll
+    for (int mb = 0; mb < RWB; ++mb) {
+      const int m_row = mb * 16 + l16;
+#pragma unroll
+      for (int dc = 0; dc < RKC; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        wfrag[mb][dc] = m_row < 127 && d0 < D ? *(const u32x4*)((const uint16_t*)a.rw + (int64_t)m_row * D + d0)
+                                              : u32x4{0, 0, 0, 0};
+      }
+    }
+    load_hfrag(0);
+  }
+
   // The first K/V tile is in flight while the bias prologue runs.
   load_k(0);
   load_v(0);
@@ -293,56 +326,50 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     // Relative position for a 64-wide grid (tile t = grid row t).
     float* relh_tab = (float*)(lds + C::BASE_BYTES);  // [gh][BM], log2 units
     float* gscr = (float*)lds + wave * 16 * C::GROW;   // per-wave scratch, overlays K/V
-    const uint16_t* rh = (const uint16_t*)a.rh;
-    const uint16_t* rw = (const uint16_t*)a.rw;
     const float inv_scale = 1.f / a.scale;
+    // relh[i][kh] = Rh[qh + gh - 1 - kh] . q_i, as C[kh][i] of an MFMA product.
+    for (int mb0 = 0; mb0 * 16 < a.gh; mb0 += RHB) {
+      if (mb0 > 0) load_hfrag(mb0);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int il0 = wq0 + qb * 16;
+#pragma unroll
+        for (int mb = 0; mb < RHB; ++mb) {
+          if ((mb0 + mb) * 16 >= a.gh) break;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < KCH; ++dc) acc = E::mfma(hfrag[mb][dc], qf[qb][dc], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kh = (mb0 + mb) * 16 + g * 4 + r;
+            if (kh < a.gh) relh_tab[kh * BM + il0 + l16] = acc[r] * kLog2e;
+          }
+        }
+      }
+    }
+    // G[m][i] = Rw[m] . q_i for every table row m, then the per-lane gather
+    // relw[i][kw] = G[qw_i + 63 - kw][i] for this lane's 16 keys.
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      const int il0 = wq0 + qb * 16;
-      const int qblk = min(q0 + il0, a.Nq - 1);
-      const int qh = qblk >> 6;  // shared by the 16 queries of the block
-      // relh[i][kh] = Rh[qh + gh - 1 - kh] . q_i, as C[kh][i] of an MFMA product.
-      for (int mb = 0; mb * 16 < a.gh; ++mb) {
-        const int kh_row = mb * 16 + l16;
+#pragma unroll
+      for (int mb = 0; mb < RWB; ++mb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < KCH; ++dc) {
-          const int d0 = dc * 32 + g * 8;
-          u32x4 af = {0, 0, 0, 0};
-          if (kh_row < a.gh && d0 < D)
-            af = *(const u32x4*)(rh + (int64_t)(qh + a.gh - 1 - kh_row) * D + d0);
-          acc = E::mfma(af, qf[qb][dc], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kh = mb * 16 + g * 4 + r;
-          if (kh < a.gh) relh_tab[kh * BM + il0 + l16] = acc[r] * kLog2e;
-        }
+        for (int dc = 0; dc < KCH; ++dc) acc = E::mfma(wfrag[mb][dc], qf[qb][dc], acc);
+        *(f32x4*)&gscr[l16 * C::GROW + mb * 16 + g * 4] = acc;
       }
-      // G[m][i] = Rw[m] . q_i for every table row m, then the per-lane gather
-      // relw[i][kw] = G[qw_i + 63 - kw][i] for this lane's 16 keys.
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int m_row = mb * 16 + l16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < KCH; ++dc) {
-          const int d0 = dc * 32 + g * 8;
-          u32x4 af = {0, 0, 0, 0};
-          if (m_row < 127 && d0 < D) af = *(const u32x4*)(rw + (int64_t)m_row * D + d0);
-          acc = E::mfma(af, qf[qb][dc], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gscr[l16 * C::GROW + mb * 16 + g * 4 + r] = acc[r];
-      }
-      __syncthreads();
-      const int qw = min(q0 + il0 + l16, a.Nq - 1) & 63;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int qw = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1) & 63;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           sinit[kb][qb][r] = gscr[l16 * C::GROW + qw + 63 - (kb * 16 + g * 4 + r)] * inv_scale;
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     relh_lds = relh_tab;
   } else if constexpr (RAUG) {
