@@ -138,6 +138,17 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
                            mfma_lds_bytes<D, kNW, kNQB, kRelAug>(a), a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
+  // Keys spanning exactly two tiles (cross-attention to short contexts):
+  // both tiles are loaded with the queries, one barrier, no waits between.
+#ifndef ATTN_WPE_TWO
+#define ATTN_WPE_TWO (D <= 40 ? 4 : (D <= 64 ? 3 : 2))
+#endif
+  if constexpr (BIAS == ATTN_BIAS_NONE && !MASK) {
+    constexpr int kWpeTwo = ATTN_WPE_TWO;
+    if (a.Nk > C::BN && a.Nk <= 2 * C::BN)
+      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kTwoTiles, kWpeTwo>, C::NT, C::BM,
+                           mfma_lds_bytes<D, kNW, kNQB, kTwoTiles>(a), a, s);
+  }
   return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kRelTables, wpe>, C::NT, C::BM,
                        mfma_lds_bytes<D, kNW, kNQB>(a), a, s);
 }

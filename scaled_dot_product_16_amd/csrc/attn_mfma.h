@@ -70,6 +70,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
 constexpr int kRelTables = 0;  // per-score lookups in LDS tables (also non-relpos biases)
 constexpr int kRelRow64 = 1;   // 64-wide grids: Rw term seeds the accumulator, Rh term per row
 constexpr int kRelAug = 2;     // gh + gw <= 32: bias folded into the QK^T contraction
+constexpr int kTwoTiles = 3;   // no bias or mask, BN < Nk <= 2 BN: both key tiles loaded up front
 
 template <int D, int NW, int NQB, bool AUG = false>
 struct MfmaCfg {
@@ -232,10 +233,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   };
   auto load_k = [&](int t) { load_rows(kbase, a.k_sn, koff, t, kreg); };
   auto load_v = [&](int t) { load_rows(vbase, a.v_sn, voff, t, vreg); };
-  auto store_k = [&](int st, int t) {
+  auto store_k_from = [&](int st, int t, const u32x4* src) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = kreg[c];
+      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = src[c];
     if constexpr (RAUG) {
       // One-hot chunk of key row `row`: ones at columns kh and gh + kw.
       for (int i = tid; i < BN * 4; i += NT) {
@@ -255,11 +256,13 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       }
     }
   };
-  auto store_v = [&](int st) {
+  auto store_v_from = [&](int st, const u32x4* src) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = vreg[c];
+      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = src[c];
   };
+  auto store_k = [&](int st, int t) { store_k_from(st, t, kreg); };
+  auto store_v = [&](int st) { store_v_from(st, vreg); };
 
   // Augmented relative position: A fragments of the stacked table [Rh; Rw]
   // ((2gh-1) + (2gw-1) <= 62 rows, so four 16-row blocks), issued before the
@@ -314,9 +317,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     load_hfrag(0);
   }
 
-  // The first K/V tile is in flight while the bias prologue runs.
+  // The first K/V tile is in flight while the bias prologue runs.  When the
+  // keys span exactly two tiles, the second one is loaded with it: both
+  // stages are then filled once and no load waits between the tiles.
   load_k(0);
   load_v(0);
+  constexpr bool TWO = RMODE == kTwoTiles;
+  static_assert(!TWO || (!PP && BIAS == ATTN_BIAS_NONE && !MASK), "two-tile form: no bias, no mask");
+  u32x4 kreg1[TWO ? CPT : 1], vreg1[TWO ? CPT : 1];
+  if constexpr (TWO) {
+    load_rows(kbase, a.k_sn, koff, 1, kreg1);
+    load_rows(vbase, a.v_sn, voff, 1, vreg1);
+  }
 
   BiasCtx bc;
   QInfo qinf[NQB];
@@ -739,6 +751,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     iter(ntiles - 1, std::true_type{});
     pv_pp(ntiles - 1);
     if (!grp_b) __syncthreads();
+  } else if constexpr (TWO) {
+  store_k(0, 0);
+  store_v(0);
+  store_k_from(1, 1, kreg1);
+  store_v_from(1, vreg1);
+  __syncthreads();
+  if (q0 + wq0 < a.Nq) {
+    qk(Ks, s_cur);
+    tile(0, std::false_type{});
+    qk(Ks + C::K_ELEMS, s_cur, RFAST ? 4 : min(4, (a.Nk - BN + 15) / 16));
+    tile(1, std::true_type{});
+  }
   } else {
   store_k(0, 0);
   store_v(0);

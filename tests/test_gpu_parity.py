@@ -83,6 +83,7 @@ BIAS_CASES = [
     ("relpos", (14, 14), "none", None),
     ("relpos", (3, 50), "none", None),
     ("relpos", (17, 64), "none", None),  # 64-wide grid, long key range (two-group schedule)
+    ("relpos", (2, 64), "none", None),  # 64-wide grid, exactly two key tiles
     ("additive", None, "none", None),
     ("none", None, "additive", None),
     ("additive", None, "additive", None),
@@ -108,6 +109,18 @@ def test_bias_and_mask_kinds(dtype, case):
                  window=window, cfg_id=200 + case)
     say(f"[bias/mask] {dtype} {bias} {grid} {mask} {window} B={B} N={n}")
     inp = with_dense_terms(w, W.make_inputs(w, seed=case), n_bias=2, n_mask=3)
+    check_full(w, inp, run_gpu(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("n", [65, 100, 128])
+def test_two_key_tiles_dense_terms(dtype, n):
+    # Keys spanning two tiles (both loaded up front), with dense additive bias
+    # and mask, one of each per batch item group.
+    d = 64 if dtype != W.F32 else 32
+    w = W.custom(dtype, B=6, H=2, Nq=n, Nk=n, d=d, bias="additive", mask="additive", cfg_id=600 + n)
+    say(f"[two tiles] {dtype} N={n}")
+    inp = with_dense_terms(w, W.make_inputs(w, seed=n), n_bias=2, n_mask=3)
     check_full(w, inp, run_gpu(w, to_device(inp)))
 
 
