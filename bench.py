@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="GPU time of untimed graph replays before the timed one (clock ramp-up)")
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -208,7 +210,20 @@ def main():
         torch.cuda.synchronize()
         if not torch.equal(sets[0]["out"], ref):
             raise RuntimeError("graph replay output differs from the eager output")
+        # After an idle gap the clocks take some 10-20 ms of sustained work to
+        # ramp up: untimed back-to-back replays (about --settle-ms of GPU
+        # time, at most 30 of them: hundreds of replays of microsecond
+        # kernels made the following timed replay noisier, not steadier) come
+        # before the timed one, so it measures the steady state.
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
         g.replay()
+        w1.record(stream)
+        torch.cuda.synchronize()
+        n_settle = min(30, max(2, math.ceil(args.settle_ms / max(w0.elapsed_time(w1), 1e-3))))
+        for _ in range(n_settle):
+            g.replay()
         torch.cuda.synchronize()
         t_start.record(stream)
         g.replay()
@@ -216,7 +231,8 @@ def main():
         torch.cuda.synchronize()
         total_ms = t_start.elapsed_time(t_end)
         mean_launch_ms = median_launch_ms = total_ms / K
-        timing = "HIP graph of K launches, HIP events around one replay"
+        timing = (f"HIP graph of K launches, HIP events around one replay, after {n_settle + 1} "
+                  f"untimed back-to-back replays that settle the clocks")
     ms_per_step = total_ms / K
 
     flops = w.flops
