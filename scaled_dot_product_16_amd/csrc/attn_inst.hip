@@ -109,7 +109,11 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
 #else
   constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);
   constexpr int kWpeRelpos = D <= 40 ? 3 : 2;
-  constexpr int kWpeAug = D <= 32 ? 3 : 2;
+#ifdef ATTN_WPE_AUG
+  constexpr int kWpeAug = ATTN_WPE_AUG;
+#else
+  constexpr int kWpeAug = D <= 64 ? 3 : 2;
+#endif
 #endif
 #ifndef ATTN_PP
 #define ATTN_PP 1

@@ -486,17 +486,25 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // takes its addend directly: zero, or the row-form relative-position term.
   // nkb: key blocks of 16 holding keys below Nk (4 except in a ragged last
   // tile, whose empty blocks are skipped: their scores are masked anyway).
+  // The contraction form holds one more K chunk and targets one more wave
+  // per SIMD than the other forms: it reads the K fragments of two key blocks
+  // at a time and the V^T fragments after the softmax, which keeps its peak
+  // register count within the smaller budget.
+  constexpr bool kLean = RAUG;
   auto qk = [&](const uint16_t* Kt, f32x4 (&s)[4][NQB], int nkb = 4) {
+    constexpr int KBB = kLean ? 2 : 4;  // key blocks whose fragments are read together
+#pragma unroll
+    for (int kb0 = 0; kb0 < 4; kb0 += KBB) {
     u32x4 kf[KCHT][4];
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = kb0; kb < kb0 + KBB; ++kb)
         if (kb < nkb) kf[dc][kb] = *(const u32x4*)&Kt[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
 #pragma unroll
     for (int dc = 0; dc < KCHT; ++dc) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = kb0; kb < kb0 + KBB; ++kb) {
         if (kb >= nkb) continue;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -508,6 +516,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           s[kb][qb] = E::mfma(kf[dc][kb], qf[qb][dc], c);
         }
       }
+    }
     }
   };
 
@@ -523,7 +532,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 
   // One key tile t: row maxima and the lazy rescale of the output, then the
   // exponentials and O^T += V^T P^T.  The V^T fragments are read from LDS
-  // before the softmax so their latency hides behind it.  Keys past Nk can
+  // before the softmax so their latency hides behind it (after it in the
+  // contraction form, for the register budget).  Keys past Nk can
   // only occur in the last tile (never with the 64-wide row form).
   f32x4 s_cur[4][NQB];
   const bool ragged = (a.Nk % BN) != 0;
@@ -534,6 +544,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     const int nkc = LAST && k0 + 32 >= a.Nk ? 1 : 2;
     const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
     u32x4 vf[2][CB];
+    auto read_vf = [&]() {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -544,6 +555,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
         vf[kc][cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
+    };
+    if constexpr (!kLean) read_vf();
     constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
     float y[NQB][16];
@@ -608,6 +621,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       exp_pack(qb);
     }
     // O^T += V^T P^T.
+    if constexpr (kLean) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_vf();
+    }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
