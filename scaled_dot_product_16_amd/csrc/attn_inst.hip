@@ -149,9 +149,13 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
 #endif
   if constexpr (BIAS == ATTN_BIAS_NONE && !MASK) {
     constexpr int kWpeTwo = ATTN_WPE_TWO;
+    // Eight-wave workgroups (256 queries share one K/V load) where the wave
+    // target is even, so that whole workgroups fill each CU.
+    constexpr int kTwoNW = kWpeTwo % 2 == 0 ? 8 : 4;
+    using T = MfmaCfg<D, kTwoNW, kNQB>;
     if (a.Nk > C::BN && a.Nk <= 2 * C::BN)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kTwoTiles, kWpeTwo>, C::NT, C::BM,
-                           mfma_lds_bytes<D, kNW, kNQB, kTwoTiles>(a), a, s);
+      return launch_kernel(attn_fwd_mfma<Elem, D, kTwoNW, kNQB, BIAS, MASK, kTwoTiles, kWpeTwo>, T::NT, T::BM,
+                           mfma_lds_bytes<D, kTwoNW, kNQB, kTwoTiles>(a), a, s);
   }
   return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kRelTables, wpe>, C::NT, C::BM,
                        mfma_lds_bytes<D, kNW, kNQB>(a), a, s);

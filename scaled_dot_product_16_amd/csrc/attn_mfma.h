@@ -160,7 +160,7 @@ template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int W
 __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
   constexpr bool RFAST = RMODE == kRelRow64;
   constexpr bool RAUG = RMODE == kRelAug;
-  constexpr bool PP = NW == 8;  // ping-pong schedule of two wave groups
+  constexpr bool PP = NW == 8 && RMODE != kTwoTiles;  // ping-pong schedule of two wave groups
   static_assert(!PP || !RAUG, "the ping-pong schedule is not built for the augmented contraction");
   using C = MfmaCfg<D, NW, NQB, RAUG>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, KCHT = C::KCHT, DK = C::DK,
@@ -540,8 +540,13 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   auto tile = [&](int t, auto last) {
     constexpr bool LAST = decltype(last)::value && !RFAST;
     const int k0 = t * BN;
-    // Keys 32..63 of a ragged last tile may all lie past Nk.
+    // Keys 32..63 of a ragged last tile may all lie past Nk, and so may
+    // whole 16-key blocks: those take no part in the softmax (their
+    // probabilities are zero).
     const int nkc = LAST && k0 + 32 >= a.Nk ? 1 : 2;
+    constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
+    constexpr bool SKIP = LAST && !kGenericBias;  // (per-score bias forms keep the full tile)
+    const int nkbt = SKIP ? min(4, (a.Nk - k0 + 15) / 16) : 4;
     const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
     u32x4 vf[2][CB];
     auto read_vf = [&]() {
@@ -557,7 +562,6 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       }
     };
     if constexpr (!kLean) read_vf();
-    constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
     float y[NQB][16];
     float nb[NQB];
@@ -565,7 +569,13 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     // p = 2^(y*cy + nb), rounded to the element type as the B operand of PV.
     auto exp_pack = [&](int qb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[qb][i] = __builtin_amdgcn_exp2f(fmaf(y[qb][i], cy, nb[qb]));
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float& e = y[qb][kb * 4 + r];
+          if (!SKIP || kb == 0 || kb < nkbt) e = __builtin_amdgcn_exp2f(fmaf(e, cy, nb[qb]));
+          else e = 0.f;
+        }
       if constexpr (!C::ONES) {
         float ps = 0.f;
 #pragma unroll
@@ -574,6 +584,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
+        if (!SKIP || kc < nkc)
         pf[qb][kc] = u32x4{E::pack2(y[qb][kc * 8 + 0], y[qb][kc * 8 + 1]),
                            E::pack2(y[qb][kc * 8 + 2], y[qb][kc * 8 + 3]),
                            E::pack2(y[qb][kc * 8 + 4], y[qb][kc * 8 + 5]),
@@ -603,10 +614,19 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           for (int r = 0; r < 4; ++r)
             if (kb * 16 + r >= lim) y[qb][kb * 4 + r] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(y[qb][0], y[qb][1]), y[qb][2]);
+      float mx;
+      if constexpr (SKIP) {
+        mx = fmaxf(fmaxf(y[qb][0], y[qb][1]), fmaxf(y[qb][2], y[qb][3]));
 #pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[qb][i]), y[qb][i + 1]);
-      mx = fmaxf(mx, y[qb][15]);
+        for (int kb = 1; kb < 4; ++kb)
+          if (kb < nkbt)
+            mx = fmaxf(mx, fmaxf(fmaxf(y[qb][kb * 4], y[qb][kb * 4 + 1]), fmaxf(y[qb][kb * 4 + 2], y[qb][kb * 4 + 3])));
+      } else {
+        mx = fmaxf(fmaxf(y[qb][0], y[qb][1]), y[qb][2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[qb][i]), y[qb][i + 1]);
+        mx = fmaxf(mx, y[qb][15]);
+      }
       mx = max_across_groups(mx);
       const float mt = fmaf(mx, cy, hh);  // tile row maximum, log2 units
       if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
