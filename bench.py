@@ -5,7 +5,8 @@ path: validation, address folding, tile loads, QK^T, bias, mask, online
 softmax, PV, epilogue).  Default workload: Swin-T stage-1 shifted-window
 attention (8 images of 56x56 tokens, 7x7 windows, shift 3, 3 heads, d=32,
 f16, table bias and region mask, image layout).  ``--config`` selects another
-workload (C1, C2, C3, C4, C4h, C5s, C5x).
+workload (C1, C2, C3, C3i, C4, C4h, C5s, C5x; C3i is C3 read from the
+unpadded 64x64 token image in the image layout).
 
 Inputs are resident in HBM before timing starts.  Several copies of the input
 set rotate so that every launch reads data that is not in the 256 MB

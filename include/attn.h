@@ -70,12 +70,15 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 /* Token layout of a tensor.
  *  BATCHED: dims = {B_eff, H, N, d}; windows are extra batch items.
  *  IMAGE:   dims = {B_img, H, img_h*img_w, d}, tokens in image row-major
- *           order.  The kernel partitions the image into win_h x win_w
- *           windows (after a cyclic shift by (shift_h, shift_w) when they are
- *           non-zero) and writes `out` back in image order, i.e. reverse
- *           partition and reverse shift.  The window geometry is taken from
+ *           order.  The kernel pads the image to whole windows (see
+ *           attn_window_t), partitions it into win_h x win_w windows (after
+ *           a cyclic shift by (shift_h, shift_w) when they are non-zero) and
+ *           writes `out` back in image order, i.e. reverse partition, reverse
+ *           shift and crop.  The window geometry is taken from
  *           mask_desc->win.  Batch item b_eff = img * nW + window, windows
- *           row-major.  q, k, v and out must all use IMAGE together.        */
+ *           row-major.  q, k, v and out must all use IMAGE together; every
+ *           element offset inside one (image, head) slice must be below 2^29
+ *           (E_UNSUPPORTED otherwise).                                       */
 typedef enum { ATTN_LAYOUT_BATCHED = 0, ATTN_LAYOUT_IMAGE = 1 } attn_layout_t;
 
 /* A strided 4-D tensor [B, H, N, d]; the d stride is 1.
@@ -123,11 +126,20 @@ typedef enum {
   ATTN_MASK_SHIFT_REGIONS = 2  /* mask[i,j] = value if region(i) != region(j), else 0     */
 } attn_mask_kind_t;
 
-/* Window geometry (Swin).  img_h, img_w: token image; win_h, win_w: window;
- * shift_h, shift_w: cyclic shift, 0 <= shift < win.  Region of a pixel of the
- * shifted image at (y, x): 3*ry + rx, with ry = 0 for y < img_h-win_h, 1 for
- * y < img_h-shift_h, 2 otherwise (same for x).  Used by SHIFT_REGIONS and by
- * ATTN_LAYOUT_IMAGE.                                                         */
+/* Window geometry (Swin, SAM).  img_h, img_w: token image; win_h, win_w:
+ * window; shift_h, shift_w: cyclic shift, 0 <= shift < win.
+ * When the image is not a whole number of windows it is zero-padded at the
+ * bottom and right to the padded grid PH = ceil(img_h/win_h)*win_h,
+ * PW = ceil(img_w/win_w)*win_w (SAM's 64x64 token grid in 14x14 windows is
+ * padded to 70x70: the windowed-encoder workload, and zero padding of the
+ * encoder input for static shapes, "Accelerating Generative AI with PyTorch:
+ * Segment Anything, Fast", section "Torch.compile").  Padded tokens have
+ * q = k = v = 0 and take part in the attention like any other token (no key
+ * masking); their outputs are not written.  The shift and the regions are
+ * taken on the padded grid: shifted pixel (Y, X) holds padded pixel
+ * ((Y+shift_h) mod PH, (X+shift_w) mod PW), and its region is 3*ry + rx with
+ * ry = 0 for Y < PH-win_h, 1 for Y < PH-shift_h, 2 otherwise (same for X).
+ * Used by SHIFT_REGIONS and by ATTN_LAYOUT_IMAGE.                            */
 typedef struct {
   int32_t img_h, img_w, win_h, win_w, shift_h, shift_w;
 } attn_window_t;
@@ -137,7 +149,7 @@ typedef struct {
  *    batch item b uses add[b % n_win].
  *  win: window geometry (SHIFT_REGIONS and IMAGE layout).  In BATCHED layout
  *    SHIFT_REGIONS labels batch item b as window b % nW of an image, where
- *    nW = (img_h/win_h)*(img_w/win_w).
+ *    nW = (PH/win_h)*(PW/win_w) windows of the padded grid.
  *  value: the additive value for pairs from different regions (Swin uses
  *    -100).                                                                  */
 typedef struct {

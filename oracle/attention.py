@@ -40,6 +40,13 @@ design notes of the repository):
   rows in [0, img_h-win_h), [img_h-win_h, img_h-sh), [img_h-sh, img_h) (same
   for columns); query/key pairs from different regions get an additive
   ``value`` (default -100);
+* an image that is not a whole number of windows is zero-padded at the bottom
+  and right up to whole windows before the shift and the partition (SAM's
+  64x64 token grid in 14x14 windows becomes 70x70; the pages pad SAM's
+  encoder input with zeros for static shapes, "Segment Anything, Fast",
+  section "Torch.compile"): padding tokens have q = k = v = 0, take part in
+  the attention like any other token, and their outputs are cropped away;
+  the shift and the region labels are taken on the padded grid;
 * an additive bias of shape [nB, Nq, Nk] applies to batch item b as b % nB,
   an additive mask [nW, Nq, Nk] as b % nW.
 
@@ -212,10 +219,17 @@ def window_reverse(w: np.ndarray, img_h: int, img_w: int, win_h: int,
     return y.reshape(B, H, img_h, img_w, d)
 
 
+def padded_extent(n: int, win: int) -> int:
+    """Image side padded up to a whole number of windows."""
+    return -(-n // win) * win
+
+
 def shift_mask(img_h: int, img_w: int, win_h: int, win_w: int, shift_h: int,
                shift_w: int, value: float = -100.0) -> np.ndarray:
-    """[nW, N, N] additive mask: ``value`` where query and key regions differ."""
-    labels = shift_region_labels(img_h, img_w, win_h, win_w, shift_h, shift_w)
+    """[nW, N, N] additive mask: ``value`` where query and key regions differ
+    (regions of the image padded to whole windows)."""
+    ph, pw = padded_extent(img_h, win_h), padded_extent(img_w, win_w)
+    labels = shift_region_labels(ph, pw, win_h, win_w, shift_h, shift_w)
     lw = window_partition(labels[None, None, :, :, None].astype(np.float64),
                           win_h, win_w)[:, 0, :, 0]           # [nW, N]
     diff = lw[:, :, None] != lw[:, None, :]
@@ -329,9 +343,10 @@ def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
     """Shifted-window attention on image-layout tensors [B, H, img_h*img_w, d].
 
     Swin talk, section 2: shift, partition, attention, reverse partition and
-    reverse shift.  The content is rolled by (-sh, -sw), partitioned into
-    windows, attended with the window bias and mask, merged back and rolled by
-    (+sh, +sw).
+    reverse shift.  The image is zero-padded at the bottom and right to whole
+    windows, the content is rolled by (-sh, -sw), partitioned into windows,
+    attended with the window bias and mask, merged back, rolled by (+sh, +sw)
+    and cropped to the image.
     """
     img_h, img_w, win_h, win_w, sh, sw = window
     q = np.asarray(q, dtype=np.float64)
@@ -339,15 +354,17 @@ def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
     assert N == img_h * img_w
+    ph, pw = padded_extent(img_h, win_h), padded_extent(img_w, win_w)
 
     def to_windows(x):
         x = x.reshape(B, H, img_h, img_w, x.shape[-1])
+        x = np.pad(x, ((0, 0), (0, 0), (0, ph - img_h), (0, pw - img_w), (0, 0)))
         x = np.roll(x, shift=(-sh, -sw), axis=(2, 3))
         return window_partition(x, win_h, win_w)
 
     ow = attention(to_windows(q), to_windows(k), to_windows(v), bias, mask)
-    o = window_reverse(ow, img_h, img_w, win_h, win_w)
-    o = np.roll(o, shift=(sh, sw), axis=(2, 3))
+    o = window_reverse(ow, ph, pw, win_h, win_w)
+    o = np.roll(o, shift=(sh, sw), axis=(2, 3))[:, :, :img_h, :img_w]
     return o.reshape(B, H, N, v.shape[-1])
 
 

@@ -51,7 +51,6 @@ int check_tensor(const attn_tensor_t* t, int es) {
 
 bool window_valid(const attn_window_t& w) {
   if (w.img_h < 1 || w.img_w < 1 || w.win_h < 1 || w.win_w < 1) return false;
-  if (w.img_h % w.win_h || w.img_w % w.win_w) return false;
   if (w.shift_h < 0 || w.shift_w < 0 || w.shift_h >= w.win_h || w.shift_w >= w.win_w) return false;
   if (w.img_h > kMaxGridSide * 16 || w.img_w > kMaxGridSide * 16) return false;
   if (w.win_h > kMaxGridSide || w.win_w > kMaxGridSide) return false;
@@ -116,8 +115,11 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
     if (!window_valid(w)) return ATTN_E_SHAPE;
     a->img_h = w.img_h; a->img_w = w.img_w; a->win_h = w.win_h; a->win_w = w.win_w;
     a->shift_h = w.shift_h; a->shift_w = w.shift_w;
-    a->nwx = w.img_w / w.win_w;
-    a->nw = (w.img_h / w.win_h) * a->nwx;
+    // Zero padding at the bottom and right up to whole windows.
+    a->pimg_h = (w.img_h + w.win_h - 1) / w.win_h * w.win_h;
+    a->pimg_w = (w.img_w + w.win_w - 1) / w.win_w * w.win_w;
+    a->nwx = a->pimg_w / w.win_w;
+    a->nw = (a->pimg_h / w.win_h) * a->nwx;
     const int64_t wt = (int64_t)w.win_h * w.win_w;
     if (layout == ATTN_LAYOUT_IMAGE) {
       if (Nq != (int64_t)w.img_h * w.img_w || Nk != Nq) return ATTN_E_SHAPE;
@@ -188,8 +190,11 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
 
   // Offsets inside one (batch item, head) slice are 32-bit in the kernels.
   const attn_tensor_t* ts[4] = {q, k, v, o};
+  // Image layout: below 2^29, so that byte offsets of 16-bit and 32-bit
+  // elements stay clear of the padding-token marker.
+  const int slice_bits = a->image ? 29 : 31;
   for (const attn_tensor_t* t : ts)
-    if ((t->dims[2] - 1) * t->strides[2] + t->dims[3] >= (int64_t(1) << 31)) return ATTN_E_UNSUPPORTED;
+    if ((t->dims[2] - 1) * t->strides[2] + t->dims[3] >= (int64_t(1) << slice_bits)) return ATTN_E_UNSUPPORTED;
 
   // out must not overlap the inputs it is computed from.
   if (overlaps(o, q, es) || overlaps(o, k, es) || overlaps(o, v, es)) return ATTN_E_ALIAS;

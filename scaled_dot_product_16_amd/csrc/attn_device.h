@@ -125,12 +125,27 @@ __device__ __forceinline__ int xcd_logical_id(int i, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Token addressing: batched layout, or image layout with the window partition
-// and the cyclic shift folded in (window w of image img, token t of the
-// window reads shifted-image pixel (wy*win_h+ty, wx*win_w+tx), which holds
-// original pixel ((y+shift_h) mod img_h, (x+shift_w) mod img_w)).  Stores use
-// the same map, which is the reverse partition and reverse shift.
+// Token addressing: batched layout, or image layout with zero padding, the
+// window partition and the cyclic shift folded in.  The image is padded at
+// the bottom and right to pimg_h x pimg_w (whole windows); window w of image
+// img, token t of the window reads shifted padded pixel (wy*win_h+ty,
+// wx*win_w+tx), which holds padded pixel ((y+shift_h) mod pimg_h,
+// (x+shift_w) mod pimg_w); a padded pixel past the image is a padding token
+// (zero q, k, v; its output is not stored).  Stores use the same map, which
+// is the reverse partition, reverse shift and crop.
 // ---------------------------------------------------------------------------
+// Image pixel index of window token (ty, tx) whose window starts at shifted
+// padded pixel (y0, x0), or -1 for a padding token.
+__device__ __forceinline__ int image_pixel(const AttnArgs& a, int y0, int x0, int ty, int tx) {
+  int y = y0 + ty + a.shift_h;
+  if (y >= a.pimg_h) y -= a.pimg_h;
+  int x = x0 + tx + a.shift_w;
+  if (x >= a.pimg_w) x -= a.pimg_w;
+  return (y < a.img_h && x < a.img_w) ? y * a.img_w + x : -1;
+}
+
+// Full element offset of token t of batch item b, head h; -1 for a padding
+// token.
 __device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_t sh, int64_t sn,
                                            int b, int h, int t) {
   if (!a.image) return (int64_t)b * sb + (int64_t)h * sh + (int64_t)t * sn;
@@ -138,16 +153,14 @@ __device__ __forceinline__ int64_t tok_off(const AttnArgs& a, int64_t sb, int64_
   const int w = b - img * a.nw;
   const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
   const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
-  int y = wy * a.win_h + ty + a.shift_h;
-  if (y >= a.img_h) y -= a.img_h;
-  int x = wx * a.win_w + tx + a.shift_w;
-  if (x >= a.img_w) x -= a.img_w;
-  return (int64_t)img * sb + (int64_t)h * sh + (int64_t)(y * a.img_w + x) * sn;
+  const int pix = image_pixel(a, wy * a.win_h, wx * a.win_w, ty, tx);
+  return pix < 0 ? -1 : (int64_t)img * sb + (int64_t)h * sh + (int64_t)pix * sn;
 }
 
 // The same map split into a per-(batch item, head) base (uniform across a
-// workgroup) and a 32-bit per-token offset; the host guarantees every
-// in-slice offset fits in 31 bits.
+// workgroup) and a 32-bit per-token offset (kPadTok for a padding token);
+// the host guarantees every in-slice offset fits in 31 bits (29 in the
+// image layout).
 __device__ __forceinline__ int64_t tok_base(const AttnArgs& a, int64_t sb, int64_t sh, int b, int h) {
   const int img = a.image ? fdiv(b, a.fd_nw) : b;
   return (int64_t)img * sb + (int64_t)h * sh;
@@ -157,20 +170,18 @@ __device__ __forceinline__ uint32_t tok_row(const AttnArgs& a, int64_t sn, int b
   const int w = b - fdiv(b, a.fd_nw) * a.nw;
   const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
   const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
-  int y = wy * a.win_h + ty + a.shift_h;
-  if (y >= a.img_h) y -= a.img_h;
-  int x = wx * a.win_w + tx + a.shift_w;
-  if (x >= a.img_w) x -= a.img_w;
-  return (uint32_t)(y * a.img_w + x) * (uint32_t)sn;
+  const int pix = image_pixel(a, wy * a.win_h, wx * a.win_w, ty, tx);
+  return pix < 0 ? kPadTok : (uint32_t)pix * (uint32_t)sn;
 }
 
-// Region (0..8) of token t of window w in the shifted image (SHIFT_REGIONS).
+// Region (0..8) of token t of window w in the shifted padded image
+// (SHIFT_REGIONS).
 __device__ __forceinline__ int region_of(const AttnArgs& a, int w, int t) {
   const int wy = fdiv(w, a.fd_nwx), wx = w - wy * a.nwx;
   const int ty = fdiv(t, a.fd_win_w), tx = t - ty * a.win_w;
   const int y = wy * a.win_h + ty, x = wx * a.win_w + tx;
-  const int ry = y < a.img_h - a.win_h ? 0 : (y < a.img_h - a.shift_h ? 1 : 2);
-  const int rx = x < a.img_w - a.win_w ? 0 : (x < a.img_w - a.shift_w ? 1 : 2);
+  const int ry = y < a.pimg_h - a.win_h ? 0 : (y < a.pimg_h - a.shift_h ? 1 : 2);
+  const int rx = x < a.pimg_w - a.win_w ? 0 : (x < a.pimg_w - a.shift_w ? 1 : 2);
   return 3 * ry + rx;
 }
 
@@ -247,8 +258,8 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
       const int64_t to = kk < a.gh ? (int64_t)(qh - kk + a.gh - 1) * a.D
                                    : (int64_t)(qw - (kk - a.gh) + a.gw - 1) * a.D;
       const void* tb = kk < a.gh ? a.rh : a.rw;
-      float acc = 0.f;
-      for (int c = 0; c < a.D; c += 4) acc += dot4<E>(a.q, qo + c, tb, to + c);
+      float acc = 0.f;  // a padding query (qo < 0) is zero
+      for (int c = 0; qo >= 0 && c < a.D; c += 4) acc += dot4<E>(a.q, qo + c, tb, to + c);
       (kk < a.gh ? relh + kk * BM : relw + (kk - a.gh) * BM)[il] = acc * kLog2e;
     }
     bc.relh = relh;
@@ -336,10 +347,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
   const QInfo qinf = make_qinfo<BIAS, MASK>(a, b, qi, tid);
   float qv[DMAX], acc[DMAX];
   {
-    const float* qp = (const float*)a.q + tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+    const int64_t qo = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
+    const float* qp = (const float*)a.q + (qo < 0 ? 0 : qo);
 #pragma unroll
     for (int c = 0; c < DMAX; c += 4) {
-      const f32x4 v = c < D ? *(const f32x4*)(qp + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 v = c < D && qo >= 0 ? *(const f32x4*)(qp + c) : f32x4{0.f, 0.f, 0.f, 0.f};
       qv[c] = v[0]; qv[c + 1] = v[1]; qv[c + 2] = v[2]; qv[c + 3] = v[3];
       acc[c] = acc[c + 1] = acc[c + 2] = acc[c + 3] = 0.f;
     }
@@ -362,8 +374,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
       const int key = t * kF32BN + row;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (key < a.Nk) {
-        kv = *(const f32x4*)((const float*)a.k + tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key) + col);
-        vv = *(const f32x4*)((const float*)a.v + tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key) + col);
+        const int64_t ko = tok_off(a, a.k_sb, a.k_sh, a.k_sn, b, h, key);
+        const int64_t vo = tok_off(a, a.v_sb, a.v_sh, a.v_sn, b, h, key);
+        if (ko >= 0) kv = *(const f32x4*)((const float*)a.k + ko + col);  // padding keys stay zero
+        if (vo >= 0) vv = *(const f32x4*)((const float*)a.v + vo + col);
       }
       *(f32x4*)&Ks[row][col] = kv;
       *(f32x4*)&Vs[row][col] = vv;
@@ -411,9 +425,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
       }
     }
   }
-  if (q0 + tid < a.Nq) {
+  const int64_t oo = q0 + tid < a.Nq ? tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, q0 + tid) : -1;
+  if (oo >= 0) {  // rows past Nq and padding tokens are not stored
     const float inv = 1.f / l;
-    float* op = (float*)a.o + tok_off(a, a.o_sb, a.o_sh, a.o_sn, b, h, q0 + tid);
+    float* op = (float*)a.o + oo;
 #pragma unroll
     for (int c = 0; c < DMAX; c += 4)
       if (c < D) *(f32x4*)(op + c) = f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};

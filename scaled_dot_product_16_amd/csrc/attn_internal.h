@@ -43,6 +43,7 @@ struct AttnArgs {
   // Window geometry (IMAGE layout address folding and SHIFT_REGIONS labels).
   int32_t image;
   int32_t img_h, img_w, win_h, win_w, shift_h, shift_w;
+  int32_t pimg_h, pimg_w;  // image padded to whole windows
   int32_t nwx, nw;
   // Bias.
   int32_t bias_kind;
@@ -77,6 +78,10 @@ int launch(const AttnArgs& a, void* stream);
 // token count of a batch item for which per-key index data fits on chip.
 constexpr int kMaxGridSide = 1024;
 constexpr int kMaxIndexedTokens = 16384;
+
+// Token offset that marks a padding token of the image layout (no memory
+// behind it: loads give zero, stores are skipped).
+constexpr uint32_t kPadTok = 0xFFFFFFFFu;
 
 }  // namespace attn
 

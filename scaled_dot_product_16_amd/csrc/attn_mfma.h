@@ -191,7 +191,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
-      qf[qb][dc] = d0 < D ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
+      // (a padding token of the image layout is a zero query)
+      qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -223,11 +224,15 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
       for (int c = 0; c < CPT; ++c) reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], 0, 0);
     } else {
-      const auto rs = buffer_rsrc(base, 0xFFFFFFFFu);
+      // Padding tokens read at a byte offset past the resource's range,
+      // which gives zero (in-slice offsets stay below 2^30 bytes).
+      const auto rs = buffer_rsrc(base, 0xFFFFFFF0u);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int key = min(t * BN + min(crow(c), BN - 1), a.Nk - 1);
-        reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * (tok_row(a, sn, b, key) + (uint32_t)ccol(c)), 0, 0);
+        const uint32_t r = tok_row(a, sn, b, key);
+        reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, r == kPadTok ? 0xFFFFFFF0u : 2 * (r + (uint32_t)ccol(c)),
+                                                       0, 0);
       }
     }
   };
@@ -838,8 +843,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     else lsum = sum_across_groups(l[qb]);
     const float inv = 1.f / lsum;
     const int qi = q0 + wq0 + qb * 16 + l16;
-    if (qi < a.Nq) {
-      const uint32_t off = tok_row(a, a.o_sn, b, qi);
+    const uint32_t off = qi < a.Nq ? tok_row(a, a.o_sn, b, qi) : kPadTok;
+    if (off != kPadTok) {  // rows past Nq and padding tokens are not stored
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int c0 = cb * 16 + g * 4;

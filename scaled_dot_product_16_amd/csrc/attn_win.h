@@ -87,20 +87,17 @@ __device__ __forceinline__ WinPos win_pos(const AttnArgs& a, int b) {
   return p;
 }
 
-// Element offset of window token (ty, tx) inside one (image, head) slice.
-__device__ __forceinline__ uint32_t win_tok_off(const AttnArgs& a, const WinPos& p, int ty, int tx,
-                                                int64_t sn) {
-  int y = p.y0 + ty + a.shift_h;
-  if (y >= a.img_h) y -= a.img_h;
-  int x = p.x0 + tx + a.shift_w;
-  if (x >= a.img_w) x -= a.img_w;
-  return (uint32_t)(y * a.img_w + x) * (uint32_t)sn;
+// Image pixel of window token (ty, tx) inside one (image, head) slice, or
+// kPadTok for a padding token.
+__device__ __forceinline__ uint32_t win_tok_pix(const AttnArgs& a, const WinPos& p, int ty, int tx) {
+  const int pix = image_pixel(a, p.y0, p.x0, ty, tx);
+  return pix < 0 ? kPadTok : (uint32_t)pix;
 }
 
 __device__ __forceinline__ int win_region(const AttnArgs& a, const WinPos& p, int ty, int tx) {
   const int y = p.y0 + ty, x = p.x0 + tx;
-  const int ry = y < a.img_h - a.win_h ? 0 : (y < a.img_h - a.shift_h ? 1 : 2);
-  const int rx = x < a.img_w - a.win_w ? 0 : (x < a.img_w - a.shift_w ? 1 : 2);
+  const int ry = y < a.pimg_h - a.win_h ? 0 : (y < a.pimg_h - a.shift_h ? 1 : 2);
+  const int rx = x < a.pimg_w - a.win_w ? 0 : (x < a.pimg_w - a.shift_w ? 1 : 2);
   return 3 * ry + rx;
 }
 
@@ -164,7 +161,7 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     if (!a.image) return (uint32_t)t;
     int ty, tx;
     split(t, ty, tx);
-    return win_tok_off(a, pos, ty, tx, 1);
+    return win_tok_pix(a, pos, ty, tx);
   };
   constexpr int ES = F32 ? 4 : 2;  // element bytes
   const char* qp = (const char*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh) * ES;
@@ -183,24 +180,29 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     for (int c = 0; c < FCPT; ++c) {
       const int ch = min(tid + c * NT, FCH - 1);
       const int c4 = (ch % CF::QC) * 4;
-      const uint32_t pix = tok_pix(min(ch / CF::QC, Nk - 1));
+      const uint32_t pix0 = tok_pix(min(ch / CF::QC, Nk - 1));
+      const uint32_t pix = pix0 == kPadTok ? 0u : pix0;
       const int col = c4 < a.D ? c4 : 0;
       kreg[c] = *(const u32x4*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * 4);
       vreg[c] = *(const u32x4*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * 4);
-      if (c4 >= a.D) kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
+      if (c4 >= a.D || pix0 == kPadTok) kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
     }
   } else {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = min(tid + c * NT, NCH - 1);
-      const uint32_t pix = tok_pix(min(ch / RCH, Nk - 1));
+      const uint32_t pix0 = tok_pix(min(ch / RCH, Nk - 1));
+      const uint32_t pix = pix0 == kPadTok ? 0u : pix0;
       const uint32_t col = (uint32_t)((ch % RCH) * 8);
       kreg[c] = *(const u32x4*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * 2);
       vreg[c] = *(const u32x4*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * 2);
+      if (pix0 == kPadTok) kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};  // padding token
     }
   }
   const int q_tok = min(wave * 16 + l16, N - 1);
-  const uint32_t q_pix = tok_pix(q_tok);
+  const uint32_t q_pix0 = tok_pix(q_tok);
+  const bool q_pad = q_pix0 == kPadTok;  // padding token: zero query, output not stored
+  const uint32_t q_pix = q_pad ? 0u : q_pix0;
   const uint32_t q_off = q_pix * (uint32_t)a.q_sn;
   u32x4 qf[F32 ? CF::QC / 4 : KCH];
   if constexpr (F32) {
@@ -208,20 +210,20 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < CF::QC / 4; ++j) {
       const int d0 = g * CF::QC + 4 * j;
-      qf[j] = d0 < a.D ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 4) : u32x4{0, 0, 0, 0};
+      qf[j] = d0 < a.D && !q_pad ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 4) : u32x4{0, 0, 0, 0};
     }
   } else {
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
-      qf[dc] = d0 < D ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 2) : u32x4{0, 0, 0, 0};
+      qf[dc] = d0 < D && !q_pad ? *(const u32x4*)(qp + (size_t)(q_off + d0) * 2) : u32x4{0, 0, 0, 0};
     }
   }
 
   // Only windows on the last window row or column of the shifted image hold
   // more than one region.
   const bool regions = MASKK == ATTN_MASK_SHIFT_REGIONS &&
-                       (pos.y0 + a.win_h > a.img_h - a.win_h || pos.x0 + a.win_w > a.img_w - a.win_w);
+                       (pos.y0 + a.win_h > a.pimg_h - a.win_h || pos.x0 + a.win_w > a.pimg_w - a.win_w);
   const int n_tab = win_tab_entries(a);
   if constexpr (kTab) {
     const float mv = a.mask_value * kLog2e;
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   }
 
   const float inv = F32 ? 1.f / sum_across_groups(ps) : __builtin_amdgcn_rcpf(sum_across_groups(ps));
-  if (wave * 16 + l16 < N) {
+  if (wave * 16 + l16 < N && !q_pad) {
     // Query row wave*16 + l16 is q_tok here, so its pixel is q_pix.
     const uint32_t off = q_pix * (uint32_t)a.o_sn;
 #pragma unroll

@@ -97,6 +97,11 @@ WORKLOADS = {
     "C3": Workload("C3", "sam_b_windowed_bf16", 3, BF16, B=8 * 25, H=12, Nq=196, Nk=196,
                    d=64, bias="relpos", grid=(14, 14),
                    note="SAM ViT-B windowed: 64x64 grid padded to 70x70, 25 windows of 14x14"),
+    "C3i": Workload("C3i", "sam_b_windowed_image_bf16", 33, BF16, B=8 * 25, H=12, Nq=196, Nk=196,
+                    d=64, bias="relpos", grid=(14, 14), layout="image", images=8,
+                    window=(64, 64, 14, 14, 0, 0),
+                    note="SAM ViT-B windowed from the 64x64 token image: zero padding to 70x70 and "
+                         "the 25 windows of 14x14 folded into the addressing"),
     "C4": Workload("C4", "sam_b_global_bf16", 4, BF16, B=8, H=12, Nq=4096, Nk=4096, d=64,
                    bias="relpos", grid=(64, 64), note="SAM ViT-B global attention, 64x64 grid"),
     "C4h": Workload("C4h", "sam_h_global_bf16", 44, BF16, B=8, H=16, Nq=4096, Nk=4096, d=80,

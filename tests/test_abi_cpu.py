@@ -84,9 +84,15 @@ def test_shape_errors(lib):
                    layout="image") == 2                                  # image size
     bad = B.Window(56, 56, 7, 7, 7, 0)                                   # shift >= window
     assert B.check(q, t(2, 3, 49, 32), t(2, 3, 49, 32), mask=B.ShiftMask(bad)) == 2
+    # An image that is not a whole number of windows is padded to one
+    # (50 -> 56 rows here), so it is accepted; its token count must still be
+    # img_h * img_w, and batched windows must still hold win_h * win_w tokens.
     nondiv = B.Window(50, 56, 7, 7, 3, 3)
     assert B.check(t(8, 3, 2800, 32), t(8, 3, 2800, 32), t(8, 3, 2800, 32),
+                   mask=B.ShiftMask(nondiv), layout="image") == 0
+    assert B.check(t(8, 3, 2801, 32), t(8, 3, 2801, 32), t(8, 3, 2801, 32),
                    mask=B.ShiftMask(nondiv), layout="image") == 2
+    assert B.check(t(8, 3, 50, 32), t(8, 3, 50, 32), t(8, 3, 50, 32), mask=B.ShiftMask(nondiv)) == 2
 
 
 def test_unsupported_and_layout_errors(lib):

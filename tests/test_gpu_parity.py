@@ -35,7 +35,7 @@ def gpu_ready():
 # The workloads at full size
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("key", ["C1", "C2", "C3"])
+@pytest.mark.parametrize("key", ["C1", "C2", "C3", "C3i"])
 def test_workload_full(key):
     w = W.WORKLOADS[key]
     say(f"[parity full] {key} {w.name}")
@@ -152,6 +152,48 @@ def test_image_layout(dtype, geom):
     devb = dict(dev, q=part(dev["q"]), k=part(dev["k"]), v=part(dev["v"]))
     outb = run_gpu(wb, devb)
     assert torch.equal(part(out), outb)
+
+
+# Images that are not a whole number of windows: zero padding at the bottom
+# and right is folded into the addressing.  (geometry, bias, head dim):
+# 49-token windows (window kernel) with the region mask, 32-token windows,
+# 81-token windows with table bias and shift (tiled kernel, table path) and
+# SAM-style 14x14 windows with the decomposed relative position.
+PADDED = [((15, 13, 7, 7, 3, 3), "table", 32), ((20, 25, 4, 8, 2, 5), "table", 32),
+          ((20, 20, 9, 9, 4, 4), "table", 64), ((30, 20, 14, 14, 0, 0), "relpos", 64)]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("case", range(len(PADDED)))
+def test_padded_image_layout(dtype, case):
+    geom, bias, d = PADDED[case]
+    ih, iw, wh, ww, sh, sw = geom
+    ph, pw = -(-ih // wh) * wh, -(-iw // ww) * ww
+    nW = (ph // wh) * (pw // ww)
+    mask = "shift" if sh or sw else "none"
+    w = W.custom(dtype, B=2 * nW, H=3, Nq=wh * ww, Nk=wh * ww, d=d, bias=bias, grid=(wh, ww),
+                 mask=mask, layout="image", images=2, window=geom, cfg_id=310 + case)
+    say(f"[padded image] {dtype} {geom} {bias} d={d}")
+    inp = W.make_inputs(w, seed=sum(geom))
+    dev = to_device(inp)
+    out = run_gpu(w, dev)
+    check_full(w, inp, out)
+
+    # Bit for bit the same as explicitly padded, shifted and partitioned
+    # inputs in the batched layout (padding rows are zeros there).
+    def part(x):
+        x = x.reshape(2, 3, ih, iw, d)
+        x = torch.nn.functional.pad(x, (0, 0, 0, pw - iw, 0, ph - ih))
+        x = torch.roll(x, shifts=(-sh, -sw), dims=(2, 3))
+        x = x.reshape(2, 3, ph // wh, wh, pw // ww, ww, d).permute(0, 2, 4, 1, 3, 5, 6)
+        return x.reshape(2 * nW, 3, wh * ww, d).contiguous()
+
+    wb = W.custom(dtype, B=2 * nW, H=3, Nq=wh * ww, Nk=wh * ww, d=d, bias=bias, grid=(wh, ww),
+                  mask=mask, layout="batched", window=geom, cfg_id=310 + case)
+    devb = dict(dev, q=part(dev["q"]), k=part(dev["k"]), v=part(dev["v"]))
+    outb = run_gpu(wb, devb)
+    real = part(torch.ones(2, 3, ih * iw, d, device=out.device)).bool()
+    assert torch.equal(part(out)[real], outb[real])
 
 
 # ---------------------------------------------------------------------------

@@ -155,6 +155,94 @@ def test_bruteforce_image_shift_window():
     np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
 
 
+def _py_padded_image(q, k, v, ih, iw, wh, ww, sh, sw, **kw):
+    """Scalar reference for the padded image layout: the grid is padded to
+    whole windows (ph, pw); window (wy, wx), token (ty, tx) reads padded pixel
+    ((wy*wh+ty+sh) % ph, (wx*ww+tx+sw) % pw), a zero vector when that pixel is
+    outside the image, and only real pixels receive an output."""
+    ph, pw = -(-ih // wh) * wh, -(-iw // ww) * ww
+    B, H, _, d = q.shape
+    regions = kw.pop("regions", False)
+
+    def region(y, x):
+        ry = 0 if y < ph - wh else (1 if y < ph - sh else 2)
+        rx = 0 if x < pw - ww else (1 if x < pw - sw else 2)
+        return 3 * ry + rx
+
+    exp = np.full(q.shape, np.nan)
+    for b in range(B):
+        for h in range(H):
+            for wy in range(ph // wh):
+                for wx in range(pw // ww):
+                    pix, labels, qw, kwn, vw = [], [], [], [], []
+                    for ty in range(wh):
+                        for tx in range(ww):
+                            y, x = wy * wh + ty, wx * ww + tx
+                            py_, px_ = (y + sh) % ph, (x + sw) % pw
+                            real = py_ < ih and px_ < iw
+                            p_ = py_ * iw + px_ if real else None
+                            pix.append(p_)
+                            labels.append(region(y, x))
+                            for dst, src in ((qw, q), (kwn, k), (vw, v)):
+                                dst.append([float(c) for c in src[b, h, p_]] if real else [0.0] * d)
+                    ow = py_attention_window(qw, kwn, vw, wh, ww, h=h,
+                                             labels=labels if regions else None, **kw)
+                    for t, p_ in enumerate(pix):
+                        if p_ is not None:
+                            exp[b, h, p_] = ow[t]
+    return exp
+
+
+def test_bruteforce_padded_image_shift_window():
+    # 5x4 image, 3x3 windows -> padded 6x6, shift 1, table bias and region
+    # mask (regions of the padded grid).  Catches padding on the wrong side,
+    # a shift taken modulo the unpadded size, labels from the unpadded size,
+    # or padding tokens masked out instead of attended as zero vectors.
+    ih, iw, wh, ww, sh, sw = 5, 4, 3, 3, 1, 1
+    B, H, d = 2, 2, 4
+    q, k, v = (rnd((B, H, ih * iw, d), s) for s in (60, 61, 62))
+    table = rnd(((2 * wh - 1) * (2 * ww - 1), H), 63)
+    win = (ih, iw, wh, ww, sh, sw)
+    got = O.attention_image(q, k, v, win, bias=O.Bias("table", grid=(wh, ww), table=table),
+                            mask=O.Mask("shift", window=win))
+    exp = _py_padded_image(q, k, v, ih, iw, wh, ww, sh, sw, table=tolist2(table), regions=True)
+    assert not np.isnan(exp).any()
+    np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
+
+
+def test_bruteforce_padded_image_relpos():
+    # 4x5 image in 3x3 windows (padded 6x6), decomposed relative position,
+    # no shift: padding queries are zero, so their own bias rows vanish, but
+    # real queries still add q.Rh + q.Rw towards padding keys.
+    ih, iw, wh, ww = 4, 5, 3, 3
+    B, H, d = 1, 2, 4
+    q, k, v = (rnd((B, H, ih * iw, d), s) for s in (64, 65, 66))
+    rh, rw = rnd((2 * wh - 1, d), 67), rnd((2 * ww - 1, d), 68)
+    win = (ih, iw, wh, ww, 0, 0)
+    got = O.attention_image(q, k, v, win, bias=O.Bias("relpos", grid=(wh, ww), rh=rh, rw=rw))
+    exp = _py_padded_image(q, k, v, ih, iw, wh, ww, 0, 0, rh=tolist2(rh), rw=tolist2(rw))
+    np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
+
+
+def test_padding_keys_add_to_the_denominator_only():
+    # Closed form: without a bias a padding key has logit 0 and value 0, so a
+    # window with n_pad padding tokens gives, for a real query,
+    #   o = sum_real e^{s_j} v_j / (sum_real e^{s_j} + n_pad).
+    # 2x3 image in 2x2 windows -> padded 2x4: the second window holds pixels
+    # (0,2), (1,2) and two padding tokens.
+    ih, iw = 2, 3
+    d = 3
+    q, k, v = (rnd((1, 1, ih * iw, d), s) for s in (69, 70, 71))
+    got = O.attention_image(q, k, v, (ih, iw, 2, 2, 0, 0))
+    real = [2, 5]  # image pixels of the second window
+    scale = 1 / math.sqrt(d)
+    for i in real:
+        s = np.array([scale * q[0, 0, i] @ k[0, 0, j] for j in real])
+        e = np.exp(s)
+        exp = (e[:, None] * v[0, 0, real]).sum(0) / (e.sum() + 2.0)
+        np.testing.assert_allclose(got[0, 0, i], exp, rtol=0, atol=1e-13)
+
+
 def test_bruteforce_additive_bias_and_mask():
     B, H, nq, nk, d = 3, 2, 3, 4, 2
     q, k, v = rnd((B, H, nq, d), 16), rnd((B, H, nk, d), 17), rnd((B, H, nk, d), 18)
