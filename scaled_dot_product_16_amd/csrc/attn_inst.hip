@@ -125,7 +125,7 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   // workgroups whose two wave groups alternate matrix and softmax phases
   // (measured faster there; without a bias the four-wave kernel is faster).
   if constexpr (ATTN_PP && !MASK && BIAS == ATTN_BIAS_RELPOS) {
-    if (a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256) {
+    if (a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256 && !a.image) {
       using P = MfmaCfg<D, 8, kNQB>;
       return launch_kernel(attn_fwd_mfma<Elem, D, 8, kNQB, BIAS, false, kRelRow64, 2>, P::NT, P::BM,
                            mfma_lds_bytes<D, 8, kNQB, kRelRow64>(a), a, s);

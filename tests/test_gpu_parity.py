@@ -196,6 +196,18 @@ def test_padded_image_layout(dtype, case):
     assert torch.equal(part(out)[real], outb[real])
 
 
+@pytest.mark.parametrize("geom", [(64, 64, 64, 64, 0, 0), (60, 62, 64, 64, 0, 0)])
+def test_image_layout_global_relpos(geom):
+    # One 64x64 window per image: SAM global attention in the image layout
+    # (the 64-wide relative-position row form), also on a padded grid.
+    w = W.custom(W.BF16, B=1, H=2, Nq=4096, Nk=4096, d=64, bias="relpos", grid=(64, 64),
+                 layout="image", images=1, window=geom, cfg_id=320)
+    say(f"[image global relpos] {geom}")
+    inp = W.make_inputs(w, seed=3)
+    err = check_full(w, inp, run_gpu(w, to_device(inp)))
+    say(f"  max abs err {err:.3e} (tol {TOL[W.BF16]:.0e})")
+
+
 # ---------------------------------------------------------------------------
 # Invariants and special cases
 # ---------------------------------------------------------------------------
