@@ -76,6 +76,22 @@ constexpr int kNW = 4;
 #endif
 constexpr int kNQB = ATTN_NQB;
 
+// The tiled kernel in the instance for the call's layout (the ping-pong
+// form, NW = 8 with a relative-position row form, exists for the batched
+// layout only).
+template <int BIAS, bool MASK, int RMODE, int WPE, int NW = kNW>
+int launch_mfma(const AttnArgs& a, hipStream_t s) {
+  constexpr int D = INST_D;
+  using C = MfmaCfg<D, NW, kNQB>;
+  const size_t lds = mfma_lds_bytes<D, NW, kNQB, RMODE>(a);
+  constexpr bool kPingPong = NW == 8 && RMODE != kTwoTiles;
+  if constexpr (!kPingPong) {
+    if (a.image)
+      return launch_kernel(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, true>, C::NT, C::BM, lds, a, s);
+  }
+  return launch_kernel(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, false>, C::NT, C::BM, lds, a, s);
+}
+
 template <int BIAS, bool MASK>
 int launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int D = INST_D;
@@ -126,20 +142,14 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   // (measured faster there; without a bias the four-wave kernel is faster).
   if constexpr (ATTN_PP && !MASK && BIAS == ATTN_BIAS_RELPOS) {
     if (a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256 && !a.image) {
-      using P = MfmaCfg<D, 8, kNQB>;
-      return launch_kernel(attn_fwd_mfma<Elem, D, 8, kNQB, BIAS, false, kRelRow64, 2>, P::NT, P::BM,
-                           mfma_lds_bytes<D, 8, kNQB, kRelRow64>(a), a, s);
+      return launch_mfma<BIAS, false, kRelRow64, 2, 8>(a, s);
     }
   }
   // Relative position: 64-wide grids take the row form, grids with
   // gh + gw <= 32 fold the bias into the QK^T contraction.
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
-    if (a.gw == 64)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelRow64, kWpeRelpos>, C::NT,
-                           C::BM, mfma_lds_bytes<D, kNW, kNQB, kRelRow64>(a), a, s);
-    if (a.gh + a.gw <= 32)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, false, kRelAug, kWpeAug>, C::NT, C::BM,
-                           mfma_lds_bytes<D, kNW, kNQB, kRelAug>(a), a, s);
+    if (a.gw == 64) return launch_mfma<BIAS, false, kRelRow64, kWpeRelpos>(a, s);
+    if (a.gh + a.gw <= 32) return launch_mfma<BIAS, false, kRelAug, kWpeAug>(a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
   // Keys spanning exactly two tiles (cross-attention to short contexts):
@@ -152,13 +162,9 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
     // Eight-wave workgroups (256 queries share one K/V load) where the wave
     // target is even, so that whole workgroups fill each CU.
     constexpr int kTwoNW = kWpeTwo % 2 == 0 ? 8 : 4;
-    using T = MfmaCfg<D, kTwoNW, kNQB>;
-    if (a.Nk > C::BN && a.Nk <= 2 * C::BN)
-      return launch_kernel(attn_fwd_mfma<Elem, D, kTwoNW, kNQB, BIAS, MASK, kTwoTiles, kWpeTwo>, T::NT, T::BM,
-                           mfma_lds_bytes<D, kTwoNW, kNQB, kTwoTiles>(a), a, s);
+    if (a.Nk > C::BN && a.Nk <= 2 * C::BN) return launch_mfma<BIAS, MASK, kTwoTiles, kWpeTwo, kTwoNW>(a, s);
   }
-  return launch_kernel(attn_fwd_mfma<Elem, D, kNW, kNQB, BIAS, MASK, kRelTables, wpe>, C::NT, C::BM,
-                       mfma_lds_bytes<D, kNW, kNQB>(a), a, s);
+  return launch_mfma<BIAS, MASK, kRelTables, wpe>(a, s);
 }
 #endif
 

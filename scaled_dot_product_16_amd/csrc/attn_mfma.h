@@ -156,15 +156,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #else
 #define ATTN_WAVES_PER_EU(n)
 #endif
-template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int WPE>
+// IMG: built with the image-layout addressing (the batched-layout instance
+// leaves it out, which keeps the key loop within fewer registers).
+template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int WPE, bool IMG>
 __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
   constexpr bool RFAST = RMODE == kRelRow64;
   constexpr bool RAUG = RMODE == kRelAug;
   constexpr bool PP = NW == 8 && RMODE != kTwoTiles;  // ping-pong schedule of two wave groups
   static_assert(!PP || !RAUG, "the ping-pong schedule is not built for the augmented contraction");
-  // The ping-pong form is launched for the batched layout only: dropping the
-  // image-layout addressing from it keeps its loop within its register budget.
-  if constexpr (PP) a.image = 0;
+  static_assert(!(PP && IMG), "the ping-pong form is launched for the batched layout only");
+  if constexpr (!IMG) a.image = 0;
   using C = MfmaCfg<D, NW, NQB, RAUG>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, KCH = C::KCH, KCHT = C::KCHT, DK = C::DK,
                 CB = C::CB, DV = C::DV, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH,
