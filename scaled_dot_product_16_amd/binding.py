@@ -242,6 +242,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
     h = lib()
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if q.numel() == 0 and k.dim() == 4 and k.shape[2] > 0:
+        # No query rows (or no batch items or heads): nothing to compute, and
+        # the library, which takes only non-empty tensors, is not called.
+        # Zero keys with queries present stay an error (a softmax over no
+        # keys is undefined): the library rejects them.
+        return out
     qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream

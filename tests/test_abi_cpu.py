@@ -95,6 +95,23 @@ def test_shape_errors(lib):
     assert B.check(t(8, 3, 50, 32), t(8, 3, 50, 32), t(8, 3, 50, 32), mask=B.ShiftMask(nondiv)) == 2
 
 
+def test_empty_tensors_are_rejected(lib):
+    # The library takes non-empty tensors only: an empty torch tensor has no
+    # storage (NULL data, E_NULL); a zero dimension with a valid pointer is
+    # E_SHAPE.  (binding.fwd returns an empty output for zero query rows
+    # without calling the library.)
+    e = t(0, 3, 49, 32)
+    assert B.check(e, e.clone(), e.clone()) == 1
+    q = t(2, 3, 49, 32)
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(q, q.clone(), q.clone(), q.clone(), None, None,
+                                                   "batched", None)
+    qc.dims[2] = 0
+    h = B.lib()
+    assert h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                        ctypes.byref(md), ctypes.byref(oc), dt) == 2
+    del keep
+
+
 def test_unsupported_and_layout_errors(lib):
     assert B.check(t(1, 1, 8, 48), t(1, 1, 8, 48), t(1, 1, 8, 48)) == 4  # d=48 not built
     assert B.check(t(1, 1, 8, 132, dtype=torch.float32), t(1, 1, 8, 132, dtype=torch.float32),
