@@ -124,6 +124,16 @@ __host__ __device__ inline size_t mfma_lds_bytes(const AttnArgs& a) {
   return n;
 }
 
+// The lane index, recomputed where it is used: the asm is opaque to the
+// compiler, so lane-constant values derived from it are not kept alive in
+// registers across the key loop (which spilled two of them in the
+// contraction form).
+__device__ __forceinline__ int lane_id_here() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 __device__ __forceinline__ float max_across_groups(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -559,12 +569,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     const uint16_t* Vt = Vs + (t & 1) * C::V_ELEMS;
     u32x4 vf[2][CB];
     auto read_vf = [&]() {
+      int vr = vt_row, vc = vt_col;
+      if constexpr (kLean) {
+        const int ln = lane_id_here();
+        vr = (ln >> 4) * 4 + ((ln & 15) >> 2);
+        vc = 4 * (ln & 3);
+      }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         if (kc >= nkc) continue;
-        const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+        const uint16_t* vp = Vt + (kc * 32 + vr) * VROW + cb * 16 + vc;
         const u32x2 lo = lds_read_tr16(vp);
         const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
         vf[kc][cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -846,7 +862,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     if constexpr (C::ONES) lsum = __shfl(o[LB < CB ? LB : 0][qb][LR], LG * 16 + l16);
     else lsum = sum_across_groups(l[qb]);
     const float inv = 1.f / lsum;
-    const int qi = q0 + wq0 + qb * 16 + l16;
+    const int qi = q0 + wq0 + qb * 16 + (kLean ? lane_id_here() & 15 : l16);
     const uint32_t off = qi < a.Nq ? tok_row(a, a.o_sn, b, qi) : kPadTok;
     if (off != kPadTok) {  // rows past Nq and padding tokens are not stored
 #pragma unroll
