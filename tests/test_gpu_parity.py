@@ -83,6 +83,7 @@ BIAS_CASES = [
     ("relpos", (14, 14), "none", None),
     ("relpos", (3, 50), "none", None),
     ("relpos", (17, 64), "none", None),  # 64-wide grid, long key range (two-group schedule)
+    ("relpos", (16, 64), "none", None),  # 64-wide grid at the two-group schedule's 1024-key threshold
     ("relpos", (2, 64), "none", None),  # 64-wide grid, exactly two key tiles
     ("additive", None, "none", None),
     ("none", None, "additive", None),
