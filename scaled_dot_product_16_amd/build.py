@@ -83,6 +83,15 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    # A plain C caller of the library (host code only), run by the GPU tests.
+    c_src = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "attn_fwd_c.c")
+    if os.path.exists(c_src) and shutil.which("gcc"):
+        rocm = os.path.dirname(os.path.dirname(os.path.realpath(cc)))
+        _run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+              "-I", os.path.join(os.path.dirname(HERE), "include"), "-I", os.path.join(rocm, "include"),
+              c_src, "-o", os.path.join(obj_dir, "attn_fwd_c"), "-L", HERE, "-lattn",
+              "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+              "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(rocm, "lib")])
     if verbose:
         print(f"built {LIB}")
     return LIB
