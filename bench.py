@@ -140,7 +140,7 @@ def main():
                          "for scaling the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
