@@ -46,6 +46,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // x 4 column slices of each 16-lane group from distinct banks (also for 64
 // banks with 32 lanes per pass).
 __host__ __device__ constexpr int v_row_pad(int dv) { return ((16 - dv % 32) + 32) % 32; }
+#ifndef ATTN_MAX2
+#define ATTN_MAX2 1  // joint cross-group maxima of a wave's two query blocks
+#endif
 #ifndef ATTN_KPAD
 #define ATTN_KPAD 16  // K tile row padding (elements; 16 measured faster than 8 and 24)
 #endif
@@ -139,6 +142,25 @@ __device__ __forceinline__ float max_across_groups(float v) {
   v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Row maxima of two values at once: on return every lane of `a` holds the
+// maximum of a over the four 16-lane groups for its lane index l16, and
+// likewise for `b`.  Seven instructions instead of twelve for two calls of
+// max_across_groups.  v_permlane16_swap(x, y) exchanges the odd 16-lane rows
+// of x with the even rows of y; v_permlane32_swap(x, y) rows 2-3 of x with
+// rows 0-1 of y.
+__device__ __forceinline__ void max_across_groups2(float& a, float& b) {
+  // [a0, b0, a2, b2] and [a1, b1, a3, b3] -> [A01, B01, A23, B23]
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  // [A01, B01, A01, B01] and [A23, B23, A23, B23] -> [A, B, A, B]
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const float n = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  // [A, A, A, A] and [B, B, B, B]
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(n), __float_as_uint(n), false, false);
+  a = __uint_as_float(t[0]);
+  b = __uint_as_float(t[1]);
 }
 
 __device__ __forceinline__ float sum_across_groups(float v) {
@@ -615,10 +637,11 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
                            E::pack2(y[qb][kc * 8 + 4], y[qb][kc * 8 + 5]),
                            E::pack2(y[qb][kc * 8 + 6], y[qb][kc * 8 + 7])};
     };
+    float hq[NQB], mq[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      float hh = 0.f;
-      if constexpr (RFAST) hh = relh_lds[t * BM + wq0 + qb * 16 + l16];
+      hq[qb] = 0.f;
+      if constexpr (RFAST) hq[qb] = relh_lds[t * BM + wq0 + qb * 16 + l16];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -652,8 +675,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[qb][i]), y[qb][i + 1]);
         mx = fmaxf(mx, y[qb][15]);
       }
-      mx = max_across_groups(mx);
-      const float mt = fmaf(mx, cy, hh);  // tile row maximum, log2 units
+      mq[qb] = mx;
+    }
+    if constexpr (NQB == 2 && ATTN_MAX2 && !kLean) {
+      max_across_groups2(mq[0], mq[1]);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mq[qb] = max_across_groups(mq[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float hh = hq[qb];
+      const float mt = fmaf(mq[qb], cy, hh);  // tile row maximum, log2 units
       if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
         const float mn = fmaxf(m[qb], mt);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qb] - mn);
@@ -688,11 +721,12 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     const int k0 = t * BN;
     constexpr bool kGenericBias = RMODE == kRelTables && (BIAS != ATTN_BIAS_NONE || MASK);
     const float cy = kGenericBias ? 1.f : c2;
+    float yy[NQB][16], hq[NQB], mq[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      float y[16];
-      float hh = 0.f;
-      if constexpr (RFAST) hh = relh_lds[t * BM + wq0 + qb * 16 + l16];
+      float* y = yy[qb];
+      hq[qb] = 0.f;
+      if constexpr (RFAST) hq[qb] = relh_lds[t * BM + wq0 + qb * 16 + l16];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -715,8 +749,19 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       float mx = fmaxf(fmaxf(y[0], y[1]), y[2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[i]), y[i + 1]);
-      mx = max_across_groups(fmaxf(mx, y[15]));
-      const float mt = fmaf(mx, cy, hh);
+      mq[qb] = fmaxf(mx, y[15]);
+    }
+    if constexpr (NQB == 2 && ATTN_MAX2) {
+      max_across_groups2(mq[0], mq[1]);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mq[qb] = max_across_groups(mq[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float* y = yy[qb];
+      const float hh = hq[qb];
+      const float mt = fmaf(mq[qb], cy, hh);
       if (__builtin_amdgcn_ballot_w64(mt > m[qb] + 8.f)) {
         const float mn = fmaxf(m[qb], mt);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qb] - mn);
