@@ -67,6 +67,25 @@ def traffic_record(w):
     return None
 
 
+def device_clocks(dev: int) -> dict:
+    """Peak engine and memory clocks (kHz) from the HIP runtime, or {}."""
+    import ctypes
+
+    # hipDeviceAttribute_t values of hipDeviceAttributeClockRate and
+    # hipDeviceAttributeMemoryClockRate in hip_runtime_api.h (ROCm 7).
+    attrs = {"peak_clock_khz": 5, "peak_memory_clock_khz": 60}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return {}
+    out = {}
+    for key, attr in attrs.items():
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(dev)) == 0:
+            out[key] = v.value
+    return out
+
+
 def cpu_baseline(w, budget_s: float = 10.0):
     """Time the fp64 oracle on this host on a bounded sample of the workload."""
     import numpy as np
@@ -267,7 +286,7 @@ def main():
 
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
-              "compute_units": props.multi_processor_count,
+              "compute_units": props.multi_processor_count, **device_clocks(dev.index or 0),
               "hip": torch.version.hip, "torch": torch.__version__,
               "peaks": {"hbm_GBs": PEAK_HBM_GBS, "bf16_fp16_mfma_TFLOPs": PEAK_MFMA_TFLOPS,
                         "fp32_TFLOPs": PEAK_F32_TFLOPS}}
