@@ -17,6 +17,7 @@ from .attention import (  # noqa: F401
     token_coords,
     table_relative_index,
     table_bias,
+    relpos_rows,
     relpos_bias,
     relpos_bias_gather,
     shift_region_labels,

@@ -34,6 +34,13 @@ design notes of the repository):
   the table is [(2gh-1)(2gw-1), H] (column = head);
 * the relative-position tables Rh [2gh-1, d], Rw [2gw-1, d] are shared by all
   heads and are dotted with the raw (unscaled) query;
+* queries and keys on grids of different sizes (the coordinate scalers
+  q_coords and k_coords that the SAM write-ups name, same section): the
+  shorter axis is stretched onto the longer one and the table row is the
+  floor of the scaled coordinate difference, in exact arithmetic
+  (``relpos_rows``); the tables then hold 2*max(q, k)-1 rows per axis.  The
+  write-ups also name a resize of the tables (rel_pos_resized) without giving
+  its rule: tables of any other length are rejected, not resized;
 * the shifted window attention rolls the image content by (-sh, -sw) before
   partitioning (shifted[y] = x[(y + sh) mod img_h]) and rolls back after;
   the region of a shifted-image pixel is 3*ry + rx, where ry is 0, 1, 2 for
@@ -56,7 +63,9 @@ receives (already rounded to the device dtype), upcast to float64.
 
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
+from fractions import Fraction
 from typing import Optional, Sequence
 
 import numpy as np
@@ -67,14 +76,17 @@ class Bias:
     """Additive bias description (mirrors the bias kinds of the attention call).
 
     kind: "none" | "table" | "relpos" | "additive"
-    grid: (gh, gw) token grid of one batch item (table, relpos)
+    grid: (gh, gw) token grid of one batch item (table, relpos); for relpos
+          the grid of the queries
+    kgrid: relpos only, (kgh, kgw) grid of the keys; None means ``grid``
     table: [(2gh-1)(2gw-1), H]
-    rh, rw: [2gh-1, d], [2gw-1, d]
+    rh, rw: [2max(gh,kgh)-1, d], [2max(gw,kgw)-1, d]
     add: [nB, Nq, Nk], batch item b uses add[b % nB]
     """
 
     kind: str = "none"
     grid: Optional[tuple] = None
+    kgrid: Optional[tuple] = None
     table: Optional[np.ndarray] = None
     rh: Optional[np.ndarray] = None
     rw: Optional[np.ndarray] = None
@@ -128,32 +140,58 @@ def table_bias(table: np.ndarray, gh: int, gw: int) -> np.ndarray:
     return np.transpose(table[idx], (2, 0, 1))
 
 
+def relpos_rows(qn: int, kn: int) -> np.ndarray:
+    """Table row used by query coordinate qc and key coordinate kc -> [qn, kn].
+
+    SAM blog, section "Bfloat16 half precision" (and the same passage of the
+    Korean and Chinese write-ups): the image encoder scales the query and key
+    coordinates (q_coords, k_coords) before they index the table.  Reading:
+    the axis with fewer positions is stretched onto the other's range, so a
+    query coordinate counts max(kn/qn, 1) units and a key coordinate
+    max(qn/kn, 1) units; the row is the floor of the scaled difference,
+    shifted by the largest scaled key coordinate so that it starts at 0:
+    floor(qc*max(kn/qn,1) - kc*max(qn/kn,1) + (kn-1)*max(qn/kn,1)).
+    Evaluated in exact rational arithmetic.  With qn == kn this is
+    qc - kc + kn - 1, and every row lies in [0, 2*max(qn, kn) - 2].
+    """
+    sq = max(Fraction(kn, qn), Fraction(1))
+    sk = max(Fraction(qn, kn), Fraction(1))
+    out = np.empty((qn, kn), dtype=np.int64)
+    for qc in range(qn):
+        for kc in range(kn):
+            out[qc, kc] = math.floor(qc * sq - kc * sk + (kn - 1) * sk)
+    return out
+
+
 def relpos_bias(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
-                rw: np.ndarray, gh: int, gw: int) -> np.ndarray:
-    """Decomposed relative-position bias for selected query rows -> [R, N].
+                rw: np.ndarray, gh: int, gw: int, kgh: Optional[int] = None,
+                kgw: Optional[int] = None) -> np.ndarray:
+    """Decomposed relative-position bias for selected query rows -> [R, Nk].
 
     SAM blog, section "Bfloat16 half precision": per-query coordinates index
-    the relative-position tables.  rel_h[i, kh] = q_i . Rh[qh_i - kh + gh - 1]
-    and rel_w[i, kw] = q_i . Rw[qw_i - kw + gw - 1]; the bias of key
-    j = (kh, kw) is rel_h[i, kh] + rel_w[i, kw].  q is the raw query row.
+    the relative-position tables.  rel_h[i, kh] = q_i . Rh[row_h(qh_i, kh)]
+    and rel_w[i, kw] = q_i . Rw[row_w(qw_i, kw)] (rows from
+    :func:`relpos_rows`; on equal grids Rh[qh_i - kh + gh - 1]); the bias of
+    key j = (kh, kw) of the kgh x kgw key grid is rel_h[i, kh] + rel_w[i, kw].
+    Queries sit on the gh x gw grid; q is the raw query row.
     """
+    kgh = gh if kgh is None else kgh
+    kgw = gw if kgw is None else kgw
     q_rows = np.asarray(q_rows, dtype=np.float64)
     rh = np.asarray(rh, dtype=np.float64)
     rw = np.asarray(rw, dtype=np.float64)
-    assert rh.shape[0] == 2 * gh - 1 and rw.shape[0] == 2 * gw - 1
+    assert rh.shape[0] == 2 * max(gh, kgh) - 1 and rw.shape[0] == 2 * max(gw, kgw) - 1
     qh, qw = np.asarray(rows) // gw, np.asarray(rows) % gw
-    kh = np.arange(gh)
-    kw = np.arange(gw)
-    rh_sel = rh[qh[:, None] - kh[None, :] + gh - 1]          # [R, gh, d]
-    rw_sel = rw[qw[:, None] - kw[None, :] + gw - 1]          # [R, gw, d]
-    rel_h = np.einsum("rc,rkc->rk", q_rows, rh_sel)          # [R, gh]
-    rel_w = np.einsum("rc,rkc->rk", q_rows, rw_sel)          # [R, gw]
-    return (rel_h[:, :, None] + rel_w[:, None, :]).reshape(len(rows), gh * gw)
+    rh_sel = rh[relpos_rows(gh, kgh)[qh]]                    # [R, kgh, d]
+    rw_sel = rw[relpos_rows(gw, kgw)[qw]]                    # [R, kgw, d]
+    rel_h = np.einsum("rc,rkc->rk", q_rows, rh_sel)          # [R, kgh]
+    rel_w = np.einsum("rc,rkc->rk", q_rows, rw_sel)          # [R, kgw]
+    return (rel_h[:, :, None] + rel_w[:, None, :]).reshape(len(rows), kgh * kgw)
 
 
 def relpos_bias_gather(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
                        rw: np.ndarray, gh: int, gw: int) -> np.ndarray:
-    """Same bias through the literal per-pair gather (small grids only).
+    """Same bias through the literal per-pair gather (small equal grids only).
 
     For every (query i, key j) pair the two table rows are gathered first,
     [R, N, d], and then dotted with q_i: q_i . Rh[dh] + q_i . Rw[dw].
@@ -253,7 +291,8 @@ def _additive_rows(b: int, h: int, rows: np.ndarray, q_rows: np.ndarray,
             add += cache[key][rows]
         elif bias.kind == "relpos":
             gh, gw = bias.grid
-            add += relpos_bias(q_rows, rows, bias.rh, bias.rw, gh, gw)
+            kgh, kgw = bias.kgrid if bias.kgrid is not None else (gh, gw)
+            add += relpos_bias(q_rows, rows, bias.rh, bias.rw, gh, gw, kgh, kgw)
         elif bias.kind == "additive":
             a = np.asarray(bias.add, dtype=np.float64)
             add += a[b % a.shape[0]][rows]
@@ -380,7 +419,8 @@ def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
     if w.bias == "table":
         bias = Bias("table", grid=w.grid, table=arrays["table"])
     elif w.bias == "relpos":
-        bias = Bias("relpos", grid=w.grid, rh=arrays["rh"], rw=arrays["rw"])
+        bias = Bias("relpos", grid=w.grid, kgrid=getattr(w, "kgrid", None), rh=arrays["rh"],
+                    rw=arrays["rw"])
     elif w.bias == "additive":
         bias = Bias("additive", add=arrays["bias_add"])
     mask = Mask("none")

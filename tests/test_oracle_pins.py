@@ -440,3 +440,95 @@ def test_select_rows_matches_full():
     sel = O.attention(q, k, v, bias=rb, select=[(1, 0, [3, 39, 0]), (0, 1, np.arange(5, 12))])
     np.testing.assert_allclose(sel[0], full[1, 0, [3, 39, 0]], atol=1e-14)
     np.testing.assert_allclose(sel[1], full[0, 1, 5:12], atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Relative position with query and key grids of different sizes (the
+# coordinate scalers of the SAM write-ups)
+# ---------------------------------------------------------------------------
+
+def py_scaled_row(qc, kc, qn, kn):
+    """Table row on axes of qn query and kn key positions where one count is
+    a whole multiple of the other: the shorter axis's coordinates are
+    multiplied by the ratio, the difference is shifted to start at 0."""
+    if qn >= kn:
+        assert qn % kn == 0
+        r = qn // kn
+        return qc - r * kc + r * (kn - 1)
+    assert kn % qn == 0
+    r = kn // qn
+    return r * qc - kc + (kn - 1)
+
+
+@pytest.mark.parametrize("qn,kn", [(1, 1), (5, 5), (7, 14), (14, 7), (2, 8), (9, 3), (64, 32)])
+def test_scaled_rows_whole_ratios_closed_form(qn, kn):
+    # Catches stretching the wrong axis, a missing shift, or a shift by the
+    # query range instead of the scaled key range.
+    rows = O.relpos_rows(qn, kn)
+    for qc in range(qn):
+        for kc in range(kn):
+            assert rows[qc, kc] == py_scaled_row(qc, kc, qn, kn), (qc, kc)
+
+
+@pytest.mark.parametrize("qn,kn", [(3, 2), (2, 3), (10, 4), (4, 10), (14, 9), (9, 14), (6, 6), (1, 5), (5, 1)])
+def test_scaled_rows_properties(qn, kn):
+    # Any grid sizes: rows rise with the query coordinate, fall with the key
+    # coordinate, stay inside the 2*max-1 table, start at row 0 (first query,
+    # last key), and a query step moves by at most max(kn/qn, 1) rounded up.
+    rows = O.relpos_rows(qn, kn)
+    n = 2 * max(qn, kn) - 1
+    assert rows.min() == 0 and rows[0, kn - 1] == 0 and rows.max() <= n - 1
+    assert (np.diff(rows, axis=0) >= 0).all() and (np.diff(rows, axis=1) <= 0).all()
+    assert (np.diff(rows, axis=0) <= math.ceil(max(kn / qn, 1))).all()
+    assert (np.diff(rows, axis=1) >= -math.ceil(max(qn / kn, 1))).all()
+    # The last query and the first key use the largest row, which is the
+    # scaled extents added: (qn-1)*max(kn/qn,1) + (kn-1)*max(qn/kn,1), floored.
+    top = (qn - 1) * max(kn / qn, 1) + (kn - 1) * max(qn / kn, 1)
+    assert rows[qn - 1, 0] == rows.max() == math.floor(top + 1e-9)
+
+
+@pytest.mark.parametrize("qgrid,kgrid", [((2, 2), (4, 2)), ((4, 3), (2, 3)), ((2, 3), (3, 2))])
+def test_bruteforce_relpos_unequal_grids(qgrid, kgrid):
+    # Pure-Python attention over explicit pairs; whole ratios use the closed
+    # form of py_scaled_row, the (2,3)/(3,2) case the floor written out.
+    (gh, gw), (kgh, kgw) = qgrid, kgrid
+    H, d = 2, 3
+    Nq, Nk = gh * gw, kgh * kgw
+    q, k, v = rnd((1, H, Nq, d), 21), rnd((1, H, Nk, d), 22), rnd((1, H, Nk, d), 23)
+    rh, rw = rnd((2 * max(gh, kgh) - 1, d), 24), rnd((2 * max(gw, kgw) - 1, d), 25)
+    got = O.attention(q, k, v, bias=O.Bias("relpos", grid=qgrid, kgrid=kgrid, rh=rh, rw=rw))
+
+    def row(qc, kc, qn, kn):
+        if qn % kn == 0 or kn % qn == 0:
+            return py_scaled_row(qc, kc, qn, kn)
+        # 2 query and 3 key positions: queries count 3/2 units each;
+        # 3 query and 2 key positions: keys count 3/2 units each.
+        if (qn, kn) == (2, 3):
+            return math.floor(qc * 1.5 - kc + 2)
+        assert (qn, kn) == (3, 2)
+        return math.floor(qc - kc * 1.5 + 1.5)
+
+    scale = 1.0 / math.sqrt(d)
+    for h in range(H):
+        qq, kk, vv = tolist2(q[0, h]), tolist2(k[0, h]), tolist2(v[0, h])
+        for i in range(Nq):
+            qr, qcol = divmod(i, gw)
+            logits = []
+            for j in range(Nk):
+                kr, kcol = divmod(j, kgw)
+                s = scale * py_dot(qq[i], kk[j])
+                s += py_dot(qq[i], rh[row(qr, kr, gh, kgh)]) + py_dot(qq[i], rw[row(qcol, kcol, gw, kgw)])
+                logits.append(s)
+            np.testing.assert_allclose(got[0, h, i], py_softmax_combine(logits, vv), rtol=0, atol=1e-12)
+
+
+def test_unequal_grids_reduce_to_equal_grids():
+    # kgrid equal to grid is the plain decomposed bias, and the table length
+    # must be 2*max-1 on each axis.
+    q = rnd((6, 4), 30)
+    rh, rw = rnd((5, 4), 31), rnd((3, 4), 32)
+    a = O.relpos_bias(q, np.arange(6), rh, rw, 3, 2)
+    b = O.relpos_bias(q, np.arange(6), rh, rw, 3, 2, 3, 2)
+    np.testing.assert_array_equal(a, b)
+    with pytest.raises(AssertionError):
+        O.relpos_bias(q, np.arange(6), rh, rw, 3, 2, 4, 2)
