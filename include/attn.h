@@ -95,7 +95,8 @@ typedef struct {
 typedef enum {
   ATTN_BIAS_NONE = 0,
   ATTN_BIAS_TABLE = 1,    /* bias[i,j] = table[(qh-kh+gh-1)*(2gw-1) + (qw-kw+gw-1), head] */
-  ATTN_BIAS_RELPOS = 2,   /* bias[i,j] = q_i.Rh[qh-kh+gh-1] + q_i.Rw[qw-kw+gw-1]          */
+  ATTN_BIAS_RELPOS = 2,   /* bias[i,j] = q_i.Rh[qh-kh+gh-1] + q_i.Rw[qw-kw+gw-1] (equal
+                             query and key grids; see kgrid_h below otherwise)         */
   ATTN_BIAS_ADDITIVE = 3  /* bias[i,j] = add[b % add_batch, i, j]                          */
 } attn_bias_kind_t;
 
@@ -103,8 +104,22 @@ typedef enum {
  *  grid_h, grid_w: token grid of one batch item (window or image); required
  *    for TABLE and RELPOS, where Nq = Nk = grid_h * grid_w and token t sits
  *    at (t / grid_w, t % grid_w).
+ *  kgrid_h, kgrid_w: RELPOS only, BATCHED layout only: the key grid when it
+ *    differs from the query grid (both 0: the key grid is grid_h x grid_w;
+ *    must be 0 for the other kinds).  Then Nq = grid_h*grid_w,
+ *    Nk = kgrid_h*kgrid_w, and per axis (n query, m key positions) the table
+ *    row of query coordinate a and key coordinate c is
+ *    floor(a*max(m/n,1) - c*max(n/m,1) + (m-1)*max(n/m,1)) in exact
+ *    arithmetic: the shorter axis is stretched onto the longer one, as the
+ *    coordinate scalers of SAM's image encoder do ("Accelerating Generative
+ *    AI with PyTorch: Segment Anything, Fast", section "Bfloat16 half
+ *    precision").  Rh and Rw then hold 2*max(grid_h,kgrid_h)-1 and
+ *    2*max(grid_w,kgrid_w)-1 rows; tables of another length are not resized
+ *    here (ATTN_E_SHAPE in the binding; the library reads exactly that many
+ *    rows).
  *  table: [(2gh-1)(2gw-1), H] contiguous, element [r, head] at r*H + head.
- *  rh: [2gh-1, d], rw: [2gw-1, d] contiguous, shared by all heads; they are
+ *  rh: [2gh-1, d], rw: [2gw-1, d] contiguous (longer with a key grid, see
+ *    above), shared by all heads; they are
  *    dotted with the raw (unscaled) query row; the bias is not scaled.
  *  add: [add_batch, Nq, Nk] with element strides add_strides[0..1] for the
  *    first two axes, last stride 1; batch item b uses add[b % add_batch].
@@ -118,6 +133,7 @@ typedef struct {
   const void* add;
   int64_t add_batch;
   int64_t add_strides[2];
+  int32_t kgrid_h, kgrid_w;
 } attn_bias_desc_t;
 
 typedef enum {

@@ -37,7 +37,8 @@ class BiasDescC(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("table", ctypes.c_void_p), ("rh", ctypes.c_void_p), ("rw", ctypes.c_void_p),
                 ("add", ctypes.c_void_p), ("add_batch", ctypes.c_int64),
-                ("add_strides", ctypes.c_int64 * 2)]
+                ("add_strides", ctypes.c_int64 * 2), ("kgrid_h", ctypes.c_int32),
+                ("kgrid_w", ctypes.c_int32)]
 
 
 class WindowC(ctypes.Structure):
@@ -108,10 +109,16 @@ class TableBias:
 
 @dataclass
 class RelposBias:
-    """SAM decomposed relative position: Rh [2gh-1, d], Rw [2gw-1, d]."""
+    """SAM decomposed relative position: Rh [2gh-1, d], Rw [2gw-1, d].
+
+    ``kgrid`` (batched layout only): the key grid when it differs from the
+    query grid ``grid``; Rh and Rw then hold 2*max(gh, kgh)-1 and
+    2*max(gw, kgw)-1 rows and the shorter axis is stretched onto the longer.
+    """
     rh: torch.Tensor
     rw: torch.Tensor
     grid: tuple
+    kgrid: Optional[tuple] = None
 
 
 @dataclass
@@ -152,6 +159,8 @@ def _descs(bias, mask, layout: int, window: Optional[Window], keep: list):
     elif isinstance(bias, RelposBias):
         keep += [bias.rh.contiguous(), bias.rw.contiguous()]
         bd.kind, (bd.grid_h, bd.grid_w) = BIAS_RELPOS, bias.grid
+        if bias.kgrid is not None:
+            bd.kgrid_h, bd.kgrid_w = bias.kgrid
         bd.rh, bd.rw = keep[-2].data_ptr(), keep[-1].data_ptr()
     elif isinstance(bias, AdditiveBias):
         a = bias.add if bias.add.dim() == 3 else bias.add.reshape(-1, *bias.add.shape[-2:])
@@ -200,8 +209,10 @@ def _check_extents(q, k, bias, mask, lay, window):
             raise ValueError(f"table must be [{(2 * gh - 1) * (2 * gw - 1)}, {H}]")
     elif isinstance(bias, RelposBias):
         gh, gw = bias.grid
-        if tuple(bias.rh.shape) != (2 * gh - 1, D) or tuple(bias.rw.shape) != (2 * gw - 1, D):
-            raise ValueError(f"rh, rw must be [{2 * gh - 1}, {D}], [{2 * gw - 1}, {D}]")
+        kgh, kgw = bias.kgrid if bias.kgrid is not None else bias.grid
+        nh, nw = 2 * max(gh, kgh) - 1, 2 * max(gw, kgw) - 1
+        if tuple(bias.rh.shape) != (nh, D) or tuple(bias.rw.shape) != (nw, D):
+            raise ValueError(f"rh, rw must be [{nh}, {D}], [{nw}, {D}]")
     elif isinstance(bias, AdditiveBias):
         if tuple(bias.add.shape[-2:]) != (nq, nk):
             raise ValueError(f"additive bias must end in [{nq}, {nk}]")

@@ -140,11 +140,23 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   if (bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS) {
     if (bias->grid_h < 1 || bias->grid_w < 1) return ATTN_E_SHAPE;
     if (bias->grid_h > kMaxGridSide || bias->grid_w > kMaxGridSide) return ATTN_E_UNSUPPORTED;
+    // Keys on a grid of their own: relative position, batched layout only.
+    int32_t kgh = bias->grid_h, kgw = bias->grid_w;
+    if (bias->kgrid_h != 0 || bias->kgrid_w != 0) {
+      if (bias_kind != ATTN_BIAS_RELPOS || a->image) return ATTN_E_SHAPE;
+      if (bias->kgrid_h < 1 || bias->kgrid_w < 1) return ATTN_E_SHAPE;
+      if (bias->kgrid_h > kMaxGridSide || bias->kgrid_w > kMaxGridSide) return ATTN_E_UNSUPPORTED;
+      kgh = bias->kgrid_h;
+      kgw = bias->kgrid_w;
+    }
     const int64_t g = (int64_t)bias->grid_h * bias->grid_w;
-    if (nq_eff != g || nk_eff != g) return ATTN_E_SHAPE;
-    if (g > kMaxIndexedTokens) return ATTN_E_UNSUPPORTED;
+    const int64_t kg = (int64_t)kgh * kgw;
+    if (nq_eff != g || nk_eff != kg) return ATTN_E_SHAPE;
+    if (g > kMaxIndexedTokens || kg > kMaxIndexedTokens) return ATTN_E_UNSUPPORTED;
     a->gh = bias->grid_h;
     a->gw = bias->grid_w;
+    a->kgh = kgh;
+    a->kgw = kgw;
     if (bias_kind == ATTN_BIAS_TABLE) {
       if (!bias->table) return ATTN_E_NULL;
       if ((int64_t)(2 * a->gh - 1) * (2 * a->gw - 1) > 16384) return ATTN_E_UNSUPPORTED;
@@ -152,7 +164,9 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
     } else {
       if (!bias->rh || !bias->rw) return ATTN_E_NULL;
       if ((uintptr_t)bias->rh % 16 || (uintptr_t)bias->rw % 16) return ATTN_E_LAYOUT;
-      if (a->gh + a->gw > 256) return ATTN_E_UNSUPPORTED;
+      // Table rows per axis: 2 * max(query, key positions) - 1.
+      if ((a->gh > a->kgh ? a->gh : a->kgh) + (a->gw > a->kgw ? a->gw : a->kgw) > 256)
+        return ATTN_E_UNSUPPORTED;
       a->rh = bias->rh;
       a->rw = bias->rw;
     }
@@ -187,6 +201,7 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   a->fd_nwx = make_fastdiv(a->nwx);
   a->fd_win_w = make_fastdiv(a->win_w);
   a->fd_gw = make_fastdiv(a->gw);
+  a->fd_kgw = make_fastdiv(a->kgw);
 
   // Offsets inside one (batch item, head) slice are 32-bit in the kernels.
   const attn_tensor_t* ts[4] = {q, k, v, o};
@@ -235,6 +250,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return (1 << 16) | 0; }
+int attn_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

@@ -185,6 +185,17 @@ __device__ __forceinline__ int region_of(const AttnArgs& a, int w, int t) {
   return 3 * ry + rx;
 }
 
+
+// Relative-position table row of query coordinate qc and key coordinate kc
+// on an axis of qn query and kn key positions: the shorter axis is
+// stretched onto the longer one and the scaled difference floored, so that
+// rows run from 0 to at most 2*max(qn, kn)-2 (equal axes: qc - kc + kn - 1).
+__device__ __forceinline__ int rel_row(int qc, int kc, int qn, int kn) {
+  if (qn == kn) return qc - kc + kn - 1;
+  if (qn > kn) return qc + (kn - 1 - kc) * qn / kn;
+  return qc * kn / qn + (kn - 1 - kc);
+}
+
 // ---------------------------------------------------------------------------
 // Bias and mask, evaluated per (query, key) from on-chip index data.
 //
@@ -197,8 +208,8 @@ __device__ __forceinline__ int region_of(const AttnArgs& a, int w, int t) {
 struct BiasCtx {
   const int* kinfo;
   const float* tbl;   // TABLE
-  const float* relh;  // RELPOS [gh][BM]
-  const float* relw;  // RELPOS [gw][BM]
+  const float* relh;  // RELPOS [kgh][BM]
+  const float* relw;  // RELPOS [kgw][BM]
 };
 
 __host__ __device__ constexpr bool needs_kinfo(int bias_kind, bool mask) {
@@ -210,7 +221,7 @@ __host__ __device__ inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
                      a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
   size_t n = kinfo ? ((size_t)a.Nk * 4 + 15) / 16 * 16 : 0;
   if (a.bias_kind == ATTN_BIAS_TABLE) n += (size_t)(2 * a.gh - 1) * (2 * a.gw - 1) * 4;
-  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)(a.gh + a.gw) * bm * 4;
+  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)(a.kgh + a.kgw) * bm * 4;
   return n;
 }
 
@@ -230,8 +241,8 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
     for (int j = tid; j < a.Nk; j += NT) {
       int v = 0;
       if (BIAS == ATTN_BIAS_TABLE || BIAS == ATTN_BIAS_RELPOS) {
-        const int kh = fdiv(j, a.fd_gw);
-        v = kh | ((j - kh * a.gw) << 11);
+        const int kh = fdiv(j, a.fd_kgw);
+        v = kh | ((j - kh * a.kgw) << 11);
       }
       if (MASK && a.mask_kind == ATTN_MASK_SHIFT_REGIONS) v |= region_of(a, w, j) << 22;
       kinfo[j] = v;
@@ -246,21 +257,22 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
     bc.tbl = tbl;
   }
   if (BIAS == ATTN_BIAS_RELPOS) {
-    // relh[kh][i] = q_i . Rh[qh_i - kh + gh - 1], relw[kw][i] = q_i . Rw[qw_i - kw + gw - 1]
+    // relh[kh][i] = q_i . Rh[rel_row(qh_i, kh)], relw[kw][i] = q_i . Rw[rel_row(qw_i, kw)]
+    // for the kgh x kgw key grid (equal grids: Rh[qh_i - kh + gh - 1]).
     float* relh = (float*)p;
-    float* relw = relh + a.gh * BM;
-    const int nk = a.gh + a.gw;
+    float* relw = relh + a.kgh * BM;
+    const int nk = a.kgh + a.kgw;
     for (int e = tid; RELPOS_VALU && e < BM * nk; e += NT) {
       const int il = e % BM, kk = e / BM;
       const int qi = min(q0 + il, a.Nq - 1);
       const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
       const int64_t qo = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
-      const int64_t to = kk < a.gh ? (int64_t)(qh - kk + a.gh - 1) * a.D
-                                   : (int64_t)(qw - (kk - a.gh) + a.gw - 1) * a.D;
-      const void* tb = kk < a.gh ? a.rh : a.rw;
+      const int64_t to = kk < a.kgh ? (int64_t)rel_row(qh, kk, a.gh, a.kgh) * a.D
+                                    : (int64_t)rel_row(qw, kk - a.kgh, a.gw, a.kgw) * a.D;
+      const void* tb = kk < a.kgh ? a.rh : a.rw;
       float acc = 0.f;  // a padding query (qo < 0) is zero
       for (int c = 0; qo >= 0 && c < a.D; c += 4) acc += dot4<E>(a.q, qo + c, tb, to + c);
-      (kk < a.gh ? relh + kk * BM : relw + (kk - a.gh) * BM)[il] = acc * kLog2e;
+      (kk < a.kgh ? relh + kk * BM : relw + (kk - a.kgh) * BM)[il] = acc * kLog2e;
     }
     bc.relh = relh;
     bc.relw = relw;

@@ -140,16 +140,19 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   // Long key ranges with the 64-wide relative-position row form: eight-wave
   // workgroups whose two wave groups alternate matrix and softmax phases
   // (measured faster there; without a bias the four-wave kernel is faster).
+  // The row and contraction forms take equal query and key grids; keys on a
+  // grid of their own go to the general table form.
+  [[maybe_unused]] const bool rel_same_grid = a.gh == a.kgh && a.gw == a.kgw;
   if constexpr (ATTN_PP && !MASK && BIAS == ATTN_BIAS_RELPOS) {
-    if (a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256 && !a.image) {
+    if (rel_same_grid && a.gw == 64 && a.Nk >= ATTN_PP_MIN_KEYS && a.Nq >= 256 && !a.image) {
       return launch_mfma<BIAS, false, kRelRow64, 2, 8>(a, s);
     }
   }
   // Relative position: 64-wide grids take the row form, grids with
   // gh + gw <= 32 fold the bias into the QK^T contraction.
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
-    if (a.gw == 64) return launch_mfma<BIAS, false, kRelRow64, kWpeRelpos>(a, s);
-    if (a.gh + a.gw <= 32) return launch_mfma<BIAS, false, kRelAug, kWpeAug>(a, s);
+    if (rel_same_grid && a.gw == 64) return launch_mfma<BIAS, false, kRelRow64, kWpeRelpos>(a, s);
+    if (rel_same_grid && a.gh + a.gw <= 32) return launch_mfma<BIAS, false, kRelAug, kWpeAug>(a, s);
   }
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
   // Keys spanning exactly two tiles (cross-attention to short contexts):

@@ -47,7 +47,8 @@ struct AttnArgs {
   int32_t nwx, nw;
   // Bias.
   int32_t bias_kind;
-  int32_t gh, gw;
+  int32_t gh, gw;    // grid of the queries (TABLE, RELPOS)
+  int32_t kgh, kgw;  // grid of the keys (== gh, gw except for RELPOS with a key grid)
   const void* table;
   const void* rh;
   const void* rw;
@@ -60,7 +61,7 @@ struct AttnArgs {
   float mask_value;
   float scale;
   // Divisors used in index arithmetic.
-  FastDiv fd_h, fd_nw, fd_nwx, fd_win_w, fd_gw, fd_qt;
+  FastDiv fd_h, fd_nw, fd_nwx, fd_win_w, fd_gw, fd_kgw, fd_qt;
   // Filled by the launcher.
   int32_t n_qtiles;
   int32_t n_blocks;  // workgroups in the grid
@@ -77,6 +78,7 @@ int launch(const AttnArgs& a, void* stream);
 // Largest grid side accepted for TABLE/RELPOS/SHIFT_REGIONS and the largest
 // token count of a batch item for which per-key index data fits on chip.
 constexpr int kMaxGridSide = 1024;
+
 constexpr int kMaxIndexedTokens = 16384;
 
 // Token offset that marks a padding token of the image layout (no memory

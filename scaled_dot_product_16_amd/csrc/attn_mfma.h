@@ -108,7 +108,10 @@ constexpr int kAugGrow = 68;
 
 // Row length (floats) of the relative-position prologue scratch.
 inline __host__ __device__ int relpos_grow(const AttnArgs& a) {
-  const int m = 2 * (a.gh > a.gw ? a.gh : a.gw) - 1;
+  int g = a.gh > a.gw ? a.gh : a.gw;
+  g = g > a.kgh ? g : a.kgh;
+  g = g > a.kgw ? g : a.kgw;
+  const int m = 2 * g - 1;
   return (m + 15) / 16 * 16 + 4;
 }
 
@@ -474,7 +477,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       qinf[qb] = make_qinfo<BIAS, MASK>(a, b, min(q0 + il, a.Nq - 1), il);
     }
     if constexpr (BIAS == ATTN_BIAS_RELPOS && !RAUG) {
-      // relh[kh][i] = q_i . Rh[qh_i - kh + gh - 1] and relw[kw][i] likewise:
+      // relh[kh][i] = q_i . Rh[rel_row(qh_i, kh)] and relw[kw][i] likewise
+      // (kh, kw on the key grid; equal grids: Rh[qh_i - kh + gh - 1]):
       // G = R Q^T on the matrix cores for every table row, then a per-lane
       // gather through this wave's scratch rows.
       const int grow = relpos_grow(a);
@@ -488,16 +492,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const int gg = part == 0 ? a.gh : a.gw;
+          const int gg = part == 0 ? a.gh : a.gw;    // query positions on this axis
+          const int kg = part == 0 ? a.kgh : a.kgw;  // key positions
+          const int nrow = 2 * (gg > kg ? gg : kg) - 1;
           const uint16_t* tab = (const uint16_t*)(part == 0 ? a.rh : a.rw);
-          for (int mb = 0; mb * 16 < 2 * gg - 1; ++mb) {
+          for (int mb = 0; mb * 16 < nrow; ++mb) {
             const int m_row = mb * 16 + l16;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dc = 0; dc < KCH; ++dc) {
               const int d0 = dc * 32 + g * 8;
               u32x4 af = {0, 0, 0, 0};
-              if (m_row < 2 * gg - 1 && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
+              if (m_row < nrow && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
               acc = E::mfma(af, qf[qb][dc], acc);
             }
 #pragma unroll
@@ -508,7 +514,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           const int qc = part == 0 ? qh : qw;
           float* dst = part == 0 ? relh : relw;
-          for (int kk = g; kk < gg; kk += 4) dst[kk * BM + il] = gscr[l16 * grow + qc - kk + gg - 1] * kLog2e;
+          for (int kk = g; kk < kg; kk += 4) dst[kk * BM + il] = gscr[l16 * grow + rel_row(qc, kk, gg, kg)] * kLog2e;
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -43,6 +43,7 @@ class Workload:
     d: int
     bias: str = "none"           # none | table | relpos | additive
     grid: Optional[tuple] = None
+    kgrid: Optional[tuple] = None    # relpos: key grid when it differs from grid
     mask: str = "none"           # none | shift | additive
     layout: str = "batched"      # batched | image
     images: Optional[int] = None
@@ -150,17 +151,19 @@ def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0) -> dict:
                                        0.02, seed), w.dtype)
     elif w.bias == "relpos":
         gh, gw = w.grid
-        out["rh"] = to_dtype(normal((2 * gh - 1, w.d), w.cfg_id, 3, 0.02, seed), w.dtype)
-        out["rw"] = to_dtype(normal((2 * gw - 1, w.d), w.cfg_id, 4, 0.02, seed), w.dtype)
+        kgh, kgw = w.kgrid or w.grid
+        out["rh"] = to_dtype(normal((2 * max(gh, kgh) - 1, w.d), w.cfg_id, 3, 0.02, seed), w.dtype)
+        out["rw"] = to_dtype(normal((2 * max(gw, kgw) - 1, w.d), w.cfg_id, 4, 0.02, seed), w.dtype)
     return out
 
 
 def custom(dtype: str, B: int, H: int, Nq: int, Nk: int, d: int, bias: str = "none",
            grid=None, mask: str = "none", layout: str = "batched", images=None,
-           window=None, cfg_id: int = 900, key: str = "custom") -> Workload:
+           window=None, cfg_id: int = 900, key: str = "custom", kgrid=None) -> Workload:
     """A workload of arbitrary shape for tests (same drawing recipe)."""
     return Workload(key, key, cfg_id, dtype, B=B, H=H, Nq=Nq, Nk=Nk, d=d, bias=bias,
-                    grid=grid, mask=mask, layout=layout, images=images, window=window)
+                    grid=grid, kgrid=kgrid, mask=mask, layout=layout, images=images,
+                    window=window)
 
 
 def device_args(w: Workload, t: dict) -> dict:
@@ -175,7 +178,7 @@ def device_args(w: Workload, t: dict) -> dict:
     if w.bias == "table":
         kw["bias"] = B.TableBias(t["table"], w.grid)
     elif w.bias == "relpos":
-        kw["bias"] = B.RelposBias(t["rh"], t["rw"], w.grid)
+        kw["bias"] = B.RelposBias(t["rh"], t["rw"], w.grid, w.kgrid)
     elif w.bias == "additive":
         kw["bias"] = B.AdditiveBias(t["bias_add"])
     win = B.Window(*w.window) if w.window is not None else None

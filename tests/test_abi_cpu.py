@@ -39,7 +39,7 @@ def test_struct_layout_matches_header(lib):
     # The binding's structs must match the C layout (sizes on x86-64).
     assert ctypes.sizeof(B.AttnTensorC) == 8 + 32 + 24 + 8
     assert ctypes.sizeof(B.WindowC) == 24
-    assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16
+    assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16 + 8
     assert ctypes.sizeof(B.MaskDescC) == 8 + 8 + 8 + 16 + 24 + 4 + 4
 
 
@@ -47,7 +47,7 @@ def test_strerror_and_version(lib):
     for st in range(8):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(99) == b"unknown status"
-    assert lib.attn_version() >> 16 == 1
+    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 1
 
 
 def t(*shape, dtype=torch.float16):
@@ -160,3 +160,44 @@ def test_invalid_enums(lib):
     md.kind = 0
     qc.layout = 4
     assert h.attn_check(*args(), dt) == 7
+
+
+def test_key_grid_validation(lib):
+    bf = torch.bfloat16
+    rp = lambda nh, nw, kg: B.RelposBias(t(nh, 64, dtype=bf), t(nw, 64, dtype=bf), (8, 8), kg)
+    q = t(1, 2, 64, 64, dtype=bf)
+    k = t(1, 2, 256, 64, dtype=bf)
+    assert B.check(q, k, k.clone(), bias=rp(31, 31, (16, 16))) == 0
+    assert B.check(q, q.clone(), q.clone(), bias=rp(31, 31, (16, 16))) == 2  # Nk != key grid
+    k2 = t(1, 2, 32, 64, dtype=bf)
+    assert B.check(q, k2, k2.clone(), bias=rp(15, 15, (4, 8))) == 0
+    with pytest.raises(ValueError):                                         # rows must be 2*max-1
+        B.check(q, k, k.clone(), bias=rp(15, 15, (16, 16)))
+    assert B.check(q, k, k.clone(), bias=B.RelposBias(t(15, 64, dtype=bf), t(255, 64, dtype=bf),
+                                                      (8, 8), (2, 128))) == 0
+    # Per-axis table rows above the limit (2 * 200 - 1 each) are unsupported.
+    kb = t(1, 2, 200 * 200, 64, dtype=bf)
+    assert B.check(q, kb, kb.clone(), bias=B.RelposBias(t(399, 64, dtype=bf), t(399, 64, dtype=bf),
+                                                        (8, 8), (200, 200))) == 4
+    # A key grid belongs to the relative-position kind and the batched layout
+    # only; one positive and one zero side is a shape error.
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(q, k, k.clone(), q.clone(), rp(31, 31, (16, 16)),
+                                                  None, "batched", None)
+    h = B.lib()
+    args = lambda: (ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                    ctypes.byref(md), ctypes.byref(oc), dt)
+    assert h.attn_check(*args()) == 0
+    bd.kgrid_w = 0
+    assert h.attn_check(*args()) == 2
+    bd.kgrid_w = 16
+    tab = t(15 * 15, 2, dtype=bf)
+    bd.kind, bd.table = 1, tab.data_ptr()
+    assert h.attn_check(*args()) == 2
+    win = B.Window(16, 16, 8, 8, 0, 0)
+    qi = t(1, 2, 256, 64, dtype=bf)
+    qc, kc, vc, bd, md, oc, dt, keep2 = B._marshal(qi, qi.clone(), qi.clone(), qi.clone(),
+                                                   rp(15, 15, None), None, "image", win)
+    assert h.attn_check(*args()) == 0
+    bd.kgrid_h, bd.kgrid_w = 8, 8
+    assert h.attn_check(*args()) == 2
+    del keep, keep2

@@ -1,0 +1,74 @@
+"""GPU parity of the decomposed relative-position bias with the keys on a
+grid of their own (SAM's coordinate scalers: the shorter axis stretched onto
+the longer one), against the fp64 oracle, every output element.
+
+The half-precision calls take the general relative-position form of the
+tiled kernel (the row and contraction forms need equal grids); fp32 calls
+take the fp32 kernel.  Ratios are whole (2:1, 1:2), fractional in one or
+both directions, and mixed between the two axes.
+"""
+
+import sys
+
+import pytest
+
+from scaled_dot_product_16_amd import workloads as W
+from tests.helpers import TOL, check_full, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from scaled_dot_product_16_amd import binding
+    binding.lib()
+
+
+CASES = [
+    # (dtype, head dim, query grid, key grid, batch, heads)
+    (W.BF16, 64, (8, 8), (16, 16), 2, 3),      # keys at twice the resolution
+    (W.F16, 64, (14, 14), (7, 7), 2, 2),       # keys at half the resolution
+    (W.BF16, 80, (10, 6), (4, 9), 3, 2),       # fractional ratios, opposite per axis
+    (W.F16, 32, (9, 14), (14, 9), 2, 2),
+    (W.BF16, 40, (20, 20), (12, 30), 1, 2),    # several query and key tiles, ragged
+    (W.F16, 64, (1, 7), (3, 5), 4, 2),         # a single query row per image
+    (W.BF16, 64, (64, 64), (32, 32), 1, 2),    # SAM's 64x64 grid against a 32x32 one
+    (W.F32, 32, (5, 7), (7, 3), 2, 2),
+    (W.F32, 64, (6, 6), (12, 4), 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_key_grid_relpos(case):
+    dtype, d, qg, kg, B, H = CASES[case]
+    nq, nk = qg[0] * qg[1], kg[0] * kg[1]
+    w = W.custom(dtype, B=B, H=H, Nq=nq, Nk=nk, d=d, bias="relpos", grid=qg, kgrid=kg,
+                 cfg_id=560 + case)
+    say(f"[key grid relpos] {dtype} d={d} q grid {qg} k grid {kg} B={B} H={H}")
+    inp = W.make_inputs(w, seed=case)
+    err = check_full(w, inp, run_gpu(w, to_device(inp)))
+    say(f"  max abs err {err:.3e} (tol {TOL[dtype]:.0e})")
+
+
+def test_equal_key_grid_matches_no_key_grid():
+    # A key grid equal to the query grid is the plain decomposed bias: the
+    # library takes the same kernel and must give identical bytes.
+    import torch
+    from scaled_dot_product_16_amd import binding as Bd
+
+    w = W.custom(W.BF16, B=2, H=2, Nq=196, Nk=196, d=64, bias="relpos", grid=(14, 14),
+                 cfg_id=580)
+    say("[key grid relpos] explicit equal key grid, 14x14")
+    t = to_device(W.make_inputs(w, seed=3))
+    a = Bd.fwd(t["q"], t["k"], t["v"], bias=Bd.RelposBias(t["rh"], t["rw"], (14, 14)))
+    b = Bd.fwd(t["q"], t["k"], t["v"], bias=Bd.RelposBias(t["rh"], t["rw"], (14, 14), (14, 14)))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
