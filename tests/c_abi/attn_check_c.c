@@ -107,6 +107,27 @@ int main(void) {
   expect("padded image relpos", attn_check(&qi, &ki, &vi, &rp, &geo, &oi, ATTN_BF16), ATTN_OK);
   geo.win.win_h = 0;
   expect("window of zero rows", attn_check(&qi, &ki, &vi, &rp, &geo, &oi, ATTN_BF16), ATTN_E_SHAPE);
+  geo.win.win_h = 14;
+  rp.kgrid_h = rp.kgrid_w = 7;
+  expect("key grid in the image layout", attn_check(&qi, &ki, &vi, &rp, &geo, &oi, ATTN_BF16),
+         ATTN_E_SHAPE);
+
+  /* SAM global queries on the 64x64 grid against keys on a 32x32 grid: the
+   * tables keep 2*64-1 rows. */
+  attn_tensor_t qg = tensor(1 * GiB, 1, 12, 4096, 64, ATTN_LAYOUT_BATCHED);
+  attn_tensor_t kg = tensor(2 * GiB, 1, 12, 1024, 64, ATTN_LAYOUT_BATCHED);
+  attn_tensor_t vg = tensor(3 * GiB, 1, 12, 1024, 64, ATTN_LAYOUT_BATCHED);
+  attn_tensor_t og = tensor(4 * GiB, 1, 12, 4096, 64, ATTN_LAYOUT_BATCHED);
+  attn_bias_desc_t kgb;
+  memset(&kgb, 0, sizeof kgb);
+  kgb.kind = ATTN_BIAS_RELPOS;
+  kgb.grid_h = kgb.grid_w = 64;
+  kgb.kgrid_h = kgb.kgrid_w = 32;
+  kgb.rh = (void*)(5 * GiB);
+  kgb.rw = (void*)(6 * GiB);
+  expect("key grid relpos", attn_check(&qg, &kg, &vg, &kgb, NULL, &og, ATTN_BF16), ATTN_OK);
+  kgb.kgrid_w = 16;
+  expect("key grid size mismatch", attn_check(&qg, &kg, &vg, &kgb, NULL, &og, ATTN_BF16), ATTN_E_SHAPE);
 
   if (attn_strerror(ATTN_E_SHAPE) == NULL || attn_strerror(12345) == NULL) {
     printf("FAIL attn_strerror returned NULL\n");
