@@ -41,6 +41,8 @@ CASES = [
     (W.BF16, 40, (20, 20), (12, 30), 1, 2),    # several query and key tiles, ragged
     (W.F16, 64, (1, 7), (3, 5), 4, 2),         # a single query row per image
     (W.BF16, 64, (64, 64), (32, 32), 1, 2),    # SAM's 64x64 grid against a 32x32 one
+    (W.BF16, 64, (8, 8), (2, 64), 1, 2),       # a long, thin key grid (Rw of 127 rows)
+    (W.F16, 32, (1, 1), (16, 16), 3, 2),       # one query
     (W.F32, 32, (5, 7), (7, 3), 2, 2),
     (W.F32, 64, (6, 6), (12, 4), 1, 2),
 ]
@@ -72,3 +74,23 @@ def test_equal_key_grid_matches_no_key_grid():
     b = Bd.fwd(t["q"], t["k"], t["v"], bias=Bd.RelposBias(t["rh"], t["rw"], (14, 14), (14, 14)))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_key_grid_tables_too_large_for_lds_are_rejected():
+    # Keys on a 2 x 128 grid: the per-query relative terms (130 rows) and the
+    # 255-row prologue scratch do not fit one workgroup's LDS next to the K/V
+    # tiles, so the launch is refused with E_UNSUPPORTED and nothing runs.
+    import torch
+    from scaled_dot_product_16_amd import binding as Bd
+
+    w = W.custom(W.BF16, B=1, H=2, Nq=64, Nk=256, d=64, bias="relpos", grid=(8, 8), kgrid=(2, 128),
+                 cfg_id=581)
+    say("[key grid relpos] 8x8 queries, 2x128 keys: E_UNSUPPORTED, nothing launched")
+    dev = to_device(W.make_inputs(w, seed=4))
+    assert Bd.check(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev)) == 0
+    out = torch.full_like(dev["q"], 7.0)
+    with pytest.raises(Bd.AttnError) as e:
+        Bd.fwd(dev["q"], dev["k"], dev["v"], out=out, **W.device_args(w, dev))
+    assert e.value.status == 4
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
