@@ -921,7 +921,12 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         const int c0 = cb * 16 + g * 4;
         if (c0 < D) {
           const f32x4 v = o[cb][qb] * inv;
-          *(u32x2*)(obase + off + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+          const u32x2 packed = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+          // Streaming (non-temporal) stores where O is most of the traffic
+          // (cross-attention to a short context): measured faster there,
+          // slower in the contraction form, neutral in the long-key forms.
+          if constexpr (TWO) __builtin_nontemporal_store(packed, (u32x2*)(obase + off + c0));
+          else *(u32x2*)(obase + off + c0) = packed;
         }
       }
     }
