@@ -907,6 +907,47 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).
   uint16_t* obase = (uint16_t*)a.o + tok_base(a, a.o_sb, a.o_sh, b, h);
   constexpr int LB = D / 16, LG = (D % 16) / 4, LR = D % 4;
+#ifndef ATTN_STAGE_O
+#define ATTN_STAGE_O 1
+#endif
+  // Two-tile form with rows stored back to back: a wave's NQB*16 output rows
+  // are one contiguous span.  It is staged through LDS (the K/V stages are
+  // free by now) and stored as 16-byte chunks, so each streaming store
+  // covers whole lines instead of 8-byte pieces of four rows.
+  if constexpr (ATTN_STAGE_O && TWO && !IMG && D % 8 == 0) {
+    if (a.o_sn == D && ((a.o_sb | a.o_sh) & 7) == 0) {
+      static_assert((size_t)NW * NQB * 16 * D * 2 <= C::KV_BYTES, "O staging must fit the K/V stages");
+      __syncthreads();  // every wave has finished reading K and V
+      uint16_t* stage = (uint16_t*)lds + wave * (NQB * 16 * D);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float lsum;
+        if constexpr (C::ONES) lsum = __shfl(o[LB < CB ? LB : 0][qb][LR], LG * 16 + l16);
+        else lsum = sum_across_groups(l[qb]);
+        const float inv = 1.f / lsum;
+        const int r = qb * 16 + (kLean ? lane_id_here() & 15 : l16);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int c0 = cb * 16 + g * 4;
+          if (c0 < D) {
+            const f32x4 v = o[cb][qb] * inv;
+            *(u32x2*)(stage + r * D + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int row0 = q0 + wq0;
+      uint16_t* dst = obase + (int64_t)row0 * D;
+      constexpr int NCH = NQB * 16 * D / 8;  // 16-byte chunks of the span
+      for (int c = lane_id_here(); c < NCH; c += 64) {
+        if (row0 + c * 8 / D < a.Nq)  // rows past Nq are not stored
+          __builtin_nontemporal_store(*(const u32x4*)(stage + c * 8), (u32x4*)(dst + c * 8));
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     float lsum;
