@@ -13,7 +13,7 @@ import sys
 import pytest
 
 from scaled_dot_product_16_amd import workloads as W
-from tests.helpers import TOL, check_full, run_gpu, to_device
+from tests.helpers import TOL, check_full, run_gpu, to_device, with_dense_terms
 
 pytestmark = pytest.mark.gpu
 
@@ -94,3 +94,15 @@ def test_key_grid_tables_too_large_for_lds_are_rejected():
     assert e.value.status == 4
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_key_grid_relpos_with_additive_mask(dtype):
+    # The relative terms on a key grid plus a dense [3, Nq, Nk] mask used as
+    # b % 3: both go through the per-score lookup of the general form.
+    w = W.custom(dtype, B=6, H=2, Nq=60, Nk=72, d=64 if dtype == W.BF16 else 32, bias="relpos",
+                 grid=(6, 10), kgrid=(8, 9), mask="additive", cfg_id=582)
+    say(f"[key grid relpos] {dtype} 6x10 queries, 8x9 keys, additive mask [3, 60, 72]")
+    inp = with_dense_terms(w, W.make_inputs(w, seed=5), n_mask=3)
+    err = check_full(w, inp, run_gpu(w, to_device(inp)))
+    say(f"  max abs err {err:.3e} (tol {TOL[dtype]:.0e})")
