@@ -2,19 +2,30 @@
 
 A step is one attn_fwd call over one batch of the workload (all steps of the
 path: validation, address folding, tile loads, QK^T, bias, mask, online
-softmax, PV, epilogue).  Default workload: Swin-T stage-1 shifted-window
+softmax, PV, epilogue).  Headline workload: Swin-T stage-1 shifted-window
 attention (8 images of 56x56 tokens, 7x7 windows, shift 3, 3 heads, d=32,
 f16, table bias and region mask, image layout).  ``--config`` selects another
-workload (C1, C2, C3, C3i, C4, C4h, C5s, C5x; C3i is C3 read from the
-unpadded 64x64 token image in the image layout).
+headline (C1, C2, C3, C3i, C4, C4h, C5s, C5x; C3i is C3 read from the
+unpadded 64x64 token image in the image layout).  Every other workload is
+timed in the same run and reported under ``workloads`` (``--extra`` picks
+them, ``--extra none`` skips them).
 
 Inputs are resident in HBM before timing starts.  Several copies of the input
 set rotate so that every launch reads data that is not in the 256 MB
 Infinity Cache (at least 512 MB of distinct buffers in total).
 
-Prints one JSON line with the throughput, a roofline record for the kernel
-(algorithmic bytes or flops per launch over the mean launch duration measured
-with HIP events on the launch stream) and the oracle's CPU throughput.
+Timing: the K steps are captured into a HIP graph; a second graph of
+back-to-back launches (at least --settle-ms of GPU time) is queued first and
+the timed graph right behind it, so the clocks have ramped up and the GPU
+never idles before the timed launches; HIP events on the launch stream
+bracket exactly the K timed steps, with device synchronisations before the
+settle work and after the timed replay.
+
+Prints one JSON line: the headline's throughput, its roofline record (bytes
+or flops per launch over the mean launch duration), its max-abs error
+against the fp64 oracle, the oracle's CPU throughput (process pool on the
+host cores), a plain device copy of the headline's bytes measured the same
+way (the copy floor), and one record per extra workload.
 """
 
 from __future__ import annotations
@@ -36,6 +47,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_MFMA_TFLOPS = 2500.0      # dense bf16/fp16 MFMA
 PEAK_F32_TFLOPS = 157.3        # fp32 vector
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+ALL = ["C1", "C2", "C3", "C3i", "C4", "C4h", "C5s", "C5x"]
+TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 2e-2}
 
 
 def kernel_source_hash() -> str:
@@ -86,45 +99,207 @@ def device_clocks(dev: int) -> dict:
     return out
 
 
-def cpu_baseline(w, budget_s: float = 10.0):
-    """Time the fp64 oracle on this host on a bounded sample of the workload."""
-    import numpy as np
+def sample_units(w, limit: int):
+    """Up to ``limit`` units of the workload, spread evenly (first and last
+    included)."""
+    from oracle import pool
 
-    import oracle
-    from scaled_dot_product_16_amd import workloads as W
+    units = pool.units_of(w)
+    if len(units) <= limit:
+        return units
+    idx = sorted({round(i * (len(units) - 1) / (limit - 1)) for i in range(limit)})
+    return [units[i] for i in idx]
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    inp = W.make_inputs(w)
-    arrs = {k: v.double().numpy() for k, v in inp.items()}
-    if w.layout == "image":
-        # Whole workload per repetition.
-        flops_per_rep = w.flops
-        sample = f"whole workload ({w.B} windows x {w.H} heads), repeated"
-        run = lambda: oracle.run_workload(w, arrs)
+
+def oracle_error(w, inp: dict, out, limit: int):
+    """Max-abs error of the GPU output against the fp64 oracle on a sample of
+    units (every output row of each), oracle units spread over the pool."""
+    from oracle import pool
+
+    units = sample_units(w, limit)
+    with pool.UnitPool(dict(inp, out=out.detach().to("cpu")), pool.spec_of(w)) as P:
+        res = P.compare(units)
+    kind = "(image, head)" if w.layout == "image" else "(batch item, head)"
+    return {"max_abs_err": max(r["err"] for r in res), "tol": TOL[w.dtype],
+            "err_sample": f"{len(units)} of {len(pool.units_of(w))} {kind} units, every output row"}
+
+
+def cpu_baseline(w, inp: dict, budget_s: float):
+    """The fp64 oracle on this host's cores (one process per core, single-
+    threaded BLAS), on a bounded sample of the workload's units."""
+    from oracle import pool
+
+    units = pool.units_of(w)
+    unit_flops = w.flops // len(units)
+    with pool.UnitPool(inp, pool.spec_of(w)) as P:
+        n = P.workers
+        # Size the sample from one round of one unit per worker.
+        t1 = P.time_units(units[:n])
+        per_round = max(t1, 1e-3)
+        rounds = max(1, int(budget_s / per_round))
+        sample = [units[i % len(units)] for i in range(rounds * n)]
+        t = P.time_units(sample)
+    kind = "(image, head)" if w.layout == "image" else "(batch item, head)"
+    return {"value": round(unit_flops * len(sample) / t / 1e12, 6), "unit": "TFLOP/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"{len(sample)} {kind} units of the workload (its {len(units)} units cycled), "
+                      f"every output row, {t:.1f} s on a pool of {n} processes with single-threaded "
+                      f"BLAS, numpy float64"}
+
+
+def roofline_of(w, mean_ms: float, timing: str):
+    flops, nbytes = w.flops, w.algorithmic_bytes
+    ai = flops / nbytes
+    if w.dtype == "f32":
+        bound = "hbm" if ai < PEAK_F32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "alu"
     else:
-        # A fixed set of (batch item, head) units, every query row of each.
-        units = []
-        rng = np.random.default_rng(7)
-        cost_unit = 4 * w.Nq * w.Nk * w.d
-        n_units = max(1, min(w.B * w.H, int(2e9 // cost_unit)))
-        for _ in range(n_units):
-            units.append((int(rng.integers(w.B)), int(rng.integers(w.H)), np.arange(w.Nq)))
-        flops_per_rep = cost_unit * n_units
-        sample = f"{n_units} (batch item, head) units, all query rows, repeated"
-        run = lambda: oracle.run_workload(w, arrs, select=units)
-    reps, t_total = 0, 0.0
-    while reps < 1 or t_total < budget_s:
-        t0 = time.perf_counter()
-        run()
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return {"value": round(flops_per_rep * reps / t_total / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{sample} {reps}x, {t_total:.1f} s, numpy float64"}
+        bound = "hbm" if ai < RIDGE else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = nbytes / (mean_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    elif bound == "alu":
+        achieved, peak, unit = flops / (mean_ms * 1e-3) / 1e12, PEAK_F32_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = flops / (mean_ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_record(w),
+            "kernel_mean_ms": round(mean_ms, 6), "timing": timing}
+
+
+def config_of(w):
+    cfg = {"workload": w.name, "batch_items": w.B, "heads": w.H, "q_tokens": w.Nq,
+           "kv_tokens": w.Nk, "head_dim": w.d, "bias": w.bias, "mask": w.mask,
+           "layout": w.layout}
+    if w.window:
+        cfg["image"] = f"{w.images}x{w.window[0]}x{w.window[1]}"
+        cfg["window"] = f"{w.window[2]}x{w.window[3]}"
+        cfg["shift"] = list(w.window[4:])
+    if w.grid:
+        cfg["grid"] = list(w.grid)
+    return cfg
+
+
+def timed_graph(torch, stream, step, K: int, settle_ms: float):
+    """Capture K launches of ``step(i)`` into a graph, size a settle graph of
+    about ``settle_ms`` of GPU time from one timed replay of it, then queue
+    the settle graph and the timed one right behind it, between two events;
+    return the timed milliseconds, a note and the graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    est_ms = t0.elapsed_time(t1) / K
+    n_settle = max(2 * K, min(20000, math.ceil(settle_ms / max(est_ms, 1e-4))))
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        for i in range(n_settle):
+            step(i)
+    torch.cuda.synchronize()
+    gs.replay()
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del gs
+    note = (f"HIP graph of K launches queued directly behind a graph of {n_settle} untimed "
+            f"back-to-back launches (about {settle_ms:.0f} ms of clock settling, no idle gap); "
+            f"HIP events around the K")
+    return t0.elapsed_time(t1), note, g
+
+
+def run_workload(torch, W, binding, w, K: int, warmup: int, settle_ms: float, no_graph: bool,
+                 check_units: int, fwd_kw=None):
+    """Time workload ``w``: rotating input sets, eager warmup, oracle check of
+    the first output, then the graph-timed K steps.  ``fwd_kw``: extra
+    arguments of the call (e.g. window_heads)."""
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    base = {k: v.to(dev) for k, v in inp.items()}
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
+        base["q"].numel() * base["q"].element_size()
+    n_sets = max(1, math.ceil(512e6 / set_bytes))
+    sets = []
+    for i in range(n_sets):
+        s = {k: (v.clone() if k in ("q", "k", "v") else v) for k, v in base.items()}
+        s["out"] = torch.empty_like(base["q"])
+        s["kw"] = dict(W.device_args(w, s), **(fwd_kw or {}))
+        sets.append(s)
+    del base
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % n_sets]
+        binding.fwd(s["q"], s["k"], s["v"], out=s["out"], **s["kw"])
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    rec = {}
+    if check_units:
+        rec.update(oracle_error(w, inp, sets[0]["out"], check_units))
+    if no_graph:
+        # Eager launches with an event pair around each one (profiler runs).
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(a.elapsed_time(b) for a, b in ev)
+        note = "eager launches, HIP event pair per launch"
+    else:
+        ref = sets[0]["out"].clone()
+        total_ms, note, g = timed_graph(torch, stream, step, K, settle_ms)
+        # A replay rewrites set 0's output from set 0's inputs: it must equal
+        # the eager result.
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(sets[0]["out"], ref):
+            raise RuntimeError(f"{w.key}: graph replay output differs from the eager output")
+        del g
+    ms = total_ms / K
+    rec.update({"ms_per_step": round(ms, 6), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 4),
+                "gb_per_s": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 2),
+                "flops_per_step": w.flops, "algorithmic_bytes_per_step": w.algorithmic_bytes,
+                "rotating_input_sets": n_sets, "roofline": roofline_of(w, ms, note)})
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
+def copy_floor(torch, nbytes: int, K: int, settle_ms: float):
+    """A plain device copy moving ``nbytes`` in all (half read, half written),
+    on rotating cold buffers, timed like the attention steps."""
+    dev = torch.device("cuda:0")
+    n = nbytes // 2 // 2  # f16 elements read (and written) per copy
+    n_sets = max(2, math.ceil(512e6 / (4 * n)))
+    src = [torch.ones(n, dtype=torch.float16, device=dev) for _ in range(n_sets)]
+    dst = [torch.empty_like(src[0]) for _ in range(n_sets)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        dst[i % n_sets].copy_(src[i % n_sets])
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    total_ms, note, g = timed_graph(torch, stream, step, K, settle_ms)
+    del g, src, dst
+    torch.cuda.empty_cache()
+    us = total_ms / K * 1e3
+    return {"us": round(us, 3), "bytes_moved": 4 * n, "gb_per_s": round(4 * n / (us * 1e-6) / 1e9, 1),
+            "what": f"torch copy_ of {2 * n} bytes of f16 into another buffer (read {2 * n}, write "
+                    f"{2 * n}: the headline's algorithmic bytes), {n_sets} rotating buffer pairs, "
+                    f"timed like the attention steps"}
 
 
 def copy_calibration(torch, mib: int):
@@ -148,9 +323,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=50.0,
-                    help="GPU time of untimed graph replays before the timed one (clock ramp-up)")
-    ap.add_argument("--config", default="C2")
+                    help="GPU time of the untimed launches queued right before the timed ones")
+    ap.add_argument("--config", default="C2", help="headline workload")
+    ap.add_argument("--extra", default="all",
+                    help="comma-separated workloads also timed in this run ('all' or 'none'; "
+                         "C2p is C2 with 3 heads of a window per workgroup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle error checks")
+    ap.add_argument("--check-units", type=int, default=16,
+                    help="oracle units compared per workload (the headline: all of them)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches with per-launch events instead of a graph replay")
@@ -163,6 +344,12 @@ def main():
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    need_pool = not (args.no_cpu_baseline and args.no_check) and not args.copy_calibration
+    if need_pool:
+        # The oracle's worker pool starts before the GPU is initialised.
+        from oracle import pool
+        pool.start()
+
     import torch
 
     if args.copy_calibration:
@@ -172,157 +359,72 @@ def main():
     from scaled_dot_product_16_amd import binding
     from scaled_dot_product_16_amd import workloads as W
 
-    w = W.WORKLOADS[args.config]
-    dev = torch.device("cuda:0")
     binding.lib()
-    inp = W.make_inputs(w)
-    base = {k: v.to(dev) for k, v in inp.items()}
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
-        base["q"].numel() * base["q"].element_size()
-    n_sets = max(1, math.ceil(512e6 / set_bytes))
-    sets = []
-    for i in range(n_sets):
-        s = {k: (v.clone() if k in ("q", "k", "v") else v) for k, v in base.items()}
-        s["out"] = torch.empty_like(base["q"])
-        s["kw"] = W.device_args(w, s)
-        sets.append(s)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        s = sets[i % n_sets]
-        binding.fwd(s["q"], s["k"], s["v"], out=s["out"], **s["kw"])
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
+    w = W.WORKLOADS[args.config]
     K = args.steps
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
-        # Eager launches with an event pair around each one.
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)]
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(K):
-            ev[i][0].record(stream)
-            step(i)
-            ev[i][1].record(stream)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_start.elapsed_time(t_end)
-        launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
-        mean_launch_ms = sum(launch_ms) / K
-        median_launch_ms = launch_ms[K // 2]
-        timing = "eager launches, HIP event pair per launch"
-    else:
-        # The K steps are captured once into a HIP graph (the library never
-        # allocates or synchronises, so its launches capture as-is) and the
-        # graph is replayed: back-to-back dispatches without host launch gaps.
-        # The replayed result is checked against the eager one first.
-        ref = sets[0]["out"].clone()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(sets[0]["out"], ref):
-            raise RuntimeError("graph replay output differs from the eager output")
-        # After an idle gap the clocks take some 10-20 ms of sustained work to
-        # ramp up: untimed back-to-back replays (about --settle-ms of GPU
-        # time, at most 30 of them: hundreds of replays of microsecond
-        # kernels made the following timed replay noisier, not steadier) come
-        # before the timed one, so it measures the steady state.
-        w0 = torch.cuda.Event(enable_timing=True)
-        w1 = torch.cuda.Event(enable_timing=True)
-        w0.record(stream)
-        g.replay()
-        w1.record(stream)
-        torch.cuda.synchronize()
-        n_settle = min(30, max(2, math.ceil(args.settle_ms / max(w0.elapsed_time(w1), 1e-3))))
-        for _ in range(n_settle):
-            g.replay()
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        g.replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_start.elapsed_time(t_end)
-        mean_launch_ms = median_launch_ms = total_ms / K
-        timing = (f"HIP graph of K launches, HIP events around one replay, after {n_settle + 1} "
-                  f"untimed back-to-back replays that settle the clocks")
-    ms_per_step = total_ms / K
+    head_units = 0
+    if not args.no_check:
+        from oracle import pool as opool
+        head_units = len(opool.units_of(w))  # the headline is checked on every unit
+    rec, inp = run_workload(torch, W, binding, w, K, args.warmup, args.settle_ms, args.no_graph,
+                            head_units)
+    ms_per_step = rec["ms_per_step"]
 
-    flops = w.flops
-    nbytes = w.algorithmic_bytes
-    tflops = flops / (ms_per_step * 1e-3) / 1e12
-    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
-    ai = flops / nbytes
-    if w.dtype == W.F32:
-        bound = "hbm" if ai < PEAK_F32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "alu"
-    else:
-        bound = "hbm" if ai < RIDGE else "mfma"
-    if bound == "hbm":
-        achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
-        peak, unit = PEAK_HBM_GBS, "GB/s"
-    elif bound == "alu":
-        achieved = flops / (mean_launch_ms * 1e-3) / 1e12
-        peak, unit = PEAK_F32_TFLOPS, "TFLOP/s"
-    else:
-        achieved = flops / (mean_launch_ms * 1e-3) / 1e12
-        peak, unit = PEAK_MFMA_TFLOPS, "TFLOP/s"
-
-    cfg = {"workload": w.name, "batch_items": w.B, "heads": w.H, "q_tokens": w.Nq,
-           "kv_tokens": w.Nk, "head_dim": w.d, "bias": w.bias, "mask": w.mask,
-           "layout": w.layout}
-    if w.window:
-        cfg["image"] = f"{w.images}x{w.window[0]}x{w.window[1]}"
-        cfg["window"] = f"{w.window[2]}x{w.window[3]}"
-        cfg["shift"] = list(w.window[4:])
-    if w.grid:
-        cfg["grid"] = list(w.grid)
-
-    props = torch.cuda.get_device_properties(dev)
+    props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
-              "compute_units": props.multi_processor_count, **device_clocks(dev.index or 0),
+              "compute_units": props.multi_processor_count, **device_clocks(0),
               "hip": torch.version.hip, "torch": torch.__version__,
               "peaks": {"hbm_GBs": PEAK_HBM_GBS, "bf16_fp16_mfma_TFLOPs": PEAK_MFMA_TFLOPS,
                         "fp32_TFLOPs": PEAK_F32_TFLOPS}}
     line = {
         "metric": METRIC,
-        "value": round(tflops, 4),
+        "value": rec["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.02^2) tables)",
-        "config": cfg,
-        "gb_per_s": round(gbs, 2),
-        "flops_per_step": flops,
-        "algorithmic_bytes_per_step": nbytes,
-        "rotating_input_sets": n_sets,
+        "config": config_of(w),
+        "gb_per_s": rec["gb_per_s"],
+        "flops_per_step": w.flops,
+        "algorithmic_bytes_per_step": w.algorithmic_bytes,
+        "rotating_input_sets": rec["rotating_input_sets"],
         "device": device,
-        "roofline": {
-            "bound": bound,
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic_record(w),
-            "kernel_mean_ms": round(mean_launch_ms, 6),
-            "kernel_median_ms": round(median_launch_ms, 6),
-            "timing": timing,
-        },
+        "roofline": rec["roofline"],
     }
+    for key in ("max_abs_err", "tol", "err_sample"):
+        if key in rec:
+            line[key] = rec[key]
+    if not args.no_graph:
+        line["copy_floor"] = copy_floor(torch, w.algorithmic_bytes, K, args.settle_ms)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    extra = [] if args.extra == "none" else (ALL + ["C2p"] if args.extra == "all" else args.extra.split(","))
+    if extra:
+        line["workloads"] = {}
+        for key in extra:
+            if key == args.config:
+                continue
+            # C2p: the Swin-T workload with its 3 heads of a window packed
+            # into one workgroup (the packed short-sequence form).
+            we = W.WORKLOADS["C2" if key == "C2p" else key]
+            fkw = {"window_heads": 3} if key == "C2p" else None
+            r, _ = run_workload(torch, W, binding, we, K, args.warmup, args.settle_ms, args.no_graph,
+                                0 if args.no_check else args.check_units, fwd_kw=fkw)
+            r["config"] = config_of(we)
+            if fkw:
+                r["config"].update(fkw)
+            r["dtype"] = we.dtype
+            line["workloads"][key] = r
+            print(f"# {key} {we.name}: {r['ms_per_step'] * 1e3:.2f} us, "
+                  f"{r['roofline']['frac']:.3f} of {r['roofline']['bound']} peak"
+                  + (f", max abs err {r['max_abs_err']:.2e}" if "max_abs_err" in r else ""),
+                  file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 

@@ -83,8 +83,8 @@ typedef enum { ATTN_LAYOUT_BATCHED = 0, ATTN_LAYOUT_IMAGE = 1 } attn_layout_t;
 
 /* A strided 4-D tensor [B, H, N, d]; the d stride is 1.
  * strides[] are in ELEMENTS for the B, H and N axes.  `data` must be 16-byte
- * aligned and every row (N stride * element size) a multiple of 16 bytes for
- * the half-precision types (4 bytes for f32).                               */
+ * aligned and every stride a multiple of 16 bytes (8 elements for f16/bf16,
+ * 4 for f32): the kernels move rows in 16-byte pieces (ATTN_E_LAYOUT).      */
 typedef struct {
   void* data;
   int64_t dims[4];
@@ -186,8 +186,13 @@ typedef struct {
  *
  *  Supported: d in {32, 40, 64, 80} for F16/BF16; d <= 128, d % 4 == 0 for
  *  F32.  Nq, Nk >= 1.  Within one (batch item, head) slice every element
- *  offset, (N-1)*N-stride + d, must be below 2^31 (else ATTN_E_UNSUPPORTED).  TABLE/RELPOS/SHIFT_REGIONS need Nq == Nk ==
- *  grid_h*grid_w (SHIFT_REGIONS: == win_h*win_w).
+ *  offset, (N-1)*N-stride + d, must be below 2^31 (else
+ *  ATTN_E_UNSUPPORTED).  TABLE/RELPOS/SHIFT_REGIONS need Nq == Nk ==
+ *  grid_h*grid_w (SHIFT_REGIONS: == win_h*win_w).  A call whose kernel would
+ *  need more than the 160 KiB of LDS of one CU for its tiles and per-query
+ *  bias tables (RELPOS on large grids other than 64 wide, key grids with
+ *  long axes) returns ATTN_E_UNSUPPORTED; so does a grid of more than
+ *  2^31-1 workgroups.
  *  Returns ATTN_OK after queueing the kernel, or an error code (nothing is
  *  queued on error).  Asynchronous: kernel faults surface at the caller's
  *  next synchronisation.                                                     */
@@ -196,16 +201,50 @@ ATTN_API int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn
              const attn_tensor_t* out, int32_t dtype, void* stream);
 
 /* attn_check: the validation attn_fwd performs, without touching the GPU.
- * Same arguments minus the stream; returns the status attn_fwd would return
- * for an argument error (ATTN_OK if the call is valid).                      */
+ * Same arguments minus the stream; returns the status attn_fwd returns for
+ * the same arguments, short of a launch failure (ATTN_OK if attn_fwd would
+ * queue the kernel), including ATTN_E_UNSUPPORTED for calls whose tiles
+ * and tables do not fit in LDS.                                              */
 ATTN_API int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
                const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
                const attn_tensor_t* out, int32_t dtype);
 
+/* Options of attn_fwd_opt / attn_check_opt.
+ *  window_heads: for windows of at most 64 tokens in half precision (TABLE
+ *    or no bias, SHIFT_REGIONS or no mask), how many heads of one window
+ *    share a workgroup.  0: the library's choice (currently one head per
+ *    workgroup, the fastest form measured on MI355X for Swin windows);
+ *    1: one head per workgroup; 2, 3 or 4: that many heads of a window per
+ *    workgroup, which then computes the window's index data (key offsets,
+ *    region labels, table staging) once for all of them -- the short-
+ *    sequence packing of windows into workgroups.  A value that does not
+ *    divide H, a value above 4, or a call outside the short-sequence path
+ *    with a value above 1 returns ATTN_E_UNSUPPORTED (negative: E_INVALID).
+ *  Zero-initialise the struct: fields added later keep 0 as "library's
+ *  choice".                                                                  */
+typedef struct {
+  int32_t window_heads;
+  int32_t reserved[7];
+} attn_options_t;
+
+/* attn_fwd_opt / attn_check_opt: attn_fwd / attn_check with options (NULL:
+ * all defaults, identical to attn_fwd / attn_check).  The packing of Swin
+ * windows into workgroups is described for the method's short sequences
+ * ("Training and inference acceleration for large vision models", section 1:
+ * attention inside each window).                                             */
+ATTN_API int attn_fwd_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                 const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+                 const attn_tensor_t* out, int32_t dtype, const attn_options_t* options,
+                 void* stream);
+ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                   const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+                   const attn_tensor_t* out, int32_t dtype, const attn_options_t* options);
+
 /* attn_strerror: static text for a status code (never NULL).                */
 ATTN_API const char* attn_strerror(int status);
 
-/* attn_version: library ABI version, (major << 16) | minor.                 */
+/* attn_version: library ABI version, (major << 16) | minor (1.2 added
+ * attn_fwd_opt and attn_check_opt).                                          */
 ATTN_API int attn_version(void);
 
 #ifdef __cplusplus

@@ -51,6 +51,10 @@ class MaskDescC(ctypes.Structure):
                 ("add_strides", ctypes.c_int64 * 2), ("win", WindowC), ("value", ctypes.c_float)]
 
 
+class OptionsC(ctypes.Structure):
+    _fields_ = [("window_heads", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"attn: {STATUS.get(status, status)}: {msg}")
@@ -75,6 +79,13 @@ def lib() -> ctypes.CDLL:
         h.attn_check.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
                                  P(MaskDescC), P(AttnTensorC), ctypes.c_int32]
         h.attn_check.restype = ctypes.c_int
+        h.attn_fwd_opt.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
+                                   P(MaskDescC), P(AttnTensorC), ctypes.c_int32, P(OptionsC),
+                                   ctypes.c_void_p]
+        h.attn_fwd_opt.restype = ctypes.c_int
+        h.attn_check_opt.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
+                                     P(MaskDescC), P(AttnTensorC), ctypes.c_int32, P(OptionsC)]
+        h.attn_check_opt.restype = ctypes.c_int
         h.attn_strerror.argtypes = [ctypes.c_int]
         h.attn_strerror.restype = ctypes.c_char_p
         h.attn_version.argtypes = []
@@ -239,18 +250,34 @@ def _marshal(q, k, v, out, bias, mask, layout, window):
             _tensor_c(out, lay), DTYPES[q.dtype], keep)
 
 
+def _options(window_heads: Optional[int]):
+    if window_heads is None:
+        return None
+    o = OptionsC()
+    o.window_heads = int(window_heads)
+    return ctypes.byref(o)
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         out: Optional[torch.Tensor] = None, layout: str = "batched",
-        window: Optional[Window] = None, stream=None) -> torch.Tensor:
+        window: Optional[Window] = None, stream=None,
+        window_heads: Optional[int] = None) -> torch.Tensor:
     """O = softmax(QK^T/sqrt(d) + bias + mask) V on the GPU via libattn.
 
     q: [B, H, Nq, d], k, v: [B, H, Nk, d] CUDA (HIP) tensors, last stride 1.
     layout "image": tensors are [B_img, H, img_h*img_w, d] and ``window`` (or
     the ShiftMask's window) gives the window geometry.  ``out`` may be given;
     otherwise it is allocated with torch.  Queued on ``stream`` (default:
-    torch's current stream); no synchronisation.
+    torch's current stream; a ``torch.cuda.Stream`` or a raw hipStream_t
+    handle), with no host synchronisation.  ``window_heads`` (windows of at
+    most 64 tokens): heads of one window per workgroup (None or 0: the
+    library's choice), passed to attn_fwd_opt.  On another stream than the current
+    one, the kernel is ordered after the work already queued on the current
+    stream (where this function makes its temporaries), and those
+    temporaries stay allocated until the kernel's stream has run it.
     """
     h = lib()
+    allocated = out is None
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if q.numel() == 0 and k.dim() == 4 and k.shape[2] > 0:
@@ -260,12 +287,26 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         # keys is undefined): the library rejects them.
         return out
     qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
+    cur = torch.cuda.current_stream(q.device)
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    st = h.attn_fwd(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
-                    ctypes.byref(md), ctypes.byref(oc), dt, ctypes.c_void_p(stream))
+        s_obj = cur
+    elif isinstance(stream, torch.cuda.Stream):
+        s_obj = stream
+    else:  # a raw hipStream_t handle
+        s_obj = torch.cuda.ExternalStream(int(stream), device=q.device)
+    if s_obj != cur:
+        # The temporaries above (contiguous copies of tables and dense terms,
+        # and ``out`` when allocated here) were made on the current stream:
+        # the kernel's stream waits for them, and the caching allocator keeps
+        # their memory until the kernel's stream has passed this point.
+        ev = torch.cuda.Event()
+        ev.record(cur)
+        s_obj.wait_event(ev)
+        for t in keep + ([out] if allocated else []):
+            t.record_stream(s_obj)
+    st = h.attn_fwd_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                        ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads),
+                        ctypes.c_void_p(s_obj.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, h.attn_strerror(st).decode())
     del keep
@@ -273,11 +314,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
 
 
 def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
-          window: Optional[Window] = None) -> int:
+          window: Optional[Window] = None, window_heads: Optional[int] = None) -> int:
     """Status attn_fwd would return for these arguments (no GPU needed)."""
     h = lib()
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
-    return h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
-                        ctypes.byref(md), ctypes.byref(oc), dt)
+    if window_heads is None:
+        return h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                            ctypes.byref(md), ctypes.byref(oc), dt)
+    return h.attn_check_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                            ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads))

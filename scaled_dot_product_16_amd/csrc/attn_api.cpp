@@ -1,12 +1,16 @@
 // Host side of the C ABI: argument validation (no HIP dependency, so it can be
 // exercised on a machine without a GPU through attn_check) and the exported
-// entry points.  The launch itself lives in attn_kernels.hip.
+// entry points.  Validation ends with the call's plan (attn_plan.h: kernel
+// choice and LDS bytes), so a call whose tiles or tables do not fit on chip
+// is refused here, by attn_check as by attn_fwd.  The launch itself lives in
+// attn_dispatch.cpp and attn_inst.hip.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
+#include "attn_plan.h"
 
 namespace attn {
 namespace {
@@ -60,7 +64,8 @@ bool window_valid(const attn_window_t& w) {
 }  // namespace
 
 int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
-             const void* maskv, const void* outv, int32_t dtype, AttnArgs* a) {
+             const void* maskv, const void* outv, int32_t dtype, const void* optv,
+             AttnArgs* a) {
   const attn_tensor_t* q = (const attn_tensor_t*)qv;
   const attn_tensor_t* k = (const attn_tensor_t*)kv;
   const attn_tensor_t* v = (const attn_tensor_t*)vv;
@@ -213,27 +218,51 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
 
   // out must not overlap the inputs it is computed from.
   if (overlaps(o, q, es) || overlaps(o, k, es) || overlaps(o, v, es)) return ATTN_E_ALIAS;
-  return ATTN_OK;
+
+  // Options.
+  const attn_options_t* opt = (const attn_options_t*)optv;
+  if (opt) {
+    if (opt->window_heads < 0) return ATTN_E_INVALID;
+    a->win_heads = opt->window_heads;
+  }
+
+  // The kernel the call takes must fit one CU's LDS (and the grid the
+  // launch limit); a requested form must exist for the call.
+  Plan plan;
+  return make_plan(*a, &plan);
 }
 
 }  // namespace attn
 
 extern "C" {
 
+int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                   const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+                   const attn_tensor_t* out, int32_t dtype, const attn_options_t* options) {
+  attn::AttnArgs a;
+  return attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, options, &a);
+}
+
+int attn_fwd_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                 const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+                 const attn_tensor_t* out, int32_t dtype, const attn_options_t* options,
+                 void* stream) {
+  attn::AttnArgs a;
+  int st = attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, options, &a);
+  if (st != ATTN_OK) return st;
+  return attn::launch(a, stream);
+}
+
 int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
                const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
                const attn_tensor_t* out, int32_t dtype) {
-  attn::AttnArgs a;
-  return attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, &a);
+  return attn_check_opt(q, k, v, bias_desc, mask_desc, out, dtype, nullptr);
 }
 
 int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
              const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
              const attn_tensor_t* out, int32_t dtype, void* stream) {
-  attn::AttnArgs a;
-  int st = attn::validate(q, k, v, bias_desc, mask_desc, out, dtype, &a);
-  if (st != ATTN_OK) return st;
-  return attn::launch(a, stream);
+  return attn_fwd_opt(q, k, v, bias_desc, mask_desc, out, dtype, nullptr, stream);
 }
 
 const char* attn_strerror(int status) {
@@ -250,6 +279,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return (1 << 16) | 1; }
+int attn_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
+#include "attn_plan.h"
 
 namespace attn {
 
@@ -212,19 +213,6 @@ struct BiasCtx {
   const float* relw;  // RELPOS [kgw][BM]
 };
 
-__host__ __device__ constexpr bool needs_kinfo(int bias_kind, bool mask) {
-  return bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS || mask;
-}
-
-__host__ __device__ inline size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
-  const bool kinfo = a.bias_kind == ATTN_BIAS_TABLE || a.bias_kind == ATTN_BIAS_RELPOS ||
-                     a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
-  size_t n = kinfo ? ((size_t)a.Nk * 4 + 15) / 16 * 16 : 0;
-  if (a.bias_kind == ATTN_BIAS_TABLE) n += (size_t)(2 * a.gh - 1) * (2 * a.gw - 1) * 4;
-  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)(a.kgh + a.kgw) * bm * 4;
-  return n;
-}
-
 // Fill kinfo and the table / relative-position terms.  `E` is the element
 // type of the tables and of q (relative-position terms use the raw query).
 // RELPOS_VALU: compute the relative-position tables here with plain dot
@@ -333,9 +321,6 @@ __device__ __forceinline__ float bias_log2(const AttnArgs& a, const BiasCtx& bc,
 // ---------------------------------------------------------------------------
 // fp32 kernel: one thread per query, key/value tiles broadcast from LDS.
 // ---------------------------------------------------------------------------
-constexpr int kF32Threads = 64;
-constexpr int kF32BN = 32;
-
 template <int DMAX, int BIAS, bool MASK>
 __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(AttnArgs a) {
   constexpr int BM = kF32Threads;

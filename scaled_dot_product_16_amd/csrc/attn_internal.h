@@ -65,12 +65,16 @@ struct AttnArgs {
   // Filled by the launcher.
   int32_t n_qtiles;
   int32_t n_blocks;  // workgroups in the grid
+  int32_t n_hgrp;    // head groups per batch item (packed window kernel)
+  FastDiv fd_hgrp;
+  int32_t win_heads; // requested heads per workgroup of the window path (0: library's choice)
 };
 
 // Host-side validation shared by attn_check and attn_fwd.  Returns an ATTN_*
 // status and fills *a on success.
 int validate(const void* q, const void* k, const void* v, const void* bias_desc,
-             const void* mask_desc, const void* out, int32_t dtype, AttnArgs* a);
+             const void* mask_desc, const void* out, int32_t dtype, const void* options,
+             AttnArgs* a);
 
 // Queue the kernel for a validated call on `stream` (a hipStream_t).
 int launch(const AttnArgs& a, void* stream);

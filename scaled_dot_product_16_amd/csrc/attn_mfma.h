@@ -37,20 +37,8 @@ namespace attn {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Build-time variants of the main loop (defaults are the measured best).
-#ifndef ATTN_ONES
-#define ATTN_ONES 1   // row sums from a ones row of V on the matrix cores
-#endif
-// V tile rows are padded to 16 elements past a multiple of 32 (row stride
-// of 8 or 24 dwords modulo 32): the transposing reads then fetch the 4 rows
-// x 4 column slices of each 16-lane group from distinct banks (also for 64
-// banks with 32 lanes per pass).
-__host__ __device__ constexpr int v_row_pad(int dv) { return ((16 - dv % 32) + 32) % 32; }
 #ifndef ATTN_MAX2
 #define ATTN_MAX2 1  // joint cross-group maxima of a wave's two query blocks
-#endif
-#ifndef ATTN_KPAD
-#define ATTN_KPAD 16  // K tile row padding (elements; 16 measured faster than 8 and 24)
 #endif
 
 // Word 3 of a buffer resource on gfx9-family chips: 32-bit data format,
@@ -69,66 +57,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
                                            (int)__builtin_amdgcn_readfirstlane(nrec), kBufferWord3);
 }
 
-// Relative-position modes of the kernel.
-constexpr int kRelTables = 0;  // per-score lookups in LDS tables (also non-relpos biases)
-constexpr int kRelRow64 = 1;   // 64-wide grids: Rw term seeds the accumulator, Rh term per row
-constexpr int kRelAug = 2;     // gh + gw <= 32: bias folded into the QK^T contraction
-constexpr int kTwoTiles = 3;   // no bias or mask, BN < Nk <= 2 BN: both key tiles loaded up front
-
-template <int D, int NW, int NQB, bool AUG = false>
-struct MfmaCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BM = NW * NQB * 16;
-  static constexpr int BN = 64;
-  static constexpr int KCH = (D + 31) / 32;  // 32-wide contraction chunks of the head dim
-  static constexpr int KCHT = KCH + (AUG ? 1 : 0);  // plus one chunk of bias one-hots
-  static constexpr int DK = KCHT * 32;
-  // The ones row needs an extra 16-row block when D is a multiple of 16; at
-  // D = 80 that block does not fit the two-waves-per-SIMD register budget.
-  static constexpr bool ONES = ATTN_ONES && !AUG && (D % 16 != 0 || D <= 64);
-  static constexpr int CB = ONES ? D / 16 + 1 : (D + 15) / 16;  // 16-row blocks of O^T
-  static constexpr int DV = CB * 16;
-  static constexpr int KROW = DK + ATTN_KPAD;  // LDS row strides (elements)
-  static constexpr int VROW = DV + v_row_pad(DV);
-  static constexpr int RCH = D / 8;          // 16-byte chunks per token row
-  static constexpr int NCH = BN * RCH;
-  static constexpr int CPT = (NCH + NT - 1) / NT;
-  static constexpr int K_ELEMS = BN * KROW;  // per stage
-  static constexpr int V_ELEMS = BN * VROW;
-  static constexpr size_t KV_BYTES = 2 * (size_t)(K_ELEMS + V_ELEMS) * 2;
-  static constexpr int GROW = 132;           // relpos prologue scratch row (floats)
-  static constexpr size_t SCRATCH_BYTES = (size_t)NW * 16 * GROW * 4;
-  static constexpr size_t BASE_BYTES =
-      ((KV_BYTES > SCRATCH_BYTES ? KV_BYTES : SCRATCH_BYTES) + 15) / 16 * 16;
-};
-
-// Scratch row (floats) of the augmented prologue: the <= 62 rows of the
-// stacked table [Rh; Rw] for one query, padded to keep 16-byte stores aligned.
-constexpr int kAugGrow = 68;
-
-// Row length (floats) of the relative-position prologue scratch.
-inline __host__ __device__ int relpos_grow(const AttnArgs& a) {
-  int g = a.gh > a.gw ? a.gh : a.gw;
-  g = g > a.kgh ? g : a.kgh;
-  g = g > a.kgw ? g : a.kgw;
-  const int m = 2 * g - 1;
-  return (m + 15) / 16 * 16 + 4;
-}
-
-// Dynamic LDS bytes of one workgroup.
-template <int D, int NW, int NQB, int RMODE = kRelTables>
-__host__ __device__ inline size_t mfma_lds_bytes(const AttnArgs& a) {
-  using C = MfmaCfg<D, NW, NQB, RMODE == kRelAug>;
-  if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
-  if (RMODE == kRelAug) {
-    const size_t scr = (size_t)NW * 16 * kAugGrow * 4;  // overlays the K/V tiles
-    return C::KV_BYTES > scr ? C::KV_BYTES : scr;
-  }
-  size_t n = C::KV_BYTES + dyn_lds_bytes(a, C::BM);
-  // Relative-position prologue scratch: G[16 queries][2g-1 rows] per wave.
-  if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)NW * 16 * relpos_grow(a) * 4;
-  return n;
-}
+// Tile geometry (MfmaCfg), the relative-position forms and the LDS byte
+// counts are in attn_plan.h, shared with the host-side kernel choice.
 
 // The lane index, recomputed where it is used: the asm is opaque to the
 // compiler, so lane-constant values derived from it are not kept alive in

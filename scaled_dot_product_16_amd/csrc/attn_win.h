@@ -19,54 +19,8 @@
 
 namespace attn {
 
-constexpr int kWinWaves = 4;
-
-template <int D>
-struct WinCfg {
-  static constexpr int NT = kWinWaves * 64;
-  static constexpr int KCH = (D + 31) / 32;
-  static constexpr int DK = KCH * 32;
-  static constexpr int CB = (D + 15) / 16;
-  static constexpr int DV = CB * 16;
-  static constexpr int KROW = DK + 8;
-  static constexpr int VROW = DV + v_row_pad(DV);
-  static constexpr int RCH = D / 8;
-  static constexpr int NCH = 64 * RCH;               // 16-byte chunks of a 64-token tile
-  static constexpr int CPT = (NCH + NT - 1) / NT;    // per thread
-  static constexpr size_t KV_BYTES = (size_t)64 * (KROW + VROW) * 2;
-};
-
-// fp32 units on v_mfma_f32_16x16x4_f32: D is the head-dim bucket DMAX (the
-// call's head dim is at most DMAX; missing columns are zero).  K is stored
-// row-major, V transposed (d rows of 64 keys) so that one 16-byte LDS read
-// yields the A operands of four consecutive K-steps.
-template <int DMAX>
-struct WinCfgF32 {
-  static constexpr int NT = kWinWaves * 64;
-  static constexpr int QC = DMAX / 4;        // K-steps of QK^T; Q floats per lane
-  static constexpr int CB = DMAX / 16;       // 16-row blocks of O^T
-  static constexpr int KROW = DMAX + 4;      // floats
-  static constexpr int VTROW = 64 + 4;       // floats (keys)
-  static constexpr size_t KV_BYTES = ((size_t)64 * KROW + (size_t)DMAX * VTROW) * 4;
-};
-
-// Entries of the bias table of a window unit: the relative-position table
-// (TABLE bias), or a single zero entry when only the region mask is present.
-inline __host__ __device__ int win_tab_entries(const AttnArgs& a) {
-  return a.bias_kind == ATTN_BIAS_TABLE ? (2 * a.gh - 1) * (2 * a.gw - 1) : 1;
-}
-
-// Bias and region mask come from one LDS table lookup per score when the
-// bias is a table and/or the mask is the shifted-window region mask.
-inline __host__ __device__ bool win_uses_table(const AttnArgs& a) {
-  return a.bias_kind == ATTN_BIAS_TABLE || a.mask_kind == ATTN_MASK_SHIFT_REGIONS;
-}
-
-inline size_t win_lds_bytes(const AttnArgs& a, size_t kv_bytes) {
-  size_t n = kv_bytes + 64 * 4;  // per-key index data
-  if (win_uses_table(a)) n += (size_t)9 * win_tab_entries(a) * 4;
-  return n;
-}
+// Tile geometry (WinCfg, WinCfgF32, WinPackCfg) and the LDS byte counts are
+// in attn_plan.h, shared with the host-side kernel choice.
 
 // Per-unit window placement (image layout and region labels).
 struct WinPos {
@@ -408,6 +362,244 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
         // stores, measured faster for the Swin window shapes.
         else __builtin_nontemporal_store(u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])},
                                          (u32x2*)(op + (size_t)(off + c0) * 2));
+      }
+    }
+  }
+}
+
+// Packed short-sequence form: one workgroup owns one window and HG of its
+// heads (all heads of a Swin window when HG = H), one wave per (head,
+// 16-query block): 4*HG waves.  The work that depends on the window only --
+// the per-key table offsets and region labels, and the staging of the bias
+// table, which holds HG floats per entry (one per head) -- is done once for
+// the HG heads; every wave then runs one head's 16 queries exactly as
+// attn_fwd_win runs a unit's, reading its head's bias at an immediate offset.
+// On gfx950 the window shapes are bound by the length of each wave's chain
+// of load, lookup, softmax and store rather than by instruction issue, so
+// the waves stay as short as in the one-unit form (measured: four waves
+// that each ran all HG heads were 1.3x slower for Swin-T, whether the heads
+// ran one after another or side by side).  V carries a ones block (column D),
+// so the row sums come out of the P.V products.
+// BIAS: ATTN_BIAS_NONE / _TABLE; MASKK: ATTN_MASK_NONE / _SHIFT_REGIONS.
+template <class E, int D, int HG, int BIAS, int MASKK>
+__global__ __launch_bounds__(kWinWaves * HG * 64) void attn_fwd_winp(AttnArgs a) {
+  using C = WinPackCfg<D>;
+  constexpr int NTH = C::NT;                 // threads staging one head's tiles
+  constexpr int NT = NTH * HG;               // threads of the workgroup
+  constexpr int KCH = C::KCH, CB = C::CB, KROW = C::KROW, VROW = C::VROW, RCH = C::RCH,
+                NCH = C::NCH, CPT = C::CPT, DK = C::DK, DV = C::DV;
+  constexpr int K_ELEMS = 64 * KROW, HEAD_ELEMS = (int)(C::HEAD_BYTES / 2);
+  constexpr bool kTab = BIAS == ATTN_BIAS_TABLE || MASKK == ATTN_MASK_SHIFT_REGIONS;
+  constexpr bool kRegions = MASKK == ATTN_MASK_SHIFT_REGIONS;
+  // Region copy the lookup lands in when query and key share a region.
+  constexpr int kCopy0 = kRegions ? 4 : 0;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  uint16_t* tiles = (uint16_t*)lds;                    // head j: K [64][KROW], V [64][VROW]
+  int* kinfo = (int*)(lds + HG * C::HEAD_BYTES);       // per key: byte offset of its table part
+  constexpr int kTabByte = HG * (int)C::HEAD_BYTES + 64 * 4;
+  float* tbl = (float*)(lds + kTabByte);               // [copy][entry][HG], log2 units
+
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = wave >> 2, qb = wave & 3;              // this wave's head and query block
+  const int ht = tid - j * NTH;                        // thread index inside its head's group
+  const int l16 = lane & 15, g = lane >> 4;
+  const int H = a.H, N = a.Nq, Nk = a.Nk;
+  const int unit = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
+  const int b = fdiv(unit, a.fd_hgrp), h0 = (unit - b * a.n_hgrp) * HG;
+
+  // Token t < 64 -> (row, column) by a float reciprocal (exact for n <= 1024,
+  // as in attn_fwd_win).
+  const float inv_ww = __builtin_amdgcn_rcpf((float)(a.win_w > 0 ? a.win_w : 1));
+  const float inv_gw = __builtin_amdgcn_rcpf((float)(a.gw > 0 ? a.gw : 1));
+  auto div_small = [](int t, float inv) { return (int)(((float)t + 0.5f) * inv); };
+  auto split = [&](int t, int& ty, int& tx) {
+    ty = div_small(t, inv_ww);
+    tx = t - ty * a.win_w;
+  };
+  const WinPos pos = win_pos(a, b);
+  const int bimg = a.image ? pos.img : b;
+  auto tok_pix = [&](int t) -> uint32_t {
+    if (!a.image) return (uint32_t)t;
+    int ty, tx;
+    split(t, ty, tx);
+    return win_tok_pix(a, pos, ty, tx);
+  };
+  // Byte bases of this wave's head.
+  const int h = h0 + j;
+  const char* qp = (const char*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh) * 2;
+  const char* kp = (const char*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh) * 2;
+  const char* vp = (const char*)a.v + ((int64_t)bimg * a.v_sb + (int64_t)h * a.v_sh) * 2;
+  char* op = (char*)a.o + ((int64_t)bimg * a.o_sb + (int64_t)h * a.o_sh) * 2;
+
+  // Loads first: this thread's K/V chunks of its head (token rows past Nk
+  // clamped to the last key, whose scores start from -inf below) and this
+  // lane's query fragments.  Every byte is read by one workgroup: streaming
+  // (non-temporal) loads.
+  u32x4 kreg[CPT], vreg[CPT], qf[KCH];
+  bool kpad[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = min(ht + c * NTH, NCH - 1);
+    const uint32_t pix0 = tok_pix(min(ch / RCH, Nk - 1));
+    kpad[c] = pix0 == kPadTok;
+    const uint32_t pix = kpad[c] ? 0u : pix0;
+    const uint32_t col = (uint32_t)((ch % RCH) * 8);
+    kreg[c] = __builtin_nontemporal_load((const u32x4*)(kp + (pix * (uint32_t)a.k_sn + col) * 2));
+    vreg[c] = __builtin_nontemporal_load((const u32x4*)(vp + (pix * (uint32_t)a.v_sn + col) * 2));
+  }
+  const int q_tok = min(qb * 16 + l16, N - 1);
+  const uint32_t q_pix0 = tok_pix(q_tok);
+  const bool q_pad = q_pix0 == kPadTok;  // padding token: zero query, output not stored
+  const uint32_t q_pix = q_pad ? 0u : q_pix0;
+#pragma unroll
+  for (int dc = 0; dc < KCH; ++dc) {
+    const int d0 = dc * 32 + g * 8;
+    qf[dc] = d0 < D && !q_pad
+                 ? __builtin_nontemporal_load((const u32x4*)(qp + (size_t)(q_pix * (uint32_t)a.q_sn + d0) * 2))
+                 : u32x4{0, 0, 0, 0};
+  }
+
+  // Padding columns of the head's tiles (independent of the loads): K
+  // columns D..DK are zero; V column D is one (the row-sum column), the
+  // rest of its last block zero.
+  constexpr int KPC = (DK - D) / 8, VPC = (DV - D) / 8;  // 16-byte chunks per row
+  uint16_t* Ks = tiles + j * HEAD_ELEMS;
+  uint16_t* Vs = Ks + K_ELEMS;
+  for (int i = ht; i < 64 * (KPC + VPC); i += NTH) {
+    const int row = i / (KPC + VPC), cc = i - row * (KPC + VPC);
+    if (cc < KPC) {
+      *(u32x4*)&Ks[row * KROW + D + cc * 8] = u32x4{0, 0, 0, 0};
+    } else {
+      const int vc = cc - KPC;
+      *(u32x4*)&Vs[row * VROW + D + vc * 8] = u32x4{vc == 0 ? (uint32_t)E::one_bits() : 0u, 0, 0, 0};
+    }
+  }
+
+  // Table (HG heads per entry) and per-key parts of the lookup address.
+  const bool regions = kRegions &&
+                       (pos.y0 + a.win_h > a.pimg_h - a.win_h || pos.x0 + a.win_w > a.pimg_w - a.win_w);
+  const int n_tab = win_tab_entries(a);
+  if constexpr (kTab) {
+    const float mv = a.mask_value * kLog2e;
+    for (int e = tid; e < n_tab * HG; e += NT) {
+      const int r = e / HG, jj = e - r * HG;
+      const float t = BIAS == ATTN_BIAS_TABLE ? load_elem<E>(a.table, (int64_t)r * H + h0 + jj) * kLog2e : 0.f;
+      tbl[kCopy0 * n_tab * HG + e] = t;
+      if (regions) {
+#pragma unroll
+        for (int c = 0; c < 9; ++c)
+          if (c != 4) tbl[c * n_tab * HG + e] = t + mv;
+      }
+    }
+    if (tid < 64) {
+      const int kk = min(tid, Nk - 1);
+      int part = kCopy0 * n_tab;
+      if constexpr (BIAS == ATTN_BIAS_TABLE) {
+        const int kh = div_small(kk, inv_gw), kw = kk - kh * a.gw;
+        part -= kh * (2 * a.gw - 1) + kw;
+      }
+      if (regions) {
+        int ty, tx;
+        split(kk, ty, tx);
+        part -= n_tab * win_region(a, pos, ty, tx);
+      }
+      kinfo[tid] = part * HG * 4;
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = ht + c * NTH;
+    if (ch < NCH) {
+      *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = kpad[c] ? u32x4{0, 0, 0, 0} : kreg[c];
+      *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = kpad[c] ? u32x4{0, 0, 0, 0} : vreg[c];
+    }
+  }
+  __syncthreads();
+  if (qb * 16 >= N) return;  // no barrier below this point
+
+  // S^T = K Q^T; keys past Nk start from -inf.
+  f32x4 s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb * 16 + 16 > Nk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kb * 16 + g * 4 + r >= Nk) s[kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const u32x4 kf = *(const u32x4*)&Ks[(kb * 16 + l16) * KROW + dc * 32 + g * 8];
+      s[kb] = E::mfma(kf, qf[dc], s[kb]);
+    }
+  }
+  // Bias and mask (log2 units): one table read per score, this wave's head
+  // at offset 4*j bytes of the entry.
+  const float c2 = a.scale * kLog2e;
+  float y[16];
+  if constexpr (kTab) {
+    int qpart = 0;
+    if constexpr (BIAS == ATTN_BIAS_TABLE) {
+      const int qh = div_small(q_tok, inv_gw), qw = q_tok - qh * a.gw;
+      qpart = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
+    }
+    if (regions) {
+      int ty, tx;
+      split(q_tok, ty, tx);
+      qpart += n_tab * win_region(a, pos, ty, tx);
+    }
+    const char* qbase = lds + kTabByte + qpart * HG * 4 + 4 * j;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 v = *(const u32x4*)&kinfo[kb * 16 + g * 4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[kb * 4 + r] = fmaf(s[kb][r], c2, *(const float*)(qbase + (int)v[r]));
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[kb * 4 + r] = s[kb][r] * c2;
+  }
+  float mx = fmaxf(fmaxf(y[0], y[1]), y[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, y[i]), y[i + 1]);
+  mx = max_across_groups(fmaxf(mx, y[15]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = __builtin_amdgcn_exp2f(y[i] - mx);
+  u32x4 pf[2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+    pf[kc] = u32x4{E::pack2(y[kc * 8 + 0], y[kc * 8 + 1]), E::pack2(y[kc * 8 + 2], y[kc * 8 + 3]),
+                   E::pack2(y[kc * 8 + 4], y[kc * 8 + 5]), E::pack2(y[kc * 8 + 6], y[kc * 8 + 7])};
+  // O^T += V^T P^T with transposing reads of the V tile; block CB-1 holds
+  // the row sums (the ones column of V).
+  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  f32x4 o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint16_t* vptr = Vs + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
+      const u32x2 lo = lds_read_tr16(vptr);
+      const u32x2 hi = lds_read_tr16(vptr + 16 * VROW);
+      o[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kc], o[cb]);
+    }
+  constexpr int LB = D / 16, LG = (D % 16) / 4, LR = D % 4;  // row-sum element of O^T
+  const float inv = __builtin_amdgcn_rcpf(__shfl(o[LB][LR], LG * 16 + l16));
+  if (qb * 16 + l16 < N && !q_pad) {
+    const uint32_t o_off = q_pix * (uint32_t)a.o_sn;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c0 = cb * 16 + g * 4;
+      if (c0 < D) {
+        const f32x4 v = o[cb] * inv;
+        __builtin_nontemporal_store(u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])},
+                                    (u32x2*)(op + (size_t)(o_off + c0) * 2));
       }
     }
   }

@@ -135,10 +135,13 @@ def to_dtype(x: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt)
 
 
-def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0) -> dict:
+def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0, std_table: float = 0.02) -> dict:
     """Draw the inputs of workload ``w`` as torch CPU tensors in its dtype.
 
     Returns q, k, v and, depending on the bias kind, table or rh/rw.
+    ``std_table`` (default 0.02, the workloads' recipe) sets the standard
+    deviation of the bias tables; tests raise it so that the bias is large
+    next to the tolerance.
     """
     out = {
         "q": to_dtype(normal(w.q_shape, w.cfg_id, 0, std_qkv, seed), w.dtype),
@@ -148,12 +151,12 @@ def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0) -> dict:
     if w.bias == "table":
         gh, gw = w.grid
         out["table"] = to_dtype(normal(((2 * gh - 1) * (2 * gw - 1), w.H), w.cfg_id, 3,
-                                       0.02, seed), w.dtype)
+                                       std_table, seed), w.dtype)
     elif w.bias == "relpos":
         gh, gw = w.grid
         kgh, kgw = w.kgrid or w.grid
-        out["rh"] = to_dtype(normal((2 * max(gh, kgh) - 1, w.d), w.cfg_id, 3, 0.02, seed), w.dtype)
-        out["rw"] = to_dtype(normal((2 * max(gw, kgw) - 1, w.d), w.cfg_id, 4, 0.02, seed), w.dtype)
+        out["rh"] = to_dtype(normal((2 * max(gh, kgh) - 1, w.d), w.cfg_id, 3, std_table, seed), w.dtype)
+        out["rw"] = to_dtype(normal((2 * max(gw, kgw) - 1, w.d), w.cfg_id, 4, std_table, seed), w.dtype)
     return out
 
 

@@ -61,13 +61,53 @@ def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
 
 
-def check_full(w: W.Workload, inp: dict, out: torch.Tensor, tol=None):
+def record(name: str, dtype: str, err: float, tol: float, elements: int, **extra):
+    """Keep a compared case's max-abs error for the end-of-run summary."""
+    from tests.parity_log import RECORDS
+
+    RECORDS.append({"name": name, "dtype": dtype, "err": float(err), "tol": float(tol),
+                           "elements": int(elements), **extra})
+
+
+def check_full(w: W.Workload, inp: dict, out: torch.Tensor, tol=None, name=None):
     ref = oracle.run_workload(w, oracle_arrays(inp))
     got = out.detach().to("cpu", torch.float64).numpy()
     err = max_abs_err(got, ref)
     tol = TOL[w.dtype] if tol is None else tol
+    if name:
+        record(name, w.dtype, err, tol, got.size)
     assert err <= tol, f"{w.key}: max abs err {err:.3e} > {tol:.1e}"
     return err
+
+
+def check_full_pooled(w: W.Workload, inp: dict, out: torch.Tensor, name: str, tol=None,
+                      drops=None):
+    """Every output element against the oracle, the (batch item, head) units
+    (image layout: (image, head)) spread over a process pool.
+
+    ``drops``: {(b, h): ("rh", "rw", "bias")}: for those units the oracle is
+    also evaluated with that term left out, and the returned dict holds the
+    smallest such change (``delta_<term>``), so a test can assert that the
+    check would see a missing term.
+    """
+    from oracle import pool
+
+    tol = TOL[w.dtype] if tol is None else tol
+    arrays = dict(inp, out=out.detach().to("cpu"))
+    units = pool.units_of(w)
+    with pool.UnitPool(arrays, pool.spec_of(w)) as P:
+        res = P.compare(units, drops=drops)
+    err = max(r["err"] for r in res)
+    summary = {"err": err, "units": len(res)}
+    for key in ("delta_rh", "delta_rw", "delta_bias"):
+        vals = [r[key] for r in res if key in r]
+        if vals:
+            summary[key] = min(vals)
+    record(name, w.dtype, err, tol, out.numel(),
+           **{k: v for k, v in summary.items() if k.startswith("delta")})
+    worst = max(res, key=lambda r: r["err"])
+    assert err <= tol, f"{name}: max abs err {err:.3e} > {tol:.1e} (b={worst['b']}, h={worst['h']})"
+    return summary
 
 
 def check_sampled(w: W.Workload, inp: dict, out: torch.Tensor, select, tol=None):

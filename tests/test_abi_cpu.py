@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_check", "attn_strerror", "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_check", "attn_strerror", "attn_version",
+                          "attn_fwd_opt", "attn_check_opt"}
     for n in names:
         assert hasattr(lib, n)
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -41,13 +42,14 @@ def test_struct_layout_matches_header(lib):
     assert ctypes.sizeof(B.WindowC) == 24
     assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16 + 8
     assert ctypes.sizeof(B.MaskDescC) == 8 + 8 + 8 + 16 + 24 + 4 + 4
+    assert ctypes.sizeof(B.OptionsC) == 32
 
 
 def test_strerror_and_version(lib):
     for st in range(8):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(99) == b"unknown status"
-    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 1
+    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 2
 
 
 def t(*shape, dtype=torch.float16):
@@ -173,8 +175,11 @@ def test_key_grid_validation(lib):
     assert B.check(q, k2, k2.clone(), bias=rp(15, 15, (4, 8))) == 0
     with pytest.raises(ValueError):                                         # rows must be 2*max-1
         B.check(q, k, k.clone(), bias=rp(15, 15, (16, 16)))
+    # A 2 x 128 key grid is a valid call whose per-query tables (130 rows)
+    # and 255-row prologue scratch do not fit one CU's LDS next to the K/V
+    # tiles: E_UNSUPPORTED from the host validation, as from attn_fwd.
     assert B.check(q, k, k.clone(), bias=B.RelposBias(t(15, 64, dtype=bf), t(255, 64, dtype=bf),
-                                                      (8, 8), (2, 128))) == 0
+                                                      (8, 8), (2, 128))) == 4
     # Per-axis table rows above the limit (2 * 200 - 1 each) are unsupported.
     kb = t(1, 2, 200 * 200, 64, dtype=bf)
     assert B.check(q, kb, kb.clone(), bias=B.RelposBias(t(399, 64, dtype=bf), t(399, 64, dtype=bf),
@@ -201,3 +206,48 @@ def test_key_grid_validation(lib):
     bd.kgrid_h, bd.kgrid_w = 8, 8
     assert h.attn_check(*args()) == 2
     del keep, keep2
+
+
+def test_lds_budget_is_part_of_validation(lib):
+    # attn_check runs the kernel choice and its LDS arithmetic (no GPU):
+    # calls whose tiles and tables fit are OK, the others E_UNSUPPORTED,
+    # exactly as attn_fwd returns them.
+    bf = torch.bfloat16
+    rp = lambda g, d: B.RelposBias(t(2 * g[0] - 1, d, dtype=bf), t(2 * g[1] - 1, d, dtype=bf), g)
+    for grid, d, want in [((64, 64), 64, 0), ((64, 64), 80, 0), ((14, 14), 64, 0),
+                          ((56, 56), 64, 0), ((100, 100), 64, 4), ((90, 90), 80, 4)]:
+        n = grid[0] * grid[1]
+        q = t(1, 1, n, d, dtype=bf)
+        assert B.check(q, q.clone(), q.clone(), bias=rp(grid, d)) == want, (grid, d)
+    # The largest table bias (64 x 64 grid, 16129 rows) fits next to 4096 keys.
+    q = t(1, 2, 4096, 32)
+    tab = B.TableBias(t(127 * 127, 2), (64, 64))
+    assert B.check(q, q.clone(), q.clone(), bias=tab) == 0
+    # fp32: its kernel keeps the per-query tables of 64 queries only, so the
+    # 100 x 100 grid fits there (about 99 KB).
+    q = t(1, 1, 10000, 32, dtype=torch.float32)
+    big = B.RelposBias(t(199, 32, dtype=torch.float32), t(199, 32, dtype=torch.float32), (100, 100))
+    assert B.check(q, q.clone(), q.clone(), bias=big) == 0
+
+
+def test_window_heads_option(lib):
+    # Heads of one window per workgroup (the packed short-sequence form):
+    # 1 to 4 when they divide H, on half-precision windows with table or no
+    # bias and region or no mask; refused otherwise, by attn_check_opt as by
+    # attn_fwd_opt.  0 (or no options) is the library's choice.
+    q = t(2, 12, 49, 32)
+    tab = B.TableBias(t(169, 12), (7, 7))
+    for hg, want in [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (5, 4), (6, 4), (12, 4), (-1, 7)]:
+        assert B.check(q, q.clone(), q.clone(), bias=tab, window_heads=hg) == want, hg
+    q3 = t(2, 3, 49, 32)
+    assert B.check(q3, q3.clone(), q3.clone(), window_heads=2) == 4    # 2 does not divide 3
+    assert B.check(q3, q3.clone(), q3.clone(), window_heads=3) == 0
+    qf = t(2, 3, 49, 32, dtype=torch.float32)
+    assert B.check(qf, qf.clone(), qf.clone(), window_heads=3) == 4    # no fp32 packed form
+    qb = t(2, 4, 49, 64, dtype=torch.bfloat16)
+    add = B.AdditiveMask(t(1, 49, 49, dtype=torch.bfloat16))
+    assert B.check(qb, qb.clone(), qb.clone(), mask=add, window_heads=2) == 4
+    assert B.check(qb, qb.clone(), qb.clone(), mask=add, window_heads=1) == 0
+    ql = t(1, 4, 300, 64)
+    assert B.check(ql, ql.clone(), ql.clone(), window_heads=2) == 4    # not a window-sized call
+    assert B.check(ql, ql.clone(), ql.clone(), window_heads=1) == 0

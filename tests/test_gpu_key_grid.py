@@ -87,7 +87,7 @@ def test_key_grid_tables_too_large_for_lds_are_rejected():
                  cfg_id=581)
     say("[key grid relpos] 8x8 queries, 2x128 keys: E_UNSUPPORTED, nothing launched")
     dev = to_device(W.make_inputs(w, seed=4))
-    assert Bd.check(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev)) == 0
+    assert Bd.check(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev)) == 4
     out = torch.full_like(dev["q"], 7.0)
     with pytest.raises(Bd.AttnError) as e:
         Bd.fwd(dev["q"], dev["k"], dev["v"], out=out, **W.device_args(w, dev))

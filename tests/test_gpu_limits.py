@@ -59,7 +59,8 @@ def test_index_data_too_large_is_rejected():
     w = W.custom(W.BF16, B=1, H=1, Nq=10000, Nk=10000, d=64, bias="relpos", grid=(100, 100), cfg_id=702)
     say("[limits] relpos on a 100x100 grid: E_UNSUPPORTED, nothing launched")
     dev = to_device(W.make_inputs(w, seed=3))
-    assert Bnd.check(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev)) == 0  # the call itself is valid
+    # The host validation already knows: attn_check gives the status attn_fwd returns.
+    assert Bnd.check(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev)) == 4
     with pytest.raises(Bnd.AttnError) as e:
         Bnd.fwd(dev["q"], dev["k"], dev["v"], **W.device_args(w, dev))
     assert e.value.status == 4

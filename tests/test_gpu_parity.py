@@ -1,9 +1,12 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Full-size workloads are compared element by element where the oracle is fast
-(Swin windows, SAM windowed) and on sampled rows otherwise (SAM global, SD);
-reduced sizes sweep head dims, dtypes, ragged tiles, every bias and mask kind
-and both layouts.  Max-abs tolerances: f32 1e-5, f16 5e-3, bf16 2e-2.
+Every workload is compared element by element at full size (SAM global and
+SD with the oracle's (batch item, head) units spread over a process pool).
+The decomposed relative position on the 64x64 grid is also run at full size
+with tables large enough that leaving out either term moves the output by
+more than ten times the measured error.  Reduced sizes sweep head dims,
+dtypes, ragged tiles, every bias and mask kind and both layouts.  Max-abs
+tolerances: f32 1e-5, f16 5e-3, bf16 2e-2.
 """
 
 import sys
@@ -13,8 +16,8 @@ import pytest
 import torch
 
 from scaled_dot_product_16_amd import workloads as W
-from tests.helpers import (TOL, check_full, check_sampled, oracle_arrays, run_gpu, sample_select,
-                           to_device, with_dense_terms)
+from tests.helpers import (TOL, check_full, check_full_pooled, run_gpu, to_device,
+                           with_dense_terms)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,19 +44,39 @@ def test_workload_full(key):
     say(f"[parity full] {key} {w.name}")
     inp = W.make_inputs(w)
     out = run_gpu(w, to_device(inp))
-    err = check_full(w, inp, out)
+    err = check_full(w, inp, out, name=f"{key} {w.name}")
     say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
 
 
 @pytest.mark.parametrize("key", ["C4", "C4h", "C5s", "C5x"])
-def test_workload_sampled(key):
+def test_workload_full_pooled(key):
+    # Every output element; the oracle's units run in a process pool.
     w = W.WORKLOADS[key]
-    say(f"[parity sampled] {key} {w.name}")
+    say(f"[parity full, pooled oracle] {key} {w.name}")
     inp = W.make_inputs(w)
     out = run_gpu(w, to_device(inp))
-    assert torch.isfinite(out).all().item()
-    err = check_sampled(w, inp, out, sample_select(w))
-    say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
+    res = check_full_pooled(w, inp, out, name=f"{key} {w.name}")
+    say(f"  max abs err {res['err']:.3e} over {res['units']} units (tol {TOL[w.dtype]:.0e})")
+
+
+@pytest.mark.parametrize("key", ["C4", "C4h"])
+def test_global_relpos_bias_is_seen(key):
+    # SAM global shapes at full size (the two-group kernel through every
+    # grid row) with Rh and Rw drawn at N(0, 1/d), so q.Rh and q.Rw are
+    # N(0, 1) per term.  On a few units the oracle is also evaluated with Rh
+    # and with Rw left out: the measured error must be at most a tenth of
+    # either change, so a kernel that lost a term would fail.
+    w = W.WORKLOADS[key]
+    std = 1.0 / float(np.sqrt(w.d))
+    say(f"[parity full, relpos tables N(0, 1/d)] {key} shape")
+    inp = W.make_inputs(w, seed=11, std_table=std)
+    out = run_gpu(w, to_device(inp))
+    drops = {u: ("rh", "rw") for u in [(0, 0), (w.B // 2, w.H // 3), (w.B - 1, w.H - 1), (3, 5)]}
+    res = check_full_pooled(w, inp, out, name=f"{key} shape, relpos tables std 1/sqrt(d)",
+                            drops=drops)
+    say(f"  max abs err {res['err']:.3e}; without Rh {res['delta_rh']:.3e}, "
+        f"without Rw {res['delta_rw']:.3e}")
+    assert res["err"] <= 0.1 * min(res["delta_rh"], res["delta_rw"])
 
 
 # ---------------------------------------------------------------------------
@@ -111,6 +134,20 @@ def test_bias_and_mask_kinds(dtype, case):
     say(f"[bias/mask] {dtype} {bias} {grid} {mask} {window} B={B} N={n}")
     inp = with_dense_terms(w, W.make_inputs(w, seed=case), n_bias=2, n_mask=3)
     check_full(w, inp, run_gpu(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [32, 40, 80])
+@pytest.mark.parametrize("grid", [(17, 64), (16, 64), (2, 64)])
+def test_relpos_64_wide_grids_head_dims(dtype, d, grid):
+    # The 64-wide row form at the head dims the other sweeps leave to the
+    # general forms: above and at the two-group schedule's key threshold and
+    # at exactly two key tiles.  Tables at N(0, 1/d) make the bias large.
+    n = grid[0] * grid[1]
+    w = W.custom(dtype, B=2, H=2, Nq=n, Nk=n, d=d, bias="relpos", grid=grid, cfg_id=250 + d)
+    say(f"[relpos 64-wide] {dtype} d={d} grid {grid}")
+    inp = W.make_inputs(w, seed=grid[0], std_table=1.0 / float(np.sqrt(d)))
+    check_full(w, inp, run_gpu(w, to_device(inp)), name=f"relpos grid {grid} d={d}")
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])

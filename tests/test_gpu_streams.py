@@ -1,0 +1,78 @@
+"""GPU: launches on a stream other than torch's current one.
+
+The binding makes contiguous copies of non-contiguous tables and dense terms
+on the current stream; the kernel on a side stream must see them complete
+(it waits on an event) and they must stay allocated until it has run.  The
+result is compared with the same call on the current stream (bit for bit)
+and with the fp64 oracle.
+"""
+
+import sys
+
+import pytest
+import torch
+
+from scaled_dot_product_16_amd import binding as Bd
+from scaled_dot_product_16_amd import workloads as W
+from tests.helpers import TOL, check_full, to_device, with_dense_terms
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    Bd.lib()
+
+
+@pytest.mark.parametrize("raw_handle", [False, True])
+def test_side_stream_with_noncontiguous_table(raw_handle):
+    w = W.custom(W.F16, B=64, H=3, Nq=49, Nk=49, d=32, bias="table", grid=(7, 7), cfg_id=640)
+    say(f"[streams] table bias as a transposed view, side stream (raw handle: {raw_handle})")
+    inp = W.make_inputs(w, seed=1, std_table=0.5)
+    dev = to_device(inp)
+    # [H, 169] storage viewed as [169, H]: not contiguous, copied by the binding.
+    tab_t = dev["table"].t().contiguous().t()
+    assert not tab_t.is_contiguous()
+    ref = Bd.fwd(dev["q"], dev["k"], dev["v"], bias=Bd.TableBias(tab_t, w.grid))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        # The current stream is kept busy first, so an unordered kernel on the
+        # side stream would read the table copy before it exists.
+        torch.cuda._sleep(2_000_000)
+        tab_t = dev["table"].t().contiguous().t()
+        stream = side.cuda_stream if raw_handle else side
+        outs.append(Bd.fwd(dev["q"], dev["k"], dev["v"], bias=Bd.TableBias(tab_t, w.grid),
+                           stream=stream))
+        del tab_t
+        torch.empty(1 << 20, dtype=torch.float16, device="cuda").fill_(7.0)  # would reuse freed memory
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+    check_full(w, inp, outs[-1], name="side stream, transposed table")
+
+
+def test_side_stream_with_noncontiguous_mask():
+    w = W.custom(W.BF16, B=4, H=2, Nq=150, Nk=150, d=64, mask="additive", cfg_id=641)
+    say("[streams] additive mask as a strided view, side stream")
+    inp = with_dense_terms(w, W.make_inputs(w, seed=2), n_mask=2)
+    dev = to_device(inp)
+    m = dev["mask_add"]
+    m_view = m.transpose(1, 2).contiguous().transpose(1, 2)  # last stride != 1
+    ref = Bd.fwd(dev["q"], dev["k"], dev["v"], mask=Bd.AdditiveMask(m))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    torch.cuda._sleep(2_000_000)
+    out = Bd.fwd(dev["q"], dev["k"], dev["v"], mask=Bd.AdditiveMask(m_view), stream=side)
+    del m_view
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    err = check_full(w, inp, out, name="side stream, strided additive mask")
+    say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
