@@ -18,6 +18,7 @@ from .attention import (  # noqa: F401
     table_relative_index,
     table_bias,
     relpos_rows,
+    rel_pos_resized,
     relpos_bias,
     relpos_bias_gather,
     shift_region_labels,

@@ -40,7 +40,9 @@ design notes of the repository):
   floor of the scaled coordinate difference, in exact arithmetic
   (``relpos_rows``); the tables then hold 2*max(q, k)-1 rows per axis.  The
   write-ups also name a resize of the tables (rel_pos_resized) without giving
-  its rule: tables of any other length are rejected, not resized;
+  its rule: a table of another length is resized to 2*max(q, k)-1 rows by
+  linear interpolation along the offset axis with both end rows kept
+  (``rel_pos_resized``);
 * the shifted window attention rolls the image content by (-sh, -sw) before
   partitioning (shifted[y] = x[(y + sh) mod img_h]) and rolls back after;
   the region of a shifted-image pixel is 3*ry + rx, where ry is 0, 1, 2 for
@@ -163,6 +165,37 @@ def relpos_rows(qn: int, kn: int) -> np.ndarray:
     return out
 
 
+def rel_pos_resized(table: np.ndarray, m: int) -> np.ndarray:
+    """A relative-position table of L rows resized to m rows -> [m, d].
+
+    SAM blog, section "Bfloat16 half precision" (and the same passage of the
+    Korean and Chinese write-ups) names ``rel_pos_resized``: the table is
+    resized when its length differs from the 2*max-1 rows the grids need, but
+    the rule is not given.  Reading (the plainest one the rest supports):
+    linear interpolation along the relative-offset axis with both ends
+    aligned -- row r of the result is the old table at position
+    p = r*(L-1)/(m-1), i.e. (1-f)*T[i] + f*T[i+1] with i = floor(p),
+    f = p - i (a table of one row is repeated; m == 1 takes row 0).  It keeps
+    the table unchanged when L == m, reproduces tables that are affine in the
+    offset exactly, and keeps the end rows.  p is taken in exact rational
+    arithmetic.
+    """
+    table = np.asarray(table, dtype=np.float64)
+    L = table.shape[0]
+    if L == m:
+        return table.copy()
+    out = np.empty((m,) + table.shape[1:])
+    for r in range(m):
+        if L == 1 or m == 1:
+            out[r] = table[0]
+            continue
+        p = Fraction(r * (L - 1), m - 1)
+        i = math.floor(p)
+        f = float(p - i)
+        out[r] = table[i] if i >= L - 1 else (1.0 - f) * table[i] + f * table[i + 1]
+    return out
+
+
 def relpos_bias(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
                 rw: np.ndarray, gh: int, gw: int, kgh: Optional[int] = None,
                 kgw: Optional[int] = None) -> np.ndarray:
@@ -173,14 +206,15 @@ def relpos_bias(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
     and rel_w[i, kw] = q_i . Rw[row_w(qw_i, kw)] (rows from
     :func:`relpos_rows`; on equal grids Rh[qh_i - kh + gh - 1]); the bias of
     key j = (kh, kw) of the kgh x kgw key grid is rel_h[i, kh] + rel_w[i, kw].
-    Queries sit on the gh x gw grid; q is the raw query row.
+    Queries sit on the gh x gw grid; q is the raw query row.  Tables of
+    another length than 2*max-1 rows are first resized to it
+    (:func:`rel_pos_resized`).
     """
     kgh = gh if kgh is None else kgh
     kgw = gw if kgw is None else kgw
     q_rows = np.asarray(q_rows, dtype=np.float64)
-    rh = np.asarray(rh, dtype=np.float64)
-    rw = np.asarray(rw, dtype=np.float64)
-    assert rh.shape[0] == 2 * max(gh, kgh) - 1 and rw.shape[0] == 2 * max(gw, kgw) - 1
+    rh = rel_pos_resized(rh, 2 * max(gh, kgh) - 1)
+    rw = rel_pos_resized(rw, 2 * max(gw, kgw) - 1)
     qh, qw = np.asarray(rows) // gw, np.asarray(rows) % gw
     rh_sel = rh[relpos_rows(gh, kgh)[qh]]                    # [R, kgh, d]
     rw_sel = rw[relpos_rows(gw, kgw)[qw]]                    # [R, kgw, d]

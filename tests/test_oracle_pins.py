@@ -523,12 +523,91 @@ def test_bruteforce_relpos_unequal_grids(qgrid, kgrid):
 
 
 def test_unequal_grids_reduce_to_equal_grids():
-    # kgrid equal to grid is the plain decomposed bias, and the table length
-    # must be 2*max-1 on each axis.
+    # kgrid equal to grid is the plain decomposed bias.
     q = rnd((6, 4), 30)
     rh, rw = rnd((5, 4), 31), rnd((3, 4), 32)
     a = O.relpos_bias(q, np.arange(6), rh, rw, 3, 2)
     b = O.relpos_bias(q, np.arange(6), rh, rw, 3, 2, 3, 2)
     np.testing.assert_array_equal(a, b)
-    with pytest.raises(AssertionError):
-        O.relpos_bias(q, np.arange(6), rh, rw, 3, 2, 4, 2)
+
+
+# ---------------------------------------------------------------------------
+# Resizing a relative-position table to the length the grids need
+# (rel_pos_resized of the SAM write-ups; reading: linear interpolation along
+# the offset axis, end rows aligned)
+# ---------------------------------------------------------------------------
+
+def py_resize(rows, m):
+    """Pure-Python resize: new row r at old position r*(L-1)/(m-1), split
+    into its integer and fractional parts by exact integer division."""
+    L = len(rows)
+    out = []
+    for r in range(m):
+        if L == 1 or m == 1:
+            out.append(list(rows[0]))
+            continue
+        num, den = r * (L - 1), m - 1
+        i, rem = divmod(num, den)
+        if i >= L - 1:
+            out.append(list(rows[L - 1]))
+            continue
+        f = rem / den
+        out.append([(1 - f) * a + f * b for a, b in zip(rows[i], rows[i + 1])])
+    return out
+
+
+@pytest.mark.parametrize("L,m", [(5, 5), (3, 7), (7, 3), (27, 15), (15, 27), (63, 127), (127, 63),
+                                 (2, 9), (1, 5), (6, 1), (31, 27)])
+def test_resize_bruteforce(L, m):
+    # Catches an off-by-one in the position (m or L instead of m-1, L-1), a
+    # swapped interpolation weight, or a floor in the wrong place.
+    t = rnd((L, 3), L * 100 + m)
+    got = O.rel_pos_resized(t, m)
+    np.testing.assert_allclose(got, np.array(py_resize(tolist2(t), m)), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("L,m", [(4, 4), (3, 11), (11, 3), (127, 27), (27, 127)])
+def test_resize_closed_forms(L, m):
+    # Identity at equal length; affine tables a + b*i stay affine with the
+    # same end rows, a + b*r*(L-1)/(m-1); constant tables stay constant.
+    t = rnd((L, 4), 7)
+    if L == m:
+        np.testing.assert_array_equal(O.rel_pos_resized(t, m), t)
+    a, b = rnd(4, 8), rnd(4, 9)
+    aff = a[None, :] + b[None, :] * np.arange(L)[:, None]
+    want = a[None, :] + b[None, :] * (np.arange(m) * (L - 1) / (m - 1))[:, None]
+    np.testing.assert_allclose(O.rel_pos_resized(aff, m), want, rtol=0, atol=1e-12)
+    got = O.rel_pos_resized(aff, m)
+    np.testing.assert_allclose(got[0], aff[0], atol=1e-14)
+    np.testing.assert_allclose(got[-1], aff[-1], atol=1e-12)
+    np.testing.assert_allclose(O.rel_pos_resized(np.ones((L, 2)) * 3.5, m), 3.5, atol=1e-14)
+
+
+@pytest.mark.parametrize("L,m", [(3, 7), (27, 15), (15, 27), (63, 127)])
+def test_resize_matches_library_interpolation(L, m):
+    # The reading equals torch's linear interpolation with aligned corners
+    # (a library routine with the same definition), in float64.
+    t = rnd((L, 5), 3)
+    lib = torch.nn.functional.interpolate(torch.from_numpy(t).T[None], size=m, mode="linear",
+                                          align_corners=True)[0].T.numpy()
+    np.testing.assert_allclose(O.rel_pos_resized(t, m), lib, rtol=0, atol=1e-12)
+
+
+def test_relpos_bias_resizes_tables():
+    # A table of another length is resized to 2*max-1 rows before use: the
+    # bias equals the bias of the explicitly resized table, and the
+    # attention equals a pure-Python brute force over the resized rows.
+    gh, gw, d = 3, 4, 3
+    q = rnd((1, 2, gh * gw, d), 40)
+    k, v = rnd((1, 2, gh * gw, d), 41), rnd((1, 2, gh * gw, d), 42)
+    rh, rw = rnd((9, d), 43), rnd((3, d), 44)          # need 5 and 7 rows
+    a = O.relpos_bias(q[0, 0], np.arange(gh * gw), rh, rw, gh, gw)
+    b = O.relpos_bias(q[0, 0], np.arange(gh * gw), O.rel_pos_resized(rh, 5), O.rel_pos_resized(rw, 7),
+                      gh, gw)
+    np.testing.assert_array_equal(a, b)
+    got = O.attention(q, k, v, bias=O.Bias("relpos", grid=(gh, gw), rh=rh, rw=rw))
+    rh5, rw7 = py_resize(tolist2(rh), 5), py_resize(tolist2(rw), 7)
+    for h in range(2):
+        want = py_attention_window(tolist2(q[0, h]), tolist2(k[0, h]), tolist2(v[0, h]), gh, gw,
+                                   rh=rh5, rw=rw7)
+        np.testing.assert_allclose(got[0, h], want, rtol=0, atol=1e-12)
