@@ -113,14 +113,20 @@ typedef enum {
  *    arithmetic: the shorter axis is stretched onto the longer one, as the
  *    coordinate scalers of SAM's image encoder do ("Accelerating Generative
  *    AI with PyTorch: Segment Anything, Fast", section "Bfloat16 half
- *    precision").  Rh and Rw then hold 2*max(grid_h,kgrid_h)-1 and
- *    2*max(grid_w,kgrid_w)-1 rows; tables of another length are not resized
- *    here (ATTN_E_SHAPE in the binding; the library reads exactly that many
- *    rows).
+ *    precision").  Rh and Rw then need 2*max(grid_h,kgrid_h)-1 and
+ *    2*max(grid_w,kgrid_w)-1 rows.
+ *  rh_rows, rw_rows: RELPOS only: the rows Rh and Rw actually hold (0: the
+ *    rows needed, above).  A table of another length (1 to 1023 rows) is
+ *    resized in the kernel to the needed length by linear interpolation
+ *    along the offset axis with both end rows kept: needed row r reads the
+ *    stored table at position r*(L-1)/(M-1) for L stored and M needed rows
+ *    (rel_pos_resized of the same SAM write-ups, which name the resize
+ *    without its rule).  Must be 0 for the other kinds.
  *  table: [(2gh-1)(2gw-1), H] contiguous, element [r, head] at r*H + head.
- *  rh: [2gh-1, d], rw: [2gw-1, d] contiguous (longer with a key grid, see
- *    above), shared by all heads; they are
- *    dotted with the raw (unscaled) query row; the bias is not scaled.
+ *  rh: [rh_rows, d], rw: [rw_rows, d] contiguous, by default [2gh-1, d] and
+ *    [2gw-1, d] (longer with a key grid, see above), shared by all heads;
+ *    they are dotted with the raw (unscaled) query row; the bias is not
+ *    scaled.  Both must be 16-byte aligned.
  *  add: [add_batch, Nq, Nk] with element strides add_strides[0..1] for the
  *    first two axes, last stride 1; batch item b uses add[b % add_batch].
  *  All bias data uses the call's dtype.                                     */
@@ -134,6 +140,7 @@ typedef struct {
   int64_t add_batch;
   int64_t add_strides[2];
   int32_t kgrid_h, kgrid_w;
+  int32_t rh_rows, rw_rows;
 } attn_bias_desc_t;
 
 typedef enum {
@@ -244,7 +251,8 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
 ATTN_API const char* attn_strerror(int status);
 
 /* attn_version: library ABI version, (major << 16) | minor (1.2 added
- * attn_fwd_opt and attn_check_opt).                                          */
+ * attn_fwd_opt, attn_check_opt and the rh_rows, rw_rows fields of
+ * attn_bias_desc_t, which grew from 80 to 88 bytes).                         */
 ATTN_API int attn_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ class BiasDescC(ctypes.Structure):
                 ("table", ctypes.c_void_p), ("rh", ctypes.c_void_p), ("rw", ctypes.c_void_p),
                 ("add", ctypes.c_void_p), ("add_batch", ctypes.c_int64),
                 ("add_strides", ctypes.c_int64 * 2), ("kgrid_h", ctypes.c_int32),
-                ("kgrid_w", ctypes.c_int32)]
+                ("kgrid_w", ctypes.c_int32), ("rh_rows", ctypes.c_int32), ("rw_rows", ctypes.c_int32)]
 
 
 class WindowC(ctypes.Structure):
@@ -123,8 +123,10 @@ class RelposBias:
     """SAM decomposed relative position: Rh [2gh-1, d], Rw [2gw-1, d].
 
     ``kgrid`` (batched layout only): the key grid when it differs from the
-    query grid ``grid``; Rh and Rw then hold 2*max(gh, kgh)-1 and
+    query grid ``grid``; Rh and Rw then need 2*max(gh, kgh)-1 and
     2*max(gw, kgw)-1 rows and the shorter axis is stretched onto the longer.
+    Tables of another length (1 to 1023 rows) are resized by the kernel to
+    the needed length (linear interpolation, end rows kept).
     """
     rh: torch.Tensor
     rw: torch.Tensor
@@ -173,6 +175,7 @@ def _descs(bias, mask, layout: int, window: Optional[Window], keep: list):
         if bias.kgrid is not None:
             bd.kgrid_h, bd.kgrid_w = bias.kgrid
         bd.rh, bd.rw = keep[-2].data_ptr(), keep[-1].data_ptr()
+        bd.rh_rows, bd.rw_rows = bias.rh.shape[0], bias.rw.shape[0]
     elif isinstance(bias, AdditiveBias):
         a = bias.add if bias.add.dim() == 3 else bias.add.reshape(-1, *bias.add.shape[-2:])
         if a.stride(2) != 1:
@@ -220,10 +223,10 @@ def _check_extents(q, k, bias, mask, lay, window):
             raise ValueError(f"table must be [{(2 * gh - 1) * (2 * gw - 1)}, {H}]")
     elif isinstance(bias, RelposBias):
         gh, gw = bias.grid
-        kgh, kgw = bias.kgrid if bias.kgrid is not None else bias.grid
-        nh, nw = 2 * max(gh, kgh) - 1, 2 * max(gw, kgw) - 1
-        if tuple(bias.rh.shape) != (nh, D) or tuple(bias.rw.shape) != (nw, D):
-            raise ValueError(f"rh, rw must be [{nh}, {D}], [{nw}, {D}]")
+        if bias.rh.dim() != 2 or bias.rw.dim() != 2 or bias.rh.shape[1] != D or bias.rw.shape[1] != D:
+            raise ValueError(f"rh, rw must be [rows, {D}]")
+        if not (1 <= bias.rh.shape[0] <= 1023 and 1 <= bias.rw.shape[0] <= 1023):
+            raise ValueError("rh, rw must hold 1 to 1023 rows")
     elif isinstance(bias, AdditiveBias):
         if tuple(bias.add.shape[-2:]) != (nq, nk):
             raise ValueError(f"additive bias must end in [{nq}, {nk}]")

@@ -142,6 +142,8 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
 
   // Bias.
   a->bias_kind = bias_kind;
+  if (bias && bias_kind != ATTN_BIAS_RELPOS && (bias->rh_rows != 0 || bias->rw_rows != 0))
+    return ATTN_E_SHAPE;  // stored table lengths belong to the relative position
   if (bias_kind == ATTN_BIAS_TABLE || bias_kind == ATTN_BIAS_RELPOS) {
     if (bias->grid_h < 1 || bias->grid_w < 1) return ATTN_E_SHAPE;
     if (bias->grid_h > kMaxGridSide || bias->grid_w > kMaxGridSide) return ATTN_E_UNSUPPORTED;
@@ -172,6 +174,12 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
       // Table rows per axis: 2 * max(query, key positions) - 1.
       if ((a->gh > a->kgh ? a->gh : a->kgh) + (a->gw > a->kgw ? a->gw : a->kgw) > 256)
         return ATTN_E_UNSUPPORTED;
+      // Stored rows (0: the rows needed); another length is resized in the
+      // kernel.
+      if (bias->rh_rows < 0 || bias->rw_rows < 0) return ATTN_E_SHAPE;
+      if (bias->rh_rows > 1023 || bias->rw_rows > 1023) return ATTN_E_UNSUPPORTED;
+      a->rh_rows = bias->rh_rows ? bias->rh_rows : 2 * (a->gh > a->kgh ? a->gh : a->kgh) - 1;
+      a->rw_rows = bias->rw_rows ? bias->rw_rows : 2 * (a->gw > a->kgw ? a->gw : a->kgw) - 1;
       a->rh = bias->rh;
       a->rw = bias->rw;
     }

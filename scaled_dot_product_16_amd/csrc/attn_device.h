@@ -197,6 +197,22 @@ __device__ __forceinline__ int rel_row(int qc, int kc, int qn, int kn) {
   return qc * kn / qn + (kn - 1 - kc);
 }
 
+// Row r of a relative-position table resized from n stored to m needed rows
+// (linear interpolation along the offset axis, end rows kept): the value is
+// (1-f)*T[i0] + f*T[i1] at position r*(n-1)/(m-1), with i0 = floor and the
+// fraction from exact integer arithmetic.  n == m gives row r itself.
+__device__ __forceinline__ void resized_row(int r, int n, int m, int& i0, int& i1, float& f) {
+  if (n == m || n == 1 || m == 1) {
+    i0 = i1 = n == m ? r : 0;
+    f = 0.f;
+    return;
+  }
+  const int num = r * (n - 1);
+  i0 = num / (m - 1);
+  i1 = i0 + 1 < n ? i0 + 1 : i0;
+  f = (float)(num - i0 * (m - 1)) * __builtin_amdgcn_rcpf((float)(m - 1));
+}
+
 // ---------------------------------------------------------------------------
 // Bias and mask, evaluated per (query, key) from on-chip index data.
 //
@@ -255,12 +271,20 @@ __device__ void setup_bias(const AttnArgs& a, char* dyn, int b, int h, int q0, B
       const int qi = min(q0 + il, a.Nq - 1);
       const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * a.gw;
       const int64_t qo = tok_off(a, a.q_sb, a.q_sh, a.q_sn, b, h, qi);
-      const int64_t to = kk < a.kgh ? (int64_t)rel_row(qh, kk, a.gh, a.kgh) * a.D
-                                    : (int64_t)rel_row(qw, kk - a.kgh, a.gw, a.kgw) * a.D;
-      const void* tb = kk < a.kgh ? a.rh : a.rw;
-      float acc = 0.f;  // a padding query (qo < 0) is zero
-      for (int c = 0; qo >= 0 && c < a.D; c += 4) acc += dot4<E>(a.q, qo + c, tb, to + c);
-      (kk < a.kgh ? relh + kk * BM : relw + (kk - a.kgh) * BM)[il] = acc * kLog2e;
+      const bool hax = kk < a.kgh;
+      const int r = hax ? rel_row(qh, kk, a.gh, a.kgh) : rel_row(qw, kk - a.kgh, a.gw, a.kgw);
+      const int need = hax ? 2 * max(a.gh, a.kgh) - 1 : 2 * max(a.gw, a.kgw) - 1;
+      int i0, i1;
+      float f;
+      resized_row(r, hax ? a.rh_rows : a.rw_rows, need, i0, i1, f);
+      const void* tb = hax ? a.rh : a.rw;
+      float acc0 = 0.f, acc1 = 0.f;  // a padding query (qo < 0) is zero
+      for (int c = 0; qo >= 0 && c < a.D; c += 4) {
+        acc0 += dot4<E>(a.q, qo + c, tb, (int64_t)i0 * a.D + c);
+        if (i1 != i0) acc1 += dot4<E>(a.q, qo + c, tb, (int64_t)i1 * a.D + c);
+      }
+      const float acc = i1 != i0 ? acc0 + f * (acc1 - acc0) : acc0;
+      (hax ? relh + kk * BM : relw + (kk - a.kgh) * BM)[il] = acc * kLog2e;
     }
     bc.relh = relh;
     bc.relw = relw;

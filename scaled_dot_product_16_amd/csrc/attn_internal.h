@@ -49,6 +49,8 @@ struct AttnArgs {
   int32_t bias_kind;
   int32_t gh, gw;    // grid of the queries (TABLE, RELPOS)
   int32_t kgh, kgw;  // grid of the keys (== gh, gw except for RELPOS with a key grid)
+  int32_t rh_rows, rw_rows;  // RELPOS: rows stored in Rh, Rw (resized in the kernel when
+                             // they differ from 2*max(gh, kgh)-1, 2*max(gw, kgw)-1)
   const void* table;
   const void* rh;
   const void* rw;

@@ -424,16 +424,17 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         for (int part = 0; part < 2; ++part) {
           const int gg = part == 0 ? a.gh : a.gw;    // query positions on this axis
           const int kg = part == 0 ? a.kgh : a.kgw;  // key positions
-          const int nrow = 2 * (gg > kg ? gg : kg) - 1;
+          const int nrow = 2 * (gg > kg ? gg : kg) - 1;  // rows the grids need
+          const int nsrc = part == 0 ? a.rh_rows : a.rw_rows;  // rows stored
           const uint16_t* tab = (const uint16_t*)(part == 0 ? a.rh : a.rw);
-          for (int mb = 0; mb * 16 < nrow; ++mb) {
+          for (int mb = 0; mb * 16 < nsrc; ++mb) {
             const int m_row = mb * 16 + l16;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dc = 0; dc < KCH; ++dc) {
               const int d0 = dc * 32 + g * 8;
               u32x4 af = {0, 0, 0, 0};
-              if (m_row < nrow && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
+              if (m_row < nsrc && d0 < D) af = *(const u32x4*)(tab + (int64_t)m_row * D + d0);
               acc = E::mfma(af, qf[qb][dc], acc);
             }
 #pragma unroll
@@ -444,7 +445,16 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           const int qc = part == 0 ? qh : qw;
           float* dst = part == 0 ? relh : relw;
-          for (int kk = g; kk < kg; kk += 4) dst[kk * BM + il] = gscr[l16 * grow + rel_row(qc, kk, gg, kg)] * kLog2e;
+          // A table stored at another length is resized here: the product
+          // with q is linear, so interpolating G between stored rows equals
+          // the product with the interpolated row.
+          for (int kk = g; kk < kg; kk += 4) {
+            int i0, i1;
+            float f;
+            resized_row(rel_row(qc, kk, gg, kg), nsrc, nrow, i0, i1, f);
+            const float g0 = gscr[l16 * grow + i0];
+            dst[kk * BM + il] = fmaf(f, gscr[l16 * grow + i1] - g0, g0) * kLog2e;
+          }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

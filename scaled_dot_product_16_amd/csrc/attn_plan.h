@@ -70,13 +70,24 @@ struct MfmaCfg {
 // stacked table [Rh; Rw] for one query, padded to keep 16-byte stores aligned.
 constexpr int kAugGrow = 68;
 
-// Row length (floats) of the relative-position prologue scratch.
+// Row length (floats) of the relative-position prologue scratch: every
+// stored or needed table row of either axis.
 constexpr int relpos_grow(const AttnArgs& a) {
   int g = a.gh > a.gw ? a.gh : a.gw;
   g = g > a.kgh ? g : a.kgh;
   g = g > a.kgw ? g : a.kgw;
-  const int m = 2 * g - 1;
+  int m = 2 * g - 1;
+  m = m > a.rh_rows ? m : a.rh_rows;
+  m = m > a.rw_rows ? m : a.rw_rows;
   return (m + 15) / 16 * 16 + 4;
+}
+
+// Whether Rh or Rw is stored at another length than the grids need (then
+// resized in the kernel).
+constexpr bool relpos_resized(const AttnArgs& a) {
+  return a.bias_kind == ATTN_BIAS_RELPOS &&
+         (a.rh_rows != 2 * (a.gh > a.kgh ? a.gh : a.kgh) - 1 ||
+          a.rw_rows != 2 * (a.gw > a.kgw ? a.gw : a.kgw) - 1);
 }
 
 constexpr bool needs_kinfo(int bias_kind, bool mask) {
@@ -270,7 +281,9 @@ inline Plan plan_half(const AttnArgs& a) {
   p.hg = 1;
   p.nw = 4;
   p.rmode = kRelTables;
-  const bool same_grid = a.gh == a.kgh && a.gw == a.kgw;
+  // The row and contraction forms read the tables directly: they take equal
+  // grids and tables of the needed length; the table form takes the rest.
+  const bool same_grid = a.gh == a.kgh && a.gw == a.kgw && !relpos_resized(a);
   if (a.bias_kind == ATTN_BIAS_RELPOS && !mask) {
     // Long key ranges on a 64-wide grid: eight-wave workgroups whose two
     // wave groups alternate matrix and softmax phases (batched layout).

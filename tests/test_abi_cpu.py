@@ -40,7 +40,7 @@ def test_struct_layout_matches_header(lib):
     # The binding's structs must match the C layout (sizes on x86-64).
     assert ctypes.sizeof(B.AttnTensorC) == 8 + 32 + 24 + 8
     assert ctypes.sizeof(B.WindowC) == 24
-    assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16 + 8
+    assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16 + 8 + 8
     assert ctypes.sizeof(B.MaskDescC) == 8 + 8 + 8 + 16 + 24 + 4 + 4
     assert ctypes.sizeof(B.OptionsC) == 32
 
@@ -173,8 +173,10 @@ def test_key_grid_validation(lib):
     assert B.check(q, q.clone(), q.clone(), bias=rp(31, 31, (16, 16))) == 2  # Nk != key grid
     k2 = t(1, 2, 32, 64, dtype=bf)
     assert B.check(q, k2, k2.clone(), bias=rp(15, 15, (4, 8))) == 0
-    with pytest.raises(ValueError):                                         # rows must be 2*max-1
-        B.check(q, k, k.clone(), bias=rp(15, 15, (16, 16)))
+    # Tables of another length than 2*max-1 are resized by the kernel.
+    assert B.check(q, k, k.clone(), bias=rp(15, 15, (16, 16))) == 0
+    with pytest.raises(ValueError):                                         # 1 to 1023 rows
+        B.check(q, k, k.clone(), bias=rp(1024, 15, (16, 16)))
     # A 2 x 128 key grid is a valid call whose per-query tables (130 rows)
     # and 255-row prologue scratch do not fit one CU's LDS next to the K/V
     # tiles: E_UNSUPPORTED from the host validation, as from attn_fwd.
@@ -251,3 +253,31 @@ def test_window_heads_option(lib):
     ql = t(1, 4, 300, 64)
     assert B.check(ql, ql.clone(), ql.clone(), window_heads=2) == 4    # not a window-sized call
     assert B.check(ql, ql.clone(), ql.clone(), window_heads=1) == 0
+
+
+def test_table_lengths_validation(lib):
+    # rh_rows / rw_rows: stored table lengths of the relative position (0 =
+    # the needed 2*max-1); other kinds must leave them 0.
+    bf = torch.bfloat16
+    q = t(1, 2, 196, 64, dtype=bf)
+    for nh, nw in [(27, 27), (15, 31), (1, 1), (127, 63)]:
+        rb = B.RelposBias(t(nh, 64, dtype=bf), t(nw, 64, dtype=bf), (14, 14))
+        assert B.check(q, q.clone(), q.clone(), bias=rb) == 0, (nh, nw)
+    rb = B.RelposBias(t(27, 64, dtype=bf), t(27, 64, dtype=bf), (14, 14))
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(q, q.clone(), q.clone(), q.clone(), rb, None,
+                                                  "batched", None)
+    h = B.lib()
+    args = lambda: (ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                    ctypes.byref(md), ctypes.byref(oc), dt)
+    assert (bd.rh_rows, bd.rw_rows) == (27, 27)
+    bd.rh_rows = 0
+    assert h.attn_check(*args()) == 0      # 0: the needed length
+    bd.rh_rows = -1
+    assert h.attn_check(*args()) == 2
+    bd.rh_rows = 1024
+    assert h.attn_check(*args()) == 4
+    bd.rh_rows = 27
+    tab = t(27 * 27, 2, dtype=bf)
+    bd.kind, bd.table = 1, tab.data_ptr()  # a table bias with table lengths set
+    assert h.attn_check(*args()) == 2
+    del keep

@@ -1,6 +1,7 @@
 """GPU parity of the decomposed relative-position bias with the keys on a
 grid of their own (SAM's coordinate scalers: the shorter axis stretched onto
-the longer one), against the fp64 oracle, every output element.
+the longer one) and with tables stored at another length than the grids
+need (resized in the kernel), against the fp64 oracle, every output element.
 
 The half-precision calls take the general relative-position form of the
 tiled kernel (the row and contraction forms need equal grids); fp32 calls
@@ -10,6 +11,7 @@ both directions, and mixed between the two axes.
 
 import sys
 
+import numpy as np
 import pytest
 
 from scaled_dot_product_16_amd import workloads as W
@@ -106,3 +108,50 @@ def test_key_grid_relpos_with_additive_mask(dtype):
     inp = with_dense_terms(w, W.make_inputs(w, seed=5), n_mask=3)
     err = check_full(w, inp, run_gpu(w, to_device(inp)))
     say(f"  max abs err {err:.3e} (tol {TOL[dtype]:.0e})")
+
+
+# Tables stored at another length than the grids need (rel_pos_resized):
+# resized in the kernel by linear interpolation along the offset axis (end
+# rows kept), compared with the oracle, which resizes the table first.
+RESIZE_CASES = [
+    # (dtype, head dim, query grid, key grid or None, stored Rh rows, stored Rw rows)
+    (W.BF16, 64, (14, 14), None, 15, 31),     # SAM windows, tables from other window sizes
+    (W.F16, 64, (14, 14), None, 27, 9),
+    (W.BF16, 64, (32, 32), None, 127, 127),   # SAM's 64x64 tables on a 32x32 grid
+    (W.BF16, 80, (16, 64), None, 63, 255),    # a 64-wide grid: the table form instead of the row form
+    (W.F16, 40, (6, 10), (9, 5), 5, 40),      # resize together with a key grid
+    (W.BF16, 32, (3, 3), None, 1, 2),         # one- and two-row tables
+    (W.F32, 32, (14, 14), None, 15, 31),
+    (W.F32, 64, (6, 10), (9, 5), 5, 40),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RESIZE_CASES)))
+def test_resized_tables(case):
+    import torch
+
+    dtype, d, qg, kg, nh, nw = RESIZE_CASES[case]
+    kgr = kg or qg
+    nq, nk = qg[0] * qg[1], kgr[0] * kgr[1]
+    w = W.custom(dtype, B=2, H=2, Nq=nq, Nk=nk, d=d, bias="relpos", grid=qg, kgrid=kg, cfg_id=590 + case)
+    say(f"[resized tables] {dtype} d={d} grid {qg} key grid {kg} stored rows {nh}, {nw}")
+    inp = W.make_inputs(w, seed=case)
+    std = 1.0 / float(np.sqrt(d))
+    inp["rh"] = W.to_dtype(W.normal((nh, d), 590 + case, 3, std), dtype)
+    inp["rw"] = W.to_dtype(W.normal((nw, d), 590 + case, 4, std), dtype)
+    err = check_full(w, inp, run_gpu(w, to_device(inp)), name=f"resized tables {qg}/{kg} rows {nh},{nw} d={d}")
+    say(f"  max abs err {err:.3e} (tol {TOL[dtype]:.0e})")
+    assert torch.cuda.is_available()
+
+
+def test_resized_tables_image_layout():
+    # SAM windows read from the unpadded image with resized tables.
+    geom = (30, 20, 14, 14, 0, 0)
+    w = W.custom(W.BF16, B=2 * 6, H=2, Nq=196, Nk=196, d=64, bias="relpos", grid=(14, 14),
+                 layout="image", images=2, window=geom, cfg_id=599)
+    say(f"[resized tables] image layout {geom}, stored rows 21, 33")
+    inp = W.make_inputs(w, seed=9)
+    inp["rh"] = W.to_dtype(W.normal((21, 64), 599, 3, 0.125), W.BF16)
+    inp["rw"] = W.to_dtype(W.normal((33, 64), 599, 4, 0.125), W.BF16)
+    err = check_full(w, inp, run_gpu(w, to_device(inp)), name="resized tables, image layout")
+    say(f"  max abs err {err:.3e} (tol {TOL[W.BF16]:.0e})")
