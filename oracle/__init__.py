@@ -28,5 +28,8 @@ from .attention import (  # noqa: F401
     attention_probs,
     attention,
     attention_image,
+    attention_backward,
+    attention_image_backward,
     run_workload,
+    run_workload_backward,
 )

@@ -441,14 +441,111 @@ def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
     return o.reshape(B, H, N, v.shape[-1])
 
 
-def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
-    """Oracle output for a workload description.
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
 
-    ``w`` is any object with the attributes bias, grid, mask, layout, window
-    (a workload record); ``arrays`` maps q, k, v and the bias tables
-    (table / rh, rw / bias_add, mask_add) to float64 numpy arrays holding the
-    exact device values.  ``select`` as in :func:`attention` (batched layout).
+def attention_backward(q, k, v, dout, bias: Optional[Bias] = None,
+                       mask: Optional[Mask] = None) -> dict:
+    """Gradients of L = sum(dout * O) for O = softmax(scale*QK^T + B + M) V.
+
+    The Swin talk, section 2, trains with a fused window op that has its own
+    backward; the gradients here are the plain chain rule of the forward
+    definition, written out per (batch item, head) in float64:
+      P = softmax rows of S,  dV = P^T dO,  dP = dO V^T,
+      dS = P * (dP - rowsum(P * dP)),
+      dQ = scale * dS K,  dK = scale * dS^T Q,
+      d_table[r, h] = sum of dS over the pairs (i, j) of head h that read
+                      table row r (summed over batch items),
+      decomposed relative position (bias q_i.Rh[row_h] + q_i.Rw[row_w]):
+      dQ_i += sum_j dS_ij (Rh[row_h(i, j)] + Rw[row_w(i, j)]),
+      dRh[m] = sum of dS_ij q_i over (b, h, i, j) with row_h(i, j) = m
+      (dRw likewise), for the tables of the needed length, then mapped to
+      the stored tables through the transpose of the resize.
+    The mask is a constant and has no gradient.  Returns dq, dk, dv and,
+    with a table bias, dtable [(2gh-1)(2gw-1), H]; with the relative
+    position, drh, drw.
     """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = 1.0 / np.sqrt(d)
+    cache: dict = {}
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    res = {}
+    if bias is not None and bias.kind == "table":
+        gh, gw = bias.grid
+        idx = table_relative_index(gh, gw)
+        dtable = np.zeros((idx.max() + 1, H))
+    if bias is not None and bias.kind == "relpos":
+        gh, gw = bias.grid
+        kgh, kgw = bias.kgrid if bias.kgrid is not None else (gh, gw)
+        rh = rel_pos_resized(bias.rh, 2 * max(gh, kgh) - 1)
+        rw = rel_pos_resized(bias.rw, 2 * max(gw, kgw) - 1)
+        row_h = relpos_rows(gh, kgh)[np.arange(Nq) // gw][:, np.arange(Nk) // kgw]   # [Nq, Nk]
+        row_w = relpos_rows(gw, kgw)[np.arange(Nq) % gw][:, np.arange(Nk) % kgw]
+        drh, drw = np.zeros_like(rh), np.zeros_like(rw)
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            s = s + _additive_rows(b, h, rows, q[b, h], Nk, bias, mask, cache)
+            p = _softmax_rows(s)
+            dv[b, h] = p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, h].T
+            ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+            if bias is not None and bias.kind == "table":
+                np.add.at(dtable[:, h], idx, ds)
+            if bias is not None and bias.kind == "relpos":
+                dq[b, h] += np.einsum("ij,ijc->ic", ds, rh[row_h]) + np.einsum("ij,ijc->ic", ds, rw[row_w])
+                np.add.at(drh, row_h, ds[:, :, None] * q[b, h][:, None, :])
+                np.add.at(drw, row_w, ds[:, :, None] * q[b, h][:, None, :])
+    res.update(dq=dq, dk=dk, dv=dv)
+    if bias is not None and bias.kind == "table":
+        res["dtable"] = dtable
+    if bias is not None and bias.kind == "relpos":
+        # Gradients of the stored tables: the resize is linear, T' = W T with
+        # W the resize of the identity, so dT = W^T dT'.
+        wh = rel_pos_resized(np.eye(np.asarray(bias.rh).shape[0]), rh.shape[0])
+        ww = rel_pos_resized(np.eye(np.asarray(bias.rw).shape[0]), rw.shape[0])
+        res["drh"], res["drw"] = wh.T @ drh, ww.T @ drw
+    return res
+
+
+def attention_image_backward(q, k, v, dout, window: tuple, bias: Optional[Bias] = None,
+                             mask: Optional[Mask] = None) -> dict:
+    """Gradients of the shifted-window attention on image-layout tensors: the
+    padding, roll and partition of :func:`attention_image` are index maps, so
+    the gradients are mapped back through the same maps (padding rows
+    dropped)."""
+    img_h, img_w, win_h, win_w, sh, sw = window
+    B, H, N, d = np.asarray(q).shape
+    ph, pw = padded_extent(img_h, win_h), padded_extent(img_w, win_w)
+
+    def to_windows(x):
+        x = np.asarray(x, dtype=np.float64).reshape(B, H, img_h, img_w, x.shape[-1])
+        x = np.pad(x, ((0, 0), (0, 0), (0, ph - img_h), (0, pw - img_w), (0, 0)))
+        x = np.roll(x, shift=(-sh, -sw), axis=(2, 3))
+        return window_partition(x, win_h, win_w)
+
+    def from_windows(g):
+        x = window_reverse(g, ph, pw, win_h, win_w)
+        x = np.roll(x, shift=(sh, sw), axis=(2, 3))[:, :, :img_h, :img_w]
+        return x.reshape(B, H, N, g.shape[-1])
+
+    res = attention_backward(to_windows(q), to_windows(k), to_windows(v), to_windows(dout), bias, mask)
+    for key in ("dq", "dk", "dv"):
+        res[key] = from_windows(res[key])
+    return res
+
+
+def _workload_terms(w, arrays: dict):
+    """The Bias and Mask of a workload record, tables taken from ``arrays``."""
     bias = Bias("none")
     if w.bias == "table":
         bias = Bias("table", grid=w.grid, table=arrays["table"])
@@ -462,7 +559,29 @@ def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
         mask = Mask("shift", window=tuple(w.window))
     elif w.mask == "additive":
         mask = Mask("additive", add=arrays["mask_add"])
+    return bias, mask
+
+
+def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
+    """Oracle output for a workload description.
+
+    ``w`` is any object with the attributes bias, grid, mask, layout, window
+    (a workload record); ``arrays`` maps q, k, v and the bias tables
+    (table / rh, rw / bias_add, mask_add) to float64 numpy arrays holding the
+    exact device values.  ``select`` as in :func:`attention` (batched layout).
+    """
+    bias, mask = _workload_terms(w, arrays)
     if w.layout == "image":
         assert select is None, "image layout is evaluated whole"
         return attention_image(arrays["q"], arrays["k"], arrays["v"], tuple(w.window), bias, mask)
     return attention(arrays["q"], arrays["k"], arrays["v"], bias, mask, select=select)
+
+
+def run_workload_backward(w, arrays: dict) -> dict:
+    """Oracle gradients for a workload description (see run_workload);
+    ``arrays`` also holds ``dout``, the gradient of the output."""
+    bias, mask = _workload_terms(w, arrays)
+    if w.layout == "image":
+        return attention_image_backward(arrays["q"], arrays["k"], arrays["v"], arrays["dout"],
+                                        tuple(w.window), bias, mask)
+    return attention_backward(arrays["q"], arrays["k"], arrays["v"], arrays["dout"], bias, mask)
