@@ -44,6 +44,7 @@
 #ifndef ATTN_H_
 #define ATTN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -247,12 +248,58 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
                    const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
                    const attn_tensor_t* out, int32_t dtype, const attn_options_t* options);
 
+/* Backward pass: gradients of L = sum(dout * O) for the forward
+ * O = softmax(scale*QK^T + bias + mask) V ("Training and inference
+ * acceleration for large vision models", section 2: Swin is trained with a
+ * fused window op that has a forward and a backward).
+ *
+ *  q, k, v, bias_desc, mask_desc, dtype: as in attn_fwd.  dout: the output
+ *  gradient, laid out like `out` of attn_fwd.  dq, dk, dv: written, shaped and
+ *  laid out like q, k, v (own strides allowed); they must overlap no input and
+ *  no other gradient.  dtable: TABLE bias only (else ignored, may be NULL): a
+ *  device fp32 array [(2gh-1)(2gw-1), H], element [r, head] at r*H + head,
+ *  overwritten with the table gradient summed over all batch items.  The
+ *  mask and an ADDITIVE bias receive no gradient.
+ *  workspace: device memory of at least the bytes attn_bwd_workspace_size
+ *  reports (B_eff * H * table rows * 4 with a TABLE bias, else 0; NULL
+ *  allowed when 0), 16-byte aligned, owned by the caller; its contents
+ *  before and after the call are unspecified.  The per-window partial table
+ *  gradients go there, so the sum over windows runs in a fixed order
+ *  (bitwise-deterministic, no atomics).
+ *
+ *  Built: half precision (F16/BF16), units of at most 64 queries and keys
+ *  (the window path: Swin windows in either layout, with shift and padding
+ *  folded in), bias NONE, TABLE or ADDITIVE, any mask.  Other calls
+ *  (fp32, longer sequences, RELPOS) return ATTN_E_UNSUPPORTED.
+ *  Asynchronous on `stream`; two kernels (units, then the table reduction).  */
+ATTN_API int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+             const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+             const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
+             const attn_tensor_t* dv, float* dtable, int32_t dtype, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* attn_bwd_check: the validation of attn_bwd without touching the GPU (the
+ * status attn_bwd returns, short of a launch failure).                       */
+ATTN_API int attn_bwd_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                   const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                   const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq,
+                   const attn_tensor_t* dk, const attn_tensor_t* dv, float* dtable,
+                   int32_t dtype, void* workspace, size_t workspace_bytes);
+
+/* attn_bwd_workspace_size: *bytes = the workspace attn_bwd needs for these
+ * arguments (validated as the forward call with dout as its output).         */
+ATTN_API int attn_bwd_workspace_size(const attn_tensor_t* q, const attn_tensor_t* k,
+                            const attn_tensor_t* v, const attn_tensor_t* dout,
+                            const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
+                            int32_t dtype, size_t* bytes);
+
 /* attn_strerror: static text for a status code (never NULL).                */
 ATTN_API const char* attn_strerror(int status);
 
 /* attn_version: library ABI version, (major << 16) | minor (1.2 added
  * attn_fwd_opt, attn_check_opt and the rh_rows, rw_rows fields of
- * attn_bias_desc_t, which grew from 80 to 88 bytes).                         */
+ * attn_bias_desc_t, which grew from 80 to 88 bytes; 1.3 the backward:
+ * attn_bwd, attn_bwd_check, attn_bwd_workspace_size).                        */
 ATTN_API int attn_version(void);
 
 #ifdef __cplusplus

@@ -86,6 +86,16 @@ def lib() -> ctypes.CDLL:
         h.attn_check_opt.argtypes = [P(AttnTensorC), P(AttnTensorC), P(AttnTensorC), P(BiasDescC),
                                      P(MaskDescC), P(AttnTensorC), ctypes.c_int32, P(OptionsC)]
         h.attn_check_opt.restype = ctypes.c_int
+        T = P(AttnTensorC)
+        h.attn_bwd.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
+                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.attn_bwd.restype = ctypes.c_int
+        h.attn_bwd_check.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
+        h.attn_bwd_check.restype = ctypes.c_int
+        h.attn_bwd_workspace_size.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), ctypes.c_int32,
+                                              P(ctypes.c_size_t)]
+        h.attn_bwd_workspace_size.restype = ctypes.c_int
         h.attn_strerror.argtypes = [ctypes.c_int]
         h.attn_strerror.restype = ctypes.c_char_p
         h.attn_version.argtypes = []
@@ -328,3 +338,47 @@ def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
                             ctypes.byref(md), ctypes.byref(oc), dt)
     return h.attn_check_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
                             ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, bias=None, mask=None,
+        layout: str = "batched", window: Optional[Window] = None, dq=None, dk=None, dv=None,
+        dtable=None, workspace=None, stream=None):
+    """Gradients of sum(dout * O) for O = fwd(q, k, v, bias, mask) via attn_bwd.
+
+    Returns (dq, dk, dv, dtable); dtable (fp32 [table rows, H]) only with a
+    TableBias, else None.  Output and workspace tensors are allocated with
+    torch when not given; the library itself allocates nothing.  Queued on
+    ``stream`` (default: torch's current stream).
+    """
+    h = lib()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, dout, bias, mask, layout, window)
+    lay = {"batched": LAYOUT_BATCHED, "image": LAYOUT_IMAGE}[layout]
+    dqc, dkc, dvc = _tensor_c(dq, lay), _tensor_c(dk, lay), _tensor_c(dv, lay)
+    if isinstance(bias, TableBias) and dtable is None:
+        dtable = torch.empty(bias.table.shape, dtype=torch.float32, device=q.device)
+    if dtable is not None and (dtable.dtype != torch.float32 or not dtable.is_contiguous()):
+        raise TypeError("dtable must be a contiguous float32 tensor")
+    need = ctypes.c_size_t(0)
+    st = h.attn_bwd_workspace_size(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
+                                   ctypes.byref(bd), ctypes.byref(md), dt, ctypes.byref(need))
+    if st != ATTN_OK:
+        raise AttnError(st, h.attn_strerror(st).decode())
+    if workspace is None and need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = h.attn_bwd(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc), ctypes.byref(bd),
+                    ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc), ctypes.byref(dvc),
+                    ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0), dt,
+                    ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0),
+                    ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+                    ctypes.c_void_p(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, h.attn_strerror(st).decode())
+    del keep
+    return dq, dk, dv, (dtable if isinstance(bias, TableBias) else None)

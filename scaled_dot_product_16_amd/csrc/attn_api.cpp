@@ -240,9 +240,116 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   return make_plan(*a, &plan);
 }
 
+int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov, const void* biasv,
+                 const void* maskv, const void* dqv, const void* dkv, const void* dvv, float* dtable,
+                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes) {
+  if (!ba || !ws_bytes) return ATTN_E_NULL;
+  memset(ba, 0, sizeof(*ba));
+  *ws_bytes = 0;
+  // The forward validation, with dO in the place of the output.
+  int st = validate(qv, kv, vv, biasv, maskv, dov, dtype, nullptr, &ba->a);
+  if (st != ATTN_OK) return st;
+  const attn_tensor_t* q = (const attn_tensor_t*)qv;
+  const attn_tensor_t* k = (const attn_tensor_t*)kv;
+  const attn_tensor_t* v = (const attn_tensor_t*)vv;
+  const attn_tensor_t* dout = (const attn_tensor_t*)dov;
+  const attn_tensor_t* dq = (const attn_tensor_t*)dqv;
+  const attn_tensor_t* dk = (const attn_tensor_t*)dkv;
+  const attn_tensor_t* dv = (const attn_tensor_t*)dvv;
+  if (!dq || !dk || !dv) return ATTN_E_NULL;
+  const int es = elem_size(dtype);
+  if ((st = check_tensor(dq, es)) || (st = check_tensor(dk, es)) || (st = check_tensor(dv, es))) return st;
+  const attn_tensor_t* pairs[3][2] = {{dq, q}, {dk, k}, {dv, v}};
+  for (auto& pr : pairs) {
+    for (int i = 0; i < 4; ++i)
+      if (pr[0]->dims[i] != pr[1]->dims[i]) return ATTN_E_SHAPE;
+    if (pr[0]->layout != pr[1]->layout) return ATTN_E_LAYOUT;
+    const int slice_bits = ba->a.image ? 29 : 31;
+    if ((pr[0]->dims[2] - 1) * pr[0]->strides[2] + pr[0]->dims[3] >= (int64_t(1) << slice_bits))
+      return ATTN_E_UNSUPPORTED;
+  }
+  // Gradients overlap neither the inputs nor each other.
+  const attn_tensor_t* ins[4] = {q, k, v, dout};
+  const attn_tensor_t* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (const attn_tensor_t* t : ins)
+      if (overlaps(outs[i], t, es)) return ATTN_E_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j], es)) return ATTN_E_ALIAS;
+  }
+  // Built: window units (at most 64 queries and keys) in half precision,
+  // with or without a table bias; no gradient of the relative position.
+  Plan plan;
+  if ((st = make_bwd_plan(ba->a, &plan)) != ATTN_OK) return st;
+  ba->dq = dq->data;
+  ba->dk = dk->data;
+  ba->dv = dv->data;
+  ba->dq_sb = dq->strides[0]; ba->dq_sh = dq->strides[1]; ba->dq_sn = dq->strides[2];
+  ba->dk_sb = dk->strides[0]; ba->dk_sh = dk->strides[1]; ba->dk_sn = dk->strides[2];
+  ba->dv_sb = dv->strides[0]; ba->dv_sh = dv->strides[1]; ba->dv_sn = dv->strides[2];
+  if (ba->a.bias_kind == ATTN_BIAS_TABLE) {
+    if (!dtable) return ATTN_E_NULL;
+    if ((uintptr_t)dtable % 4) return ATTN_E_LAYOUT;
+    ba->n_tab = (2 * ba->a.gh - 1) * (2 * ba->a.gw - 1);
+    ba->dtable = dtable;
+    *ws_bytes = (size_t)ba->a.B * ba->a.H * ba->n_tab * 4;
+  }
+  return ATTN_OK;
+}
+
+namespace {
+
+int check_workspace(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return ATTN_OK;
+  if (!ws) return ATTN_E_NULL;
+  if ((uintptr_t)ws % 16) return ATTN_E_LAYOUT;
+  if (ws_bytes < need) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
 }  // namespace attn
 
 extern "C" {
+
+int attn_bwd_workspace_size(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                            const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                            const attn_mask_desc_t* mask_desc, int32_t dtype, size_t* bytes) {
+  if (!bytes) return ATTN_E_NULL;
+  *bytes = 0;
+  attn::AttnArgs a;
+  const int st = attn::validate(q, k, v, bias_desc, mask_desc, dout, dtype, nullptr, &a);
+  if (st != ATTN_OK) return st;
+  if (a.bias_kind == ATTN_BIAS_TABLE) *bytes = (size_t)a.B * a.H * (2 * a.gh - 1) * (2 * a.gw - 1) * 4;
+  return ATTN_OK;
+}
+
+int attn_bwd_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                   const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                   const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
+                   const attn_tensor_t* dv, float* dtable, int32_t dtype, void* workspace,
+                   size_t workspace_bytes) {
+  attn::AttnBwdArgs ba;
+  size_t need = 0;
+  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need);
+  if (st != ATTN_OK) return st;
+  return attn::check_workspace(workspace, workspace_bytes, need);
+}
+
+int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+             const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+             const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
+             const attn_tensor_t* dv, float* dtable, int32_t dtype, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  attn::AttnBwdArgs ba;
+  size_t need = 0;
+  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need);
+  if (st != ATTN_OK) return st;
+  if ((st = attn::check_workspace(workspace, workspace_bytes, need)) != ATTN_OK) return st;
+  ba.ws = (float*)workspace;
+  return attn::launch_bwd(ba, stream);
+}
 
 int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
                    const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
@@ -287,6 +394,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return (1 << 16) | 2; }
+int attn_version(void) { return (1 << 16) | 3; }
 
 }  // extern "C"

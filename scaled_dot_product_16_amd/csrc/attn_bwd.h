@@ -1,0 +1,357 @@
+// Backward pass of window attention (at most 64 queries and keys per unit)
+// on gfx950: dQ, dK, dV and the gradient of the relative-position bias
+// table, for the shifted-window attention the Swin talk trains with a fused
+// window op (section 2).  The chain rule of O = softmax(scale*QK^T + B + M) V
+// per (window, head):
+//   P = softmax(S),  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P*dP)),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,
+//   d_table[r, h] = sum of dS over the pairs of head h that read row r.
+// A window is one tile, so P is recomputed exactly (no statistics from the
+// forward are needed).  One workgroup of four waves owns one unit; Q, K, V
+// and dO are staged in LDS, wave w owns queries 16w..16w+15 for S^T = K Q^T
+// and dP^T = V dO^T and keys 16w..16w+15 for dK and dV.  The products run on
+// v_mfma_f32_16x16x32 with the layouts of the forward kernel: the transposed
+// operands (K^T, Q^T, dO^T) come from transposing LDS reads, dS and P are
+// rounded to the element type as MFMA operands.  The table gradient is
+// summed per unit in a fixed order (one thread per table row, over the
+// unit's pairs with that offset) into a workspace, and a second kernel adds
+// the units of each head in order: no atomics, bitwise-deterministic.
+#ifndef ATTN_BWD_H_
+#define ATTN_BWD_H_
+
+#include "attn_win.h"
+
+namespace attn {
+
+template <class E, int D, int BIAS, int MASKK>
+__global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
+  using C = WinBwdCfg<D>;
+  constexpr int NT = C::NT, KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW, PROW = C::PROW,
+                FROW = C::FROW, RCH = C::RCH, NCH = C::NCH, CPT = C::CPT;
+  constexpr int TILE = 64 * ROW;
+  constexpr bool kTab = BIAS == ATTN_BIAS_TABLE || MASKK == ATTN_MASK_SHIFT_REGIONS;
+  const AttnArgs& a = ba.a;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  uint16_t* Ks = (uint16_t*)lds;          // [64][ROW] each: K, V, Q, dO
+  uint16_t* Vs = Ks + TILE;
+  uint16_t* Qs = Vs + TILE;
+  uint16_t* Os = Qs + TILE;               // dO
+  uint16_t* Pt = Os + TILE;               // [64 keys][PROW] P^T, element type
+  uint16_t* St = Pt + 64 * PROW;          // [64 keys][PROW] dS^T, element type
+  float* Sf = (float*)(St + 64 * PROW);   // [64 keys][FROW] dS^T, fp32 (table gradient)
+  int* kinfo = (int*)(Sf + 64 * FROW);
+  float* tbl = (float*)(kinfo + 64);      // 9 table copies, log2 units
+
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int H = a.H, N = a.Nq, Nk = a.Nk;
+  const int unit = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
+  const int b = fdiv(unit, a.fd_h), h = unit - b * H;
+
+  const float inv_ww = __builtin_amdgcn_rcpf((float)(a.win_w > 0 ? a.win_w : 1));
+  const float inv_gw = __builtin_amdgcn_rcpf((float)(a.gw > 0 ? a.gw : 1));
+  auto div_small = [](int t, float inv) { return (int)(((float)t + 0.5f) * inv); };
+  auto split = [&](int t, int& ty, int& tx) {
+    ty = div_small(t, inv_ww);
+    tx = t - ty * a.win_w;
+  };
+  const WinPos pos = win_pos(a, b);
+  const int bimg = a.image ? pos.img : b;
+  auto tok_pix = [&](int t) -> uint32_t {
+    if (!a.image) return (uint32_t)t;
+    int ty, tx;
+    split(t, ty, tx);
+    return win_tok_pix(a, pos, ty, tx);
+  };
+  auto base = [&](const void* p, int64_t sb, int64_t sh) {
+    return (const char*)p + ((int64_t)bimg * sb + (int64_t)h * sh) * 2;
+  };
+  const char* qp = base(a.q, a.q_sb, a.q_sh);
+  const char* kp = base(a.k, a.k_sb, a.k_sh);
+  const char* vp = base(a.v, a.v_sb, a.v_sh);
+  const char* op = base(a.o, a.o_sb, a.o_sh);  // dO
+
+  // Tiles: token rows past Nq (q, dO) or Nk (k, v) are clamped to the last
+  // row, padding tokens of the image layout read as zero.
+  u32x4 reg[4][CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = min(tid + c * NT, NCH - 1);
+    const int row = ch / RCH;
+    const uint32_t col = (uint32_t)((ch % RCH) * 8);
+    const uint32_t kpix0 = tok_pix(min(row, Nk - 1)), qpix0 = tok_pix(min(row, N - 1));
+    const uint32_t kpix = kpix0 == kPadTok ? 0u : kpix0, qpix = qpix0 == kPadTok ? 0u : qpix0;
+    reg[0][c] = *(const u32x4*)(kp + (size_t)(kpix * (uint32_t)a.k_sn + col) * 2);
+    reg[1][c] = *(const u32x4*)(vp + (size_t)(kpix * (uint32_t)a.v_sn + col) * 2);
+    reg[2][c] = *(const u32x4*)(qp + (size_t)(qpix * (uint32_t)a.q_sn + col) * 2);
+    reg[3][c] = *(const u32x4*)(op + (size_t)(qpix * (uint32_t)a.o_sn + col) * 2);
+    if (kpix0 == kPadTok) reg[0][c] = reg[1][c] = u32x4{0, 0, 0, 0};
+    if (qpix0 == kPadTok) reg[2][c] = reg[3][c] = u32x4{0, 0, 0, 0};
+  }
+
+  // Table (with its region copies) and per-key lookup parts, as in the
+  // forward window kernel.
+  const bool regions = MASKK == ATTN_MASK_SHIFT_REGIONS &&
+                       (pos.y0 + a.win_h > a.pimg_h - a.win_h || pos.x0 + a.win_w > a.pimg_w - a.win_w);
+  const int n_tab = win_tab_entries(a);
+  if constexpr (kTab) {
+    const float mv = a.mask_value * kLog2e;
+    for (int r = tid; r < n_tab; r += NT) {
+      const float t = BIAS == ATTN_BIAS_TABLE ? load_elem<E>(a.table, (int64_t)r * H + h) * kLog2e : 0.f;
+      tbl[4 * n_tab + r] = t;
+      if (regions) {
+#pragma unroll
+        for (int c = 0; c < 9; ++c)
+          if (c != 4) tbl[c * n_tab + r] = t + mv;
+      }
+    }
+    if (tid < 64) {
+      const int j = min(tid, Nk - 1);
+      int part = 4 * n_tab;
+      if constexpr (BIAS == ATTN_BIAS_TABLE) {
+        const int kh = div_small(j, inv_gw), kw = j - kh * a.gw;
+        part -= kh * (2 * a.gw - 1) + kw;
+      }
+      if (regions) {
+        int ty, tx;
+        split(j, ty, tx);
+        part -= n_tab * win_region(a, pos, ty, tx);
+      }
+      kinfo[tid] = part * 4;
+    }
+  }
+  // Head-dim padding columns D..DK of the four tiles are zero.
+  if constexpr (DK > D) {
+    for (int i = tid; i < 4 * 64 * (DK - D); i += NT) {
+      const int t = i / (64 * (DK - D)), r = i - t * 64 * (DK - D);
+      Ks[t * TILE + (r / (DK - D)) * ROW + D + r % (DK - D)] = 0;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * NT;
+    if (ch < NCH) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *(u32x4*)&Ks[t * TILE + (ch / RCH) * ROW + (ch % RCH) * 8] = reg[t][c];
+    }
+  }
+  __syncthreads();
+
+  // ---- Per query block: P, dP, dS; dQ -------------------------------------
+  const int qrow = wave * 16 + l16;
+  const bool qvalid = qrow < N;
+  const int q_tok = min(qrow, N - 1);
+  u32x4 qf[KCH], df[KCH];
+#pragma unroll
+  for (int dc = 0; dc < KCH; ++dc) {
+    qf[dc] = *(const u32x4*)&Qs[qrow * ROW + dc * 32 + g * 8];
+    df[dc] = *(const u32x4*)&Os[qrow * ROW + dc * 32 + g * 8];
+  }
+  f32x4 s[4], dp[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb * 16 + 16 > Nk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kb * 16 + g * 4 + r >= Nk) s[kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const u32x4 kf = *(const u32x4*)&Ks[(kb * 16 + l16) * ROW + dc * 32 + g * 8];
+      const u32x4 vf = *(const u32x4*)&Vs[(kb * 16 + l16) * ROW + dc * 32 + g * 8];
+      s[kb] = E::mfma(kf, qf[dc], s[kb]);
+      dp[kb] = E::mfma(vf, df[dc], dp[kb]);
+    }
+  }
+  const float c2 = a.scale * kLog2e;
+  constexpr bool kDense = BIAS == ATTN_BIAS_ADDITIVE || MASKK == ATTN_MASK_ADDITIVE;
+  auto dense = [&](int kb, int r) -> float {
+    const int j = min(kb * 16 + g * 4 + r, Nk - 1);
+    float t = 0.f;
+    if constexpr (BIAS == ATTN_BIAS_ADDITIVE)
+      t = load_elem<E>(a.badd, (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)q_tok * a.badd_s1 + j) * kLog2e;
+    if constexpr (MASKK == ATTN_MASK_ADDITIVE)
+      t += load_elem<E>(a.madd, (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)q_tok * a.madd_s1 + j) * kLog2e;
+    return t;
+  };
+  float p[16];
+  if constexpr (kTab) {
+    int qpart = 0;
+    if constexpr (BIAS == ATTN_BIAS_TABLE) {
+      const int qh = div_small(q_tok, inv_gw), qw = q_tok - qh * a.gw;
+      qpart = (qh + a.gh - 1) * (2 * a.gw - 1) + qw + a.gw - 1;
+    }
+    if (regions) {
+      int ty, tx;
+      split(q_tok, ty, tx);
+      qpart += n_tab * win_region(a, pos, ty, tx);
+    }
+    const char* qbase = (const char*)tbl + qpart * 4;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 v = *(const u32x4*)&kinfo[kb * 16 + g * 4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float t = *(const float*)(qbase + (int)v[r]);
+        if constexpr (kDense) t += dense(kb, r);
+        p[kb * 4 + r] = fmaf(s[kb][r], c2, t);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[kb * 4 + r] = fmaf(s[kb][r], c2, dense(kb, r));
+  }
+  // Exact softmax of the row (the whole key range is this tile).
+  float mx = fmaxf(fmaxf(p[0], p[1]), p[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, p[i]), p[i + 1]);
+  mx = max_across_groups(fmaxf(mx, p[15]));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(p[i] - mx);
+    sum += p[i];
+  }
+  const float inv = 1.f / sum_across_groups(sum);
+  // Rows past Nq take no part in dK and dV: their P and dS are zero.
+  float pd = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = qvalid ? p[i] * inv : 0.f;
+    pd = fmaf(p[i], dp[i >> 2][i & 3], pd);
+  }
+  const float dsum = sum_across_groups(pd);  // sum_j P_ij dP_ij
+  float ds[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp[i >> 2][i & 3] - dsum);
+  // P^T and dS^T of this query column into LDS (keys kb*16 + g*4 + r).
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = kb * 16 + g * 4 + r;
+      const uint32_t pp = E::pack2(p[kb * 4 + r], ds[kb * 4 + r]);
+      Pt[key * PROW + qrow] = (uint16_t)(pp & 0xffff);
+      St[key * PROW + qrow] = (uint16_t)(pp >> 16);
+      Sf[key * FROW + qrow] = ds[kb * 4 + r];
+    }
+  // dQ^T = K^T dS^T: dS^T packed as the B operand (the forward's P layout),
+  // K^T from transposing reads of the K tile.
+  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  {
+    u32x4 sf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+      sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                     E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+    f32x4 acc[CBD];
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const uint16_t* ptr = Ks + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const u32x2 lo = lds_read_tr16(ptr);
+        const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
+        acc[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[kc], acc[cb]);
+      }
+    const uint32_t qpix = tok_pix(q_tok);
+    if (qvalid && qpix != kPadTok) {
+      char* dq = (char*)ba.dq + ((int64_t)bimg * ba.dq_sb + (int64_t)h * ba.dq_sh) * 2;
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 v = acc[cb] * a.scale;
+          *(u32x2*)(dq + (size_t)(qpix * (uint32_t)ba.dq_sn + c0) * 2) =
+              u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+        }
+      }
+    }
+  }
+  __syncthreads();  // P^T, dS^T complete
+
+  // ---- Per key block: dK = scale * dS^T Q, dV = P^T dO ----------------------
+  // Keys 16w .. 16w+15 are the column block; the contraction runs over the
+  // 64 query rows in two chunks, Q^T and dO^T from transposing reads, the B
+  // operand from rows of dS^T / P^T in the forward's key-permuted order.
+  const int krow = wave * 16 + l16;
+  if (wave * 16 < Nk) {
+    f32x4 dk[CBD], dv[CBD];
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x2 s0 = *(const u32x2*)&St[krow * PROW + kc * 32 + g * 4];
+      const u32x2 s1 = *(const u32x2*)&St[krow * PROW + kc * 32 + 16 + g * 4];
+      const u32x2 p0 = *(const u32x2*)&Pt[krow * PROW + kc * 32 + g * 4];
+      const u32x2 p1 = *(const u32x2*)&Pt[krow * PROW + kc * 32 + 16 + g * 4];
+      const u32x4 sb = {s0[0], s0[1], s1[0], s1[1]}, pb = {p0[0], p0[1], p1[0], p1[1]};
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const uint16_t* qptr = Qs + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const uint16_t* optr = Os + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const u32x2 ql = lds_read_tr16(qptr), qh = lds_read_tr16(qptr + 16 * ROW);
+        const u32x2 ol = lds_read_tr16(optr), oh = lds_read_tr16(optr + 16 * ROW);
+        dk[cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sb, dk[cb]);
+        dv[cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pb, dv[cb]);
+      }
+    }
+    const uint32_t kpix = krow < Nk ? tok_pix(krow) : kPadTok;
+    if (kpix != kPadTok) {
+      char* dkp = (char*)ba.dk + ((int64_t)bimg * ba.dk_sb + (int64_t)h * ba.dk_sh) * 2;
+      char* dvp = (char*)ba.dv + ((int64_t)bimg * ba.dv_sb + (int64_t)h * ba.dv_sh) * 2;
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 k4 = dk[cb] * a.scale, v4 = dv[cb];
+          *(u32x2*)(dkp + (size_t)(kpix * (uint32_t)ba.dk_sn + c0) * 2) =
+              u32x2{E::pack2(k4[0], k4[1]), E::pack2(k4[2], k4[3])};
+          *(u32x2*)(dvp + (size_t)(kpix * (uint32_t)ba.dv_sn + c0) * 2) =
+              u32x2{E::pack2(v4[0], v4[1]), E::pack2(v4[2], v4[3])};
+        }
+      }
+    }
+  }
+
+  // ---- Table gradient of this unit --------------------------------------
+  // Row r of the table holds offset (dh, dw) = query - key; its gradient is
+  // the sum of dS over the unit's pairs with that offset, summed here in
+  // query order by one thread (fixed order: deterministic).
+  if constexpr (BIAS == ATTN_BIAS_TABLE) {
+    const int gh = a.gh, gw = a.gw, tw = 2 * gw - 1;
+    for (int r = tid; r < n_tab; r += NT) {
+      const int oh = r / tw - (gh - 1), ow = r % tw - (gw - 1);
+      float acc = 0.f;
+      for (int qh = max(0, oh); qh < min(gh, gh + oh); ++qh)
+        for (int qw = max(0, ow); qw < min(gw, gw + ow); ++qw)
+          acc += Sf[((qh - oh) * gw + (qw - ow)) * FROW + qh * gw + qw];
+      ba.ws[(int64_t)unit * n_tab + r] = acc;  // unit = b * H + h
+    }
+  }
+}
+
+// d_table[r, h] = sum over the batch items b (windows) of the per-unit
+// partial sums, in order of b.  One thread per (row, head).  (A template
+// only so that every compiled instance may carry its copy.)
+template <int kUnused>
+__global__ __launch_bounds__(256) void attn_bwd_table_reduce(const float* ws, float* dtable, int B,
+                                                             int H, int n_tab) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // i = r * H + h
+  if (i >= n_tab * H) return;
+  const int r = i / H, h = i - r * H;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) acc += ws[((int64_t)b * H + h) * n_tab + r];
+  dtable[i] = acc;
+}
+
+}  // namespace attn
+
+#endif  // ATTN_BWD_H_

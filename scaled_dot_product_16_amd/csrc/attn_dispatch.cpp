@@ -32,4 +32,24 @@ int launch(const AttnArgs& a, void* stream) {
   }
 }
 
+int launch_bwd(const AttnBwdArgs& ba, void* stream) {
+  const int dt = ba.a.dtype, d = ba.a.D;
+  if (dt == ATTN_BF16) {
+    switch (d) {
+      case 32: return launch_bwd_inst<ATTN_BF16, 32>(ba, stream);
+      case 40: return launch_bwd_inst<ATTN_BF16, 40>(ba, stream);
+      case 64: return launch_bwd_inst<ATTN_BF16, 64>(ba, stream);
+      case 80: return launch_bwd_inst<ATTN_BF16, 80>(ba, stream);
+    }
+  } else if (dt == ATTN_F16) {
+    switch (d) {
+      case 32: return launch_bwd_inst<ATTN_F16, 32>(ba, stream);
+      case 40: return launch_bwd_inst<ATTN_F16, 40>(ba, stream);
+      case 64: return launch_bwd_inst<ATTN_F16, 64>(ba, stream);
+      case 80: return launch_bwd_inst<ATTN_F16, 80>(ba, stream);
+    }
+  }
+  return ATTN_E_UNSUPPORTED;
+}
+
 }  // namespace attn

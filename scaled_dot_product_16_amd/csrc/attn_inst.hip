@@ -5,6 +5,7 @@
 #include "attn_device.h"
 #include "attn_mfma.h"
 #include "attn_win.h"
+#include "attn_bwd.h"
 #include "attn_launch.h"
 
 #ifndef INST_DT
@@ -132,9 +133,58 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
   return launch_mfma<BIAS, MASK, kRelTables, wpe>(p, a, s);
 }
+
+// Backward of window units, then (table bias) the reduction of the per-unit
+// table gradients.
+template <int BIAS, int MASKK>
+int launch_bwd_one(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
+  AttnBwdArgs ba = ba0;
+  ba.a.n_qtiles = 1;
+  ba.a.fd_qt = make_fastdiv(1);
+  ba.a.n_blocks = (int)p.blocks;
+  auto kern = attn_bwd_win<Elem, INST_D, BIAS, MASKK>;
+  if (p.lds > 32 * 1024 &&
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
+          hipSuccess)
+    return ATTN_E_LAUNCH;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.blocks), dim3(kWinWaves * 64), p.lds, s, ba);
+  if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+  if constexpr (BIAS == ATTN_BIAS_TABLE) {
+    const int n = ba.n_tab * ba.a.H;
+    hipLaunchKernelGGL(attn_bwd_table_reduce<0>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float*)ba.ws, ba.dtable, ba.a.B, ba.a.H, ba.n_tab);
+    if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+template <int BIAS>
+int launch_bwd_bias(const AttnBwdArgs& ba, const Plan& p, hipStream_t s) {
+  switch (ba.a.mask_kind) {
+    case ATTN_MASK_NONE: return launch_bwd_one<BIAS, ATTN_MASK_NONE>(ba, p, s);
+    case ATTN_MASK_ADDITIVE: return launch_bwd_one<BIAS, ATTN_MASK_ADDITIVE>(ba, p, s);
+    default: return launch_bwd_one<BIAS, ATTN_MASK_SHIFT_REGIONS>(ba, p, s);
+  }
+}
 #endif
 
 }  // namespace
+
+#if INST_DT != 0
+template <>
+int launch_bwd_inst<INST_DT, INST_D>(const AttnBwdArgs& ba, void* stream) {
+  Plan p;
+  const int st = make_bwd_plan(ba.a, &p);
+  if (st != ATTN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  switch (ba.a.bias_kind) {
+    case ATTN_BIAS_NONE: return launch_bwd_bias<ATTN_BIAS_NONE>(ba, p, s);
+    case ATTN_BIAS_TABLE: return launch_bwd_bias<ATTN_BIAS_TABLE>(ba, p, s);
+    case ATTN_BIAS_ADDITIVE: return launch_bwd_bias<ATTN_BIAS_ADDITIVE>(ba, p, s);
+    default: return ATTN_E_UNSUPPORTED;
+  }
+}
+#endif
 
 template <>
 int launch_inst<INST_DT, INST_D>(const AttnArgs& a, void* stream) {

@@ -72,6 +72,21 @@ struct AttnArgs {
   int32_t win_heads; // requested heads per workgroup of the window path (0: library's choice)
 };
 
+// A validated backward call: the forward call (its `o` is the output
+// gradient dO) and the gradient outputs.
+struct AttnBwdArgs {
+  AttnArgs a;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  float* dtable;  // [n_tab, H] (TABLE bias) or null
+  float* ws;      // per-unit partial table gradients [B][H][n_tab]
+  int32_t n_tab;  // table rows (TABLE bias), else 0
+};
+
 // Host-side validation shared by attn_check and attn_fwd.  Returns an ATTN_*
 // status and fills *a on success.
 int validate(const void* q, const void* k, const void* v, const void* bias_desc,
@@ -80,6 +95,15 @@ int validate(const void* q, const void* k, const void* v, const void* bias_desc,
 
 // Queue the kernel for a validated call on `stream` (a hipStream_t).
 int launch(const AttnArgs& a, void* stream);
+
+// Validation of a backward call; fills *ba (and *ws_bytes, the workspace the
+// call needs) on success.
+int validate_bwd(const void* q, const void* k, const void* v, const void* dout, const void* bias_desc,
+                 const void* mask_desc, const void* dq, const void* dk, const void* dv, float* dtable,
+                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes);
+
+// Queue the backward kernels of a validated call.
+int launch_bwd(const AttnBwdArgs& ba, void* stream);
 
 // Largest grid side accepted for TABLE/RELPOS/SHIFT_REGIONS and the largest
 // token count of a batch item for which per-key index data fits on chip.

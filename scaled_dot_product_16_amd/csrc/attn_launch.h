@@ -12,6 +12,10 @@ namespace attn {
 template <int DT, int D>
 int launch_inst(const AttnArgs& a, void* stream);
 
+// The backward of a validated call (half precision only).
+template <int DT, int D>
+int launch_bwd_inst(const AttnBwdArgs& ba, void* stream);
+
 }  // namespace attn
 
 #endif  // ATTN_LAUNCH_H_

@@ -208,6 +208,30 @@ constexpr size_t win_pack_lds_bytes(const AttnArgs& a, size_t head_bytes, int hg
   return n;
 }
 
+// Window backward kernel (attn_bwd_win): Q, K, V and dO tiles of 64 rows
+// (head dim padded to the 32-wide contraction), P^T and dS^T in the element
+// type (64 keys x 64 queries, rows padded by 8), dS^T in fp32 for the table
+// gradient (rows of 65), then the per-key lookup parts and the table.
+template <int D>
+struct WinBwdCfg {
+  static constexpr int NT = kWinWaves * 64;
+  static constexpr int KCH = (D + 31) / 32;
+  static constexpr int DK = KCH * 32;
+  static constexpr int CBD = (D + 15) / 16;   // 16-wide blocks of dQ, dK, dV columns
+  static constexpr int ROW = DK + 8;
+  static constexpr int PROW = 64 + 8;
+  static constexpr int FROW = 64 + 1;
+  static constexpr int RCH = D / 8;
+  static constexpr int NCH = 64 * RCH;
+  static constexpr int CPT = (NCH + NT - 1) / NT;
+  static constexpr size_t BYTES = (size_t)4 * 64 * ROW * 2 + (size_t)2 * 64 * PROW * 2 +
+                                  (size_t)64 * FROW * 4 + 64 * 4;
+};
+
+constexpr size_t win_bwd_lds_bytes(const AttnArgs& a, size_t base) {
+  return base + (win_uses_table(a) ? (size_t)9 * win_tab_entries(a) * 4 : 0);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 tiled kernel
 // ---------------------------------------------------------------------------
@@ -344,6 +368,36 @@ inline int make_plan(const AttnArgs& a, Plan* p) {
         case 80: *p = plan_half<80>(a); break;
         default: return ATTN_E_UNSUPPORTED;
       }
+  }
+  if (p->kernel < 0 || p->lds > kMaxLds || p->blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// The backward of a validated call: window units only (at most 64 queries
+// and keys), half precision, relative-position bias excluded.
+template <int D>
+inline Plan plan_bwd_half(const AttnArgs& a) {
+  Plan p{};
+  if (a.Nq > 64 || a.Nk > 64 || a.bias_kind == ATTN_BIAS_RELPOS) {
+    p.kernel = -1;
+    return p;
+  }
+  p.kernel = kKernWin;
+  p.nw = kWinWaves;
+  p.hg = 1;
+  p.blocks = (int64_t)a.B * a.H;
+  p.lds = win_bwd_lds_bytes(a, WinBwdCfg<D>::BYTES);
+  return p;
+}
+
+inline int make_bwd_plan(const AttnArgs& a, Plan* p) {
+  if (a.dtype == ATTN_F32) return ATTN_E_UNSUPPORTED;
+  switch (a.D) {
+    case 32: *p = plan_bwd_half<32>(a); break;
+    case 40: *p = plan_bwd_half<40>(a); break;
+    case 64: *p = plan_bwd_half<64>(a); break;
+    case 80: *p = plan_bwd_half<80>(a); break;
+    default: return ATTN_E_UNSUPPORTED;
   }
   if (p->kernel < 0 || p->lds > kMaxLds || p->blocks > 0x7fffffff) return ATTN_E_UNSUPPORTED;
   return ATTN_OK;

@@ -267,8 +267,20 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     }
   }
 
-  // Bias and mask (log2 units).
+  // Bias and mask (log2 units): a table lookup (table bias and/or region
+  // mask) plus dense additive terms (additive bias and/or mask); a call may
+  // have both, e.g. a table bias with an additive mask.
   const float c2 = a.scale * kLog2e;
+  constexpr bool kDense = BIAS == ATTN_BIAS_ADDITIVE || MASKK == ATTN_MASK_ADDITIVE;
+  auto dense = [&](int kb, int r) -> float {
+    const int j = min(kb * 16 + g * 4 + r, Nk - 1);
+    float t = 0.f;
+    if constexpr (BIAS == ATTN_BIAS_ADDITIVE)
+      t = load_elem<E>(a.badd, (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)q_tok * a.badd_s1 + j) * kLog2e;
+    if constexpr (MASKK == ATTN_MASK_ADDITIVE)
+      t += load_elem<E>(a.madd, (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)q_tok * a.madd_s1 + j) * kLog2e;
+    return t;
+  };
   float y[16];
   if constexpr (kTab) {
     int qpart = 0;
@@ -287,21 +299,17 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     for (int kb = 0; kb < 4; ++kb) {
       const u32x4 v = *(const u32x4*)&kinfo[kb * 16 + g * 4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[kb * 4 + r] = fmaf(s[kb][r], c2, *(const float*)(qbase + (int)v[r]));
+      for (int r = 0; r < 4; ++r) {
+        float t = *(const float*)(qbase + (int)v[r]);
+        if constexpr (kDense) t += dense(kb, r);
+        y[kb * 4 + r] = fmaf(s[kb][r], c2, t);
+      }
     }
   } else {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = min(kb * 16 + g * 4 + r, Nk - 1);
-        float bias = 0.f;
-        if constexpr (BIAS == ATTN_BIAS_ADDITIVE)
-          bias = load_elem<E>(a.badd, (int64_t)(b % a.badd_n) * a.badd_s0 + (int64_t)q_tok * a.badd_s1 + j) * kLog2e;
-        if constexpr (MASKK == ATTN_MASK_ADDITIVE)
-          bias += load_elem<E>(a.madd, (int64_t)(b % a.madd_n) * a.madd_s0 + (int64_t)q_tok * a.madd_s1 + j) * kLog2e;
-        y[kb * 4 + r] = fmaf(s[kb][r], c2, bias);
-      }
+      for (int r = 0; r < 4; ++r) y[kb * 4 + r] = fmaf(s[kb][r], c2, dense(kb, r));
   }
 
   // Softmax over the single key tile.

@@ -30,7 +30,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_check", "attn_strerror", "attn_version",
-                          "attn_fwd_opt", "attn_check_opt"}
+                          "attn_fwd_opt", "attn_check_opt", "attn_bwd", "attn_bwd_check",
+                          "attn_bwd_workspace_size"}
     for n in names:
         assert hasattr(lib, n)
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -49,7 +50,7 @@ def test_strerror_and_version(lib):
     for st in range(8):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(99) == b"unknown status"
-    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 2
+    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 3
 
 
 def t(*shape, dtype=torch.float16):
@@ -281,3 +282,44 @@ def test_table_lengths_validation(lib):
     bd.kind, bd.table = 1, tab.data_ptr()  # a table bias with table lengths set
     assert h.attn_check(*args()) == 2
     del keep
+
+
+def test_backward_validation(lib):
+    # attn_bwd_check: the gradients are shaped like q, k, v, must not
+    # overlap inputs or each other; a table bias needs dtable and a
+    # workspace of B_eff*H*rows*4 bytes; only window units in half
+    # precision are built.
+    h = B.lib()
+    q, k, v, do = (t(4, 3, 49, 32) for _ in range(4))
+    dq, dk, dv = t(4, 3, 49, 32), t(4, 3, 49, 32), t(4, 3, 49, 32)
+    tab = B.TableBias(t(169, 3), (7, 7))
+    dtab = torch.zeros(169, 3)
+    ws = torch.zeros(4 * 3 * 169 * 4 // 4)  # float32 elements: exactly the bytes needed
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(q, k, v, do, tab, None, "batched", None)
+    T = lambda x: B._tensor_c(x, 0)
+    dqc, dkc, dvc = T(dq), T(dk), T(dv)
+    def chk(dtable=dtab, w=ws, wbytes=None, dqx=None):
+        return h.attn_bwd_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
+                                ctypes.byref(bd), ctypes.byref(md), ctypes.byref(dqx or dqc),
+                                ctypes.byref(dkc), ctypes.byref(dvc),
+                                ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0), dt,
+                                ctypes.c_void_p(w.data_ptr() if w is not None else 0),
+                                ctypes.c_size_t(w.numel() * 4 if (w is not None and wbytes is None) else (wbytes or 0)))
+    need = ctypes.c_size_t(0)
+    assert h.attn_bwd_workspace_size(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
+                                     ctypes.byref(bd), ctypes.byref(md), dt, ctypes.byref(need)) == 0
+    assert need.value == 4 * 3 * 169 * 4
+    assert chk() == 0
+    assert chk(dtable=None) == 1                       # table gradient output missing
+    assert chk(w=None) == 1                            # workspace missing
+    assert chk(wbytes=need.value - 4) == 2             # workspace too small
+    assert chk(dqx=T(q)) == 5                          # dq is q
+    assert chk(dqx=T(t(4, 3, 50, 32))) == 2            # dq shaped unlike q
+    ins = [t(1, 2, 100, 64) for _ in range(4)]  # kept alive: distinct addresses
+    qc2, kc2, vc2, bd2, md2, oc2, dt2, keep2 = B._marshal(*ins, None, None, "batched", None)
+    grads = [t(1, 2, 100, 64) for _ in range(3)]  # kept alive: distinct addresses
+    d1, d2, d3 = (T(x) for x in grads)
+    assert h.attn_bwd_check(ctypes.byref(qc2), ctypes.byref(kc2), ctypes.byref(vc2), ctypes.byref(oc2),
+                            ctypes.byref(bd2), ctypes.byref(md2), ctypes.byref(d1), ctypes.byref(d2),
+                            ctypes.byref(d3), None, dt2, None, 0) == 4   # longer than a window
+    del keep, keep2

@@ -1,0 +1,166 @@
+"""GPU parity of the backward pass (attn_bwd) against the oracle's fp64
+gradients, every element: dQ, dK, dV and the table gradient, for Swin
+windows in both layouts (shift, region mask and zero padding folded into
+the addressing), every head dim, ragged windows, every bias and mask kind
+the window path takes.
+
+Tolerance: the forward's max-abs bound for the dtype (f16 5e-3, bf16 2e-2),
+scaled by max(1, max |reference|) of each gradient: gradients are not N(0,1)
+(the table gradient sums dS over all windows), the products round dS and P
+to the element type, and the outputs are rounded to it (a relative error of
+2^-11 / 2^-8 per element).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scaled_dot_product_16_amd import binding as Bd
+from scaled_dot_product_16_amd import workloads as W
+from tests.helpers import TOL, oracle_arrays, record, to_device, with_dense_terms
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    Bd.lib()
+
+
+def run_bwd(w, dev):
+    kw = W.device_args(w, dev)
+    out = Bd.bwd(dev["q"], dev["k"], dev["v"], dev["dout"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_grads(w, inp, got, name=None):
+    arrs = oracle_arrays(inp)
+    ref = oracle.run_workload_backward(w, arrs)
+    worst = {}
+    for key, g in zip(("dq", "dk", "dv", "dtable"), got):
+        if g is None:
+            assert key == "dtable" and w.bias != "table"
+            continue
+        r = ref[key]
+        gg = g.detach().to("cpu", torch.float64).numpy()
+        assert np.all(np.isfinite(gg)), key
+        err = float(np.max(np.abs(gg - r)))
+        tol = TOL[w.dtype] * max(1.0, float(np.max(np.abs(r))))
+        worst[key] = err
+        if name:
+            record(f"{name} {key}", w.dtype, err, tol, gg.size)
+        assert err <= tol, f"{key}: max abs err {err:.3e} > {tol:.3e}"
+    return worst
+
+
+def inputs(w, seed=0, std_table=0.5):
+    inp = W.make_inputs(w, seed=seed, std_table=std_table)
+    inp["dout"] = W.to_dtype(W.normal(w.q_shape, w.cfg_id, 7, 1.0, seed), w.dtype)
+    return inp
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_swin_t_stage1_backward(dtype):
+    # The Swin-T stage-1 shifted-window workload at full size (image layout,
+    # table bias, region mask).
+    base = W.WORKLOADS["C2"]
+    w = W.custom(dtype, B=base.B, H=base.H, Nq=49, Nk=49, d=32, bias="table", grid=(7, 7),
+                 mask="shift", layout="image", images=8, window=base.window, cfg_id=base.cfg_id)
+    say(f"[backward] Swin-T stage 1 at full size, {dtype}")
+    inp = inputs(w, std_table=0.02)
+    worst = check_grads(w, inp, run_bwd(w, to_device(inp)), name=f"backward C2 shape {dtype}")
+    say(f"  max abs errors {worst}")
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [32, 40, 64, 80])
+@pytest.mark.parametrize("nq,nk", [(49, 49), (64, 64), (7, 64), (64, 1), (33, 50)])
+def test_backward_shapes(dtype, d, nq, nk):
+    w = W.custom(dtype, B=3, H=2, Nq=nq, Nk=nk, d=d, cfg_id=800 + d)
+    say(f"[backward] {dtype} d={d} Nq={nq} Nk={nk}")
+    inp = inputs(w, seed=nq * 100 + nk)
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+CASES = [
+    ("table", (7, 7), "none", None),
+    ("table", (8, 8), "none", None),
+    ("table", (4, 9), "none", None),
+    ("none", None, "shift", (16, 16, 4, 8, 2, 5)),
+    ("table", (7, 7), "shift", (28, 21, 7, 7, 3, 2)),
+    ("additive", None, "none", None),
+    ("none", None, "additive", None),
+    ("table", (7, 7), "additive", None),
+    ("additive", None, "shift", (14, 14, 7, 7, 3, 3)),
+]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_backward_bias_and_mask(dtype, case):
+    bias, grid, mask, window = CASES[case]
+    if mask == "shift":
+        ih, iw, wh, ww = window[:4]
+        n, B = wh * ww, 2 * (ih // wh) * (iw // ww)
+    else:
+        n, B = (grid[0] * grid[1] if grid else 60), 6
+    w = W.custom(dtype, B=B, H=3, Nq=n, Nk=n, d=32, bias=bias, grid=grid, mask=mask, window=window,
+                 cfg_id=820 + case)
+    say(f"[backward] {dtype} {bias} {grid} {mask} {window}")
+    inp = with_dense_terms(w, inputs(w, seed=case), n_bias=2, n_mask=3)
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("geom", [(15, 13, 7, 7, 3, 3), (20, 25, 4, 8, 2, 5), (14, 14, 7, 7, 0, 0)])
+def test_backward_padded_image_layout(geom):
+    ih, iw, wh, ww, sh, sw = geom
+    ph, pw = -(-ih // wh) * wh, -(-iw // ww) * ww
+    nW = (ph // wh) * (pw // ww)
+    mask = "shift" if sh or sw else "none"
+    w = W.custom(W.F16, B=2 * nW, H=3, Nq=wh * ww, Nk=wh * ww, d=32, bias="table", grid=(wh, ww),
+                 mask=mask, layout="image", images=2, window=geom, cfg_id=840)
+    say(f"[backward] padded image {geom}")
+    inp = inputs(w, seed=sum(geom))
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+def test_backward_deterministic_and_strided():
+    w = W.custom(W.BF16, B=64, H=3, Nq=49, Nk=49, d=32, bias="table", grid=(7, 7), cfg_id=850)
+    say("[backward] determinism and [B, N, H, d] strides")
+    inp = inputs(w, seed=5)
+    dev = to_device(inp)
+    a = run_bwd(w, dev)
+    b = run_bwd(w, dev)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # The same call on [B, N, H, d] storage viewed as [B, H, N, d].
+    devs = {k: (v.transpose(1, 2).contiguous().transpose(1, 2) if k in ("q", "k", "v", "dout") else v)
+            for k, v in dev.items()}
+    outs = [torch.empty(w.B, w.Nq, w.H, w.d, dtype=dev["q"].dtype, device="cuda").transpose(1, 2)
+            for _ in range(3)]
+    kw = W.device_args(w, devs)
+    c = Bd.bwd(devs["q"], devs["k"], devs["v"], devs["dout"], dq=outs[0], dk=outs[1], dv=outs[2], **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(a, c):
+        assert torch.equal(x, y)
+
+
+def test_backward_unsupported_calls():
+    q = torch.zeros(1, 2, 100, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(Bd.AttnError) as e:
+        Bd.bwd(q, q.clone(), q.clone(), q.clone())       # longer than one window
+    assert e.value.status == 4
+    q = torch.zeros(1, 2, 49, 32, dtype=torch.float32, device="cuda")
+    with pytest.raises(Bd.AttnError) as e:
+        Bd.bwd(q, q.clone(), q.clone(), q.clone())       # fp32
+    assert e.value.status == 4

@@ -112,6 +112,10 @@ BIAS_CASES = [
     ("none", None, "additive", None),
     ("additive", None, "additive", None),
     ("table", (7, 7), "shift", (28, 21, 7, 7, 3, 2)),
+    # a table lookup together with a dense term on the window path
+    ("table", (7, 7), "additive", None),
+    ("additive", None, "shift", (14, 14, 7, 7, 3, 3)),
+    ("table", (8, 8), "additive", None),
     ("none", None, "shift", (16, 16, 4, 8, 2, 5)),
     ("relpos", (4, 8), "shift", (16, 16, 4, 8, 1, 3)),
 ]
