@@ -26,7 +26,9 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller; they must
  *    stay valid until the work queued on `stream` has finished.  The library
  *    allocates nothing, keeps no pointer after returning, holds no mutable
- *    global state, and is safe to call from several host threads.
+ *    global state (apart from the per-device address of attn_bwd_noalloc's
+ *    fixed array, taken once), and is safe to call from several host
+ *    threads.
  *  - attn_fwd never synchronises the device and never copies host memory to
  *    the device: every index computation (bias gathers, window and shift
  *    maps, region labels) happens inside the kernel from by-value integers.
@@ -292,6 +294,23 @@ ATTN_API int attn_bwd_workspace_size(const attn_tensor_t* q, const attn_tensor_t
                             const attn_tensor_t* v, const attn_tensor_t* dout,
                             const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
                             int32_t dtype, size_t* bytes);
+
+/* attn_bwd_noalloc: attn_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The per-window table
+ * gradients go to a fixed 16 MiB device array of the library (one per
+ * device, held until the process ends) instead: a call whose workspace
+ * would exceed it (attn_bwd_workspace_size > 16 MiB, e.g. more than 8272
+ * windows of 7x7 tokens with 3 heads) returns ATTN_E_UNSUPPORTED.  No
+ * allocation of any kind.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (other streams or host
+ * threads) race on it; sequential calls on one stream are safe.  Otherwise
+ * identical to attn_bwd (same validation, kernels and results).             */
+ATTN_API int attn_bwd_noalloc(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                     const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                     const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq,
+                     const attn_tensor_t* dk, const attn_tensor_t* dv, float* dtable,
+                     int32_t dtype, void* stream);
 
 /* attn_strerror: static text for a status code (never NULL).                */
 ATTN_API const char* attn_strerror(int status);

@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
         h.attn_bwd_workspace_size.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), ctypes.c_int32,
                                               P(ctypes.c_size_t)]
         h.attn_bwd_workspace_size.restype = ctypes.c_int
+        h.attn_bwd_noalloc.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
+                                       ctypes.c_int32, ctypes.c_void_p]
+        h.attn_bwd_noalloc.restype = ctypes.c_int
         h.attn_strerror.argtypes = [ctypes.c_int]
         h.attn_strerror.restype = ctypes.c_char_p
         h.attn_version.argtypes = []
@@ -342,13 +345,15 @@ def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, bias=None, mask=None,
         layout: str = "batched", window: Optional[Window] = None, dq=None, dk=None, dv=None,
-        dtable=None, workspace=None, stream=None):
+        dtable=None, workspace=None, stream=None, no_alloc: bool = False):
     """Gradients of sum(dout * O) for O = fwd(q, k, v, bias, mask) via attn_bwd.
 
     Returns (dq, dk, dv, dtable); dtable (fp32 [table rows, H]) only with a
     TableBias, else None.  Output and workspace tensors are allocated with
     torch when not given; the library itself allocates nothing.  Queued on
-    ``stream`` (default: torch's current stream).
+    ``stream`` (default: torch's current stream).  ``no_alloc``: call
+    attn_bwd_noalloc (the library's fixed device array instead of a
+    workspace; ``workspace`` is then ignored and none is allocated).
     """
     h = lib()
     dq = torch.empty_like(q) if dq is None else dq
@@ -361,6 +366,19 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
         dtable = torch.empty(bias.table.shape, dtype=torch.float32, device=q.device)
     if dtable is not None and (dtable.dtype != torch.float32 or not dtable.is_contiguous()):
         raise TypeError("dtable must be a contiguous float32 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    if no_alloc:
+        st = h.attn_bwd_noalloc(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
+                                ctypes.byref(bd), ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc),
+                                ctypes.byref(dvc), ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0),
+                                dt, ctypes.c_void_p(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, h.attn_strerror(st).decode())
+        del keep
+        return dq, dk, dv, (dtable if isinstance(bias, TableBias) else None)
     need = ctypes.c_size_t(0)
     st = h.attn_bwd_workspace_size(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
                                    ctypes.byref(bd), ctypes.byref(md), dt, ctypes.byref(need))
@@ -368,10 +386,6 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
         raise AttnError(st, h.attn_strerror(st).decode())
     if workspace is None and need.value:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
     st = h.attn_bwd(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc), ctypes.byref(bd),
                     ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc), ctypes.byref(dvc),
                     ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0), dt,

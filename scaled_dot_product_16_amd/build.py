@@ -72,6 +72,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-c",
                      os.path.join(CSRC, name + ".cpp"), "-o", o])
         objs.append(o)
+    # The backward entry point that allocates nothing (its fixed device array).
+    o = os.path.join(obj_dir, "attn_noalloc.o")
+    cmds.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, "attn_noalloc.hip"), "-o", o])
+    objs.append(o)
     for dt, d in INSTANCES:
         o = os.path.join(obj_dir, f"attn_inst_{dt}_{d}.o")
         cmds.append([cc, *HIP_FLAGS, f"-DINST_DT={dt}", f"-DINST_D={d}", "-c",

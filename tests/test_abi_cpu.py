@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_check", "attn_strerror", "attn_version",
                           "attn_fwd_opt", "attn_check_opt", "attn_bwd", "attn_bwd_check",
-                          "attn_bwd_workspace_size"}
+                          "attn_bwd_workspace_size", "attn_bwd_noalloc"}
     for n in names:
         assert hasattr(lib, n)
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
