@@ -185,7 +185,15 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     koff[c] = r < BN && 2 * ko < 0xFFFFFFF0ll ? (uint32_t)(2 * ko) : 0xFFFFFFF0u;
     voff[c] = r < BN && 2 * vo < 0xFFFFFFF0ll ? (uint32_t)(2 * vo) : 0xFFFFFFF0u;
   }
-  auto load_rows = [&](const uint16_t* base, int64_t sn, const uint32_t* off, int t, u32x4* reg) {
+  // Image layout: key j's window-map pixel (kPadTok for padding), filled
+  // once below; the tile loads after the first barrier read it instead of
+  // evaluating the map per chunk and tile.
+  uint32_t* kpix = (uint32_t*)(lds + mfma_lds_bytes<D, NW, NQB, RMODE>(a) - img_key_bytes(a));
+  if constexpr (IMG) {
+    for (int j = tid; j < a.Nk; j += NT) kpix[j] = tok_row(a, 1, b, j);
+  }
+  auto load_rows = [&](const uint16_t* base, int64_t sn, const uint32_t* off, int t, u32x4* reg,
+                       bool direct = false) {
     if (!a.image) {
       const int64_t k0 = (int64_t)t * BN;
       const uint32_t nrec = (uint32_t)(2 * ((a.Nk - 1 - k0) * sn + D));
@@ -199,7 +207,13 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int key = min(t * BN + min(crow(c), BN - 1), a.Nk - 1);
-        const uint32_t r = tok_row(a, sn, b, key);
+        uint32_t r;
+        if (direct) {
+          r = tok_row(a, sn, b, key);  // before the first barrier: kpix is not ready
+        } else {
+          const uint32_t px = kpix[key];
+          r = px == kPadTok ? kPadTok : px * (uint32_t)sn;
+        }
         reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, r == kPadTok ? 0xFFFFFFF0u : 2 * (r + (uint32_t)ccol(c)),
                                                        0, 0);
       }
@@ -294,14 +308,14 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // The first K/V tile is in flight while the bias prologue runs.  When the
   // keys span exactly two tiles, the second one is loaded with it: both
   // stages are then filled once and no load waits between the tiles.
-  load_k(0);
-  load_v(0);
+  load_rows(kbase, a.k_sn, koff, 0, kreg, true);
+  load_rows(vbase, a.v_sn, voff, 0, vreg, true);
   constexpr bool TWO = RMODE == kTwoTiles;
   static_assert(!TWO || (!PP && BIAS == ATTN_BIAS_NONE && !MASK), "two-tile form: no bias, no mask");
   u32x4 kreg1[TWO ? CPT : 1], vreg1[TWO ? CPT : 1];
   if constexpr (TWO) {
-    load_rows(kbase, a.k_sn, koff, 1, kreg1);
-    load_rows(vbase, a.v_sn, voff, 1, vreg1);
+    load_rows(kbase, a.k_sn, koff, 1, kreg1, true);
+    load_rows(vbase, a.v_sn, voff, 1, vreg1, true);
   }
 
   BiasCtx bc;
@@ -412,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       // G = R Q^T on the matrix cores for every table row, then a per-lane
       // gather through this wave's scratch rows.
       const int grow = relpos_grow(a);
-      float* gscr = (float*)(lds + mfma_lds_bytes<D, NW, NQB>(a)) - (NW - wave) * 16 * grow;
+      float* gscr = (float*)(lds + mfma_lds_bytes<D, NW, NQB>(a) - img_key_bytes(a)) - (NW - wave) * 16 * grow;
       float* relh = (float*)bc.relh;
       float* relw = (float*)bc.relw;
 #pragma unroll

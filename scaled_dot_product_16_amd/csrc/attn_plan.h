@@ -105,19 +105,25 @@ constexpr size_t dyn_lds_bytes(const AttnArgs& a, int bm) {
   return n;
 }
 
+// Image layout: the window-map pixel of every key of the workgroup's unit,
+// computed once and read by the K/V tile loads (at the end of the LDS).
+constexpr size_t img_key_bytes(const AttnArgs& a) {
+  return a.image ? ((size_t)a.Nk * 4 + 15) / 16 * 16 : 0;
+}
+
 // Dynamic LDS bytes of one workgroup of the tiled kernel.
 template <int D, int NW, int NQB, int RMODE = kRelTables>
 constexpr size_t mfma_lds_bytes(const AttnArgs& a) {
   using C = MfmaCfg<D, NW, NQB, RMODE == kRelAug>;
-  if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4;
+  if (RMODE == kRelRow64) return C::BASE_BYTES + (size_t)a.gh * C::BM * 4 + img_key_bytes(a);
   if (RMODE == kRelAug) {
     const size_t scr = (size_t)NW * 16 * kAugGrow * 4;  // overlays the K/V tiles
-    return C::KV_BYTES > scr ? C::KV_BYTES : scr;
+    return (C::KV_BYTES > scr ? C::KV_BYTES : scr) + img_key_bytes(a);
   }
   size_t n = C::KV_BYTES + dyn_lds_bytes(a, C::BM);
   // Relative-position prologue scratch: G[16 queries][2g-1 rows] per wave.
   if (a.bias_kind == ATTN_BIAS_RELPOS) n += (size_t)NW * 16 * relpos_grow(a) * 4;
-  return n;
+  return n + img_key_bytes(a);
 }
 
 // ---------------------------------------------------------------------------
