@@ -263,17 +263,21 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
  *  overwritten with the table gradient summed over all batch items.  The
  *  mask and an ADDITIVE bias receive no gradient.
  *  workspace: device memory of at least the bytes attn_bwd_workspace_size
- *  reports (B_eff * H * table rows * 4 with a TABLE bias, else 0; NULL
- *  allowed when 0), 16-byte aligned, owned by the caller; its contents
- *  before and after the call are unspecified.  The per-window partial table
- *  gradients go there, so the sum over windows runs in a fixed order
- *  (bitwise-deterministic, no atomics).
+ *    reports, 16-byte aligned, owned by the caller (NULL allowed when that is
+ *    0); its contents before and after the call are unspecified.  Window
+ *    units: B_eff * H * table rows * 4 bytes with a TABLE bias (the
+ *    per-window partial table gradients, summed over windows in a fixed
+ *    order by a second kernel), else 0.  Longer sequences: 2 * B * H * Nq * 4
+ *    bytes (each query row's log-sum-exp and sum_j P_ij dP_ij).
+ *    Bitwise-deterministic, no atomics.
  *
- *  Built: half precision (F16/BF16), units of at most 64 queries and keys
+ *  Built: half precision (F16/BF16).  Units of at most 64 queries and keys
  *  (the window path: Swin windows in either layout, with shift and padding
- *  folded in), bias NONE, TABLE or ADDITIVE, any mask.  Other calls
- *  (fp32, longer sequences, RELPOS) return ATTN_E_UNSUPPORTED.
- *  Asynchronous on `stream`; two kernels (units, then the table reduction).  */
+ *  folded in) with bias NONE, TABLE or ADDITIVE and any mask; longer
+ *  sequences in the batched layout without bias or mask (SD-style self- and
+ *  cross-attention): a row kernel (log-sum-exp, D, dQ) and a column kernel
+ *  (dK, dV).  Other calls (fp32, RELPOS, biases or masks on long sequences)
+ *  return ATTN_E_UNSUPPORTED.  Asynchronous on `stream`.                      */
 ATTN_API int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
              const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
              const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
@@ -298,8 +302,9 @@ ATTN_API int attn_bwd_workspace_size(const attn_tensor_t* q, const attn_tensor_t
 /* attn_bwd_noalloc: attn_bwd without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc).  The per-window table
- * gradients go to a fixed 16 MiB device array of the library (one per
- * device, held until the process ends) instead: a call whose workspace
+ * gradients (or the rows' statistics) go to a fixed 16 MiB device array of
+ * the library (one per device, held until the process ends) instead: a call
+ * whose workspace
  * would exceed it (attn_bwd_workspace_size > 16 MiB, e.g. more than 8272
  * windows of 7x7 tokens with 3 heads) returns ATTN_E_UNSUPPORTED.  No
  * allocation of any kind.  Every call on a device shares that device's

@@ -292,8 +292,8 @@ int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov
     if ((uintptr_t)dtable % 4) return ATTN_E_LAYOUT;
     ba->n_tab = (2 * ba->a.gh - 1) * (2 * ba->a.gw - 1);
     ba->dtable = dtable;
-    *ws_bytes = (size_t)ba->a.B * ba->a.H * ba->n_tab * 4;
   }
+  *ws_bytes = bwd_workspace_bytes(ba->a, plan.kernel);
   return ATTN_OK;
 }
 
@@ -319,9 +319,11 @@ int attn_bwd_workspace_size(const attn_tensor_t* q, const attn_tensor_t* k, cons
   if (!bytes) return ATTN_E_NULL;
   *bytes = 0;
   attn::AttnArgs a;
-  const int st = attn::validate(q, k, v, bias_desc, mask_desc, dout, dtype, nullptr, &a);
+  int st = attn::validate(q, k, v, bias_desc, mask_desc, dout, dtype, nullptr, &a);
   if (st != ATTN_OK) return st;
-  if (a.bias_kind == ATTN_BIAS_TABLE) *bytes = (size_t)a.B * a.H * (2 * a.gh - 1) * (2 * a.gw - 1) * 4;
+  attn::Plan plan;
+  if ((st = attn::make_bwd_plan(a, &plan)) != ATTN_OK) return st;
+  *bytes = attn::bwd_workspace_bytes(a, plan.kernel);
   return ATTN_OK;
 }
 

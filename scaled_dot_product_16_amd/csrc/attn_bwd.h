@@ -352,6 +352,289 @@ __global__ __launch_bounds__(256) void attn_bwd_table_reduce(const float* ws, fl
   dtable[i] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass of long sequences (no bias, no mask, batched layout): two
+// kernels, no atomics.
+//
+// Row kernel (attn_bwd_rows): one workgroup of four waves owns 64 queries of
+// one (batch item, head), Q and dO rows in registers, and streams the K/V
+// tiles three times: (1) the row log-sum-exp L (base 2) of the scaled
+// logits, (2) D = sum_j P_ij dP_ij with P = 2^(S*log2e*scale - L) and
+// dP = dO V^T, (3) dS = P (dP - D) and dQ = scale * dS K.  L and D go to the
+// workspace.
+// Column kernel (attn_bwd_cols): one workgroup owns 64 keys, K and V rows in
+// registers, and streams Q, dO (and L, D) tiles: S = Q K^T, P, dP = dO V^T,
+// dS; dV = P^T dO and dK = scale * dS^T Q accumulate over all queries.
+// Both use the forward's MFMA layouts (transposed operands from transposing
+// LDS reads, probabilities packed as B operands).
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdTileCfg {
+  static constexpr int NT = 256;
+  static constexpr int KCH = (D + 31) / 32;
+  static constexpr int DK = KCH * 32;
+  static constexpr int CBD = (D + 15) / 16;
+  static constexpr int ROW = DK + 8;
+  static constexpr int RCH = D / 8;
+  static constexpr int NCH = 64 * RCH;
+  static constexpr int CPT = (NCH + NT - 1) / NT;
+};
+
+// Rows [r0, r0 + 64) of a [N, D] slice (rows clamped to N-1) into an LDS
+// tile of row stride ROW.
+template <int D>
+__device__ __forceinline__ void stage_rows(uint16_t* tile, const uint16_t* src, int64_t sn, int r0, int n,
+                                           int tid) {
+  using C = BwdTileCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::CPT; ++c) {
+    const int ch = tid + c * C::NT;
+    if (ch < C::NCH) {
+      const int row = ch / C::RCH, col = (ch % C::RCH) * 8;
+      const int r = min(r0 + row, n - 1);
+      *(u32x4*)&tile[row * C::ROW + col] = *(const u32x4*)(src + (int64_t)r * sn + col);
+    }
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
+  using C = BwdTileCfg<D>;
+  constexpr int KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW;
+  const AttnArgs& a = ba.a;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  uint16_t* Ks = (uint16_t*)lds;  // [64][ROW]
+  uint16_t* Vs = Ks + 64 * ROW;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
+  const int qt_div = fdiv(bid, a.fd_qt);
+  const int qt = bid - qt_div * a.n_qtiles;
+  const int b = fdiv(qt_div, a.fd_h), h = qt_div - b * a.H;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int qrow = qt * 64 + wave * 16 + l16;
+  const int qi = min(qrow, Nq - 1);
+  const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  const uint16_t* op = (const uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;  // dO
+  u32x4 qf[KCH], df[KCH];
+#pragma unroll
+  for (int dc = 0; dc < KCH; ++dc) {
+    const int d0 = dc * 32 + g * 8;
+    qf[dc] = d0 < D ? *(const u32x4*)(qp + (int64_t)qi * a.q_sn + d0) : u32x4{0, 0, 0, 0};
+    df[dc] = d0 < D ? *(const u32x4*)(op + (int64_t)qi * a.o_sn + d0) : u32x4{0, 0, 0, 0};
+  }
+  if constexpr (DK > D) {  // head-dim padding columns of the tiles
+    for (int i = tid; i < 2 * 64 * (DK - D); i += 256) {
+      const int t = i / (64 * (DK - D)), r = i - t * 64 * (DK - D);
+      Ks[t * 64 * ROW + (r / (DK - D)) * ROW + D + r % (DK - D)] = 0;
+    }
+  }
+  const float c2 = a.scale * kLog2e;
+  const int ntiles = (Nk + 63) / 64;
+  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  float m = -INFINITY, l = 0.f, L = 0.f, Dacc = 0.f, Dq = 0.f;
+  f32x4 acc[CBD];
+#pragma unroll
+  for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();  // the previous tile's reads are done
+      stage_rows<D>(Ks, kp, a.k_sn, t * 64, Nk, tid);
+      if (pass > 0) stage_rows<D>(Vs, vp, a.v_sn, t * 64, Nk, tid);
+      __syncthreads();
+      f32x4 s[4], dp[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) {
+          s[kb] = E::mfma(*(const u32x4*)&Ks[(kb * 16 + l16) * ROW + dc * 32 + g * 8], qf[dc], s[kb]);
+          if (pass > 0) dp[kb] = E::mfma(*(const u32x4*)&Vs[(kb * 16 + l16) * ROW + dc * 32 + g * 8], df[dc], dp[kb]);
+        }
+      }
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
+        y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
+      }
+      if (pass == 0) {
+        float mx = y[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
+        const float mn = fmaxf(m, max_across_groups(mx));
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(y[i] - mn);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + ps;  // per-lane partial sums
+        m = mn;
+      } else {
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(y[i] - L);
+          if (pass == 1) Dacc = fmaf(p, dp[i >> 2][i & 3], Dacc);
+          else ds[i] = p * (dp[i >> 2][i & 3] - Dq);
+        }
+        if (pass == 2) {
+          u32x4 sf[2];
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+            sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                           E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int cb = 0; cb < CBD; ++cb) {
+              const uint16_t* ptr = Ks + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+              const u32x2 lo = lds_read_tr16(ptr);
+              const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
+              acc[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[kc], acc[cb]);
+            }
+        }
+      }
+    }
+    if (pass == 0) L = m + __builtin_amdgcn_logf(sum_across_groups(l));  // log2 of the row sum
+    if (pass == 1) Dq = sum_across_groups(Dacc);
+  }
+  float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
+  float* wsD = wsL + (int64_t)a.B * a.H * Nq;
+  if (qrow < Nq) {
+    if (g == 0) {
+      wsL[qrow] = L;
+      wsD[qrow] = Dq;
+    }
+    uint16_t* dq = (uint16_t*)ba.dq + (int64_t)b * ba.dq_sb + (int64_t)h * ba.dq_sh + (int64_t)qrow * ba.dq_sn;
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) {
+      const int c0 = cb * 16 + g * 4;
+      if (c0 < D) {
+        const f32x4 v = acc[cb] * a.scale;
+        *(u32x2*)(dq + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+      }
+    }
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
+  using C = BwdTileCfg<D>;
+  constexpr int KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW;
+  const AttnArgs& a = ba.a;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  uint16_t* Qs = (uint16_t*)lds;  // [64][ROW]
+  uint16_t* Os = Qs + 64 * ROW;   // dO
+  float* Ls = (float*)(Os + 64 * ROW);
+  float* Ds = Ls + 64;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int bid = xcd_logical_id(__builtin_amdgcn_workgroup_id_x(), a.n_blocks);
+  const int kt_div = fdiv(bid, a.fd_qt);  // key tiles
+  const int kt = bid - kt_div * a.n_qtiles;
+  const int b = fdiv(kt_div, a.fd_h), h = kt_div - b * a.H;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int krow = kt * 64 + wave * 16 + l16;
+  const int ki = min(krow, Nk - 1);
+  const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  const uint16_t* op = (const uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;  // dO
+  // K and V rows of this lane's key as B operands (lane = key column).
+  u32x4 kf[KCH], vf[KCH];
+#pragma unroll
+  for (int dc = 0; dc < KCH; ++dc) {
+    const int d0 = dc * 32 + g * 8;
+    kf[dc] = d0 < D ? *(const u32x4*)(kp + (int64_t)ki * a.k_sn + d0) : u32x4{0, 0, 0, 0};
+    vf[dc] = d0 < D ? *(const u32x4*)(vp + (int64_t)ki * a.v_sn + d0) : u32x4{0, 0, 0, 0};
+  }
+  if constexpr (DK > D) {
+    for (int i = tid; i < 2 * 64 * (DK - D); i += 256) {
+      const int t = i / (64 * (DK - D)), r = i - t * 64 * (DK - D);
+      Qs[t * 64 * ROW + (r / (DK - D)) * ROW + D + r % (DK - D)] = 0;
+    }
+  }
+  const float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
+  const float* wsD = wsL + (int64_t)a.B * a.H * Nq;
+  const float c2 = a.scale * kLog2e;
+  const int ntiles = (Nq + 63) / 64;
+  const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  f32x4 dk[CBD], dv[CBD];
+#pragma unroll
+  for (int cb = 0; cb < CBD; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    stage_rows<D>(Qs, qp, a.q_sn, t * 64, Nq, tid);
+    stage_rows<D>(Os, op, a.o_sn, t * 64, Nq, tid);
+    if (tid < 64) {
+      const int q = t * 64 + tid;
+      Ls[tid] = q < Nq ? wsL[q] : INFINITY;  // rows past Nq: P = 0
+      Ds[tid] = q < Nq ? wsD[q] : 0.f;
+    }
+    __syncthreads();
+    // S = Q K^T and dP = dO V^T: rows are queries qb*16 + g*4 + r, the
+    // column is this lane's key.
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      s[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        s[qb] = E::mfma(*(const u32x4*)&Qs[(qb * 16 + l16) * ROW + dc * 32 + g * 8], kf[dc], s[qb]);
+        dp[qb] = E::mfma(*(const u32x4*)&Os[(qb * 16 + l16) * ROW + dc * 32 + g * 8], vf[dc], dp[qb]);
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4 Lq = *(const f32x4*)&Ls[qb * 16 + g * 4];
+      const f32x4 Dv = *(const f32x4*)&Ds[qb * 16 + g * 4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(s[qb][r] * c2 - Lq[r]);
+        p[qb * 4 + r] = pv;
+        ds[qb * 4 + r] = pv * (dp[qb][r] - Dv[r]);
+      }
+    }
+    u32x4 pf[2], sf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      pf[kc] = u32x4{E::pack2(p[kc * 8 + 0], p[kc * 8 + 1]), E::pack2(p[kc * 8 + 2], p[kc * 8 + 3]),
+                     E::pack2(p[kc * 8 + 4], p[kc * 8 + 5]), E::pack2(p[kc * 8 + 6], p[kc * 8 + 7])};
+      sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                     E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the tiles).
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const uint16_t* optr = Os + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const uint16_t* qptr = Qs + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const u32x2 ol = lds_read_tr16(optr), oh = lds_read_tr16(optr + 16 * ROW);
+        const u32x2 ql = lds_read_tr16(qptr), qh = lds_read_tr16(qptr + 16 * ROW);
+        dv[cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pf[kc], dv[cb]);
+        dk[cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kc], dk[cb]);
+      }
+  }
+  if (krow < Nk) {
+    uint16_t* dkp = (uint16_t*)ba.dk + (int64_t)b * ba.dk_sb + (int64_t)h * ba.dk_sh + (int64_t)krow * ba.dk_sn;
+    uint16_t* dvp = (uint16_t*)ba.dv + (int64_t)b * ba.dv_sb + (int64_t)h * ba.dv_sh + (int64_t)krow * ba.dv_sn;
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) {
+      const int c0 = cb * 16 + g * 4;
+      if (c0 < D) {
+        const f32x4 k4 = dk[cb] * a.scale, v4 = dv[cb];
+        *(u32x2*)(dkp + c0) = u32x2{E::pack2(k4[0], k4[1]), E::pack2(k4[2], k4[3])};
+        *(u32x2*)(dvp + c0) = u32x2{E::pack2(v4[0], v4[1]), E::pack2(v4[2], v4[3])};
+      }
+    }
+  }
+}
+
 }  // namespace attn
 
 #endif  // ATTN_BWD_H_

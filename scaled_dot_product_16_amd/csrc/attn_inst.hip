@@ -171,12 +171,31 @@ int launch_bwd_bias(const AttnBwdArgs& ba, const Plan& p, hipStream_t s) {
 }  // namespace
 
 #if INST_DT != 0
+// Long sequences: the row kernel (L, D, dQ), then the column kernel (dK, dV).
+static int launch_bwd_tiled(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
+  constexpr int D = INST_D;
+  AttnBwdArgs ba = ba0;
+  ba.a.n_qtiles = (ba.a.Nq + 63) / 64;
+  ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
+  ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
+  auto rows = attn_bwd_rows<Elem, D>;
+  auto cols = attn_bwd_cols<Elem, D>;
+  hipLaunchKernelGGL(rows, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
+  if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+  ba.a.n_qtiles = (ba.a.Nk + 63) / 64;  // key tiles for the column kernel
+  ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
+  ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
+  hipLaunchKernelGGL(cols, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 template <>
 int launch_bwd_inst<INST_DT, INST_D>(const AttnBwdArgs& ba, void* stream) {
   Plan p;
   const int st = make_bwd_plan(ba.a, &p);
   if (st != ATTN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (p.kernel == kKernMfma) return launch_bwd_tiled(ba, p, s);
   switch (ba.a.bias_kind) {
     case ATTN_BIAS_NONE: return launch_bwd_bias<ATTN_BIAS_NONE>(ba, p, s);
     case ATTN_BIAS_TABLE: return launch_bwd_bias<ATTN_BIAS_TABLE>(ba, p, s);

@@ -379,21 +379,42 @@ inline int make_plan(const AttnArgs& a, Plan* p) {
   return ATTN_OK;
 }
 
-// The backward of a validated call: window units only (at most 64 queries
-// and keys), half precision, relative-position bias excluded.
+// The backward of a validated call (half precision): window units (at most
+// 64 queries and keys; any bias but the relative position, any mask), or
+// the tiled row/column kernels for longer sequences without bias or mask in
+// the batched layout.  blocks: the larger of the two tiled grids.
 template <int D>
 inline Plan plan_bwd_half(const AttnArgs& a) {
   Plan p{};
-  if (a.Nq > 64 || a.Nk > 64 || a.bias_kind == ATTN_BIAS_RELPOS) {
+  p.hg = 1;
+  p.nw = kWinWaves;
+  if (a.Nq <= 64 && a.Nk <= 64 && a.bias_kind != ATTN_BIAS_RELPOS) {
+    p.kernel = kKernWin;
+    p.blocks = (int64_t)a.B * a.H;
+    p.lds = win_bwd_lds_bytes(a, WinBwdCfg<D>::BYTES);
+    return p;
+  }
+  if (a.bias_kind != ATTN_BIAS_NONE || a.mask_kind != ATTN_MASK_NONE || a.image) {
     p.kernel = -1;
     return p;
   }
-  p.kernel = kKernWin;
-  p.nw = kWinWaves;
-  p.hg = 1;
-  p.blocks = (int64_t)a.B * a.H;
-  p.lds = win_bwd_lds_bytes(a, WinBwdCfg<D>::BYTES);
+  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  p.kernel = kKernMfma;
+  p.bm = 64;
+  const int64_t nt = (a.Nq > a.Nk ? a.Nq : a.Nk) + 63;
+  p.blocks = nt / 64 * a.H * a.B;
+  p.lds = (size_t)2 * 64 * ROW * 2 + 2 * 64 * 4;
   return p;
+}
+
+// Workspace bytes of the backward: per-unit table gradients (window path
+// with a table bias) or the rows' L and D (tiled path).
+constexpr size_t bwd_workspace_bytes(const AttnArgs& a, int kernel) {
+  if (kernel == kKernWin)
+    return a.bias_kind == ATTN_BIAS_TABLE
+               ? (size_t)a.B * a.H * (size_t)((2 * a.gh - 1) * (2 * a.gw - 1)) * 4
+               : 0;
+  return (size_t)2 * a.B * a.H * a.Nq * 4;
 }
 
 inline int make_bwd_plan(const AttnArgs& a, Plan* p) {

@@ -319,7 +319,18 @@ def test_backward_validation(lib):
     qc2, kc2, vc2, bd2, md2, oc2, dt2, keep2 = B._marshal(*ins, None, None, "batched", None)
     grads = [t(1, 2, 100, 64) for _ in range(3)]  # kept alive: distinct addresses
     d1, d2, d3 = (T(x) for x in grads)
-    assert h.attn_bwd_check(ctypes.byref(qc2), ctypes.byref(kc2), ctypes.byref(vc2), ctypes.byref(oc2),
-                            ctypes.byref(bd2), ctypes.byref(md2), ctypes.byref(d1), ctypes.byref(d2),
-                            ctypes.byref(d3), None, dt2, None, 0) == 4   # longer than a window
-    del keep, keep2
+    # Longer than a window without bias: the tiled backward, whose workspace
+    # holds each row's log-sum-exp and D (2 * B * H * Nq floats).
+    args2 = lambda w, n: (ctypes.byref(qc2), ctypes.byref(kc2), ctypes.byref(vc2), ctypes.byref(oc2),
+                          ctypes.byref(bd2), ctypes.byref(md2), ctypes.byref(d1), ctypes.byref(d2),
+                          ctypes.byref(d3), None, dt2, w, n)
+    assert h.attn_bwd_check(*args2(None, 0)) == 1
+    wsl = torch.zeros(2 * 1 * 2 * 100)
+    assert h.attn_bwd_check(*args2(ctypes.c_void_p(wsl.data_ptr()), 2 * 2 * 100 * 4)) == 0
+    # A relative-position bias on a long sequence has no backward here.
+    rb = B.RelposBias(t(19, 64), t(19, 64), (10, 10))
+    qc3, kc3, vc3, bd3, md3, oc3, dt3, keep3 = B._marshal(*ins, rb, None, "batched", None)
+    assert h.attn_bwd_check(ctypes.byref(qc3), ctypes.byref(kc3), ctypes.byref(vc3), ctypes.byref(oc3),
+                            ctypes.byref(bd3), ctypes.byref(md3), ctypes.byref(d1), ctypes.byref(d2),
+                            ctypes.byref(d3), None, dt3, ctypes.c_void_p(wsl.data_ptr()), 1 << 20) == 4
+    del keep, keep2, keep3

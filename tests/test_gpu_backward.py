@@ -155,10 +155,34 @@ def test_backward_deterministic_and_strided():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [32, 40, 64, 80])
+@pytest.mark.parametrize("nq,nk", [(65, 65), (200, 300), (300, 77), (129, 1000), (1, 130)])
+def test_tiled_backward_shapes(dtype, d, nq, nk):
+    # Longer than one window: the row kernel (log-sum-exp, D, dQ) and the
+    # column kernel (dK, dV), ragged query and key tiles.
+    w = W.custom(dtype, B=2, H=2, Nq=nq, Nk=nk, d=d, cfg_id=870 + d)
+    say(f"[tiled backward] {dtype} d={d} Nq={nq} Nk={nk}")
+    inp = inputs(w, seed=nq + nk)
+    check_grads(w, inp, run_bwd(w, to_device(inp)), name=f"tiled backward {nq}x{nk} d={d}")
+
+
+@pytest.mark.parametrize("key", ["C5s", "C5x"])
+def test_tiled_backward_sd_shapes(key):
+    # SD UNet self- and cross-attention shapes, every element compared on a
+    # slice of 2 batch items (the oracle's gradient is per (b, h) anyway).
+    base = W.WORKLOADS[key]
+    w = W.custom(base.dtype, B=2, H=base.H, Nq=base.Nq, Nk=base.Nk, d=base.d, cfg_id=base.cfg_id)
+    say(f"[tiled backward] {key} shape, 2 of {base.B} batch items")
+    inp = inputs(w, seed=1)
+    check_grads(w, inp, run_bwd(w, to_device(inp)), name=f"tiled backward {key} shape (2 batch items)")
+
+
 def test_backward_unsupported_calls():
-    q = torch.zeros(1, 2, 100, 64, dtype=torch.float16, device="cuda")
-    with pytest.raises(Bd.AttnError) as e:
-        Bd.bwd(q, q.clone(), q.clone(), q.clone())       # longer than one window
+    w = W.custom(W.F16, B=1, H=2, Nq=100, Nk=100, d=64, bias="relpos", grid=(10, 10), cfg_id=880)
+    dev = to_device(inputs(w))
+    with pytest.raises(Bd.AttnError) as e:                # relative position on a long sequence
+        Bd.bwd(dev["q"], dev["k"], dev["v"], dev["dout"], **W.device_args(w, dev))
     assert e.value.status == 4
     q = torch.zeros(1, 2, 49, 32, dtype=torch.float32, device="cuda")
     with pytest.raises(Bd.AttnError) as e:
