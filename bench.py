@@ -276,6 +276,107 @@ def run_workload(torch, W, binding, w, K: int, warmup: int, settle_ms: float, no
     return rec, inp
 
 
+def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, check_units: int):
+    """Time the backward pass of workload ``w`` (attn_bwd: dQ, dK, dV and,
+    with a table bias, the table gradient), like run_workload.  Algorithmic
+    work: the five products S, dP, dV, dK, dQ (10*B*H*Nq*Nk*d flops); bytes:
+    Q, K, V, dO read and dQ, dK, dV written (plus the table and its
+    gradient)."""
+    import numpy as np
+
+    import oracle
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    inp["dout"] = W.to_dtype(W.normal(w.q_shape, w.cfg_id, 7, 1.0), w.dtype)
+    base = {k: v.to(dev) for k, v in inp.items()}
+    per_set = 7 * base["q"].numel() * base["q"].element_size()
+    n_sets = max(1, math.ceil(512e6 / per_set))
+    sets = []
+    for i in range(n_sets):
+        s = {k: (v.clone() if k in ("q", "k", "v", "dout") else v) for k, v in base.items()}
+        s["kw"] = W.device_args(w, s)
+        s["dq"], s["dk"], s["dv"] = (torch.empty_like(s["q"]) for _ in range(3))
+        s["dtable"] = (torch.empty(base["table"].shape, dtype=torch.float32, device=dev)
+                       if w.bias == "table" else None)
+        sets.append(s)
+    # One workspace, reused by every launch (they run one after another).
+    s0 = sets[0]
+    binding.bwd(s0["q"], s0["k"], s0["v"], s0["dout"], dq=s0["dq"], dk=s0["dk"], dv=s0["dv"],
+                dtable=s0["dtable"], **s0["kw"])
+    import ctypes
+    need = ctypes.c_size_t(0)
+    qc, kc, vc, bd, md, oc, dt, keep = binding._marshal(s0["q"], s0["k"], s0["v"], s0["dout"],
+                                                        s0["kw"].get("bias"), s0["kw"].get("mask"),
+                                                        w.layout, s0["kw"].get("window"))
+    binding.lib().attn_bwd_workspace_size(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc),
+                                          ctypes.byref(oc), ctypes.byref(bd), ctypes.byref(md), dt,
+                                          ctypes.byref(need))
+    ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    del keep
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % n_sets]
+        binding.bwd(s["q"], s["k"], s["v"], s["dout"], dq=s["dq"], dk=s["dk"], dv=s["dv"],
+                    dtable=s["dtable"], workspace=ws, **s["kw"])
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    rec = {}
+    if check_units:
+        # Oracle gradients: the whole workload in the image layout, else the
+        # first and last (batch item, head) units (no bias: each unit's
+        # gradients depend on its own slice only).
+        arrs = {k: v.double().numpy() for k, v in inp.items()}
+        got = [sets[0][k].detach().double().cpu().numpy() for k in ("dq", "dk", "dv")]
+        errs = []
+        if w.layout == "image" or w.bias != "none":
+            ref = oracle.run_workload_backward(w, arrs)
+            errs = [float(np.max(np.abs(g - ref[k]))) for g, k in zip(got, ("dq", "dk", "dv"))]
+            sample = "whole workload"
+            if w.bias == "table":
+                errs.append(float(np.max(np.abs(sets[0]["dtable"].double().cpu().numpy() - ref["dtable"]))))
+        else:
+            for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+                sl = {k: v[b:b + 1, h:h + 1] for k, v in arrs.items()}
+                ref = oracle.attention_backward(sl["q"], sl["k"], sl["v"], sl["dout"])
+                errs += [float(np.max(np.abs(g[b, h] - ref[k][0, 0]))) for g, k in zip(got, ("dq", "dk", "dv"))]
+            sample = "2 (batch item, head) units, every row"
+        rec.update({"max_abs_err": max(errs), "err_sample": sample})
+    ref_out = sets[0]["dq"].clone()
+    total_ms, note, g = timed_graph(torch, stream, step, K, settle_ms)
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(sets[0]["dq"], ref_out):
+        raise RuntimeError(f"{w.key} backward: graph replay output differs from the eager output")
+    del g
+    ms = total_ms / K
+    flops = 10 * w.B * w.H * w.Nq * w.Nk * w.d
+    e = w.bytes_per_elem()
+    nbytes = 7 * int(np.prod(w.q_shape)) * e
+    if w.bias == "table":
+        nbytes += base["table"].numel() * (e + 4)
+    ai = flops / nbytes
+    if ai < RIDGE:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 3), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 3), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof.update({"frac": round(roof["achieved"] / roof["peak"], 4), "traffic": None,
+                 "kernel_mean_ms": round(ms, 6), "timing": note})
+    rec.update({"ms_per_step": round(ms, 6), "tflops": round(flops / (ms * 1e-3) / 1e12, 4),
+                "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 2), "flops_per_step": flops,
+                "algorithmic_bytes_per_step": nbytes, "rotating_input_sets": n_sets, "roofline": roof,
+                "pass": "backward (attn_bwd)"})
+    del sets, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def copy_floor(torch, nbytes: int, K: int, settle_ms: float):
     """A plain device copy moving ``nbytes`` in all (half read, half written),
     on rotating cold buffers, timed like the attention steps."""
@@ -327,7 +428,8 @@ def main():
     ap.add_argument("--config", default="C2", help="headline workload")
     ap.add_argument("--extra", default="all",
                     help="comma-separated workloads also timed in this run ('all' or 'none'; "
-                         "C2p is C2 with 3 heads of a window per workgroup)")
+                         "C2p is C2 with 3 heads of a window per workgroup; C2b and C5sb are the "
+                         "backward passes of C2 and C5s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle error checks")
     ap.add_argument("--check-units", type=int, default=16,
@@ -404,11 +506,24 @@ def main():
         line["copy_floor"] = copy_floor(torch, w.algorithmic_bytes, K, args.settle_ms)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
-    extra = [] if args.extra == "none" else (ALL + ["C2p"] if args.extra == "all" else args.extra.split(","))
+    extra = [] if args.extra == "none" else (ALL + ["C2p", "C2b", "C5sb"] if args.extra == "all"
+                                             else args.extra.split(","))
     if extra:
         line["workloads"] = {}
         for key in extra:
             if key == args.config:
+                continue
+            if key in ("C2b", "C5sb"):  # backward passes of Swin-T and SD self-attention
+                we = W.WORKLOADS[key[:-1]]
+                r = run_backward(torch, W, binding, we, K, args.warmup, args.settle_ms,
+                                 0 if args.no_check else 1)
+                r["config"] = config_of(we)
+                r["dtype"] = we.dtype
+                line["workloads"][key] = r
+                print(f"# {key} {we.name} backward: {r['ms_per_step'] * 1e3:.2f} us, "
+                      f"{r['roofline']['frac']:.3f} of {r['roofline']['bound']} peak"
+                      + (f", max abs err {r['max_abs_err']:.2e}" if "max_abs_err" in r else ""),
+                      file=sys.stderr, flush=True)
                 continue
             # C2p: the Swin-T workload with its 3 heads of a window packed
             # into one workgroup (the packed short-sequence form).

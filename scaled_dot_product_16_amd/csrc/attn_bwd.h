@@ -333,23 +333,32 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
       for (int qh = max(0, oh); qh < min(gh, gh + oh); ++qh)
         for (int qw = max(0, ow); qw < min(gw, gw + ow); ++qw)
           acc += Sf[((qh - oh) * gw + (qw - ow)) * FROW + qh * gw + qw];
-      ba.ws[(int64_t)unit * n_tab + r] = acc;  // unit = b * H + h
+      ba.ws[((int64_t)h * n_tab + r) * a.B + b] = acc;  // [H][n_tab][B]: windows contiguous
     }
   }
 }
 
 // d_table[r, h] = sum over the batch items b (windows) of the per-unit
-// partial sums, in order of b.  One thread per (row, head).  (A template
-// only so that every compiled instance may carry its copy.)
+// partial sums ws[h][r][b].  One workgroup per (row, head): each thread adds
+// a strided slice of the windows, then a fixed tree in LDS adds the 256
+// partial sums (the same order every run: deterministic).  (A template only
+// so that every compiled instance may carry its copy.)
 template <int kUnused>
 __global__ __launch_bounds__(256) void attn_bwd_table_reduce(const float* ws, float* dtable, int B,
                                                              int H, int n_tab) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // i = r * H + h
-  if (i >= n_tab * H) return;
+  __shared__ float part[256];
+  const int i = blockIdx.x;  // i = r * H + h
   const int r = i / H, h = i - r * H;
+  const float* src = ws + ((int64_t)h * n_tab + r) * B;
   float acc = 0.f;
-  for (int b = 0; b < B; ++b) acc += ws[((int64_t)b * H + h) * n_tab + r];
-  dtable[i] = acc;
+  for (int b = threadIdx.x; b < B; b += 256) acc += src[b];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dtable[i] = part[0];
 }
 
 // ---------------------------------------------------------------------------

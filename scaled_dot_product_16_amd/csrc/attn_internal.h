@@ -83,7 +83,7 @@ struct AttnBwdArgs {
   int64_t dk_sb, dk_sh, dk_sn;
   int64_t dv_sb, dv_sh, dv_sn;
   float* dtable;  // [n_tab, H] (TABLE bias) or null
-  float* ws;      // per-unit partial table gradients [B][H][n_tab]
+  float* ws;      // workspace: per-window table gradients [H][n_tab][B], or rows' L and D
   int32_t n_tab;  // table rows (TABLE bias), else 0
 };
 
