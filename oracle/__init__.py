@@ -19,6 +19,8 @@ from .attention import (  # noqa: F401
     table_bias,
     relpos_rows,
     rel_pos_resized,
+    e4m3_decode,
+    dequantize_e4m3,
     relpos_bias,
     relpos_bias_gather,
     shift_region_labels,

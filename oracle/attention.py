@@ -57,7 +57,16 @@ design notes of the repository):
   the attention like any other token, and their outputs are cropped away;
   the shift and the region labels are taken on the padded grid;
 * an additive bias of shape [nB, Nq, Nk] applies to batch item b as b % nB,
-  an additive mask [nW, Nq, Nk] as b % nW.
+  an additive mask [nW, Nq, Nk] as b % nW;
+* low-precision inputs: the SAM write-ups speed the model up with GPU
+  quantization ("Segment Anything, Fast", introduction), and the Swin talk
+  (section 3, inference optimisation) runs 8-bit matrix products whose
+  quantization and dequantization are fused into the neighbouring
+  operators.  Reading for this attention: q, k and v may arrive as 8-bit
+  floating-point codes (E4M3 of the OCP 8-bit floating point
+  specification), each tensor with one scale; the attention is computed on
+  the dequantized values code * scale, exactly as on any other input, and
+  the output has the compute dtype (``e4m3_decode``, ``dequantize_e4m3``).
 
 Everything is numpy float64.  The inputs are the exact values the device
 receives (already rounded to the device dtype), upcast to float64.
@@ -194,6 +203,32 @@ def rel_pos_resized(table: np.ndarray, m: int) -> np.ndarray:
         f = float(p - i)
         out[r] = table[i] if i >= L - 1 else (1.0 - f) * table[i] + f * table[i + 1]
     return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of 8-bit E4M3 floating-point codes -> float64 array.
+
+    E4M3 as the OCP 8-bit floating point specification defines it: bit 7
+    sign, bits 6..3 exponent e with bias 7, bits 2..0 mantissa m.  e > 0:
+    (-1)^s * 2^(e-7) * (1 + m/8); e == 0: subnormal (-1)^s * 2^-6 * m/8.
+    There are no infinities; the codes with e == 15 and m == 7 (0x7F, 0xFF)
+    are NaN, so the largest finite magnitude is 2^8 * 1.75 = 448.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    if np.any((c < 0) | (c > 255)):
+        raise ValueError("E4M3 codes are bytes 0..255")
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def dequantize_e4m3(codes, scale: float) -> np.ndarray:
+    """code * scale in float64: the value an 8-bit input stands for, with its
+    tensor's scale (see the low-precision reading in the module notes)."""
+    return e4m3_decode(codes) * float(scale)
 
 
 def relpos_bias(q_rows: np.ndarray, rows: np.ndarray, rh: np.ndarray,
@@ -544,6 +579,19 @@ def attention_image_backward(q, k, v, dout, window: tuple, bias: Optional[Bias] 
     return res
 
 
+def _dequantized(w, arrays: dict) -> dict:
+    """``arrays`` with q, k, v dequantized when workload ``w`` stores them as
+    E4M3 codes (attribute ``qkv`` == "e4m3"; ``arrays["descale"]`` holds the
+    scales of q, k and v in that order)."""
+    if getattr(w, "qkv", "same") != "e4m3":
+        return arrays
+    s = np.asarray(arrays["descale"], dtype=np.float64).reshape(-1)
+    out = dict(arrays)
+    for i, name in enumerate(("q", "k", "v")):
+        out[name] = dequantize_e4m3(arrays[name], s[i])
+    return out
+
+
 def _workload_terms(w, arrays: dict):
     """The Bias and Mask of a workload record, tables taken from ``arrays``."""
     bias = Bias("none")
@@ -570,6 +618,7 @@ def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
     (table / rh, rw / bias_add, mask_add) to float64 numpy arrays holding the
     exact device values.  ``select`` as in :func:`attention` (batched layout).
     """
+    arrays = _dequantized(w, arrays)
     bias, mask = _workload_terms(w, arrays)
     if w.layout == "image":
         assert select is None, "image layout is evaluated whole"

@@ -13,8 +13,8 @@ GPU context or device file.  Each worker runs single-threaded BLAS, so the
 pool's parallelism is its process count, which is reported.
 
 Inputs travel through ``.npy`` files in a temporary directory (float32 holds
-every f16/bf16 value exactly; f32 inputs are stored as they are), opened by
-the workers as read-only memory maps.
+every f16/bf16 value and every 8-bit code exactly; f32 inputs are stored as
+they are), opened by the workers as read-only memory maps.
 """
 
 from __future__ import annotations
@@ -103,6 +103,11 @@ def _unit_inputs(b: int, h: int, drop: Optional[str] = None):
     q = f(A["q"][b:b + 1, h:h + 1])
     k = f(A["k"][b:b + 1, h:h + 1])
     v = f(A["v"][b:b + 1, h:h + 1])
+    if S.get("qkv", "same") == "e4m3":
+        # 8-bit inputs: the arrays hold E4M3 codes, "descale" their scales.
+        from oracle.attention import dequantize_e4m3
+        s = np.asarray(A["descale"], dtype=np.float64).reshape(-1)
+        q, k, v = (dequantize_e4m3(x, s[i]) for i, x in enumerate((q, k, v)))
     bias = Bias("none")
     if S["bias"] == "table":
         bias = Bias("table", grid=S["grid"], table=f(A["table"][:, h:h + 1]))
@@ -176,7 +181,7 @@ def _timing_job(job):
 def spec_of(w) -> dict:
     """The description a pool needs of a workload record."""
     return {"bias": w.bias, "grid": w.grid, "kgrid": getattr(w, "kgrid", None), "mask": w.mask,
-            "layout": w.layout, "window": w.window}
+            "layout": w.layout, "window": w.window, "qkv": getattr(w, "qkv", "same")}
 
 
 def units_of(w) -> list:

@@ -18,6 +18,13 @@ SeedSequence([16, cfg_id, tensor_id])))`` as float32 standard normals
 ~ N(0, 0.02^2).  Values are then rounded to the device dtype with torch on
 the CPU (round to nearest even).  An optional ``seed`` offsets the sequence so
 tests can draw independent cases.
+
+Workloads with 8-bit inputs (``qkv="e4m3"``) draw q, k and v the same way
+and store each as E4M3 codes with one scale per tensor, the scale being the
+tensor's largest magnitude / 448 (the largest finite E4M3 value): torch
+divides by the scale and rounds to E4M3 (nearest even) on the CPU.  Their
+tables and output use the compute dtype.  This is input preparation, as a
+quantizing producer would do it; the attention consumes the codes and scales.
 """
 
 from __future__ import annotations
@@ -49,6 +56,7 @@ class Workload:
     images: Optional[int] = None
     window: Optional[tuple] = None   # (img_h, img_w, win_h, win_w, shift_h, shift_w)
     note: str = ""
+    qkv: str = "same"            # same (q, k, v in dtype) | e4m3 (8-bit codes + scales)
 
     @property
     def q_shape(self):
@@ -71,12 +79,25 @@ class Workload:
     def bytes_per_elem(self) -> int:
         return {F32: 4, F16: 2, BF16: 2}[self.dtype]
 
+    def input_bytes_per_elem(self) -> int:
+        """Bytes of one q, k or v element (1 for 8-bit codes)."""
+        return 1 if self.qkv == "e4m3" else self.bytes_per_elem()
+
     @property
     def algorithmic_bytes(self) -> int:
         """Q + K + V read once, O written once, plus the bias tables."""
         e = self.bytes_per_elem()
+        if self.qkv == "e4m3":
+            n_q = int(np.prod(self.q_shape))
+            n_kv = int(np.prod(self.kv_shape))
+            return 2 * n_kv + n_q + n_q * e + self.algorithmic_bytes_tables()
         qo = 2 * int(np.prod(self.q_shape))
         kv = 2 * int(np.prod(self.kv_shape))
+        return (qo + kv) * e + self.algorithmic_bytes_tables()
+
+    def algorithmic_bytes_tables(self) -> int:
+        """Bytes of the bias tables (read once)."""
+        e = self.bytes_per_elem()
         tables = 0
         if self.bias == "table":
             gh, gw = self.grid
@@ -84,7 +105,7 @@ class Workload:
         elif self.bias == "relpos":
             gh, gw = self.grid
             tables = (2 * gh - 1 + 2 * gw - 1) * self.d
-        return (qo + kv + tables) * e
+        return tables * e
 
 
 WORKLOADS = {
@@ -111,6 +132,15 @@ WORKLOADS = {
                     note="SD 1.5 UNet self-attention at 64x64 latent, CFG batch 16"),
     "C5x": Workload("C5x", "sd15_unet_cross_f16", 55, F16, B=16, H=8, Nq=4096, Nk=77, d=40,
                     note="SD 1.5 UNet cross-attention, 77 context tokens"),
+    # 8-bit inputs (E4M3 codes, one scale per tensor), f16 compute and output.
+    "C2f8": Workload("C2f8", "swin_t_stage1_shifted_e4m3_f16", 62, F16, B=8 * 64, H=3, Nq=49,
+                     Nk=49, d=32, bias="table", grid=(7, 7), mask="shift", layout="image",
+                     images=8, window=(56, 56, 7, 7, 3, 3), qkv="e4m3",
+                     note="the Swin-T stage-1 workload with q, k, v as E4M3 codes"),
+    "C5sf8": Workload("C5sf8", "sd15_unet_self_e4m3_f16", 65, F16, B=16, H=8, Nq=4096, Nk=4096,
+                      d=40, qkv="e4m3", note="SD 1.5 UNet self-attention, q, k, v as E4M3 codes"),
+    "C5xf8": Workload("C5xf8", "sd15_unet_cross_e4m3_f16", 66, F16, B=16, H=8, Nq=4096, Nk=77,
+                      d=40, qkv="e4m3", note="SD 1.5 UNet cross-attention, q, k, v as E4M3 codes"),
 }
 
 
@@ -135,19 +165,41 @@ def to_dtype(x: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt)
 
 
+def to_e4m3(x: np.ndarray):
+    """float32 values -> (E4M3 codes as a uint8 tensor, float32 scale): the
+    scale is max|x| / 448 (1 for an all-zero tensor), and x / scale is
+    rounded to E4M3 by torch on the CPU (nearest even)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = float(t.abs().max()) if t.numel() else 0.0
+    scale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    codes = (t / torch.tensor(scale)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8), float(scale)
+
+
 def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0, std_table: float = 0.02) -> dict:
     """Draw the inputs of workload ``w`` as torch CPU tensors in its dtype.
 
     Returns q, k, v and, depending on the bias kind, table or rh/rw.
     ``std_table`` (default 0.02, the workloads' recipe) sets the standard
     deviation of the bias tables; tests raise it so that the bias is large
-    next to the tolerance.
+    next to the tolerance.  For 8-bit inputs q, k, v are uint8 tensors of
+    E4M3 codes and ``descale`` a float32 tensor of their three scales.
     """
-    out = {
-        "q": to_dtype(normal(w.q_shape, w.cfg_id, 0, std_qkv, seed), w.dtype),
-        "k": to_dtype(normal(w.kv_shape, w.cfg_id, 1, std_qkv, seed), w.dtype),
-        "v": to_dtype(normal(w.kv_shape, w.cfg_id, 2, std_qkv, seed), w.dtype),
-    }
+    draws = {"q": normal(w.q_shape, w.cfg_id, 0, std_qkv, seed),
+             "k": normal(w.kv_shape, w.cfg_id, 1, std_qkv, seed),
+             "v": normal(w.kv_shape, w.cfg_id, 2, std_qkv, seed)}
+    if w.qkv == "e4m3":
+        import torch
+
+        out, scales = {}, []
+        for name in ("q", "k", "v"):
+            out[name], s = to_e4m3(draws[name])
+            scales.append(s)
+        out["descale"] = torch.tensor(scales, dtype=torch.float32)
+    else:
+        out = {name: to_dtype(x, w.dtype) for name, x in draws.items()}
     if w.bias == "table":
         gh, gw = w.grid
         out["table"] = to_dtype(normal(((2 * gh - 1) * (2 * gw - 1), w.H), w.cfg_id, 3,
@@ -162,11 +214,12 @@ def make_inputs(w: Workload, seed: int = 0, std_qkv: float = 1.0, std_table: flo
 
 def custom(dtype: str, B: int, H: int, Nq: int, Nk: int, d: int, bias: str = "none",
            grid=None, mask: str = "none", layout: str = "batched", images=None,
-           window=None, cfg_id: int = 900, key: str = "custom", kgrid=None) -> Workload:
+           window=None, cfg_id: int = 900, key: str = "custom", kgrid=None,
+           qkv: str = "same") -> Workload:
     """A workload of arbitrary shape for tests (same drawing recipe)."""
     return Workload(key, key, cfg_id, dtype, B=B, H=H, Nq=Nq, Nk=Nk, d=d, bias=bias,
                     grid=grid, kgrid=kgrid, mask=mask, layout=layout, images=images,
-                    window=window)
+                    window=window, qkv=qkv)
 
 
 def device_args(w: Workload, t: dict) -> dict:
@@ -191,4 +244,6 @@ def device_args(w: Workload, t: dict) -> dict:
         kw["mask"] = B.AdditiveMask(t["mask_add"])
     if w.layout == "image":
         kw["window"] = win
+    if w.qkv == "e4m3":
+        kw["qkv_descale"] = tuple(float(x) for x in t["descale"].to("cpu"))
     return kw
