@@ -48,6 +48,8 @@ PEAK_MFMA_TFLOPS = 2500.0      # dense bf16/fp16 MFMA
 PEAK_F32_TFLOPS = 157.3        # fp32 vector
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 ALL = ["C1", "C2", "C3", "C3i", "C4", "C4h", "C5s", "C5x"]
+# The Swin-T and SD workloads with q, k, v as 8-bit E4M3 codes (f16 compute).
+LOW_PRECISION = ["C2f8", "C5sf8", "C5xf8"]
 TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 2e-2}
 
 
@@ -175,6 +177,8 @@ def config_of(w):
         cfg["shift"] = list(w.window[4:])
     if w.grid:
         cfg["grid"] = list(w.grid)
+    if w.qkv != "same":
+        cfg["qkv"] = f"{w.qkv} codes, one scale per tensor; {w.dtype} compute and output"
     return cfg
 
 
@@ -221,13 +225,14 @@ def run_workload(torch, W, binding, w, K: int, warmup: int, settle_ms: float, no
     dev = torch.device("cuda:0")
     inp = W.make_inputs(w)
     base = {k: v.to(dev) for k, v in inp.items()}
+    out_dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + \
-        base["q"].numel() * base["q"].element_size()
+        base["q"].numel() * w.bytes_per_elem()
     n_sets = max(1, math.ceil(512e6 / set_bytes))
     sets = []
     for i in range(n_sets):
         s = {k: (v.clone() if k in ("q", "k", "v") else v) for k, v in base.items()}
-        s["out"] = torch.empty_like(base["q"])
+        s["out"] = torch.empty(base["q"].shape, dtype=out_dtype, device=dev)
         s["kw"] = dict(W.device_args(w, s), **(fwd_kw or {}))
         sets.append(s)
     del base
@@ -429,7 +434,8 @@ def main():
     ap.add_argument("--extra", default="all",
                     help="comma-separated workloads also timed in this run ('all' or 'none'; "
                          "C2p is C2 with 3 heads of a window per workgroup; C2b and C5sb are the "
-                         "backward passes of C2 and C5s)")
+                         "backward passes of C2 and C5s; C2f8, C5sf8, C5xf8 take q, k, v as "
+                         "E4M3 codes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle error checks")
     ap.add_argument("--check-units", type=int, default=16,
@@ -506,8 +512,8 @@ def main():
         line["copy_floor"] = copy_floor(torch, w.algorithmic_bytes, K, args.settle_ms)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
-    extra = [] if args.extra == "none" else (ALL + ["C2p", "C2b", "C5sb"] if args.extra == "all"
-                                             else args.extra.split(","))
+    extra = [] if args.extra == "none" else (ALL + ["C2p", "C2b", "C5sb"] + LOW_PRECISION
+                                             if args.extra == "all" else args.extra.split(","))
     if extra:
         line["workloads"] = {}
         for key in extra:

@@ -87,7 +87,10 @@ typedef enum { ATTN_LAYOUT_BATCHED = 0, ATTN_LAYOUT_IMAGE = 1 } attn_layout_t;
 /* A strided 4-D tensor [B, H, N, d]; the d stride is 1.
  * strides[] are in ELEMENTS for the B, H and N axes.  `data` must be 16-byte
  * aligned and every stride a multiple of 16 bytes (8 elements for f16/bf16,
- * 4 for f32): the kernels move rows in 16-byte pieces (ATTN_E_LAYOUT).      */
+ * 4 for f32): the kernels move rows in 16-byte pieces (ATTN_E_LAYOUT).
+ * Exception: q, k and v given as 8-bit codes (attn_options_t.qkv_format =
+ * ATTN_QKV_E4M3) need 8-byte alignment of `data` and strides that are
+ * multiples of 8 elements; they are moved in 8-byte pieces.                 */
 typedef struct {
   void* data;
   int64_t dims[4];
@@ -219,6 +222,23 @@ ATTN_API int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const at
                const attn_bias_desc_t* bias_desc, const attn_mask_desc_t* mask_desc,
                const attn_tensor_t* out, int32_t dtype);
 
+/* Storage format of q, k and v (attn_options_t.qkv_format).
+ *  DTYPE: elements of the call's dtype, like out and the tables.
+ *  E4M3:  one byte per element, the E4M3 format of the OCP 8-bit floating
+ *         point specification (sign, 4-bit exponent with bias 7, 3-bit
+ *         mantissa, subnormals, no infinities, S.1111.111 = NaN), each
+ *         tensor with one scale: the value of a code is code * scale.  The
+ *         attention is computed on those values exactly as on dtype inputs
+ *         (dtype must be F16 or BF16, the matrix-core compute and output
+ *         type).  The low-precision reading follows the pages' use of
+ *         quantized products whose quantization and dequantization are fused
+ *         into the neighbouring operators ("Training and inference
+ *         acceleration for large vision models", section 3; "Accelerating
+ *         Generative AI with PyTorch: Segment Anything, Fast", introduction,
+ *         GPU quantization): here the dequantization is fused into the
+ *         attention's loads.                                                 */
+typedef enum { ATTN_QKV_DTYPE = 0, ATTN_QKV_E4M3 = 1 } attn_qkv_format_t;
+
 /* Options of attn_fwd_opt / attn_check_opt.
  *  window_heads: for windows of at most 64 tokens in half precision (TABLE
  *    or no bias, SHIFT_REGIONS or no mask), how many heads of one window
@@ -230,11 +250,18 @@ ATTN_API int attn_check(const attn_tensor_t* q, const attn_tensor_t* k, const at
  *    sequence packing of windows into workgroups.  A value that does not
  *    divide H, a value above 4, or a call outside the short-sequence path
  *    with a value above 1 returns ATTN_E_UNSUPPORTED (negative: E_INVALID).
+ *  qkv_format: attn_qkv_format_t of q, k and v (0: the call's dtype).  With
+ *    ATTN_QKV_E4M3, q_descale, k_descale and v_descale are the three
+ *    tensors' scales (finite and > 0, else ATTN_E_INVALID); dtype F32 and
+ *    the RELPOS bias return ATTN_E_UNSUPPORTED, and so does window_heads
+ *    above 1.  Tables, dense bias/mask tensors and out keep the dtype.
  *  Zero-initialise the struct: fields added later keep 0 as "library's
  *  choice".                                                                  */
 typedef struct {
   int32_t window_heads;
-  int32_t reserved[7];
+  int32_t qkv_format;
+  float q_descale, k_descale, v_descale;
+  int32_t reserved[3];
 } attn_options_t;
 
 /* attn_fwd_opt / attn_check_opt: attn_fwd / attn_check with options (NULL:
@@ -323,7 +350,9 @@ ATTN_API const char* attn_strerror(int status);
 /* attn_version: library ABI version, (major << 16) | minor (1.2 added
  * attn_fwd_opt, attn_check_opt and the rh_rows, rw_rows fields of
  * attn_bias_desc_t, which grew from 80 to 88 bytes; 1.3 the backward:
- * attn_bwd, attn_bwd_check, attn_bwd_workspace_size).                        */
+ * attn_bwd, attn_bwd_check, attn_bwd_workspace_size; 1.4 8-bit q, k, v:
+ * qkv_format and the three scales in attn_options_t, whose size is
+ * unchanged).                                                                */
 ATTN_API int attn_version(void);
 
 #ifdef __cplusplus

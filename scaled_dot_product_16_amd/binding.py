@@ -24,6 +24,9 @@ STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_LAYOUT", 4: "E_UNSUPPORTED",
           6: "E_LAUNCH", 7: "E_INVALID"}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 LAYOUT_BATCHED, LAYOUT_IMAGE = 0, 1
+QKV_DTYPE, QKV_E4M3 = 0, 1
+# Torch dtypes accepted for 8-bit E4M3 q, k, v (the codes as bytes).
+E4M3_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 BIAS_NONE, BIAS_TABLE, BIAS_RELPOS, BIAS_ADDITIVE = 0, 1, 2, 3
 MASK_NONE, MASK_ADDITIVE, MASK_SHIFT_REGIONS = 0, 1, 2
 
@@ -52,7 +55,9 @@ class MaskDescC(ctypes.Structure):
 
 
 class OptionsC(ctypes.Structure):
-    _fields_ = [("window_heads", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("window_heads", ctypes.c_int32), ("qkv_format", ctypes.c_int32),
+                ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float),
+                ("v_descale", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
 
 
 class AttnError(RuntimeError):
@@ -247,37 +252,45 @@ def _check_extents(q, k, bias, mask, lay, window):
         raise ValueError(f"additive mask must end in [{nq}, {nk}]")
 
 
-def _marshal(q, k, v, out, bias, mask, layout, window):
+def _marshal(q, k, v, out, bias, mask, layout, window, e4m3: bool = False):
+    """Descriptors of a call.  The compute dtype is out's; q, k, v have it
+    too, or are E4M3 codes (uint8 or float8_e4m3fn) when ``e4m3``."""
     lay = {"batched": LAYOUT_BATCHED, "image": LAYOUT_IMAGE}[layout]
-    if q.dtype not in DTYPES:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    for name, t in (("k", k), ("v", v), ("out", out)):
-        if t.dtype != q.dtype:
-            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if out.dtype not in DTYPES:
+        raise TypeError(f"unsupported dtype {out.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if e4m3 and t.dtype not in E4M3_DTYPES:
+            raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), not {t.dtype}")
+        if not e4m3 and t.dtype != out.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, out has {out.dtype}")
     keep: list = []
     bd, md = _descs(bias, mask, lay, window, keep)
     for t in keep:
-        if t.dtype != q.dtype:
-            raise TypeError("bias/mask tensors must have the dtype of q")
+        if t.dtype != out.dtype:
+            raise TypeError("bias/mask tensors must have the compute dtype")
         if t.device != q.device:
             raise ValueError("bias/mask tensors must be on the device of q")
     _check_extents(q, k, bias, mask, lay, window)
     return (_tensor_c(q, lay), _tensor_c(k, lay), _tensor_c(v, lay), bd, md,
-            _tensor_c(out, lay), DTYPES[q.dtype], keep)
+            _tensor_c(out, lay), DTYPES[out.dtype], keep)
 
 
-def _options(window_heads: Optional[int]):
-    if window_heads is None:
+def _options(window_heads: Optional[int], qkv_descale=None):
+    if window_heads is None and qkv_descale is None:
         return None
     o = OptionsC()
-    o.window_heads = int(window_heads)
+    o.window_heads = int(window_heads or 0)
+    if qkv_descale is not None:
+        o.qkv_format = QKV_E4M3
+        o.q_descale, o.k_descale, o.v_descale = (float(x) for x in qkv_descale)
     return ctypes.byref(o)
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         out: Optional[torch.Tensor] = None, layout: str = "batched",
         window: Optional[Window] = None, stream=None,
-        window_heads: Optional[int] = None) -> torch.Tensor:
+        window_heads: Optional[int] = None, qkv_descale=None,
+        out_dtype: torch.dtype = torch.float16) -> torch.Tensor:
     """O = softmax(QK^T/sqrt(d) + bias + mask) V on the GPU via libattn.
 
     q: [B, H, Nq, d], k, v: [B, H, Nk, d] CUDA (HIP) tensors, last stride 1.
@@ -291,18 +304,24 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
     one, the kernel is ordered after the work already queued on the current
     stream (where this function makes its temporaries), and those
     temporaries stay allocated until the kernel's stream has run it.
+
+    ``qkv_descale`` = (q scale, k scale, v scale): q, k and v are E4M3 codes
+    (uint8 or float8_e4m3fn tensors) standing for code * scale; the compute
+    and output dtype is then ``out``'s, or ``out_dtype`` (f16 or bf16) when
+    ``out`` is allocated here, and the tables must have it.
     """
     h = lib()
+    e4m3 = qkv_descale is not None
     allocated = out is None
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        out = torch.empty(q.shape, dtype=out_dtype if e4m3 else q.dtype, device=q.device)
     if q.numel() == 0 and k.dim() == 4 and k.shape[2] > 0:
         # No query rows (or no batch items or heads): nothing to compute, and
         # the library, which takes only non-empty tensors, is not called.
         # Zero keys with queries present stay an error (a softmax over no
         # keys is undefined): the library rejects them.
         return out
-    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
+    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window, e4m3)
     cur = torch.cuda.current_stream(q.device)
     if stream is None:
         s_obj = cur
@@ -321,7 +340,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         for t in keep + ([out] if allocated else []):
             t.record_stream(s_obj)
     st = h.attn_fwd_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
-                        ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads),
+                        ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads, qkv_descale),
                         ctypes.c_void_p(s_obj.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, h.attn_strerror(st).decode())
@@ -330,17 +349,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
 
 
 def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
-          window: Optional[Window] = None, window_heads: Optional[int] = None) -> int:
+          window: Optional[Window] = None, window_heads: Optional[int] = None,
+          qkv_descale=None, out_dtype: torch.dtype = torch.float16) -> int:
     """Status attn_fwd would return for these arguments (no GPU needed)."""
     h = lib()
+    e4m3 = qkv_descale is not None
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window)
-    if window_heads is None:
+        out = torch.empty(q.shape, dtype=out_dtype if e4m3 else q.dtype, device=q.device)
+    qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window, e4m3)
+    opts = _options(window_heads, qkv_descale)
+    if opts is None:
         return h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
                             ctypes.byref(md), ctypes.byref(oc), dt)
     return h.attn_check_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
-                            ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads))
+                            ctypes.byref(md), ctypes.byref(oc), dt, opts)
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, bias=None, mask=None,

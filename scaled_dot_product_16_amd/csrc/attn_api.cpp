@@ -31,22 +31,25 @@ void extent(const attn_tensor_t* t, int es, uintptr_t* lo, uintptr_t* hi) {
   *hi = (uintptr_t)t->data + (uintptr_t)((last + 1) * es);
 }
 
-bool overlaps(const attn_tensor_t* a, const attn_tensor_t* b, int es) {
+bool overlaps(const attn_tensor_t* a, int ea, const attn_tensor_t* b, int eb) {
   uintptr_t alo, ahi, blo, bhi;
-  extent(a, es, &alo, &ahi);
-  extent(b, es, &blo, &bhi);
+  extent(a, ea, &alo, &ahi);
+  extent(b, eb, &blo, &bhi);
   return alo < bhi && blo < ahi;
 }
 
-int check_tensor(const attn_tensor_t* t, int es) {
+bool overlaps(const attn_tensor_t* a, const attn_tensor_t* b, int es) { return overlaps(a, es, b, es); }
+
+// `align`: bytes the kernels move per row piece (16; 8 for 8-bit q, k, v).
+int check_tensor(const attn_tensor_t* t, int es, int align = 16) {
   if (!t->data) return ATTN_E_NULL;
   for (int i = 0; i < 4; ++i)
     if (t->dims[i] < 1 || t->dims[i] > (int64_t(1) << 30)) return ATTN_E_SHAPE;
   for (int i = 0; i < 3; ++i)
     if (t->strides[i] < 0) return ATTN_E_LAYOUT;
-  // Vector loads move 16 bytes: base and every row start must be 16-byte aligned.
-  const int64_t vec = 16 / es;
-  if ((uintptr_t)t->data % 16) return ATTN_E_LAYOUT;
+  // Vector loads move `align` bytes: base and every row start must be aligned to it.
+  const int64_t vec = align / es;
+  if ((uintptr_t)t->data % align) return ATTN_E_LAYOUT;
   for (int i = 0; i < 3; ++i)
     if (t->strides[i] % vec) return ATTN_E_LAYOUT;
   if (t->layout != ATTN_LAYOUT_BATCHED && t->layout != ATTN_LAYOUT_IMAGE) return ATTN_E_INVALID;
@@ -74,10 +77,24 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   const attn_mask_desc_t* mask = (const attn_mask_desc_t*)maskv;
   if (!q || !k || !v || !o || !a) return ATTN_E_NULL;
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  // Options that change how q, k and v are read come first.
+  const attn_options_t* opt = (const attn_options_t*)optv;
+  const int32_t qkv_format = opt ? opt->qkv_format : ATTN_QKV_DTYPE;
+  if (qkv_format != ATTN_QKV_DTYPE && qkv_format != ATTN_QKV_E4M3) return ATTN_E_INVALID;
+  const bool f8 = qkv_format == ATTN_QKV_E4M3;
+  if (f8) {
+    const float sc[3] = {opt->q_descale, opt->k_descale, opt->v_descale};
+    for (float x : sc)
+      if (!(x > 0.f) || !isfinite(x)) return ATTN_E_INVALID;
+    if (dtype == ATTN_F32) return ATTN_E_UNSUPPORTED;
+  }
+  if (opt && opt->window_heads < 0) return ATTN_E_INVALID;
   const int es = elem_size(dtype);
+  const int ies = f8 ? 1 : es;  // bytes of a q, k or v element
+  const int ialign = f8 ? 8 : 16;
   int st;
-  if ((st = check_tensor(q, es)) || (st = check_tensor(k, es)) || (st = check_tensor(v, es)) ||
-      (st = check_tensor(o, es)))
+  if ((st = check_tensor(q, ies, ialign)) || (st = check_tensor(k, ies, ialign)) ||
+      (st = check_tensor(v, ies, ialign)) || (st = check_tensor(o, es)))
     return st;
 
   // Shapes: [B, H, N, d] with shared B, H, d; k and v share N; out matches q.
@@ -110,6 +127,13 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   a->H = (int32_t)H;
   a->D = (int32_t)D;
   a->scale = (float)(1.0 / sqrt((double)D));
+  if (f8) {
+    // q and k scales multiply every score, so they join the softmax scale.
+    a->f8 = 1;
+    a->scale = (float)((double)opt->q_descale * (double)opt->k_descale / sqrt((double)D));
+    a->v_descale = opt->v_descale;
+    if (!(a->scale > 0.f) || !isfinite(a->scale)) return ATTN_E_INVALID;
+  }
 
   // Window geometry: needed by IMAGE layout and by SHIFT_REGIONS.
   const bool need_win = layout == ATTN_LAYOUT_IMAGE || mask_kind == ATTN_MASK_SHIFT_REGIONS;
@@ -225,14 +249,9 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
     if ((t->dims[2] - 1) * t->strides[2] + t->dims[3] >= (int64_t(1) << slice_bits)) return ATTN_E_UNSUPPORTED;
 
   // out must not overlap the inputs it is computed from.
-  if (overlaps(o, q, es) || overlaps(o, k, es) || overlaps(o, v, es)) return ATTN_E_ALIAS;
+  if (overlaps(o, es, q, ies) || overlaps(o, es, k, ies) || overlaps(o, es, v, ies)) return ATTN_E_ALIAS;
 
-  // Options.
-  const attn_options_t* opt = (const attn_options_t*)optv;
-  if (opt) {
-    if (opt->window_heads < 0) return ATTN_E_INVALID;
-    a->win_heads = opt->window_heads;
-  }
+  if (opt) a->win_heads = opt->window_heads;
 
   // The kernel the call takes must fit one CU's LDS (and the grid the
   // launch limit); a requested form must exist for the call.
@@ -396,6 +415,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return (1 << 16) | 3; }
+int attn_version(void) { return (1 << 16) | 4; }
 
 }  // extern "C"

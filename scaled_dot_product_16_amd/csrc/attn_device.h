@@ -85,6 +85,25 @@ __device__ __forceinline__ float load_elem<F32E>(const void* p, int64_t i) {
   return ((const float*)p)[i];
 }
 
+// Eight E4M3 codes (one per byte, in order) -> the eight elements of E they
+// encode.  Every E4M3 value is exact in f16 and in bf16, so the widening is
+// exact; gfx950 converts the OCP E4M3 format (bias 7, S.1111.111 = NaN) with
+// v_cvt_scalef32_pk_{f16,bf16}_fp8, two codes per instruction (scale 1).
+template <class E>
+__device__ __forceinline__ u32x4 widen_e4m3(u32x2 w) {
+  if constexpr (std::is_same<E, F16>::value) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.f, true))};
+  } else {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true))};
+  }
+}
+
 // Dot product of 4 consecutive elements of two arrays (8-byte / 16-byte loads).
 template <class E>
 __device__ __forceinline__ float dot4(const void* x, int64_t i, const void* y, int64_t j) {

@@ -29,14 +29,14 @@ int launch_grid(K kernel, int threads, const Plan& p, const AttnArgs& a, hipStre
 }
 
 // One workgroup per (window, head) unit.
-template <class E, int DK, int BIAS, bool MASK>
+template <class E, int DK, int BIAS, bool MASK, bool F8 = false>
 int launch_win(const Plan& p, AttnArgs a, hipStream_t s) {
   a.n_qtiles = 1;
   a.fd_qt = make_fastdiv(1);
   a.n_blocks = (int)p.blocks;
-  auto kern = !MASK ? attn_fwd_win<E, DK, BIAS, ATTN_MASK_NONE>
-              : a.mask_kind == ATTN_MASK_ADDITIVE ? attn_fwd_win<E, DK, BIAS, ATTN_MASK_ADDITIVE>
-                                                  : attn_fwd_win<E, DK, BIAS, ATTN_MASK_SHIFT_REGIONS>;
+  auto kern = !MASK ? attn_fwd_win<E, DK, BIAS, ATTN_MASK_NONE, F8>
+              : a.mask_kind == ATTN_MASK_ADDITIVE ? attn_fwd_win<E, DK, BIAS, ATTN_MASK_ADDITIVE, F8>
+                                                  : attn_fwd_win<E, DK, BIAS, ATTN_MASK_SHIFT_REGIONS, F8>;
   return launch_grid(kern, kWinWaves * 64, p, a, s);
 }
 
@@ -67,7 +67,7 @@ using Elem = F16;
 
 // The tiled kernel in the form and instance the plan names (the ping-pong
 // form, NW = 8 with the row form, exists for the batched layout only).
-template <int BIAS, bool MASK, int RMODE, int WPE, int NW = 4>
+template <int BIAS, bool MASK, int RMODE, int WPE, int NW = 4, bool F8 = false>
 int launch_mfma(const Plan& p, const AttnArgs& a, hipStream_t s) {
   constexpr int D = INST_D;
   using C = MfmaCfg<D, NW, kNQB>;
@@ -78,9 +78,31 @@ int launch_mfma(const Plan& p, const AttnArgs& a, hipStream_t s) {
   constexpr bool kPingPong = NW == 8 && RMODE != kTwoTiles;
   if constexpr (!kPingPong) {
     if (a.image)
-      return launch_grid(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, true>, C::NT, p, t, s);
+      return launch_grid(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, true, F8>, C::NT, p, t, s);
   }
-  return launch_grid(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, false>, C::NT, p, t, s);
+  return launch_grid(attn_fwd_mfma<Elem, D, NW, kNQB, BIAS, MASK, RMODE, WPE, false, F8>, C::NT, p, t, s);
+}
+
+// Waves per SIMD the register allocation of the tiled kernel targets: the
+// most that still fit the tile state without spilling (checked per head dim).
+constexpr int kWpeNone = INST_D <= 32 ? 4 : (INST_D <= 40 ? 3 : 2);
+constexpr int kWpeRelpos = INST_D <= 40 ? 3 : 2;
+constexpr int kWpeAug = INST_D <= 64 ? 3 : 2;
+
+// 8-bit (E4M3) q, k, v: the window form or the tiled forms without relative
+// position, with the loads widening the codes.
+template <int BIAS, bool MASK>
+int launch_f8(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  constexpr int D = INST_D;
+  if (p.kernel == kKernWin) return launch_win<Elem, D, BIAS, MASK, true>(p, a, s);
+  if (p.kernel != kKernMfma) return ATTN_E_UNSUPPORTED;
+  if constexpr (BIAS == ATTN_BIAS_NONE && !MASK) {
+    if (p.rmode == kTwoTiles)
+      return launch_mfma<BIAS, MASK, kTwoTiles, two_tile_wpe<D>(), two_tile_nw<D>(), true>(p, a, s);
+  }
+  if (p.rmode != kRelTables) return ATTN_E_UNSUPPORTED;
+  constexpr int wpe = (BIAS == ATTN_BIAS_NONE && !MASK) ? kWpeNone : 1;
+  return launch_mfma<BIAS, MASK, kRelTables, wpe, 4, true>(p, a, s);
 }
 
 // HG heads of a window in one workgroup (the packed short-sequence form).
@@ -111,13 +133,10 @@ int launch_one(const AttnArgs& a, hipStream_t s) {
     }
   }
   if constexpr (BIAS != ATTN_BIAS_RELPOS) {
+    if (a.f8) return launch_f8<BIAS, MASK>(p, a, s);
     if (p.kernel == kKernWin) return launch_win<Elem, D, BIAS, MASK>(p, a, s);
   }
-  // Waves per SIMD the register allocation targets: the most that still
-  // fit the tile state without spilling (checked per head dim).
-  constexpr int kWpeNone = D <= 32 ? 4 : (D <= 40 ? 3 : 2);
-  constexpr int kWpeRelpos = D <= 40 ? 3 : 2;
-  constexpr int kWpeAug = D <= 64 ? 3 : 2;
+  if (a.f8) return ATTN_E_UNSUPPORTED;
   if constexpr (BIAS == ATTN_BIAS_RELPOS && !MASK) {
     if (p.rmode == kRelRow64)
       return p.nw == 8 ? launch_mfma<BIAS, false, kRelRow64, 2, 8>(p, a, s)

@@ -70,6 +70,8 @@ struct AttnArgs {
   int32_t n_hgrp;    // head groups per batch item (packed window kernel)
   FastDiv fd_hgrp;
   int32_t win_heads; // requested heads per workgroup of the window path (0: library's choice)
+  int32_t f8;        // q, k, v are E4M3 codes (their q and k scales are folded into `scale`)
+  float v_descale;   // E4M3 inputs: the scale of v, applied with the row-sum division
 };
 
 // A validated backward call: the forward call (its `o` is the output

@@ -123,8 +123,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #endif
 // IMG: built with the image-layout addressing (the batched-layout instance
 // leaves it out, which keeps the key loop within fewer registers).
-template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int WPE, bool IMG>
+template <class E, int D, int NW, int NQB, int BIAS, bool MASK, int RMODE, int WPE, bool IMG,
+          bool F8 = false>
 __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(AttnArgs a) {
+  // F8: q, k, v are E4M3 codes, loaded as 8-byte pieces per 8 elements and
+  // widened exactly to E (Q in registers, K/V on their way into LDS); the q
+  // and k scales ride in a.scale, the v scale is applied with the row-sum
+  // division.  Built for the forms without relative position.
+  static_assert(!F8 || (BIAS != ATTN_BIAS_RELPOS && (RMODE == kRelTables || RMODE == kTwoTiles)),
+                "8-bit inputs are built for the forms without relative position");
+  constexpr int IES = F8 ? 1 : 2;                     // bytes of a q, k or v element
+  using LdT = std::conditional_t<F8, u32x2, u32x4>;  // one 8-element chunk as loaded
   constexpr bool RFAST = RMODE == kRelRow64;
   constexpr bool RAUG = RMODE == kRelAug;
   constexpr bool PP = NW == 8 && RMODE != kTwoTiles;  // ping-pong schedule of two wave groups
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 
   // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
   u32x4 qf[NQB][KCHT];
-  const uint16_t* qbase = (const uint16_t*)a.q + tok_base(a, a.q_sb, a.q_sh, b, h);
+  const char* qbase = (const char*)a.q + IES * tok_base(a, a.q_sb, a.q_sh, b, h);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
@@ -161,7 +170,11 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
       // (a padding token of the image layout is a zero query)
-      qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + off + d0) : u32x4{0, 0, 0, 0};
+      if constexpr (F8)
+        qf[qb][dc] = d0 < D && off != kPadTok ? widen_e4m3<E>(*(const u32x2*)(qbase + off + d0))
+                                              : u32x4{0, 0, 0, 0};
+      else
+        qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -172,9 +185,9 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // memory access.  Image layout: per-key offsets through the window map,
   // with keys past Nk clamped to Nk-1.  Either way those keys' scores are
   // set to -inf before the softmax.
-  const uint16_t* kbase = (const uint16_t*)a.k + tok_base(a, a.k_sb, a.k_sh, b, h);
-  const uint16_t* vbase = (const uint16_t*)a.v + tok_base(a, a.v_sb, a.v_sh, b, h);
-  u32x4 kreg[CPT], vreg[CPT];
+  const char* kbase = (const char*)a.k + IES * tok_base(a, a.k_sb, a.k_sh, b, h);
+  const char* vbase = (const char*)a.v + IES * tok_base(a, a.v_sb, a.v_sh, b, h);
+  LdT kreg[CPT], vreg[CPT];
   auto crow = [&](int c) { const int ch = tid + c * NT; return ch < NCH ? ch / RCH : (1 << 29); };
   auto ccol = [&](int c) { return ((tid + c * NT) % RCH) * 8; };
   uint32_t koff[CPT], voff[CPT];  // batched layout: chunk byte offsets inside a tile
@@ -182,8 +195,8 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   for (int c = 0; c < CPT; ++c) {
     const int r = crow(c);
     const int64_t ko = (int64_t)r * a.k_sn + ccol(c), vo = (int64_t)r * a.v_sn + ccol(c);
-    koff[c] = r < BN && 2 * ko < 0xFFFFFFF0ll ? (uint32_t)(2 * ko) : 0xFFFFFFF0u;
-    voff[c] = r < BN && 2 * vo < 0xFFFFFFF0ll ? (uint32_t)(2 * vo) : 0xFFFFFFF0u;
+    koff[c] = r < BN && IES * ko < 0xFFFFFFF0ll ? (uint32_t)(IES * ko) : 0xFFFFFFF0u;
+    voff[c] = r < BN && IES * vo < 0xFFFFFFF0ll ? (uint32_t)(IES * vo) : 0xFFFFFFF0u;
   }
   // Image layout: key j's window-map pixel (kPadTok for padding), filled
   // once below; the tile loads after the first barrier read it instead of
@@ -192,14 +205,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   if constexpr (IMG) {
     for (int j = tid; j < a.Nk; j += NT) kpix[j] = tok_row(a, 1, b, j);
   }
-  auto load_rows = [&](const uint16_t* base, int64_t sn, const uint32_t* off, int t, u32x4* reg,
+  auto buf_load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off) -> LdT {
+    if constexpr (F8) return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  };
+  auto load_rows = [&](const char* base, int64_t sn, const uint32_t* off, int t, LdT* reg,
                        bool direct = false) {
     if (!a.image) {
       const int64_t k0 = (int64_t)t * BN;
-      const uint32_t nrec = (uint32_t)(2 * ((a.Nk - 1 - k0) * sn + D));
-      const auto rs = buffer_rsrc(base + k0 * sn, nrec);
+      const uint32_t nrec = (uint32_t)(IES * ((a.Nk - 1 - k0) * sn + D));
+      const auto rs = buffer_rsrc(base + IES * k0 * sn, nrec);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], 0, 0);
+      for (int c = 0; c < CPT; ++c) reg[c] = buf_load(rs, off[c]);
     } else {
       // Padding tokens read at a byte offset past the resource's range,
       // which gives zero (in-slice offsets stay below 2^30 bytes).
@@ -214,17 +231,20 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           const uint32_t px = kpix[key];
           r = px == kPadTok ? kPadTok : px * (uint32_t)sn;
         }
-        reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, r == kPadTok ? 0xFFFFFFF0u : 2 * (r + (uint32_t)ccol(c)),
-                                                       0, 0);
+        reg[c] = buf_load(rs, r == kPadTok ? 0xFFFFFFF0u : IES * (r + (uint32_t)ccol(c)));
       }
     }
   };
   auto load_k = [&](int t) { load_rows(kbase, a.k_sn, koff, t, kreg); };
   auto load_v = [&](int t) { load_rows(vbase, a.v_sn, voff, t, vreg); };
-  auto store_k_from = [&](int st, int t, const u32x4* src) {
+  auto widen = [&](LdT x) -> u32x4 {
+    if constexpr (F8) return widen_e4m3<E>(x);
+    else return x;
+  };
+  auto store_k_from = [&](int st, int t, const LdT* src) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = src[c];
+      if (crow(c) < BN) *(u32x4*)&Ks[st * C::K_ELEMS + crow(c) * KROW + ccol(c)] = widen(src[c]);
     if constexpr (RAUG) {
       // One-hot chunk of key row `row`: ones at columns kh and gh + kw.
       for (int i = tid; i < BN * 4; i += NT) {
@@ -244,10 +264,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       }
     }
   };
-  auto store_v_from = [&](int st, const u32x4* src) {
+  auto store_v_from = [&](int st, const LdT* src) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = src[c];
+      if (crow(c) < BN) *(u32x4*)&Vs[st * C::V_ELEMS + crow(c) * VROW + ccol(c)] = widen(src[c]);
   };
   auto store_k = [&](int st, int t) { store_k_from(st, t, kreg); };
   auto store_v = [&](int st) { store_v_from(st, vreg); };
@@ -312,7 +332,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   load_rows(vbase, a.v_sn, voff, 0, vreg, true);
   constexpr bool TWO = RMODE == kTwoTiles;
   static_assert(!TWO || (!PP && BIAS == ATTN_BIAS_NONE && !MASK), "two-tile form: no bias, no mask");
-  u32x4 kreg1[TWO ? CPT : 1], vreg1[TWO ? CPT : 1];
+  LdT kreg1[TWO ? CPT : 1], vreg1[TWO ? CPT : 1];
   if constexpr (TWO) {
     load_rows(kbase, a.k_sn, koff, 1, kreg1, true);
     load_rows(vbase, a.v_sn, voff, 1, vreg1, true);
@@ -878,7 +898,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         float lsum;
         if constexpr (C::ONES) lsum = __shfl(o[LB < CB ? LB : 0][qb][LR], LG * 16 + l16);
         else lsum = sum_across_groups(l[qb]);
-        const float inv = 1.f / lsum;
+        const float inv = (F8 ? a.v_descale : 1.f) / lsum;
         const int r = qb * 16 + (kLean ? lane_id_here() & 15 : l16);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -907,7 +927,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     float lsum;
     if constexpr (C::ONES) lsum = __shfl(o[LB < CB ? LB : 0][qb][LR], LG * 16 + l16);
     else lsum = sum_across_groups(l[qb]);
-    const float inv = 1.f / lsum;
+    const float inv = (F8 ? a.v_descale : 1.f) / lsum;
     const int qi = q0 + wq0 + qb * 16 + (kLean ? lane_id_here() & 15 : l16);
     const uint32_t off = qi < a.Nq ? tok_row(a, a.o_sn, b, qi) : kPadTok;
     if (off != kPadTok) {  // rows past Nq and padding tokens are not stored

@@ -281,6 +281,12 @@ template <int D>
 inline Plan plan_half(const AttnArgs& a) {
   Plan p{};
   const bool mask = a.mask_kind != ATTN_MASK_NONE;
+  // 8-bit inputs: built for the one-head window form and the tiled forms
+  // without relative position.
+  if (a.f8 && (a.bias_kind == ATTN_BIAS_RELPOS || a.win_heads > 1)) {
+    p.kernel = -1;
+    return p;
+  }
   if (a.bias_kind != ATTN_BIAS_RELPOS && a.Nq <= 64 && a.Nk <= 64) {
     p.nw = kWinWaves;
     // Heads per workgroup: one unless the caller asks for more (one head

@@ -72,9 +72,15 @@ __device__ __forceinline__ int win_region(const AttnArgs& a, const WinPos& p, in
 //
 // E = F32E selects the fp32 form (WinCfgF32): same structure, with
 // v_mfma_f32_16x16x4_f32 products and fp32 tiles.
-template <class E, int D, int BIAS, int MASKK>
+//
+// F8: q, k and v are E4M3 codes (half precision only).  They are loaded as
+// 8-byte pieces, widened exactly to E in registers and then take the same
+// path; the q and k scales ride in a.scale and the v scale is applied with
+// the row-sum division.
+template <class E, int D, int BIAS, int MASKK, bool F8 = false>
 __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
   constexpr bool F32 = std::is_same<E, F32E>::value;
+  static_assert(!(F8 && F32), "8-bit inputs are widened to a half-precision type");
   using C = WinCfg<F32 ? 32 : D>;
   using CF = WinCfgF32<F32 ? D : 32>;
   constexpr int NT = C::NT, KCH = C::KCH, CB = F32 ? CF::CB : C::CB, KROW = C::KROW, VROW = C::VROW,
@@ -118,17 +124,19 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     return win_tok_pix(a, pos, ty, tx);
   };
   constexpr int ES = F32 ? 4 : 2;  // element bytes
-  const char* qp = (const char*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh) * ES;
-  const char* kp = (const char*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh) * ES;
-  const char* vp = (const char*)a.v + ((int64_t)bimg * a.v_sb + (int64_t)h * a.v_sh) * ES;
+  constexpr int IES = F8 ? 1 : ES;  // element bytes of q, k, v
+  const char* qp = (const char*)a.q + ((int64_t)bimg * a.q_sb + (int64_t)h * a.q_sh) * IES;
+  const char* kp = (const char*)a.k + ((int64_t)bimg * a.k_sb + (int64_t)h * a.k_sh) * IES;
+  const char* vp = (const char*)a.v + ((int64_t)bimg * a.v_sb + (int64_t)h * a.v_sh) * IES;
   char* op = (char*)a.o + ((int64_t)bimg * a.o_sb + (int64_t)h * a.o_sh) * ES;
+  using LdT = std::conditional_t<F8, u32x2, u32x4>;  // one 8-element chunk as loaded
 
   // Global loads first.  Token rows past N are clamped to the last token, so
   // every load is unconditional; those keys start from -inf below, so their
   // probabilities are exactly zero and their finite values never reach O.
   constexpr int FCH = F32 ? 64 * CF::QC : 1;          // fp32: 16-byte chunks of a tile (QC per row)
   constexpr int FCPT = (FCH + NT - 1) / NT;
-  u32x4 kreg[F32 ? FCPT : CPT], vreg[F32 ? FCPT : CPT];
+  LdT kreg[F32 ? FCPT : CPT], vreg[F32 ? FCPT : CPT];
   if constexpr (F32) {
 #pragma unroll
     for (int c = 0; c < FCPT; ++c) {
@@ -150,9 +158,9 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
       const uint32_t col = (uint32_t)((ch % RCH) * 8);
       // Every q, k and v byte is read by exactly one workgroup: streaming
       // (non-temporal) loads, measured faster for the Swin window shapes.
-      kreg[c] = __builtin_nontemporal_load((const u32x4*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * 2));
-      vreg[c] = __builtin_nontemporal_load((const u32x4*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * 2));
-      if (pix0 == kPadTok) kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};  // padding token
+      kreg[c] = __builtin_nontemporal_load((const LdT*)(kp + (size_t)(pix * (uint32_t)a.k_sn + col) * IES));
+      vreg[c] = __builtin_nontemporal_load((const LdT*)(vp + (size_t)(pix * (uint32_t)a.v_sn + col) * IES));
+      if (pix0 == kPadTok) kreg[c] = vreg[c] = LdT{};  // padding token (code 0 is +0 too)
     }
   }
   const int q_tok = min(wave * 16 + l16, N - 1);
@@ -172,8 +180,12 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
-      qf[dc] = d0 < D && !q_pad ? __builtin_nontemporal_load((const u32x4*)(qp + (size_t)(q_off + d0) * 2))
-                                : u32x4{0, 0, 0, 0};
+      if constexpr (F8)
+        qf[dc] = d0 < D && !q_pad ? widen_e4m3<E>(__builtin_nontemporal_load((const u32x2*)(qp + q_off + d0)))
+                                  : u32x4{0, 0, 0, 0};
+      else
+        qf[dc] = d0 < D && !q_pad ? __builtin_nontemporal_load((const u32x4*)(qp + (size_t)(q_off + d0) * 2))
+                                  : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -231,8 +243,13 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * NT;
       if (ch < NCH) {
-        *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = kreg[c];
-        *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = vreg[c];
+        if constexpr (F8) {
+          *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = widen_e4m3<E>(kreg[c]);
+          *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = widen_e4m3<E>(vreg[c]);
+        } else {
+          *(u32x4*)&Ks[(ch / RCH) * KROW + (ch % RCH) * 8] = kreg[c];
+          *(u32x4*)&Vs[(ch / RCH) * VROW + (ch % RCH) * 8] = vreg[c];
+        }
       }
     }
   }
@@ -356,7 +373,8 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
       }
   }
 
-  const float inv = F32 ? 1.f / sum_across_groups(ps) : __builtin_amdgcn_rcpf(sum_across_groups(ps));
+  float inv = F32 ? 1.f / sum_across_groups(ps) : __builtin_amdgcn_rcpf(sum_across_groups(ps));
+  if constexpr (F8) inv *= a.v_descale;
   if (wave * 16 + l16 < N && !q_pad) {
     // Query row wave*16 + l16 is q_tok here, so its pixel is q_pix.
     const uint32_t off = q_pix * (uint32_t)a.o_sn;

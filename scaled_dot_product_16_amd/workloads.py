@@ -245,5 +245,8 @@ def device_args(w: Workload, t: dict) -> dict:
     if w.layout == "image":
         kw["window"] = win
     if w.qkv == "e4m3":
+        import torch
+
         kw["qkv_descale"] = tuple(float(x) for x in t["descale"].to("cpu"))
+        kw["out_dtype"] = {F16: torch.float16, BF16: torch.bfloat16}[w.dtype]
     return kw

@@ -44,13 +44,16 @@ def test_struct_layout_matches_header(lib):
     assert ctypes.sizeof(B.BiasDescC) == 4 * 3 + 4 + 8 * 4 + 8 + 16 + 8 + 8
     assert ctypes.sizeof(B.MaskDescC) == 8 + 8 + 8 + 16 + 24 + 4 + 4
     assert ctypes.sizeof(B.OptionsC) == 32
+    assert [B.OptionsC.__dict__[f].offset for f in ("window_heads", "qkv_format", "q_descale",
+                                                   "k_descale", "v_descale", "reserved")] == \
+        [0, 4, 8, 12, 16, 20]
 
 
 def test_strerror_and_version(lib):
     for st in range(8):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(99) == b"unknown status"
-    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 3
+    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 4
 
 
 def t(*shape, dtype=torch.float16):
@@ -334,3 +337,69 @@ def test_backward_validation(lib):
                             ctypes.byref(bd3), ctypes.byref(md3), ctypes.byref(d1), ctypes.byref(d2),
                             ctypes.byref(d3), None, dt3, ctypes.c_void_p(wsl.data_ptr()), 1 << 20) == 4
     del keep, keep2, keep3
+
+
+def test_e4m3_inputs_validation(lib):
+    # q, k, v as 8-bit E4M3 codes with one scale each (options.qkv_format);
+    # the compute and output dtype is the call's dtype (f16 or bf16).
+    def q8(*shape):
+        return torch.zeros(*shape, dtype=torch.uint8)
+    sc = (0.01, 0.02, 0.03)
+    geom = B.Window(56, 56, 7, 7, 3, 3)
+    qi = q8(2, 3, 56 * 56, 32)
+    tab = B.TableBias(t(169, 3), (7, 7))
+    # The Swin-T shifted windows, image layout.
+    assert B.check(qi, qi.clone(), qi.clone(), bias=tab, mask=B.ShiftMask(geom), layout="image",
+                   qkv_descale=sc) == 0
+    # SD self- and cross-attention, d = 40: rows of 40 bytes (8-byte aligned).
+    qs = q8(2, 8, 4096, 40)
+    assert B.check(qs, qs.clone(), qs.clone(), qkv_descale=sc) == 0
+    kx = q8(2, 8, 77, 40)
+    assert B.check(qs, kx, kx.clone(), qkv_descale=sc) == 0
+    assert B.check(qs, kx, kx.clone(), qkv_descale=sc, out_dtype=torch.bfloat16) == 0
+    # float8_e4m3fn tensors are taken as the same codes.
+    qe = qs.view(torch.float8_e4m3fn)
+    assert B.check(qe, qe.clone(), qe.clone(), qkv_descale=sc) == 0
+    # Scales must be finite and positive.
+    for bad in [(0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, float("nan")), (float("inf"), 1.0, 1.0)]:
+        assert B.check(qs, qs.clone(), qs.clone(), qkv_descale=bad) == 7, bad
+    # No fp32 compute, no relative position, no packed windows with 8-bit inputs.
+    assert B.check(qs, qs.clone(), qs.clone(), qkv_descale=sc, out_dtype=torch.float32) == 4
+    g = q8(1, 2, 196, 64)
+    rel = B.RelposBias(t(27, 64), t(27, 64), (14, 14))
+    assert B.check(g, g.clone(), g.clone(), bias=rel, qkv_descale=sc) == 4
+    w = q8(4, 3, 49, 32)
+    assert B.check(w, w.clone(), w.clone(), bias=tab, qkv_descale=sc) == 0
+    assert B.check(w, w.clone(), w.clone(), bias=tab, qkv_descale=sc, window_heads=3) == 4
+    # 8-byte alignment: a stride of 8 elements is fine, 4 is not; a base
+    # pointer 8 bytes past a 16-byte boundary is fine, 4 bytes is not.
+    buf = q8(2 * 8 * 77 * 48 + 16)
+    k48 = buf[:2 * 8 * 77 * 48].view(2, 8, 77, 48)[..., :40]
+    assert B.check(qs, k48, k48, qkv_descale=sc) == 0
+    k44 = buf[:2 * 8 * 77 * 44].view(2, 8, 77, 44)[..., :40]
+    assert B.check(qs, k44, k44, qkv_descale=sc) == 3
+    base = q8(2 * 8 * 77 * 40 + 64)
+    off = (-base.data_ptr()) % 16
+    k_plus8 = base[off + 8:off + 8 + 2 * 8 * 77 * 40].view(2, 8, 77, 40)
+    assert B.check(qs, k_plus8, k_plus8.clone(), qkv_descale=sc) == 0
+    k_plus4 = base[off + 4:off + 4 + 2 * 8 * 77 * 40].view(2, 8, 77, 40)
+    assert B.check(qs, k_plus4, kx, qkv_descale=sc) == 3
+    # An unknown format is an invalid field; dtype tensors with a format of
+    # codes (or codes without it) are refused by the binding.
+    o = B.OptionsC()
+    o.qkv_format = 2
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(qs, qs, qs, t(2, 8, 4096, 40), None, None, "batched",
+                                                 None, True)
+    assert lib.attn_check_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                              ctypes.byref(md), ctypes.byref(oc), dt, ctypes.byref(o)) == 7
+    with pytest.raises(TypeError):
+        B.check(t(2, 8, 4096, 40), qs, qs, qkv_descale=sc)
+    with pytest.raises(TypeError):
+        B.check(qs, qs.clone(), qs.clone())
+    # out may not overlap the codes: their extent is counted in bytes.
+    raw = torch.zeros(2 * 8 * 4096 * 40 * 3, dtype=torch.uint8)
+    qa = raw[:2 * 8 * 4096 * 40].view(2, 8, 4096, 40)
+    oa = raw.view(torch.float16)[:2 * 8 * 4096 * 40].view(2, 8, 4096, 40)
+    assert B.check(qa, qs, qs.clone(), out=oa, qkv_descale=sc) == 5
+    ob = raw.view(torch.float16)[2 * 8 * 4096 * 40 // 2:].view(2, 8, 4096, 40)  # starts past q's bytes
+    assert B.check(qa, qs, qs.clone(), out=ob, qkv_descale=sc) == 0
