@@ -367,16 +367,21 @@ __global__ __launch_bounds__(256) void attn_bwd_table_reduce(const float* ws, fl
 //
 // Row kernel (attn_bwd_rows): one workgroup of four waves owns 64 queries of
 // one (batch item, head), Q and dO rows in registers, and streams the K/V
-// tiles three times: (1) the row log-sum-exp L (base 2) of the scaled
-// logits, (2) D = sum_j P_ij dP_ij with P = 2^(S*log2e*scale - L) and
-// dP = dO V^T, (3) dS = P (dP - D) and dQ = scale * dS K.  L and D go to the
-// workspace.
+// tiles twice: (1) with S = QK^T and dP = dO V^T, the row log-sum-exp L
+// (base 2) of the scaled logits and D = sum_j P_ij dP_ij, both kept online
+// against a running row maximum (D = [sum_j 2^(s_ij - m) dP_ij] /
+// [sum_j 2^(s_ij - m)], rescaled when m grows); (2) dS = P (dP - D) with
+// P = 2^(s - L) and dQ = scale * dS K.  L and D go to the workspace.
 // Column kernel (attn_bwd_cols): one workgroup owns 64 keys, K and V rows in
 // registers, and streams Q, dO (and L, D) tiles: S = Q K^T, P, dP = dO V^T,
 // dS; dV = P^T dO and dK = scale * dS^T Q accumulate over all queries.
 // Both use the forward's MFMA layouts (transposed operands from transposing
-// LDS reads, probabilities packed as B operands).
+// LDS reads, probabilities packed as B operands).  The streamed tiles are
+// software-pipelined: the next tile's global loads are issued into registers
+// before the current tile's products and written to the other of two LDS
+// stages after them, with one barrier per tile.
 // ---------------------------------------------------------------------------
+
 template <int D>
 struct BwdTileCfg {
   static constexpr int NT = 256;
@@ -387,21 +392,42 @@ struct BwdTileCfg {
   static constexpr int RCH = D / 8;
   static constexpr int NCH = 64 * RCH;
   static constexpr int CPT = (NCH + NT - 1) / NT;
+  static constexpr int TILE = 64 * ROW;  // elements of one staged tile
 };
 
-// Rows [r0, r0 + 64) of a [N, D] slice (rows clamped to N-1) into an LDS
-// tile of row stride ROW.
+// The CPT 16-byte chunks this thread moves of rows [r0, r0 + 64) of a [N, D]
+// slice (rows clamped to N-1): global -> registers, registers -> LDS tile.
 template <int D>
-__device__ __forceinline__ void stage_rows(uint16_t* tile, const uint16_t* src, int64_t sn, int r0, int n,
-                                           int tid) {
+__device__ __forceinline__ void load_rows_regs(u32x4* reg, const uint16_t* src, int64_t sn, int r0, int n,
+                                               int tid) {
+  using C = BwdTileCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::CPT; ++c) {
+    const int ch = min(tid + c * C::NT, C::NCH - 1);
+    const int row = ch / C::RCH, col = (ch % C::RCH) * 8;
+    reg[c] = *(const u32x4*)(src + (int64_t)min(r0 + row, n - 1) * sn + col);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows_regs(uint16_t* tile, const u32x4* reg, int tid) {
   using C = BwdTileCfg<D>;
 #pragma unroll
   for (int c = 0; c < C::CPT; ++c) {
     const int ch = tid + c * C::NT;
-    if (ch < C::NCH) {
-      const int row = ch / C::RCH, col = (ch % C::RCH) * 8;
-      const int r = min(r0 + row, n - 1);
-      *(u32x4*)&tile[row * C::ROW + col] = *(const u32x4*)(src + (int64_t)r * sn + col);
+    if (ch < C::NCH) *(u32x4*)&tile[(ch / C::RCH) * C::ROW + (ch % C::RCH) * 8] = reg[c];
+  }
+}
+
+// Zero the head-dim padding columns [D, DK) of `ntile` staged tiles.
+template <int D>
+__device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int tid) {
+  using C = BwdTileCfg<D>;
+  if constexpr (C::DK > D) {
+    constexpr int P = C::DK - D;
+    for (int i = tid; i < ntile * 64 * P; i += C::NT) {
+      const int t = i / (64 * P), r = i - t * 64 * P;
+      tiles[t * C::TILE + (r / P) * C::ROW + D + r % P] = 0;
     }
   }
 }
@@ -409,11 +435,11 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, const uint16_t* src, 
 template <class E, int D>
 __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   using C = BwdTileCfg<D>;
-  constexpr int KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW;
+  constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
   const AttnArgs& a = ba.a;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  uint16_t* Ks = (uint16_t*)lds;  // [64][ROW]
-  uint16_t* Vs = Ks + 64 * ROW;
+  uint16_t* Ks = (uint16_t*)lds;  // [2][64][ROW]
+  uint16_t* Vs = Ks + 2 * TILE;   // [2][64][ROW]
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -428,6 +454,10 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
   const uint16_t* op = (const uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;  // dO
+  const int ntiles = (Nk + 63) / 64;
+  u32x4 kreg[C::CPT], vreg[C::CPT];
+  load_rows_regs<D>(kreg, kp, a.k_sn, 0, Nk, tid);
+  load_rows_regs<D>(vreg, vp, a.v_sn, 0, Nk, tid);
   u32x4 qf[KCH], df[KCH];
 #pragma unroll
   for (int dc = 0; dc < KCH; ++dc) {
@@ -435,79 +465,95 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     qf[dc] = d0 < D ? *(const u32x4*)(qp + (int64_t)qi * a.q_sn + d0) : u32x4{0, 0, 0, 0};
     df[dc] = d0 < D ? *(const u32x4*)(op + (int64_t)qi * a.o_sn + d0) : u32x4{0, 0, 0, 0};
   }
-  if constexpr (DK > D) {  // head-dim padding columns of the tiles
-    for (int i = tid; i < 2 * 64 * (DK - D); i += 256) {
-      const int t = i / (64 * (DK - D)), r = i - t * 64 * (DK - D);
-      Ks[t * 64 * ROW + (r / (DK - D)) * ROW + D + r % (DK - D)] = 0;
-    }
-  }
+  zero_pad_cols<D>(Ks, 4, tid);  // both stages of K and V
+  store_rows_regs<D>(Ks, kreg, tid);
+  store_rows_regs<D>(Vs, vreg, tid);
+  __syncthreads();
+
   const float c2 = a.scale * kLog2e;
-  const int ntiles = (Nk + 63) / 64;
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
-  float m = -INFINITY, l = 0.f, L = 0.f, Dacc = 0.f, Dq = 0.f;
+  // Pass 1 state (per lane: partial sums over its keys, against the row
+  // maximum m shared by the four lane groups).
+  float m = -INFINITY, l = 0.f, t = 0.f, L = 0.f, Dq = 0.f;
   f32x4 acc[CBD];
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int pass = 0; pass < 3; ++pass) {
-    for (int t = 0; t < ntiles; ++t) {
-      __syncthreads();  // the previous tile's reads are done
-      stage_rows<D>(Ks, kp, a.k_sn, t * 64, Nk, tid);
-      if (pass > 0) stage_rows<D>(Vs, vp, a.v_sn, t * 64, Nk, tid);
-      __syncthreads();
-      f32x4 s[4], dp[4];
+  const int n_it = 2 * ntiles;
+  for (int it = 0; it < n_it; ++it) {
+    const bool second = it >= ntiles;
+    const int tile = second ? it - ntiles : it;
+    const int st = it & 1;
+    const bool more = it + 1 < n_it;
+    if (more) {  // the next tile's loads, in flight during this tile
+      const int nt = it + 1 >= ntiles ? it + 1 - ntiles : it + 1;
+      load_rows_regs<D>(kreg, kp, a.k_sn, nt * 64, Nk, tid);
+      load_rows_regs<D>(vreg, vp, a.v_sn, nt * 64, Nk, tid);
+    }
+    const uint16_t* Kt = Ks + st * TILE;
+    const uint16_t* Vt = Vs + st * TILE;
+    f32x4 s[4], dp[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < KCH; ++dc) {
-          s[kb] = E::mfma(*(const u32x4*)&Ks[(kb * 16 + l16) * ROW + dc * 32 + g * 8], qf[dc], s[kb]);
-          if (pass > 0) dp[kb] = E::mfma(*(const u32x4*)&Vs[(kb * 16 + l16) * ROW + dc * 32 + g * 8], df[dc], dp[kb]);
-        }
-      }
-      float y[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = t * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
-        y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
-      }
-      if (pass == 0) {
-        float mx = y[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
-        const float mn = fmaxf(m, max_across_groups(mx));
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(y[i] - mn);
-        l = l * __builtin_amdgcn_exp2f(m - mn) + ps;  // per-lane partial sums
-        m = mn;
-      } else {
-        float ds[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(y[i] - L);
-          if (pass == 1) Dacc = fmaf(p, dp[i >> 2][i & 3], Dacc);
-          else ds[i] = p * (dp[i >> 2][i & 3] - Dq);
-        }
-        if (pass == 2) {
-          u32x4 sf[2];
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-            sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
-                           E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int cb = 0; cb < CBD; ++cb) {
-              const uint16_t* ptr = Ks + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
-              const u32x2 lo = lds_read_tr16(ptr);
-              const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
-              acc[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[kc], acc[cb]);
-            }
-        }
+      for (int dc = 0; dc < KCH; ++dc) {
+        s[kb] = E::mfma(*(const u32x4*)&Kt[(kb * 16 + l16) * ROW + dc * 32 + g * 8], qf[dc], s[kb]);
+        dp[kb] = E::mfma(*(const u32x4*)&Vt[(kb * 16 + l16) * ROW + dc * 32 + g * 8], df[dc], dp[kb]);
       }
     }
-    if (pass == 0) L = m + __builtin_amdgcn_logf(sum_across_groups(l));  // log2 of the row sum
-    if (pass == 1) Dq = sum_across_groups(Dacc);
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
+      y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
+    }
+    if (!second) {
+      float mx = y[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
+      const float mn = fmaxf(m, max_across_groups(mx));
+      float ps = 0.f, pd = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(y[i] - mn);
+        ps += e;
+        pd = fmaf(e, dp[i >> 2][i & 3], pd);
+      }
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile
+      l = fmaf(l, alpha, ps);
+      t = fmaf(t, alpha, pd);
+      m = mn;
+      if (it == ntiles - 1) {
+        const float lt = sum_across_groups(l);
+        L = m + __builtin_amdgcn_logf(lt);  // log2 of the row sum
+        Dq = sum_across_groups(t) / lt;
+      }
+    } else {
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i] - L) * (dp[i >> 2][i & 3] - Dq);
+      u32x4 sf[2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                       E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int cb = 0; cb < CBD; ++cb) {
+          const uint16_t* ptr = Kt + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+          const u32x2 lo = lds_read_tr16(ptr);
+          const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
+          acc[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[kc], acc[cb]);
+        }
+    }
+    if (more) {
+      // Stage st^1 was last read in the previous tile, before the barrier
+      // that ended it; this tile's reads of stage st end at the barrier below.
+      store_rows_regs<D>(Ks + (st ^ 1) * TILE, kreg, tid);
+      store_rows_regs<D>(Vs + (st ^ 1) * TILE, vreg, tid);
+    }
+    __syncthreads();
   }
   float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
   float* wsD = wsL + (int64_t)a.B * a.H * Nq;
@@ -531,13 +577,13 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 template <class E, int D>
 __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   using C = BwdTileCfg<D>;
-  constexpr int KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW;
+  constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
   const AttnArgs& a = ba.a;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  uint16_t* Qs = (uint16_t*)lds;  // [64][ROW]
-  uint16_t* Os = Qs + 64 * ROW;   // dO
-  float* Ls = (float*)(Os + 64 * ROW);
-  float* Ds = Ls + 64;
+  uint16_t* Qs = (uint16_t*)lds;  // [2][64][ROW]
+  uint16_t* Os = Qs + 2 * TILE;   // dO, [2][64][ROW]
+  float* Ls = (float*)(Os + 2 * TILE);  // [2][64]
+  float* Ds = Ls + 2 * 64;              // [2][64]
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -552,6 +598,29 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
   const uint16_t* op = (const uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;  // dO
+  const float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
+  const float* wsD = wsL + (int64_t)a.B * a.H * Nq;
+  const int ntiles = (Nq + 63) / 64;
+  u32x4 qreg[C::CPT], oreg[C::CPT];
+  float lreg = INFINITY, dreg = 0.f;  // rows past Nq: P = 0
+  auto load_tile = [&](int t) {
+    load_rows_regs<D>(qreg, qp, a.q_sn, t * 64, Nq, tid);
+    load_rows_regs<D>(oreg, op, a.o_sn, t * 64, Nq, tid);
+    if (tid < 64) {
+      const int q = t * 64 + tid;
+      lreg = q < Nq ? wsL[q] : INFINITY;
+      dreg = q < Nq ? wsD[q] : 0.f;
+    }
+  };
+  auto store_tile = [&](int st) {
+    store_rows_regs<D>(Qs + st * TILE, qreg, tid);
+    store_rows_regs<D>(Os + st * TILE, oreg, tid);
+    if (tid < 64) {
+      Ls[st * 64 + tid] = lreg;
+      Ds[st * 64 + tid] = dreg;
+    }
+  };
+  load_tile(0);
   // K and V rows of this lane's key as B operands (lane = key column).
   u32x4 kf[KCH], vf[KCH];
 #pragma unroll
@@ -560,30 +629,22 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     kf[dc] = d0 < D ? *(const u32x4*)(kp + (int64_t)ki * a.k_sn + d0) : u32x4{0, 0, 0, 0};
     vf[dc] = d0 < D ? *(const u32x4*)(vp + (int64_t)ki * a.v_sn + d0) : u32x4{0, 0, 0, 0};
   }
-  if constexpr (DK > D) {
-    for (int i = tid; i < 2 * 64 * (DK - D); i += 256) {
-      const int t = i / (64 * (DK - D)), r = i - t * 64 * (DK - D);
-      Qs[t * 64 * ROW + (r / (DK - D)) * ROW + D + r % (DK - D)] = 0;
-    }
-  }
-  const float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
-  const float* wsD = wsL + (int64_t)a.B * a.H * Nq;
+  zero_pad_cols<D>(Qs, 4, tid);  // both stages of Q and dO
+  store_tile(0);
+  __syncthreads();
   const float c2 = a.scale * kLog2e;
-  const int ntiles = (Nq + 63) / 64;
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
   f32x4 dk[CBD], dv[CBD];
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    stage_rows<D>(Qs, qp, a.q_sn, t * 64, Nq, tid);
-    stage_rows<D>(Os, op, a.o_sn, t * 64, Nq, tid);
-    if (tid < 64) {
-      const int q = t * 64 + tid;
-      Ls[tid] = q < Nq ? wsL[q] : INFINITY;  // rows past Nq: P = 0
-      Ds[tid] = q < Nq ? wsD[q] : 0.f;
-    }
-    __syncthreads();
+    const int st = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);  // in flight during this tile
+    const uint16_t* Qt = Qs + st * TILE;
+    const uint16_t* Ot = Os + st * TILE;
+    const float* Lt = Ls + st * 64;
+    const float* Dt = Ds + st * 64;
     // S = Q K^T and dP = dO V^T: rows are queries qb*16 + g*4 + r, the
     // column is this lane's key.
     f32x4 s[4], dp[4];
@@ -592,15 +653,15 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
       s[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < KCH; ++dc) {
-        s[qb] = E::mfma(*(const u32x4*)&Qs[(qb * 16 + l16) * ROW + dc * 32 + g * 8], kf[dc], s[qb]);
-        dp[qb] = E::mfma(*(const u32x4*)&Os[(qb * 16 + l16) * ROW + dc * 32 + g * 8], vf[dc], dp[qb]);
+        s[qb] = E::mfma(*(const u32x4*)&Qt[(qb * 16 + l16) * ROW + dc * 32 + g * 8], kf[dc], s[qb]);
+        dp[qb] = E::mfma(*(const u32x4*)&Ot[(qb * 16 + l16) * ROW + dc * 32 + g * 8], vf[dc], dp[qb]);
       }
     }
     float p[16], ds[16];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 Lq = *(const f32x4*)&Ls[qb * 16 + g * 4];
-      const f32x4 Dv = *(const f32x4*)&Ds[qb * 16 + g * 4];
+      const f32x4 Lq = *(const f32x4*)&Lt[qb * 16 + g * 4];
+      const f32x4 Dv = *(const f32x4*)&Dt[qb * 16 + g * 4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pv = __builtin_amdgcn_exp2f(s[qb][r] * c2 - Lq[r]);
@@ -621,13 +682,15 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int cb = 0; cb < CBD; ++cb) {
-        const uint16_t* optr = Os + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
-        const uint16_t* qptr = Qs + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const uint16_t* optr = Ot + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+        const uint16_t* qptr = Qt + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
         const u32x2 ol = lds_read_tr16(optr), oh = lds_read_tr16(optr + 16 * ROW);
         const u32x2 ql = lds_read_tr16(qptr), qh = lds_read_tr16(qptr + 16 * ROW);
         dv[cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pf[kc], dv[cb]);
         dk[cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kc], dk[cb]);
       }
+    if (more) store_tile(st ^ 1);  // stage st^1 was last read before the previous barrier
+    __syncthreads();
   }
   if (krow < Nk) {
     uint16_t* dkp = (uint16_t*)ba.dk + (int64_t)b * ba.dk_sb + (int64_t)h * ba.dk_sh + (int64_t)krow * ba.dk_sn;

@@ -199,6 +199,12 @@ static int launch_bwd_tiled(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   auto rows = attn_bwd_rows<Elem, D>;
   auto cols = attn_bwd_cols<Elem, D>;
+  if (p.lds > 32 * 1024 &&
+      (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
+           hipSuccess ||
+       hipFuncSetAttribute((const void*)cols, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
+           hipSuccess))
+    return ATTN_E_LAUNCH;
   hipLaunchKernelGGL(rows, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
   if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
   ba.a.n_qtiles = (ba.a.Nk + 63) / 64;  // key tiles for the column kernel

@@ -409,7 +409,9 @@ inline Plan plan_bwd_half(const AttnArgs& a) {
   p.bm = 64;
   const int64_t nt = (a.Nq > a.Nk ? a.Nq : a.Nk) + 63;
   p.blocks = nt / 64 * a.H * a.B;
-  p.lds = (size_t)2 * 64 * ROW * 2 + 2 * 64 * 4;
+  // Two LDS stages of two 64-row tiles (K and V, or Q and dO), and two
+  // stages of the 64 rows' L and D.
+  p.lds = (size_t)4 * 64 * ROW * 2 + 4 * 64 * 4;
   return p;
 }
 
