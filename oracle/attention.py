@@ -492,11 +492,18 @@ def attention_backward(q, k, v, dout, bias: Optional[Bias] = None,
       dQ = scale * dS K,  dK = scale * dS^T Q,
       d_table[r, h] = sum of dS over the pairs (i, j) of head h that read
                       table row r (summed over batch items),
-      decomposed relative position (bias q_i.Rh[row_h] + q_i.Rw[row_w]):
-      dQ_i += sum_j dS_ij (Rh[row_h(i, j)] + Rw[row_w(i, j)]),
-      dRh[m] = sum of dS_ij q_i over (b, h, i, j) with row_h(i, j) = m
-      (dRw likewise), for the tables of the needed length, then mapped to
-      the stored tables through the transpose of the resize.
+      decomposed relative position: the bias is rel_h[i, kh] + rel_w[i, kw]
+      with rel_h[i, kh] = q_i . Rh[row_h(qh_i, kh)] (SAM blog, section
+      "Bfloat16 half precision"; see relpos_bias), so through that
+      decomposition
+        dRelH[i, kh] = sum over kw of dS[i, (kh, kw)],
+        dRelW[i, kw] = sum over kh of dS[i, (kh, kw)],
+        dQ_i += sum_kh dRelH[i, kh] Rh[row_h(qh_i, kh)]
+                + sum_kw dRelW[i, kw] Rw[row_w(qw_i, kw)],
+        dRh[m] = sum of dRelH[i, kh] q_i over (b, h, i, kh) with
+                 row_h(qh_i, kh) = m (dRw likewise),
+      for the tables of the needed length, then mapped to the stored tables
+      through the transpose of the resize.
     The mask is a constant and has no gradient.  Returns dq, dk, dv and,
     with a table bias, dtable [(2gh-1)(2gw-1), H]; with the relative
     position, drh, drw.
@@ -520,8 +527,8 @@ def attention_backward(q, k, v, dout, bias: Optional[Bias] = None,
         kgh, kgw = bias.kgrid if bias.kgrid is not None else (gh, gw)
         rh = rel_pos_resized(bias.rh, 2 * max(gh, kgh) - 1)
         rw = rel_pos_resized(bias.rw, 2 * max(gw, kgw) - 1)
-        row_h = relpos_rows(gh, kgh)[np.arange(Nq) // gw][:, np.arange(Nk) // kgw]   # [Nq, Nk]
-        row_w = relpos_rows(gw, kgw)[np.arange(Nq) % gw][:, np.arange(Nk) % kgw]
+        row_h = relpos_rows(gh, kgh)[np.arange(Nq) // gw]    # [Nq, kgh]: table row of (query, kh)
+        row_w = relpos_rows(gw, kgw)[np.arange(Nq) % gw]     # [Nq, kgw]
         drh, drw = np.zeros_like(rh), np.zeros_like(rw)
     rows = np.arange(Nq)
     for b in range(B):
@@ -537,9 +544,12 @@ def attention_backward(q, k, v, dout, bias: Optional[Bias] = None,
             if bias is not None and bias.kind == "table":
                 np.add.at(dtable[:, h], idx, ds)
             if bias is not None and bias.kind == "relpos":
-                dq[b, h] += np.einsum("ij,ijc->ic", ds, rh[row_h]) + np.einsum("ij,ijc->ic", ds, rw[row_w])
-                np.add.at(drh, row_h, ds[:, :, None] * q[b, h][:, None, :])
-                np.add.at(drw, row_w, ds[:, :, None] * q[b, h][:, None, :])
+                ds3 = ds.reshape(Nq, kgh, kgw)
+                d_relh, d_relw = ds3.sum(axis=2), ds3.sum(axis=1)     # [Nq, kgh], [Nq, kgw]
+                dq[b, h] += (np.einsum("ik,ikc->ic", d_relh, rh[row_h])
+                             + np.einsum("ik,ikc->ic", d_relw, rw[row_w]))
+                np.add.at(drh, row_h, d_relh[:, :, None] * q[b, h][:, None, :])
+                np.add.at(drw, row_w, d_relw[:, :, None] * q[b, h][:, None, :])
     res.update(dq=dq, dk=dk, dv=dv)
     if bias is not None and bias.kind == "table":
         res["dtable"] = dtable

@@ -86,6 +86,16 @@ def test_relpos_bias(grid, kgrid, nh, nw):
     check_against_fd(q, k, v, rnd((1, 2, nq, d), 25), bias, None, ["dq", "dk", "dv", "drh", "drw"])
 
 
+def test_relpos_bias_wider_grid_two_batch_items():
+    # A 4x6 grid (rows and columns of different lengths) over two batch items
+    # and two heads: the table gradients sum over every (b, h, i, kh / kw).
+    grid, d = (4, 6), 2
+    n = grid[0] * grid[1]
+    q, k, v = rnd((2, 2, n, d), 50), rnd((2, 2, n, d), 51), rnd((2, 2, n, d), 52)
+    bias = O.Bias("relpos", grid=grid, rh=rnd((7, d), 53), rw=rnd((11, d), 54))
+    check_against_fd(q, k, v, rnd((2, 2, n, d), 55), bias, None, ["dq", "dk", "drh", "drw"])
+
+
 def test_shift_mask_image_layout_with_padding():
     # 5x4 image in 3x3 windows (padded to 6x6), shift 1, table bias, regions.
     window = (5, 4, 3, 3, 1, 1)
