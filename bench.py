@@ -50,6 +50,9 @@ RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 ALL = ["C1", "C2", "C3", "C3i", "C4", "C4h", "C5s", "C5x"]
 # The Swin-T and SD workloads with q, k, v as 8-bit E4M3 codes (f16 compute).
 LOW_PRECISION = ["C2f8", "C5sf8", "C5xf8"]
+# Backward passes (attn_bwd) of Swin-T, SAM-B windowed and global, and SD
+# self-attention: the workload key with a trailing "b".
+BACKWARD = ["C2b", "C3b", "C4b", "C5sb"]
 TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 2e-2}
 
 
@@ -303,7 +306,10 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
         s["kw"] = W.device_args(w, s)
         s["dq"], s["dk"], s["dv"] = (torch.empty_like(s["q"]) for _ in range(3))
         s["dtable"] = (torch.empty(base["table"].shape, dtype=torch.float32, device=dev)
-                       if w.bias == "table" else None)
+                       if w.bias == "table" else
+                       torch.empty(base["rh"].shape[0] + base["rw"].shape[0], w.d, dtype=torch.float32,
+                                   device=dev)
+                       if w.bias == "relpos" else None)
         sets.append(s)
     # One workspace, reused by every launch (they run one after another).
     s0 = sets[0]
@@ -331,22 +337,26 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
     torch.cuda.synchronize()
     rec = {}
     if check_units:
-        # Oracle gradients: the whole workload in the image layout, else the
-        # first and last (batch item, head) units (no bias: each unit's
-        # gradients depend on its own slice only).
+        # Oracle gradients: the whole workload in the image layout or with a
+        # table bias, else the first and last (batch item, head) units (no
+        # bias or the relative position: each unit's dQ, dK, dV depend on its
+        # own slice and the shared tables only; the table gradients, which
+        # sum over all units, are checked at reduced sizes by the tests).
         arrs = {k: v.double().numpy() for k, v in inp.items()}
         got = [sets[0][k].detach().double().cpu().numpy() for k in ("dq", "dk", "dv")]
         errs = []
-        if w.layout == "image" or w.bias != "none":
+        if w.layout == "image" or w.bias == "table":
             ref = oracle.run_workload_backward(w, arrs)
             errs = [float(np.max(np.abs(g - ref[k]))) for g, k in zip(got, ("dq", "dk", "dv"))]
             sample = "whole workload"
             if w.bias == "table":
                 errs.append(float(np.max(np.abs(sets[0]["dtable"].double().cpu().numpy() - ref["dtable"]))))
         else:
+            bias = (oracle.Bias("relpos", grid=w.grid, rh=arrs["rh"], rw=arrs["rw"])
+                    if w.bias == "relpos" else None)
             for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
-                sl = {k: v[b:b + 1, h:h + 1] for k, v in arrs.items()}
-                ref = oracle.attention_backward(sl["q"], sl["k"], sl["v"], sl["dout"])
+                sl = {k: v[b:b + 1, h:h + 1] for k, v in arrs.items() if k in ("q", "k", "v", "dout")}
+                ref = oracle.attention_backward(sl["q"], sl["k"], sl["v"], sl["dout"], bias)
                 errs += [float(np.max(np.abs(g[b, h] - ref[k][0, 0]))) for g, k in zip(got, ("dq", "dk", "dv"))]
             sample = "2 (batch item, head) units, every row"
         rec.update({"max_abs_err": max(errs), "err_sample": sample})
@@ -433,9 +443,9 @@ def main():
     ap.add_argument("--config", default="C2", help="headline workload")
     ap.add_argument("--extra", default="all",
                     help="comma-separated workloads also timed in this run ('all' or 'none'; "
-                         "C2p is C2 with 3 heads of a window per workgroup; C2b and C5sb are the "
-                         "backward passes of C2 and C5s; C2f8, C5sf8, C5xf8 take q, k, v as "
-                         "E4M3 codes)")
+                         "C2p is C2 with 3 heads of a window per workgroup; C2b, C3b, C4b and "
+                         "C5sb are the backward passes of C2, C3, C4 and C5s; C2f8, C5sf8, C5xf8 "
+                         "take q, k, v as E4M3 codes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle error checks")
     ap.add_argument("--check-units", type=int, default=16,
@@ -512,14 +522,14 @@ def main():
         line["copy_floor"] = copy_floor(torch, w.algorithmic_bytes, K, args.settle_ms)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
-    extra = [] if args.extra == "none" else (ALL + ["C2p", "C2b", "C5sb"] + LOW_PRECISION
+    extra = [] if args.extra == "none" else (ALL + ["C2p"] + BACKWARD + LOW_PRECISION
                                              if args.extra == "all" else args.extra.split(","))
     if extra:
         line["workloads"] = {}
         for key in extra:
             if key == args.config:
                 continue
-            if key in ("C2b", "C5sb"):  # backward passes of Swin-T and SD self-attention
+            if key in BACKWARD:  # backward passes
                 we = W.WORKLOADS[key[:-1]]
                 r = run_backward(torch, W, binding, we, K, args.warmup, args.settle_ms,
                                  0 if args.no_check else 1)

@@ -285,26 +285,37 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
  *  q, k, v, bias_desc, mask_desc, dtype: as in attn_fwd.  dout: the output
  *  gradient, laid out like `out` of attn_fwd.  dq, dk, dv: written, shaped and
  *  laid out like q, k, v (own strides allowed); they must overlap no input and
- *  no other gradient.  dtable: TABLE bias only (else ignored, may be NULL): a
- *  device fp32 array [(2gh-1)(2gw-1), H], element [r, head] at r*H + head,
- *  overwritten with the table gradient summed over all batch items.  The
- *  mask and an ADDITIVE bias receive no gradient.
+ *  no other gradient.  dtable (4-byte aligned device fp32, overwritten; may
+ *  be NULL for the other bias kinds): TABLE bias: [(2gh-1)(2gw-1), H],
+ *  element [r, head] at r*H + head, the table gradient summed over all
+ *  batch items and windows.  RELPOS: [(2gh-1) + (2gw-1), d], the gradient
+ *  of Rh (its 2gh-1 rows first) and then of Rw, summed over all batch items
+ *  and heads -- through the decomposed bias rel_h[i][kh] + rel_w[i][kw]
+ *  ("Accelerating Generative AI with PyTorch: Segment Anything, Fast",
+ *  section "Bfloat16").  The mask and an ADDITIVE bias receive no gradient.
  *  workspace: device memory of at least the bytes attn_bwd_workspace_size
  *    reports, 16-byte aligned, owned by the caller (NULL allowed when that is
  *    0); its contents before and after the call are unspecified.  Window
  *    units: B_eff * H * table rows * 4 bytes with a TABLE bias (the
  *    per-window partial table gradients, summed over windows in a fixed
  *    order by a second kernel), else 0.  Longer sequences: 2 * B * H * Nq * 4
- *    bytes (each query row's log-sum-exp and sum_j P_ij dP_ij).
+ *    bytes (each query row's log-sum-exp and sum_j P_ij dP_ij); with RELPOS
+ *    also each query's rel_h / rel_w rows (B * H * Nq * (gh + gw) floats)
+ *    and one partial [dRh; dRw] per 64 query rows (B * H * ceil(Nq / 64) *
+ *    ((2gh-1) + (2gw-1)) * d floats), summed in a fixed order.
  *    Bitwise-deterministic, no atomics.
  *
  *  Built: half precision (F16/BF16).  Units of at most 64 queries and keys
  *  (the window path: Swin windows in either layout, with shift and padding
  *  folded in) with bias NONE, TABLE or ADDITIVE and any mask; longer
- *  sequences in the batched layout without bias or mask (SD-style self- and
- *  cross-attention): a row kernel (log-sum-exp, D, dQ) and a column kernel
- *  (dK, dV).  Other calls (fp32, RELPOS, biases or masks on long sequences)
- *  return ATTN_E_UNSUPPORTED.  Asynchronous on `stream`.                      */
+ *  sequences in the batched layout without a mask and with no bias (SD-
+ *  style self- and cross-attention) or the RELPOS bias on equal query and
+ *  key grids with tables of 2g-1 rows (SAM's windowed and global layers;
+ *  grid width 64, or gh + gw <= 84): a row kernel (log-sum-exp, D, dQ and
+ *  the relative-position terms) and a column kernel (dK, dV).  Other calls
+ *  (fp32, key grids or resized tables, other biases or masks on long
+ *  sequences, the image layout beyond 64 tokens) return
+ *  ATTN_E_UNSUPPORTED.  Asynchronous on `stream`.                             */
 ATTN_API int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
              const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
              const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,

@@ -370,8 +370,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
         dtable=None, workspace=None, stream=None, no_alloc: bool = False):
     """Gradients of sum(dout * O) for O = fwd(q, k, v, bias, mask) via attn_bwd.
 
-    Returns (dq, dk, dv, dtable); dtable (fp32 [table rows, H]) only with a
-    TableBias, else None.  Output and workspace tensors are allocated with
+    Returns (dq, dk, dv, dtable): dtable is fp32 [table rows, H] with a
+    TableBias, the pair (dRh, dRw) (fp32 views [rows, d] of one
+    [Rh rows + Rw rows, d] buffer) with a RelposBias, else None.  A given
+    ``dtable`` must be that buffer.  Output and workspace tensors are allocated with
     torch when not given; the library itself allocates nothing.  Queued on
     ``stream`` (default: torch's current stream).  ``no_alloc``: call
     attn_bwd_noalloc (the library's fixed device array instead of a
@@ -386,6 +388,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
     dqc, dkc, dvc = _tensor_c(dq, lay), _tensor_c(dk, lay), _tensor_c(dv, lay)
     if isinstance(bias, TableBias) and dtable is None:
         dtable = torch.empty(bias.table.shape, dtype=torch.float32, device=q.device)
+    if isinstance(bias, RelposBias) and dtable is None:
+        dtable = torch.empty(bias.rh.shape[0] + bias.rw.shape[0], q.shape[3], dtype=torch.float32,
+                             device=q.device)
     if dtable is not None and (dtable.dtype != torch.float32 or not dtable.is_contiguous()):
         raise TypeError("dtable must be a contiguous float32 tensor")
     if stream is None:
@@ -400,7 +405,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
         if st != ATTN_OK:
             raise AttnError(st, h.attn_strerror(st).decode())
         del keep
-        return dq, dk, dv, (dtable if isinstance(bias, TableBias) else None)
+        return dq, dk, dv, _table_grads(bias, dtable)
     need = ctypes.c_size_t(0)
     st = h.attn_bwd_workspace_size(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
                                    ctypes.byref(bd), ctypes.byref(md), dt, ctypes.byref(need))
@@ -417,4 +422,13 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
     if st != ATTN_OK:
         raise AttnError(st, h.attn_strerror(st).decode())
     del keep
-    return dq, dk, dv, (dtable if isinstance(bias, TableBias) else None)
+    return dq, dk, dv, _table_grads(bias, dtable)
+
+
+def _table_grads(bias, dtable):
+    if isinstance(bias, TableBias):
+        return dtable
+    if isinstance(bias, RelposBias):
+        nh = bias.rh.shape[0]
+        return dtable[:nh], dtable[nh:]
+    return None

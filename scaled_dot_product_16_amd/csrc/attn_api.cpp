@@ -296,8 +296,10 @@ int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov
     for (int j = i + 1; j < 3; ++j)
       if (overlaps(outs[i], outs[j], es)) return ATTN_E_ALIAS;
   }
-  // Built: window units (at most 64 queries and keys) in half precision,
-  // with or without a table bias; no gradient of the relative position.
+  // Built (the backward plan): window units (at most 64 queries and keys,
+  // any bias but the relative position, any mask), and the tiled path for
+  // longer sequences with no bias or the relative position (equal grids,
+  // tables of the needed length), no mask, batched layout.
   Plan plan;
   if ((st = make_bwd_plan(ba->a, &plan)) != ATTN_OK) return st;
   ba->dq = dq->data;
@@ -306,10 +308,12 @@ int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov
   ba->dq_sb = dq->strides[0]; ba->dq_sh = dq->strides[1]; ba->dq_sn = dq->strides[2];
   ba->dk_sb = dk->strides[0]; ba->dk_sh = dk->strides[1]; ba->dk_sn = dk->strides[2];
   ba->dv_sb = dv->strides[0]; ba->dv_sh = dv->strides[1]; ba->dv_sn = dv->strides[2];
-  if (ba->a.bias_kind == ATTN_BIAS_TABLE) {
+  if (ba->a.bias_kind == ATTN_BIAS_TABLE || ba->a.bias_kind == ATTN_BIAS_RELPOS) {
+    // TABLE: [(2gh-1)(2gw-1), H]; RELPOS: the stacked [dRh; dRw] rows of d.
     if (!dtable) return ATTN_E_NULL;
     if ((uintptr_t)dtable % 4) return ATTN_E_LAYOUT;
-    ba->n_tab = (2 * ba->a.gh - 1) * (2 * ba->a.gw - 1);
+    ba->n_tab = ba->a.bias_kind == ATTN_BIAS_TABLE ? (2 * ba->a.gh - 1) * (2 * ba->a.gw - 1)
+                                                   : bwd_rel_rows(ba->a);
     ba->dtable = dtable;
   }
   *ws_bytes = bwd_workspace_bytes(ba->a, plan.kernel);

@@ -432,7 +432,35 @@ __device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int ti
   }
 }
 
+// Dot product of two rows of D elements of E (16-byte aligned), in fp32.
 template <class E, int D>
+__device__ __forceinline__ float dot_rows(const uint16_t* x, const uint16_t* y) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const u32x4 xv = *(const u32x4*)(x + c), yv = *(const u32x4*)(y + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(E::to_f((uint16_t)(xv[e] & 0xFFFF)), E::to_f((uint16_t)(yv[e] & 0xFFFF)), s);
+      s = fmaf(E::to_f((uint16_t)(xv[e] >> 16)), E::to_f((uint16_t)(yv[e] >> 16)), s);
+    }
+  }
+  return s;
+}
+
+// RP: relative-position form (kBwdRelNone / kBwdRelGeneral / kBwdRelRow64).
+// With the relative position (equal gh x gw grids, tables of 2g-1 rows) the
+// bias of query i and key j = (kh, kw) is rel_h[i][kh] + rel_w[i][kw],
+// rel_h[i][kh] = q_i . Rh[qh_i - kh + gh - 1] (rel_w likewise); the row
+// kernel computes these rows for its 64 queries (and stores them for the
+// column kernel), adds the bias to every score, and in its second pass also
+// gathers dRelH[i][kh] = sum over kw of dS and dRelW[i][kw] = sum over kh.
+// After the key loop it adds the bias path to dQ,
+//   dQ_i += sum_kh dRelH[i][kh] Rh[..] + sum_kw dRelW[i][kw] Rw[..],
+// and writes this workgroup's part of the table gradients,
+//   [dRh; dRw][r][c] = sum_i A[r][i] Q[i][c]  with  A[r][i] = dRelH[i][qh_i + gh - 1 - r]
+// (Rh rows; Rw rows likewise), as one small MFMA product Q^T A^T.
+template <class E, int D, int RP = kBwdRelNone>
 __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   using C = BwdTileCfg<D>;
   constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
@@ -448,7 +476,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   const int qt = bid - qt_div * a.n_qtiles;
   const int b = fdiv(qt_div, a.fd_h), h = qt_div - b * a.H;
   const int Nq = a.Nq, Nk = a.Nk;
-  const int qrow = qt * 64 + wave * 16 + l16;
+  const int qloc = wave * 16 + l16;
+  const int qrow = qt * 64 + qloc;
   const int qi = min(qrow, Nq - 1);
   const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
@@ -465,6 +494,55 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     qf[dc] = d0 < D ? *(const u32x4*)(qp + (int64_t)qi * a.q_sn + d0) : u32x4{0, 0, 0, 0};
     df[dc] = d0 < D ? *(const u32x4*)(op + (int64_t)qi * a.o_sn + d0) : u32x4{0, 0, 0, 0};
   }
+
+  // Relative position: rel_h / rel_w of this workgroup's queries.
+  const int gh = a.gh, gw = a.gw, G = gh + gw;
+  const int RS = RP == kBwdRelGeneral ? G : 64;  // row length of `rel` (floats)
+  const size_t stage_bytes = bwd_stage_bytes<D>(a);
+  float* rel = (float*)(lds + stage_bytes);  // general: [64][G]; row form: rel_h [64][64]
+  float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - (RP == kBwdRelGeneral ? 256 * G * 4 : 64 * 64 * 4)) / 4;
+  const BwdWs wl = bwd_ws_layout(a);
+  const int64_t bh = (int64_t)b * a.H + h;
+  float* ws_rel = ba.ws + wl.rel + bh * Nq * G;  // [Nq][G] of this (batch item, head)
+  const uint16_t* rhp = (const uint16_t*)a.rh;
+  const uint16_t* rwp = (const uint16_t*)a.rw;
+  float wreg[RP == kBwdRelRow64 ? 16 : 1], wacc[RP == kBwdRelRow64 ? 16 : 1];
+  if constexpr (RP == kBwdRelGeneral) {
+    for (int e = tid; e < 64 * G; e += 256) {
+      const int ql = e / G, x = e - ql * G;
+      const int qr = min(qt * 64 + ql, Nq - 1);
+      const int qh = fdiv(qr, a.fd_gw), qw = qr - qh * gw;
+      const uint16_t* trow = x < gh ? rhp + (int64_t)(qh - x + gh - 1) * D : rwp + (int64_t)(qw - (x - gh) + gw - 1) * D;
+      const float val = dot_rows<E, D>(qp + (int64_t)qr * a.q_sn, trow);
+      rel[e] = val;
+      if (qt * 64 + ql < Nq) ws_rel[(int64_t)(qt * 64 + ql) * G + x] = val;
+    }
+    for (int e = tid; e < 256 * G; e += 256) dacc[e] = 0.f;
+  } else if constexpr (RP == kBwdRelRow64) {
+    // gw = 64: a wave's 16 queries and a 64-key tile lie in one grid row
+    // each.  rel_h[q][kh] for kh = 16g.. (LDS); rel_w of this lane's 16 key
+    // slots kw = 16kb + 4g + r (registers).
+    const int qh = qi >> 6, qw = qi & 63;
+    const uint16_t* qr = qp + (int64_t)qi * a.q_sn;
+#pragma unroll 1
+    for (int j = 0; j < 16; ++j) {
+      const int kh = g * 16 + j;
+      if (kh < gh) {
+        const float val = dot_rows<E, D>(qr, rhp + (int64_t)(qh - kh + gh - 1) * D);
+        rel[qloc * 64 + kh] = val;
+        if (qrow < Nq) ws_rel[(int64_t)qrow * G + kh] = val;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kw = (i >> 2) * 16 + g * 4 + (i & 3);
+      wreg[i] = dot_rows<E, D>(qr, rwp + (int64_t)(qw - kw + 63) * D);
+      if (qrow < Nq) ws_rel[(int64_t)qrow * G + gh + kw] = wreg[i];
+      wacc[i] = 0.f;
+    }
+    for (int e = tid; e < 64 * 64; e += 256) dacc[e] = 0.f;
+  }
+
   zero_pad_cols<D>(Ks, 4, tid);  // both stages of K and V
   store_rows_regs<D>(Ks, kreg, tid);
   store_rows_regs<D>(Vs, vreg, tid);
@@ -502,10 +580,21 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
     }
     float y[16];
+    int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
-      y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
+      float bias = 0.f;
+      if constexpr (RP == kBwdRelGeneral) {
+        const int kc = min(key, Nk - 1);
+        kh_i[i] = fdiv(kc, a.fd_gw);
+        kw_i[i] = kc - kh_i[i] * gw;
+        bias = rel[qloc * RS + kh_i[i]] + rel[qloc * RS + gh + kw_i[i]];
+      } else if constexpr (RP == kBwdRelRow64) {
+        bias = rel[qloc * 64 + tile] + wreg[i];
+      }
+      y[i] = key < Nk ? (RP == kBwdRelNone ? s[i >> 2][i & 3] * c2 : fmaf(bias, kLog2e, s[i >> 2][i & 3] * c2))
+                      : -INFINITY;
     }
     if (!second) {
       float mx = y[0];
@@ -532,6 +621,24 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i] - L) * (dp[i >> 2][i & 3] - Dq);
+      if constexpr (RP == kBwdRelGeneral) {
+        // Private sums of this lane (keys past Nk have dS = 0).
+        float* my = dacc + tid * G;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          my[kh_i[i]] += ds[i];
+          my[gh + kw_i[i]] += ds[i];
+        }
+      } else if constexpr (RP == kBwdRelRow64) {
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          rs += ds[i];
+          wacc[i] += ds[i];
+        }
+        rs = sum_across_groups(rs);
+        if (g == 0) dacc[qloc * 64 + tile] = rs;
+      }
       u32x4 sf[2];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
@@ -557,6 +664,111 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   }
   float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
   float* wsD = wsL + (int64_t)a.B * a.H * Nq;
+  f32x4 bq[CBD];  // bias path of dQ (already in final units)
+#pragma unroll
+  for (int cb = 0; cb < CBD; ++cb) bq[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (RP != kBwdRelNone) {
+    const int RH = 2 * gh - 1, RT = RH + 2 * gw - 1;
+    // dRel of this workgroup's queries: general grids sum the four lane
+    // groups' private rows into `rel` [64][G]; the row form has dRelH in
+    // `dacc` [64][64] and writes dRelW from registers into `rel` [64][64].
+    if constexpr (RP == kBwdRelGeneral) {
+      for (int e = tid; e < 64 * G; e += 256) {
+        const int ql = e / G, x = e - ql * G;
+        const int base = (ql >> 4) * 64 + (ql & 15);
+        rel[e] = ((dacc[base * G + x] + dacc[(base + 16) * G + x]) + dacc[(base + 32) * G + x]) +
+                 dacc[(base + 48) * G + x];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rel[qloc * 64 + (i >> 2) * 16 + g * 4 + (i & 3)] = wacc[i];
+    }
+    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : dacc[ql * 64 + x]; };
+    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : rel[ql * 64 + x]; };
+    // The stacked tables [Rh; Rw] into the free K/V stages.
+    uint16_t* Rs = (uint16_t*)lds;
+    for (int e = tid * 8; e < RT * D; e += 256 * 8)
+      *(u32x4*)&Rs[e] = e < RH * D ? *(const u32x4*)(rhp + e) : *(const u32x4*)(rwp + (e - RH * D));
+    __syncthreads();
+    {
+      const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * gw;
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          f32x4 tq = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int x = 0; x < gh; ++x) {
+            const float w = d_relh(qloc, x);
+            const u32x2 r2 = *(const u32x2*)&Rs[(qh - x + gh - 1) * D + c0];
+            tq[0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), tq[0]);
+            tq[1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), tq[1]);
+            tq[2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), tq[2]);
+            tq[3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), tq[3]);
+          }
+          for (int x = 0; x < gw; ++x) {
+            const float w = d_relw(qloc, x);
+            const u32x2 r2 = *(const u32x2*)&Rs[(RH + qw - x + gw - 1) * D + c0];
+            tq[0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), tq[0]);
+            tq[1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), tq[1]);
+            tq[2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), tq[2]);
+            tq[3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), tq[3]);
+          }
+          bq[cb] = tq;
+        }
+      }
+    }
+    __syncthreads();  // the stages are rewritten below
+    // Coefficients A[r][i] (E, rows padded to a multiple of 16 with zeros).
+    const int RB = (RT + 15) / 16;
+    uint16_t* Am = (uint16_t*)lds;  // [RB*16][kBwdARow]
+    for (int e = tid; e < RB * 16 * 64; e += 256) {
+      const int r = e >> 6, ql = e & 63, qr = qt * 64 + ql;
+      float v = 0.f;
+      if (r < RT && qr < Nq) {
+        const int qh = fdiv(qr, a.fd_gw), qw = qr - qh * gw;
+        if (r < RH) {
+          const int x = qh + gh - 1 - r;
+          if (x >= 0 && x < gh) v = d_relh(ql, x);
+        } else {
+          const int x = qw + gw - 1 - (r - RH);
+          if (x >= 0 && x < gw) v = d_relw(ql, x);
+        }
+      }
+      Am[r * kBwdARow + ql] = (uint16_t)(E::pack2(v, 0.f) & 0xFFFF);
+    }
+    __syncthreads();  // `rel` and `dacc` are free: the Q tile goes there
+    uint16_t* Qs = (uint16_t*)rel;
+    {
+      u32x4 qreg[C::CPT];
+      load_rows_regs<D>(qreg, qp, a.q_sn, qt * 64, Nq, tid);
+      zero_pad_cols<D>(Qs, 1, tid);
+      store_rows_regs<D>(Qs, qreg, tid);
+    }
+    __syncthreads();
+    // part^T[c][r] = sum_i Q[i][c] A[r][i]: A operand Q^T by transposing
+    // reads of the Q tile, B operand A^T (lane = table row r), both in the
+    // query order the transposing reads produce.
+    float* part = ba.ws + wl.part + (int64_t)bid * RT * D;
+    for (int rb = wave; rb < RB; rb += 4) {
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        f32x4 pr = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const uint16_t* ptr = Qs + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
+          const u32x2 lo = lds_read_tr16(ptr);
+          const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
+          // B operand in the key order of the transposing reads: slot j of
+          // lane group g is query kc*32 + (j/4)*16 + 4g + j%4.
+          const uint16_t* arow = Am + (rb * 16 + l16) * kBwdARow + kc * 32 + g * 4;
+          const u32x2 alo = *(const u32x2*)arow, ahi = *(const u32x2*)(arow + 16);
+          pr = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, u32x4{alo[0], alo[1], ahi[0], ahi[1]}, pr);
+        }
+        const int r = rb * 16 + l16, c0 = cb * 16 + g * 4;
+        if (r < RT && c0 < D) *(f32x4*)&part[(int64_t)r * D + c0] = pr;
+      }
+    }
+  }
   if (qrow < Nq) {
     if (g == 0) {
       wsL[qrow] = L;
@@ -567,14 +779,18 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     for (int cb = 0; cb < CBD; ++cb) {
       const int c0 = cb * 16 + g * 4;
       if (c0 < D) {
-        const f32x4 v = acc[cb] * a.scale;
+        const f32x4 v = acc[cb] * a.scale + bq[cb];
         *(u32x2*)(dq + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
       }
     }
   }
 }
 
-template <class E, int D>
+// RP: as for the row kernel; the bias of (query i, this lane's key) comes
+// from the rel_h / rel_w rows the row kernel stored, staged per query tile
+// ([columns][64] floats: all gh + gw columns, or the key tile's grid row
+// and the 64 columns of the 64-wide form).
+template <class E, int D, int RP = kBwdRelNone>
 __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   using C = BwdTileCfg<D>;
   constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
@@ -601,6 +817,19 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   const float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
   const float* wsD = wsL + (int64_t)a.B * a.H * Nq;
   const int ntiles = (Nq + 63) / 64;
+  // Relative position: staged columns NC, this lane's two of them.
+  const int gh = a.gh, G = gh + a.gw;
+  const int NC = bwd_cols_rel_cols(a);
+  float* Rst = Ds + 2 * 64;  // [2][NC][64]
+  const float* ws_rel = ba.ws + bwd_ws_layout(a).rel + ((int64_t)b * a.H + h) * Nq * G;
+  int xh = 0, xw = 0;
+  if constexpr (RP != kBwdRelNone) {
+    const int kh = fdiv(ki, a.fd_gw), kw = ki - kh * a.gw;
+    xh = RP == kBwdRelGeneral ? kh : 0;
+    xw = RP == kBwdRelGeneral ? gh + kw : 1 + kw;
+  }
+  constexpr int RC = RP == kBwdRelNone ? 1 : RP == kBwdRelRow64 ? 17 : (kBwdRelMaxCols * 64 + 255) / 256;
+  float rreg[RC];
   u32x4 qreg[C::CPT], oreg[C::CPT];
   float lreg = INFINITY, dreg = 0.f;  // rows past Nq: P = 0
   auto load_tile = [&](int t) {
@@ -611,6 +840,16 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
       lreg = q < Nq ? wsL[q] : INFINITY;
       dreg = q < Nq ? wsD[q] : 0.f;
     }
+    if constexpr (RP != kBwdRelNone) {
+#pragma unroll
+      for (int c = 0; c < RC; ++c) {
+        const int e = tid + c * 256, x = e >> 6, q = t * 64 + (e & 63);
+        // Column x of the stage: rel_h / rel_w column (the 64-wide form
+        // stages column kt of rel_h, then the 64 rel_w columns).
+        const int col = RP == kBwdRelGeneral ? x : (x == 0 ? kt : gh + x - 1);
+        rreg[c] = e < 64 * NC && q < Nq ? ws_rel[(int64_t)q * G + col] : 0.f;
+      }
+    }
   };
   auto store_tile = [&](int st) {
     store_rows_regs<D>(Qs + st * TILE, qreg, tid);
@@ -618,6 +857,13 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     if (tid < 64) {
       Ls[st * 64 + tid] = lreg;
       Ds[st * 64 + tid] = dreg;
+    }
+    if constexpr (RP != kBwdRelNone) {
+#pragma unroll
+      for (int c = 0; c < RC; ++c) {
+        const int e = tid + c * 256;
+        if (e < 64 * NC) Rst[st * 64 * NC + e] = rreg[c];
+      }
     }
   };
   load_tile(0);
@@ -664,7 +910,12 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
       const f32x4 Dv = *(const f32x4*)&Dt[qb * 16 + g * 4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(s[qb][r] * c2 - Lq[r]);
+        float y = s[qb][r] * c2;
+        if constexpr (RP != kBwdRelNone) {
+          const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4 + r;
+          y = fmaf(rs[xh * 64] + rs[xw * 64], kLog2e, y);
+        }
+        const float pv = __builtin_amdgcn_exp2f(y - Lq[r]);
         p[qb * 4 + r] = pv;
         ds[qb * 4 + r] = pv * (dp[qb][r] - Dv[r]);
       }
@@ -704,6 +955,30 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         *(u32x2*)(dvp + c0) = u32x2{E::pack2(v4[0], v4[1]), E::pack2(v4[2], v4[3])};
       }
     }
+  }
+}
+
+// Relative-position table gradients: out[o] = sum over the row-kernel
+// workgroups p of part[p][o] (o = r*D + c over the stacked [Rh; Rw] rows).
+// One workgroup of 16 waves per 64 outputs: wave w adds p = w, w+16, ... in
+// order, then the 16 partial sums are added in a fixed order (bitwise
+// deterministic).  (A template only so that every compiled instance may
+// carry its copy.)
+template <int>
+__global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* out, int n_out, int n_part) {
+  __shared__ float red[16][64];
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, w = tid >> 6;
+  const int o = __builtin_amdgcn_workgroup_id_x() * 64 + lane;
+  float acc = 0.f;
+  if (o < n_out)
+    for (int p = w; p < n_part; p += 16) acc += part[(size_t)p * n_out + o];
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && o < n_out) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t += red[j][lane];
+    out[o] = t;
   }
 }
 

@@ -191,14 +191,16 @@ int launch_bwd_bias(const AttnBwdArgs& ba, const Plan& p, hipStream_t s) {
 
 #if INST_DT != 0
 // Long sequences: the row kernel (L, D, dQ), then the column kernel (dK, dV).
-static int launch_bwd_tiled(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
+template <int RP>
+static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
   constexpr int D = INST_D;
   AttnBwdArgs ba = ba0;
   ba.a.n_qtiles = (ba.a.Nq + 63) / 64;
   ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
-  auto rows = attn_bwd_rows<Elem, D>;
-  auto cols = attn_bwd_cols<Elem, D>;
+  const int n_row_wg = ba.a.n_blocks;
+  auto rows = attn_bwd_rows<Elem, D, RP>;
+  auto cols = attn_bwd_cols<Elem, D, RP>;
   if (p.lds > 32 * 1024 &&
       (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
            hipSuccess ||
@@ -211,7 +213,25 @@ static int launch_bwd_tiled(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s
   ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   hipLaunchKernelGGL(cols, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+  if constexpr (RP != kBwdRelNone) {
+    // [dRh; dRw] = fixed-order sum of the row kernel's per-workgroup parts.
+    const int n_out = bwd_rel_rows(ba.a) * D;
+    auto red = attn_bwd_part_reduce<0>;
+    hipLaunchKernelGGL(red, dim3((unsigned)((n_out + 63) / 64)), dim3(1024), 0, s,
+                       (const float*)(ba.ws + bwd_ws_layout(ba.a).part), ba.dtable, n_out, n_row_wg);
+    if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+static int launch_bwd_tiled(const AttnBwdArgs& ba, const Plan& p, hipStream_t s) {
+  switch (p.rmode) {
+    case kBwdRelNone: return launch_bwd_tiled_rp<kBwdRelNone>(ba, p, s);
+    case kBwdRelGeneral: return launch_bwd_tiled_rp<kBwdRelGeneral>(ba, p, s);
+    case kBwdRelRow64: return launch_bwd_tiled_rp<kBwdRelRow64>(ba, p, s);
+    default: return ATTN_E_UNSUPPORTED;
+  }
 }
 
 template <>

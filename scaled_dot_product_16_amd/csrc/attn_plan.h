@@ -385,10 +385,95 @@ inline int make_plan(const AttnArgs& a, Plan* p) {
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Tiled backward (attn_bwd_rows / attn_bwd_cols) geometry
+// ---------------------------------------------------------------------------
+
+// Relative-position forms of the tiled backward: none; general grids (the
+// row kernel keeps per-lane private sums of dRelH/dRelW in LDS, 1280 bytes
+// per column of gh + gw, so gh + gw <= kBwdRelMaxCols); 64-wide grids
+// (a 64-key tile is one grid row: dRelH is a row sum per tile, dRelW and
+// rel_w stay in registers per key slot).
+constexpr int kBwdRelNone = 0, kBwdRelGeneral = 1, kBwdRelRow64 = 2;
+constexpr int kBwdRelMaxCols = 84;
+
+constexpr int bwd_rel_mode(const AttnArgs& a) {
+  return a.bias_kind != ATTN_BIAS_RELPOS ? kBwdRelNone
+         : (a.gw == 64 && a.gh <= 64)     ? kBwdRelRow64
+                                          : kBwdRelGeneral;
+}
+
+// Rows of the stacked table [Rh; Rw] (equal grids, tables of the needed length).
+constexpr int bwd_rel_rows(const AttnArgs& a) { return 2 * a.gh - 1 + 2 * a.gw - 1; }
+
+// Workspace of the tiled backward, in floats: the rows' L and D (B*H*Nq
+// each), then with the relative position the rel_h / rel_w rows of every
+// query ([B*H*Nq][gh + gw], written by the row kernel, read by the column
+// kernel) and one partial [Rh; Rw] gradient per row-kernel workgroup
+// ([B*H*ceil(Nq/64)][rows][D], summed in a fixed order afterwards).
+struct BwdWs {
+  size_t L, D, rel, part, total;
+};
+constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
+  const size_t n = (size_t)a.B * a.H * a.Nq;
+  BwdWs w{0, n, 0, 0, 0};
+  size_t off = (2 * n + 3) / 4 * 4;
+  w.rel = off;
+  if (a.bias_kind == ATTN_BIAS_RELPOS) {
+    off = (off + n * (size_t)(a.gh + a.gw) + 3) / 4 * 4;
+    w.part = off;
+    off += (size_t)a.B * a.H * (size_t)((a.Nq + 63) / 64) * (size_t)bwd_rel_rows(a) * (size_t)a.D;
+  } else {
+    w.part = off;
+  }
+  w.total = off;
+  return w;
+}
+
+// LDS of the row kernel: the K/V stages, also used after the key loop for
+// the stacked tables [Rh; Rw] (elements) and the coefficient matrix of the
+// table-gradient product ([16*ceil(rows/16)][kBwdARow] elements); then the
+// relative-position region: rel_h/rel_w (later dRel and the Q tile) and the
+// dRel sums.
+constexpr int kBwdARow = 72;
+template <int D>
+constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
+  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  size_t s = (size_t)4 * 64 * ROW * 2;
+  if (a.bias_kind == ATTN_BIAS_RELPOS) {
+    const size_t rows = (size_t)bwd_rel_rows(a);
+    const size_t am = (rows + 15) / 16 * 16 * kBwdARow * 2, tb = rows * D * 2;
+    s = s > am ? s : am;
+    s = s > tb ? s : tb;
+  }
+  return (s + 15) / 16 * 16;
+}
+template <int D>
+constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
+  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  const int mode = bwd_rel_mode(a);
+  if (mode == kBwdRelNone) return 0;
+  const size_t g = (size_t)(a.gh + a.gw);
+  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : (size_t)64 * 64 * 4;
+  const size_t qt = (size_t)64 * ROW * 2;
+  rel = (rel > qt ? rel : qt);
+  rel = (rel + 15) / 16 * 16;
+  const size_t acc = mode == kBwdRelGeneral ? 256 * g * 4 : (size_t)64 * 64 * 4;
+  return rel + acc;
+}
+// Columns of rel_h / rel_w the column kernel stages per query: all of them
+// (general grids), or the key tile's grid row and the 64 columns.
+constexpr int bwd_cols_rel_cols(const AttnArgs& a) {
+  const int mode = bwd_rel_mode(a);
+  return mode == kBwdRelNone ? 0 : mode == kBwdRelGeneral ? a.gh + a.gw : 1 + a.gw;
+}
+
 // The backward of a validated call (half precision): window units (at most
 // 64 queries and keys; any bias but the relative position, any mask), or
-// the tiled row/column kernels for longer sequences without bias or mask in
-// the batched layout.  blocks: the larger of the two tiled grids.
+// the tiled row/column kernels for longer sequences in the batched layout
+// without a mask and with no bias or the relative position (equal grids,
+// tables of the needed length).  blocks: the larger of the two tiled grids;
+// rmode: the relative-position form.
 template <int D>
 inline Plan plan_bwd_half(const AttnArgs& a) {
   Plan p{};
@@ -400,29 +485,36 @@ inline Plan plan_bwd_half(const AttnArgs& a) {
     p.lds = win_bwd_lds_bytes(a, WinBwdCfg<D>::BYTES);
     return p;
   }
-  if (a.bias_kind != ATTN_BIAS_NONE || a.mask_kind != ATTN_MASK_NONE || a.image) {
+  const bool rel_ok = a.bias_kind == ATTN_BIAS_RELPOS && a.gh == a.kgh && a.gw == a.kgw &&
+                      !relpos_resized(a) &&
+                      (bwd_rel_mode(a) == kBwdRelRow64 || a.gh + a.gw <= kBwdRelMaxCols);
+  if ((a.bias_kind != ATTN_BIAS_NONE && !rel_ok) || a.mask_kind != ATTN_MASK_NONE || a.image) {
     p.kernel = -1;
     return p;
   }
   constexpr int ROW = (D + 31) / 32 * 32 + 8;
   p.kernel = kKernMfma;
+  p.rmode = bwd_rel_mode(a);
   p.bm = 64;
   const int64_t nt = (a.Nq > a.Nk ? a.Nq : a.Nk) + 63;
   p.blocks = nt / 64 * a.H * a.B;
-  // Two LDS stages of two 64-row tiles (K and V, or Q and dO), and two
-  // stages of the 64 rows' L and D.
-  p.lds = (size_t)4 * 64 * ROW * 2 + 4 * 64 * 4;
+  // Row kernel: two LDS stages of the K and V tiles (and the relative-
+  // position regions); column kernel: two stages of the Q and dO tiles, of
+  // the 64 rows' L and D, and of the staged rel_h / rel_w columns.
+  const size_t rows = bwd_stage_bytes<D>(a) + bwd_rows_rel_bytes<D>(a);
+  const size_t cols = (size_t)4 * 64 * ROW * 2 + 4 * 64 * 4 + (size_t)2 * 64 * bwd_cols_rel_cols(a) * 4;
+  p.lds = rows > cols ? rows : cols;
   return p;
 }
 
 // Workspace bytes of the backward: per-unit table gradients (window path
-// with a table bias) or the rows' L and D (tiled path).
+// with a table bias) or the tiled path's (bwd_ws_layout).
 constexpr size_t bwd_workspace_bytes(const AttnArgs& a, int kernel) {
   if (kernel == kKernWin)
     return a.bias_kind == ATTN_BIAS_TABLE
                ? (size_t)a.B * a.H * (size_t)((2 * a.gh - 1) * (2 * a.gw - 1)) * 4
                : 0;
-  return (size_t)2 * a.B * a.H * a.Nq * 4;
+  return bwd_ws_layout(a).total * 4;
 }
 
 inline int make_bwd_plan(const AttnArgs& a, Plan* p) {

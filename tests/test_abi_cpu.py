@@ -330,12 +330,48 @@ def test_backward_validation(lib):
     assert h.attn_bwd_check(*args2(None, 0)) == 1
     wsl = torch.zeros(2 * 1 * 2 * 100)
     assert h.attn_bwd_check(*args2(ctypes.c_void_p(wsl.data_ptr()), 2 * 2 * 100 * 4)) == 0
-    # A relative-position bias on a long sequence has no backward here.
+    # The relative position on a long sequence (10x10 grid, equal key grid,
+    # tables of 19 rows): dtable = [dRh; dRw] (19 + 19 rows of d floats) and
+    # a workspace of L, D (2*B*H*Nq), the rel_h / rel_w rows (B*H*Nq*(gh+gw))
+    # and one partial per 64 query rows (B*H*ceil(Nq/64)*(19+19)*d), each
+    # region rounded up to 4 floats.
     rb = B.RelposBias(t(19, 64), t(19, 64), (10, 10))
     qc3, kc3, vc3, bd3, md3, oc3, dt3, keep3 = B._marshal(*ins, rb, None, "batched", None)
-    assert h.attn_bwd_check(ctypes.byref(qc3), ctypes.byref(kc3), ctypes.byref(vc3), ctypes.byref(oc3),
-                            ctypes.byref(bd3), ctypes.byref(md3), ctypes.byref(d1), ctypes.byref(d2),
-                            ctypes.byref(d3), None, dt3, ctypes.c_void_p(wsl.data_ptr()), 1 << 20) == 4
+    need3 = ctypes.c_size_t(0)
+    assert h.attn_bwd_workspace_size(ctypes.byref(qc3), ctypes.byref(kc3), ctypes.byref(vc3),
+                                     ctypes.byref(oc3), ctypes.byref(bd3), ctypes.byref(md3), dt3,
+                                     ctypes.byref(need3)) == 0
+    up4 = lambda n: (n + 3) // 4 * 4
+    assert need3.value == 4 * (up4(up4(2 * 2 * 100) + 2 * 100 * 20) + 2 * 2 * 38 * 64)
+    dr = torch.zeros(38, 64)
+    wsr = torch.zeros(need3.value // 4)
+    args3 = lambda dtab, n: (ctypes.byref(qc3), ctypes.byref(kc3), ctypes.byref(vc3), ctypes.byref(oc3),
+                             ctypes.byref(bd3), ctypes.byref(md3), ctypes.byref(d1), ctypes.byref(d2),
+                             ctypes.byref(d3), dtab, dt3, ctypes.c_void_p(wsr.data_ptr()), n)
+    assert h.attn_bwd_check(*args3(ctypes.c_void_p(dr.data_ptr()), need3.value)) == 0
+    assert h.attn_bwd_check(*args3(None, need3.value)) == 1              # no [dRh; dRw] output
+    assert h.attn_bwd_check(*args3(ctypes.c_void_p(dr.data_ptr()), need3.value - 4)) == 2
+    # Not built: keys on their own grid, resized tables, a mask, the image
+    # layout beyond windows, and general grids with gh + gw > 84.
+    def bwd_status(qq, kk, bias, mask=None, layout="batched", window=None):
+        args = B._marshal(qq, kk, kk.clone(), qq.clone(), bias, mask, layout, window)
+        qx, kx, vx, bx, mx, ox, dx, kp = args
+        n = ctypes.c_size_t(0)
+        return h.attn_bwd_workspace_size(ctypes.byref(qx), ctypes.byref(kx), ctypes.byref(vx), ctypes.byref(ox),
+                                         ctypes.byref(bx), ctypes.byref(mx), dx, ctypes.byref(n))
+    q100, k64 = t(1, 2, 100, 64), t(1, 2, 64, 64)
+    assert bwd_status(q100, k64, B.RelposBias(t(19, 64), t(19, 64), (10, 10), (8, 8))) == 4
+    assert bwd_status(q100, q100, B.RelposBias(t(27, 64), t(19, 64), (10, 10))) == 4
+    assert bwd_status(q100, q100, rb, mask=B.AdditiveMask(t(1, 100, 100))) == 4
+    q2500 = t(1, 1, 2500, 32)
+    assert bwd_status(q2500, q2500, B.RelposBias(t(99, 32), t(99, 32), (50, 50))) == 4
+    q1600 = t(1, 1, 1600, 32)
+    assert bwd_status(q1600, q1600, B.RelposBias(t(79, 32), t(79, 32), (40, 40))) == 0   # gh + gw = 80
+    q4096 = t(1, 1, 4096, 64)
+    assert bwd_status(q4096, q4096, B.RelposBias(t(127, 64), t(127, 64), (64, 64))) == 0  # 64-wide form
+    qi = t(1, 2, 64 * 64, 64)
+    img = B.Window(64, 64, 14, 14, 0, 0)
+    assert bwd_status(qi, qi, B.RelposBias(t(27, 64), t(27, 64), (14, 14)), layout="image", window=img) == 4
     del keep, keep2, keep3
 
 

@@ -47,10 +47,14 @@ def check_grads(w, inp, got, name=None):
     arrs = oracle_arrays(inp)
     ref = oracle.run_workload_backward(w, arrs)
     worst = {}
-    for key, g in zip(("dq", "dk", "dv", "dtable"), got):
-        if g is None:
-            assert key == "dtable" and w.bias != "table"
-            continue
+    pairs = list(zip(("dq", "dk", "dv"), got[:3]))
+    if w.bias == "relpos":
+        pairs += [("drh", got[3][0]), ("drw", got[3][1])]
+    elif w.bias == "table":
+        pairs += [("dtable", got[3])]
+    else:
+        assert got[3] is None
+    for key, g in pairs:
         r = ref[key]
         gg = g.detach().to("cpu", torch.float64).numpy()
         assert np.all(np.isfinite(gg)), key
@@ -179,12 +183,82 @@ def test_tiled_backward_sd_shapes(key):
 
 
 def test_backward_unsupported_calls():
-    w = W.custom(W.F16, B=1, H=2, Nq=100, Nk=100, d=64, bias="relpos", grid=(10, 10), cfg_id=880)
+    w = W.custom(W.F16, B=1, H=2, Nq=100, Nk=64, d=64, bias="relpos", grid=(10, 10), kgrid=(8, 8),
+                 cfg_id=880)
     dev = to_device(inputs(w))
-    with pytest.raises(Bd.AttnError) as e:                # relative position on a long sequence
+    with pytest.raises(Bd.AttnError) as e:                # relative position with a key grid
         Bd.bwd(dev["q"], dev["k"], dev["v"], dev["dout"], **W.device_args(w, dev))
     assert e.value.status == 4
     q = torch.zeros(1, 2, 49, 32, dtype=torch.float32, device="cuda")
     with pytest.raises(Bd.AttnError) as e:
         Bd.bwd(q, q.clone(), q.clone(), q.clone())       # fp32
     assert e.value.status == 4
+
+
+# Relative-position backward (tiled path): equal grids, tables of 2g-1 rows.
+RELPOS_GRIDS = [(2, 3), (7, 7), (14, 14), (8, 12), (5, 16), (30, 30), (1, 64), (3, 64), (16, 64)]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("grid", RELPOS_GRIDS)
+def test_relpos_backward_grids(dtype, grid):
+    n = grid[0] * grid[1]
+    w = W.custom(dtype, B=2, H=3, Nq=n, Nk=n, d=64, bias="relpos", grid=grid, cfg_id=860)
+    say(f"[backward] relpos {dtype} grid {grid}")
+    inp = inputs(w, seed=n, std_table=0.5)
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [32, 40, 64, 80])
+@pytest.mark.parametrize("grid", [(14, 14), (4, 64)])
+def test_relpos_backward_head_dims(dtype, d, grid):
+    n = grid[0] * grid[1]
+    w = W.custom(dtype, B=2, H=2, Nq=n, Nk=n, d=d, bias="relpos", grid=grid, cfg_id=870 + d)
+    say(f"[backward] relpos {dtype} d={d} grid {grid}")
+    inp = inputs(w, seed=d, std_table=0.5)
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+def test_relpos_backward_sam_windows():
+    # SAM ViT-B windowed attention: 25 windows of 14x14 (one 64x64 image
+    # padded to 70x70), 12 heads, d=64, bf16, tables at the workload's
+    # N(0, 0.02^2).
+    w = W.custom(W.BF16, B=25, H=12, Nq=196, Nk=196, d=64, bias="relpos", grid=(14, 14), cfg_id=3)
+    say("[backward] SAM-B windowed, one image")
+    inp = inputs(w, std_table=0.02)
+    worst = check_grads(w, inp, run_bwd(w, to_device(inp)), name="relpos backward SAM-B windows")
+    say(f"  max abs errors {worst}")
+
+
+@pytest.mark.parametrize("d,heads", [(64, 2), (80, 2)])
+def test_relpos_backward_sam_global(d, heads):
+    # SAM global attention: the 64x64 grid at full length (4096 tokens),
+    # one image and two heads (the oracle's fp64 backward of a 4096-token
+    # unit takes a few seconds).
+    w = W.custom(W.BF16, B=1, H=heads, Nq=4096, Nk=4096, d=d, bias="relpos", grid=(64, 64),
+                 cfg_id=4 if d == 64 else 44)
+    say(f"[backward] SAM global 64x64, d={d}")
+    inp = inputs(w, std_table=0.02)
+    worst = check_grads(w, inp, run_bwd(w, to_device(inp)), name=f"relpos backward SAM global d={d}")
+    say(f"  max abs errors {worst}")
+
+
+def test_relpos_backward_bias_is_seen_and_deterministic():
+    # The table gradients and the bias path into dQ are large next to the
+    # tolerance with tables of std 0.5; two calls agree bitwise.
+    w = W.custom(W.BF16, B=2, H=2, Nq=128 * 2, Nk=128 * 2, d=64, bias="relpos", grid=(4, 64),
+                 cfg_id=890)
+    inp = inputs(w, seed=3, std_table=0.5)
+    dev = to_device(inp)
+    a = run_bwd(w, dev)
+    b = run_bwd(w, dev)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[3][0], b[3][0]) and torch.equal(a[3][1], b[3][1])
+    ref = oracle.run_workload_backward(w, oracle_arrays(inp))
+    plain = oracle.run_workload_backward(
+        W.custom(W.BF16, B=2, H=2, Nq=256, Nk=256, d=64, cfg_id=890), oracle_arrays(inp))
+    # The bias changes dq by far more than the tolerance.
+    assert np.max(np.abs(ref["dq"] - plain["dq"])) > 10 * TOL[W.BF16]
+    assert np.max(np.abs(ref["drh"])) > 10 * TOL[W.BF16]
