@@ -432,7 +432,8 @@ __device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int ti
   }
 }
 
-// Dot product of two rows of D elements of E (16-byte aligned), in fp32.
+// Dot product of two rows of D elements of E (16-byte aligned), in fp32,
+// two elements per instruction.
 template <class E, int D>
 __device__ __forceinline__ float dot_rows(const uint16_t* x, const uint16_t* y) {
   float s = 0.f;
@@ -440,10 +441,7 @@ __device__ __forceinline__ float dot_rows(const uint16_t* x, const uint16_t* y) 
   for (int c = 0; c < D; c += 8) {
     const u32x4 xv = *(const u32x4*)(x + c), yv = *(const u32x4*)(y + c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s = fmaf(E::to_f((uint16_t)(xv[e] & 0xFFFF)), E::to_f((uint16_t)(yv[e] & 0xFFFF)), s);
-      s = fmaf(E::to_f((uint16_t)(xv[e] >> 16)), E::to_f((uint16_t)(yv[e] >> 16)), s);
-    }
+    for (int e = 0; e < 4; ++e) s = E::dot2(xv[e], yv[e], s);
   }
   return s;
 }
@@ -503,7 +501,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - (RP == kBwdRelGeneral ? 256 * G * 4 : 64 * 64 * 4)) / 4;
   const BwdWs wl = bwd_ws_layout(a);
   const int64_t bh = (int64_t)b * a.H + h;
-  float* ws_rel = ba.ws + wl.rel + bh * Nq * G;  // [Nq][G] of this (batch item, head)
+  float* ws_rel = ba.ws + wl.rel + bh * Nq * G;  // [G][Nq] of this (batch item, head)
   const uint16_t* rhp = (const uint16_t*)a.rh;
   const uint16_t* rwp = (const uint16_t*)a.rw;
   float wreg[RP == kBwdRelRow64 ? 16 : 1], wacc[RP == kBwdRelRow64 ? 16 : 1];
@@ -515,32 +513,59 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       const uint16_t* trow = x < gh ? rhp + (int64_t)(qh - x + gh - 1) * D : rwp + (int64_t)(qw - (x - gh) + gw - 1) * D;
       const float val = dot_rows<E, D>(qp + (int64_t)qr * a.q_sn, trow);
       rel[e] = val;
-      if (qt * 64 + ql < Nq) ws_rel[(int64_t)(qt * 64 + ql) * G + x] = val;
+      if (qt * 64 + ql < Nq) ws_rel[(int64_t)x * Nq + qt * 64 + ql] = val;
     }
     for (int e = tid; e < 256 * G; e += 256) dacc[e] = 0.f;
   } else if constexpr (RP == kBwdRelRow64) {
-    // gw = 64: a wave's 16 queries and a 64-key tile lie in one grid row
-    // each.  rel_h[q][kh] for kh = 16g.. (LDS); rel_w of this lane's 16 key
-    // slots kw = 16kb + 4g + r (registers).
-    const int qh = qi >> 6, qw = qi & 63;
-    const uint16_t* qr = qp + (int64_t)qi * a.q_sn;
-#pragma unroll 1
-    for (int j = 0; j < 16; ++j) {
-      const int kh = g * 16 + j;
-      if (kh < gh) {
-        const float val = dot_rows<E, D>(qr, rhp + (int64_t)(qh - kh + gh - 1) * D);
-        rel[qloc * 64 + kh] = val;
-        if (qrow < Nq) ws_rel[(int64_t)qrow * G + kh] = val;
+    // gw = 64: the workgroup's 64 queries are grid row qt, and a 64-key tile
+    // is one grid row.  rel_h^T[kh][q] = Rh[qt + gh - 1 - kh] . q and
+    // G_w[m][q] = Rw[m] . q (all 127 rows) on the matrix cores, with the
+    // query fragments already in registers as the B operand.
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int kh = mb * 16 + l16;
+      f32x4 acc_h = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        const u32x4 af = kh < gh && d0 < D ? *(const u32x4*)(rhp + (int64_t)(qt + gh - 1 - kh) * D + d0)
+                                           : u32x4{0, 0, 0, 0};
+        acc_h = E::mfma(af, qf[dc], acc_h);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // lane (l16, g) holds rel_h[qloc][16mb + 4g + i]
+        const int kh2 = mb * 16 + g * 4 + i;
+        if (kh2 < gh) {
+          rel[qloc * 64 + kh2] = acc_h[i];
+          if (qrow < Nq) ws_rel[(int64_t)kh2 * Nq + qrow] = acc_h[i];
+        }
       }
     }
+    float* gwl = (float*)lds;  // [128][64] in the K/V stages (free until tile 0 is stored)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int m = mb * 16 + l16;
+      f32x4 acc_w = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        const u32x4 af = m < 127 && d0 < D ? *(const u32x4*)(rwp + (int64_t)m * D + d0) : u32x4{0, 0, 0, 0};
+        acc_w = E::mfma(af, qf[dc], acc_w);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gwl[(mb * 16 + g * 4 + i) * 64 + qloc] = acc_w[i];
+    }
+    __syncthreads();
+    // rel_w[qloc][kw] = G_w[qloc - kw + 63][qloc] for this lane's key slots.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kw = (i >> 2) * 16 + g * 4 + (i & 3);
-      wreg[i] = dot_rows<E, D>(qr, rwp + (int64_t)(qw - kw + 63) * D);
-      if (qrow < Nq) ws_rel[(int64_t)qrow * G + gh + kw] = wreg[i];
+      wreg[i] = gwl[(qloc - kw + 63) * 64 + qloc];
+      if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = wreg[i];
       wacc[i] = 0.f;
     }
     for (int e = tid; e < 64 * 64; e += 256) dacc[e] = 0.f;
+    __syncthreads();  // the stages are written below
   }
 
   zero_pad_cols<D>(Ks, 4, tid);  // both stages of K and V
@@ -581,20 +606,27 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     }
     float y[16];
     int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
+    float bias_row = 0.f;  // 64-wide form: rel_h of this tile's grid row
+    if constexpr (RP == kBwdRelRow64) bias_row = rel[qloc * 64 + tile];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
-      float bias = 0.f;
-      if constexpr (RP == kBwdRelGeneral) {
-        const int kc = min(key, Nk - 1);
-        kh_i[i] = fdiv(kc, a.fd_gw);
-        kw_i[i] = kc - kh_i[i] * gw;
-        bias = rel[qloc * RS + kh_i[i]] + rel[qloc * RS + gh + kw_i[i]];
-      } else if constexpr (RP == kBwdRelRow64) {
-        bias = rel[qloc * 64 + tile] + wreg[i];
+      if constexpr (RP == kBwdRelNone) {
+        y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
+      } else {
+        // The bias is read for every slot (keys past Nk read the last key's
+        // entries) and those keys get -inf added: no branch around the reads.
+        float bias;
+        if constexpr (RP == kBwdRelGeneral) {
+          const int kc = min(key, Nk - 1);
+          kh_i[i] = fdiv(kc, a.fd_gw);
+          kw_i[i] = kc - kh_i[i] * gw;
+          bias = rel[qloc * RS + kh_i[i]] + rel[qloc * RS + gh + kw_i[i]];
+        } else {
+          bias = bias_row + wreg[i];
+        }
+        y[i] = fmaf(bias, kLog2e, s[i >> 2][i & 3] * c2) + (key < Nk ? 0.f : -INFINITY);
       }
-      y[i] = key < Nk ? (RP == kBwdRelNone ? s[i >> 2][i & 3] * c2 : fmaf(bias, kLog2e, s[i >> 2][i & 3] * c2))
-                      : -INFINITY;
     }
     if (!second) {
       float mx = y[0];
@@ -692,30 +724,22 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     __syncthreads();
     {
       const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * gw;
+      const int c0 = g * 4;  // this lane's columns: cb*16 + c0 .. +3
+      auto add_rows = [&](float w, int row) {
+        const uint16_t* rr = Rs + row * D + c0;
 #pragma unroll
-      for (int cb = 0; cb < CBD; ++cb) {
-        const int c0 = cb * 16 + g * 4;
-        if (c0 < D) {
-          f32x4 tq = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int x = 0; x < gh; ++x) {
-            const float w = d_relh(qloc, x);
-            const u32x2 r2 = *(const u32x2*)&Rs[(qh - x + gh - 1) * D + c0];
-            tq[0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), tq[0]);
-            tq[1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), tq[1]);
-            tq[2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), tq[2]);
-            tq[3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), tq[3]);
+        for (int cb = 0; cb < CBD; ++cb) {
+          if (cb * 16 + c0 < D) {
+            const u32x2 r2 = *(const u32x2*)(rr + cb * 16);
+            bq[cb][0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), bq[cb][0]);
+            bq[cb][1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), bq[cb][1]);
+            bq[cb][2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), bq[cb][2]);
+            bq[cb][3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), bq[cb][3]);
           }
-          for (int x = 0; x < gw; ++x) {
-            const float w = d_relw(qloc, x);
-            const u32x2 r2 = *(const u32x2*)&Rs[(RH + qw - x + gw - 1) * D + c0];
-            tq[0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), tq[0]);
-            tq[1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), tq[1]);
-            tq[2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), tq[2]);
-            tq[3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), tq[3]);
-          }
-          bq[cb] = tq;
         }
-      }
+      };
+      for (int x = 0; x < gh; ++x) add_rows(d_relh(qloc, x), qh - x + gh - 1);
+      for (int x = 0; x < gw; ++x) add_rows(d_relw(qloc, x), RH + qw - x + gw - 1);
     }
     __syncthreads();  // the stages are rewritten below
     // Coefficients A[r][i] (E, rows padded to a multiple of 16 with zeros).
@@ -847,7 +871,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         // Column x of the stage: rel_h / rel_w column (the 64-wide form
         // stages column kt of rel_h, then the 64 rel_w columns).
         const int col = RP == kBwdRelGeneral ? x : (x == 0 ? kt : gh + x - 1);
-        rreg[c] = e < 64 * NC && q < Nq ? ws_rel[(int64_t)q * G + col] : 0.f;
+        rreg[c] = e < 64 * NC && q < Nq ? ws_rel[(int64_t)col * Nq + q] : 0.f;
       }
     }
   };

@@ -445,6 +445,8 @@ constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
     const size_t am = (rows + 15) / 16 * 16 * kBwdARow * 2, tb = rows * D * 2;
     s = s > am ? s : am;
     s = s > tb ? s : tb;
+    // 64-wide form: the prologue's G_w[128][64] floats.
+    if (bwd_rel_mode(a) == kBwdRelRow64 && s < (size_t)128 * 64 * 4) s = (size_t)128 * 64 * 4;
   }
   return (s + 15) / 16 * 16;
 }
