@@ -28,10 +28,13 @@ from .attention import (  # noqa: F401
     window_reverse,
     shift_mask,
     attention_probs,
+    attention_logsumexp,
     attention,
     attention_image,
+    attention_image_logsumexp,
     attention_backward,
     attention_image_backward,
     run_workload,
+    run_workload_logsumexp,
     run_workload_backward,
 )

@@ -406,6 +406,32 @@ def attention_probs(q, k, bias: Optional[Bias] = None,
     return out
 
 
+def attention_logsumexp(q, k, bias: Optional[Bias] = None,
+                        mask: Optional[Mask] = None) -> np.ndarray:
+    """Per-row log-sum-exp of the logits, [B, H, Nq]:
+    L_i = log sum_j exp(scale * q_i.k_j + bias_ij + mask_ij) (natural log).
+
+    The normaliser of the softmax rows of :func:`attention_probs`
+    (P_ij = exp(s_ij - L_i)); an attention kernel can report it so that a
+    backward pass recomputes P without a pass of its own over the keys.
+    Computed as max + log(sum(exp(s - max))) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = 1.0 / np.sqrt(d)
+    cache: dict = {}
+    out = np.empty((B, H, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T) + _additive_rows(b, h, rows, q[b, h], Nk, bias, mask, cache)
+            m = s.max(axis=-1)
+            out[b, h] = m + np.log(np.exp(s - m[:, None]).sum(axis=-1))
+    return out
+
+
 def attention(q, k, v, bias: Optional[Bias] = None, mask: Optional[Mask] = None,
               select: Optional[Sequence] = None, row_block: int = 512):
     """O = softmax(scale*QK^T + bias + mask) V in float64.
@@ -474,6 +500,30 @@ def attention_image(q, k, v, window: tuple, bias: Optional[Bias] = None,
     o = window_reverse(ow, ph, pw, win_h, win_w)
     o = np.roll(o, shift=(sh, sw), axis=(2, 3))[:, :, :img_h, :img_w]
     return o.reshape(B, H, N, v.shape[-1])
+
+
+def attention_image_logsumexp(q, k, window: tuple, bias: Optional[Bias] = None,
+                              mask: Optional[Mask] = None) -> np.ndarray:
+    """Per-token log-sum-exp of the shifted-window attention in image order,
+    [B, H, img_h*img_w]: the windows' :func:`attention_logsumexp`, mapped back
+    through the reverse partition, reverse shift and crop of
+    :func:`attention_image`."""
+    img_h, img_w, win_h, win_w, sh, sw = window
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, N, d = q.shape
+    ph, pw = padded_extent(img_h, win_h), padded_extent(img_w, win_w)
+
+    def to_windows(x):
+        x = x.reshape(B, H, img_h, img_w, x.shape[-1])
+        x = np.pad(x, ((0, 0), (0, 0), (0, ph - img_h), (0, pw - img_w), (0, 0)))
+        x = np.roll(x, shift=(-sh, -sw), axis=(2, 3))
+        return window_partition(x, win_h, win_w)
+
+    lw = attention_logsumexp(to_windows(q), to_windows(k), bias, mask)[..., None]
+    lo = window_reverse(lw, ph, pw, win_h, win_w)
+    lo = np.roll(lo, shift=(sh, sw), axis=(2, 3))[:, :, :img_h, :img_w]
+    return lo.reshape(B, H, N)
 
 
 # ---------------------------------------------------------------------------
@@ -634,6 +684,16 @@ def run_workload(w, arrays: dict, select: Optional[Sequence] = None):
         assert select is None, "image layout is evaluated whole"
         return attention_image(arrays["q"], arrays["k"], arrays["v"], tuple(w.window), bias, mask)
     return attention(arrays["q"], arrays["k"], arrays["v"], bias, mask, select=select)
+
+
+def run_workload_logsumexp(w, arrays: dict) -> np.ndarray:
+    """Oracle per-row log-sum-exp for a workload description (see
+    run_workload): [B, H, Nq], in image order for the image layout."""
+    arrays = _dequantized(w, arrays)
+    bias, mask = _workload_terms(w, arrays)
+    if w.layout == "image":
+        return attention_image_logsumexp(arrays["q"], arrays["k"], tuple(w.window), bias, mask)
+    return attention_logsumexp(arrays["q"], arrays["k"], bias, mask)
 
 
 def run_workload_backward(w, arrays: dict) -> dict:

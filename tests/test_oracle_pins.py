@@ -611,3 +611,67 @@ def test_relpos_bias_resizes_tables():
         want = py_attention_window(tolist2(q[0, h]), tolist2(k[0, h]), tolist2(v[0, h]), gh, gw,
                                    rh=rh5, rw=rw7)
         np.testing.assert_allclose(got[0, h], want, rtol=0, atol=1e-12)
+
+
+def test_logsumexp_matches_torch_and_normalises_the_probabilities():
+    # L_i against torch.logsumexp of the same logits (a library routine), on
+    # a table bias with a shift-free additive mask; and exp(s - L) are the
+    # oracle's own softmax rows.
+    r = np.random.default_rng(7)
+    q, k = r.standard_normal((2, 3, 9, 4)), r.standard_normal((2, 3, 9, 4))
+    table = r.standard_normal((25, 3))
+    bias = O.Bias("table", grid=(3, 3), table=table)
+    madd = r.standard_normal((2, 9, 9))
+    mask = O.Mask("additive", add=madd)
+    lse = O.attention_logsumexp(q, k, bias, mask)
+    tb = O.table_bias(table, 3, 3)                          # [H, N, N]
+    s = torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2) / 2.0
+    s = s + torch.from_numpy(tb)[None] + torch.from_numpy(madd)[:, None]
+    assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+    p = O.attention_probs(q, k, bias, mask)
+    assert np.allclose(np.exp(s.numpy() - lse[..., None]), p, rtol=0, atol=1e-12)
+
+
+def test_logsumexp_closed_forms():
+    # Q = 0: every logit is 0, L = log Nk; one key: L = scale * q.k.
+    q = np.zeros((1, 1, 3, 8))
+    k = np.random.default_rng(1).standard_normal((1, 1, 5, 8))
+    assert np.allclose(O.attention_logsumexp(q, k), np.log(5.0))
+    q1 = np.random.default_rng(2).standard_normal((1, 2, 4, 8))
+    k1 = np.random.default_rng(3).standard_normal((1, 2, 1, 8))
+    expect = np.einsum("bhqc,bhkc->bhq", q1, k1) / np.sqrt(8.0)
+    assert np.allclose(O.attention_logsumexp(q1, k1), expect, rtol=0, atol=1e-12)
+
+
+def test_image_logsumexp_follows_the_pixels():
+    # 5x4 image in 3x3 windows (padded to 6x6), shift 1, table bias and
+    # regions: every real pixel's L equals the log-sum-exp of its own row of
+    # logits, found by brute force from the pixel's window (same scalar
+    # brute force as the attention pin above).
+    r = np.random.default_rng(11)
+    window = (5, 4, 3, 3, 1, 1)
+    q, k = r.standard_normal((1, 2, 20, 4)), r.standard_normal((1, 2, 20, 4))
+    bias = O.Bias("table", grid=(3, 3), table=r.standard_normal((25, 2)))
+    mask = O.Mask("shift", window=window)
+    lse = O.attention_image_logsumexp(q, k, window, bias, mask)
+    ph = pw = 6
+    lab = O.shift_region_labels(ph, pw, 3, 3, 1, 1)
+    for h in range(2):
+        for pix in range(20):
+            y, x = divmod(pix, 4)
+            # shifted position of this pixel and its window
+            sy, sx = (y - 1) % ph, (x - 1) % pw
+            wy, wx = sy // 3, sx // 3
+            logits = []
+            for ty in range(3):
+                for tx in range(3):
+                    ky, kx = (wy * 3 + ty + 1) % ph, (wx * 3 + tx + 1) % pw
+                    kvec = k[0, h, ky * 4 + kx] if ky < 5 and kx < 4 else np.zeros(4)
+                    qvec = q[0, h, pix]
+                    dh, dw = (sy % 3) - ty, (sx % 3) - tx
+                    b = bias.table[(dh + 2) * 5 + (dw + 2), h]
+                    same = lab[sy, sx] == lab[wy * 3 + ty, wx * 3 + tx]
+                    logits.append(qvec @ kvec / 2.0 + b + (0.0 if same else -100.0))
+            logits = np.array(logits)
+            m = logits.max()
+            assert abs(lse[0, h, pix] - (m + np.log(np.exp(logits - m).sum()))) < 1e-12
