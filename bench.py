@@ -285,8 +285,9 @@ def run_workload(torch, W, binding, w, K: int, warmup: int, settle_ms: float, no
 
 
 def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, check_units: int):
-    """Time the backward pass of workload ``w`` (attn_bwd: dQ, dK, dV and,
-    with a table bias, the table gradient), like run_workload.  Algorithmic
+    """Time the backward pass of workload ``w`` (attn_bwd_opt: dQ, dK, dV
+    and the table gradients, given the forward's O and log-sum-exp as a
+    training step has them), like run_workload.  Algorithmic
     work: the five products S, dP, dV, dK, dQ (10*B*H*Nq*Nk*d flops); bytes:
     Q, K, V, dO read and dQ, dK, dV written (plus the table and its
     gradient)."""
@@ -298,12 +299,16 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
     inp = W.make_inputs(w)
     inp["dout"] = W.to_dtype(W.normal(w.q_shape, w.cfg_id, 7, 1.0), w.dtype)
     base = {k: v.to(dev) for k, v in inp.items()}
-    per_set = 7 * base["q"].numel() * base["q"].element_size()
+    per_set = 8 * base["q"].numel() * base["q"].element_size()
     n_sets = max(1, math.ceil(512e6 / per_set))
     sets = []
     for i in range(n_sets):
         s = {k: (v.clone() if k in ("q", "k", "v", "dout") else v) for k, v in base.items()}
         s["kw"] = W.device_args(w, s)
+        # The forward's output and log-sum-exp, as a training step has them
+        # (computed here, outside the timed region).
+        s["lse"] = torch.empty(tuple(s["q"].shape[:3]), dtype=torch.float32, device=dev)
+        s["out"] = binding.fwd(s["q"], s["k"], s["v"], lse=s["lse"], **s["kw"])
         s["dq"], s["dk"], s["dv"] = (torch.empty_like(s["q"]) for _ in range(3))
         s["dtable"] = (torch.empty(base["table"].shape, dtype=torch.float32, device=dev)
                        if w.bias == "table" else
@@ -314,7 +319,7 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
     # One workspace, reused by every launch (they run one after another).
     s0 = sets[0]
     binding.bwd(s0["q"], s0["k"], s0["v"], s0["dout"], dq=s0["dq"], dk=s0["dk"], dv=s0["dv"],
-                dtable=s0["dtable"], **s0["kw"])
+                dtable=s0["dtable"], out=s0["out"], lse=s0["lse"], **s0["kw"])
     import ctypes
     need = ctypes.c_size_t(0)
     qc, kc, vc, bd, md, oc, dt, keep = binding._marshal(s0["q"], s0["k"], s0["v"], s0["dout"],
@@ -330,7 +335,7 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
     def step(i):
         s = sets[i % n_sets]
         binding.bwd(s["q"], s["k"], s["v"], s["dout"], dq=s["dq"], dk=s["dk"], dv=s["dv"],
-                    dtable=s["dtable"], workspace=ws, **s["kw"])
+                    dtable=s["dtable"], workspace=ws, out=s["out"], lse=s["lse"], **s["kw"])
 
     for i in range(max(warmup, 1)):
         step(i)
@@ -385,7 +390,7 @@ def run_backward(torch, W, binding, w, K: int, warmup: int, settle_ms: float, ch
     rec.update({"ms_per_step": round(ms, 6), "tflops": round(flops / (ms * 1e-3) / 1e12, 4),
                 "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 2), "flops_per_step": flops,
                 "algorithmic_bytes_per_step": nbytes, "rotating_input_sets": n_sets, "roofline": roof,
-                "pass": "backward (attn_bwd)"})
+                "pass": "backward (attn_bwd_opt, given the forward's O and log-sum-exp)"})
     del sets, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

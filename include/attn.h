@@ -255,13 +255,21 @@ typedef enum { ATTN_QKV_DTYPE = 0, ATTN_QKV_E4M3 = 1 } attn_qkv_format_t;
  *    tensors' scales (finite and > 0, else ATTN_E_INVALID); dtype F32 and
  *    the RELPOS bias return ATTN_E_UNSUPPORTED, and so does window_heads
  *    above 1.  Tables, dense bias/mask tensors and out keep the dtype.
+ *  lse: NULL, or device fp32 memory (4-byte aligned, overlapping no input
+ *    or output) that receives each query row's log-sum-exp of its logits,
+ *    L_i = log sum_j exp(scale*q_i.k_j + bias_ij + mask_ij) (natural log):
+ *    [B, H, Nq] contiguous, in the IMAGE layout [images, H, img_h*img_w]
+ *    in image order (padding tokens have no entry).  attn_bwd_opt takes it
+ *    back.  Half precision only (also with 8-bit inputs) and window_heads
+ *    at most 1, else ATTN_E_UNSUPPORTED.
  *  Zero-initialise the struct: fields added later keep 0 as "library's
  *  choice".                                                                  */
 typedef struct {
   int32_t window_heads;
   int32_t qkv_format;
   float q_descale, k_descale, v_descale;
-  int32_t reserved[3];
+  int32_t reserved;
+  float* lse;
 } attn_options_t;
 
 /* attn_fwd_opt / attn_check_opt: attn_fwd / attn_check with options (NULL:
@@ -322,6 +330,29 @@ ATTN_API int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn
              const attn_tensor_t* dv, float* dtable, int32_t dtype, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/* Options of attn_bwd_opt: the forward's results for the same call.
+ *  out: the forward output O (laid out like dout) and lse: its per-row
+ *    log-sum-exp (attn_options_t.lse of the forward).  Given together
+ *    (both non-NULL), the tiled path takes each row's normaliser from lse
+ *    and D_i = sum_j P_ij dP_ij from dO_i . O_i instead of a pass over the
+ *    keys of its own (the identity sum_j P_ij (dO_i . v_j) = dO_i . O_i);
+ *    the window path, which recomputes P exactly, ignores them.  Both NULL:
+ *    identical to attn_bwd.  One of them NULL: ATTN_E_NULL.
+ *  Zero-initialise the struct.                                               */
+typedef struct {
+  const attn_tensor_t* out;
+  const float* lse;
+  int32_t reserved[4];
+} attn_bwd_options_t;
+
+/* attn_bwd_opt: attn_bwd with options (NULL: identical to attn_bwd).        */
+ATTN_API int attn_bwd_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                 const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                 const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
+                 const attn_tensor_t* dv, float* dtable, int32_t dtype,
+                 const attn_bwd_options_t* options, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* attn_bwd_check: the validation of attn_bwd without touching the GPU (the
  * status attn_bwd returns, short of a launch failure).                       */
 ATTN_API int attn_bwd_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
@@ -363,7 +394,7 @@ ATTN_API const char* attn_strerror(int status);
  * attn_bias_desc_t, which grew from 80 to 88 bytes; 1.3 the backward:
  * attn_bwd, attn_bwd_check, attn_bwd_workspace_size; 1.4 8-bit q, k, v:
  * qkv_format and the three scales in attn_options_t, whose size is
- * unchanged).                                                                */
+ * unchanged; 1.5 the lse output of attn_options_t and attn_bwd_opt).        */
 ATTN_API int attn_version(void);
 
 #ifdef __cplusplus

@@ -57,7 +57,12 @@ class MaskDescC(ctypes.Structure):
 class OptionsC(ctypes.Structure):
     _fields_ = [("window_heads", ctypes.c_int32), ("qkv_format", ctypes.c_int32),
                 ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float),
-                ("v_descale", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
+                ("v_descale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("lse", ctypes.c_void_p)]
+
+
+class BwdOptionsC(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("reserved", ctypes.c_int32 * 4)]
 
 
 class AttnError(RuntimeError):
@@ -95,6 +100,10 @@ def lib() -> ctypes.CDLL:
         h.attn_bwd.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         h.attn_bwd.restype = ctypes.c_int
+        h.attn_bwd_opt.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
+                                   ctypes.c_int32, P(BwdOptionsC), ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+        h.attn_bwd_opt.restype = ctypes.c_int
         h.attn_bwd_check.argtypes = [T, T, T, T, P(BiasDescC), P(MaskDescC), T, T, T, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
         h.attn_bwd_check.restype = ctypes.c_int
@@ -275,22 +284,33 @@ def _marshal(q, k, v, out, bias, mask, layout, window, e4m3: bool = False):
             _tensor_c(out, lay), DTYPES[out.dtype], keep)
 
 
-def _options(window_heads: Optional[int], qkv_descale=None):
-    if window_heads is None and qkv_descale is None:
+def _options(window_heads: Optional[int], qkv_descale=None, lse=None):
+    if window_heads is None and qkv_descale is None and lse is None:
         return None
     o = OptionsC()
     o.window_heads = int(window_heads or 0)
     if qkv_descale is not None:
         o.qkv_format = QKV_E4M3
         o.q_descale, o.k_descale, o.v_descale = (float(x) for x in qkv_descale)
+    if lse is not None:
+        o.lse = lse.data_ptr()
     return ctypes.byref(o)
+
+
+def _check_lse(lse, q):
+    if lse is None:
+        return
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise TypeError(f"lse must be a contiguous float32 tensor of shape {tuple(q.shape[:3])}")
+    if lse.device != q.device:
+        raise ValueError("lse must be on the device of q")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         out: Optional[torch.Tensor] = None, layout: str = "batched",
         window: Optional[Window] = None, stream=None,
         window_heads: Optional[int] = None, qkv_descale=None,
-        out_dtype: torch.dtype = torch.float16) -> torch.Tensor:
+        out_dtype: torch.dtype = torch.float16, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O = softmax(QK^T/sqrt(d) + bias + mask) V on the GPU via libattn.
 
     q: [B, H, Nq, d], k, v: [B, H, Nk, d] CUDA (HIP) tensors, last stride 1.
@@ -308,7 +328,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
     ``qkv_descale`` = (q scale, k scale, v scale): q, k and v are E4M3 codes
     (uint8 or float8_e4m3fn tensors) standing for code * scale; the compute
     and output dtype is then ``out``'s, or ``out_dtype`` (f16 or bf16) when
-    ``out`` is allocated here, and the tables must have it.
+    ``out`` is allocated here, and the tables must have it.  ``lse``: an
+    optional float32 tensor [B, H, N] (q's first three dims) that receives
+    each query row's log-sum-exp of its logits (natural log), for ``bwd``.
     """
     h = lib()
     e4m3 = qkv_descale is not None
@@ -322,6 +344,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         # keys is undefined): the library rejects them.
         return out
     qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window, e4m3)
+    _check_lse(lse, q)
     cur = torch.cuda.current_stream(q.device)
     if stream is None:
         s_obj = cur
@@ -340,7 +363,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
         for t in keep + ([out] if allocated else []):
             t.record_stream(s_obj)
     st = h.attn_fwd_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
-                        ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads, qkv_descale),
+                        ctypes.byref(md), ctypes.byref(oc), dt, _options(window_heads, qkv_descale, lse),
                         ctypes.c_void_p(s_obj.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, h.attn_strerror(st).decode())
@@ -350,14 +373,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias=None, mask=None,
 
 def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
           window: Optional[Window] = None, window_heads: Optional[int] = None,
-          qkv_descale=None, out_dtype: torch.dtype = torch.float16) -> int:
+          qkv_descale=None, out_dtype: torch.dtype = torch.float16, lse=None) -> int:
     """Status attn_fwd would return for these arguments (no GPU needed)."""
     h = lib()
     e4m3 = qkv_descale is not None
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype if e4m3 else q.dtype, device=q.device)
     qc, kc, vc, bd, md, oc, dt, keep = _marshal(q, k, v, out, bias, mask, layout, window, e4m3)
-    opts = _options(window_heads, qkv_descale)
+    opts = _options(window_heads, qkv_descale, lse)
     if opts is None:
         return h.attn_check(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
                             ctypes.byref(md), ctypes.byref(oc), dt)
@@ -367,7 +390,8 @@ def check(q, k, v, bias=None, mask=None, out=None, layout: str = "batched",
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, bias=None, mask=None,
         layout: str = "batched", window: Optional[Window] = None, dq=None, dk=None, dv=None,
-        dtable=None, workspace=None, stream=None, no_alloc: bool = False):
+        dtable=None, workspace=None, stream=None, no_alloc: bool = False,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """Gradients of sum(dout * O) for O = fwd(q, k, v, bias, mask) via attn_bwd.
 
     Returns (dq, dk, dv, dtable): dtable is fp32 [table rows, H] with a
@@ -377,7 +401,12 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
     torch when not given; the library itself allocates nothing.  Queued on
     ``stream`` (default: torch's current stream).  ``no_alloc``: call
     attn_bwd_noalloc (the library's fixed device array instead of a
-    workspace; ``workspace`` is then ignored and none is allocated).
+    workspace; ``workspace`` is then ignored and none is allocated).  On a
+    stream other than torch's current one, the kernels are ordered after the
+    work queued on the current stream and the tensors made or passed here
+    stay allocated until the kernels' stream has run them.  ``out`` and
+    ``lse``: the forward's output and log-sum-exp (``fwd(..., lse=...)``),
+    passed to attn_bwd_opt so the tiled path skips its statistics pass.
     """
     h = lib()
     dq = torch.empty_like(q) if dq is None else dq
@@ -393,11 +422,30 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
                              device=q.device)
     if dtable is not None and (dtable.dtype != torch.float32 or not dtable.is_contiguous()):
         raise TypeError("dtable must be a contiguous float32 tensor")
+    # Temporaries made here (contiguous table copies, outputs and workspace
+    # allocated here) live on torch's current stream: a kernel queued on
+    # another stream waits for them, and they stay allocated until that
+    # stream has run it (as in fwd).
+    cur = torch.cuda.current_stream(q.device)
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+        s_obj = cur
+    elif isinstance(stream, torch.cuda.Stream):
+        s_obj = stream
+    else:  # a raw hipStream_t handle
+        s_obj = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)), device=q.device)
+    stream = s_obj.cuda_stream
+    side = s_obj != cur
+
+    def order_temporaries(extra):
+        if side:
+            ev = torch.cuda.Event()
+            ev.record(cur)
+            s_obj.wait_event(ev)
+            for t in keep + [x for x in extra if x is not None]:
+                t.record_stream(s_obj)
+
     if no_alloc:
+        order_temporaries([dq, dk, dv, dtable])
         st = h.attn_bwd_noalloc(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
                                 ctypes.byref(bd), ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc),
                                 ctypes.byref(dvc), ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0),
@@ -413,12 +461,25 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, b
         raise AttnError(st, h.attn_strerror(st).decode())
     if workspace is None and need.value:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    st = h.attn_bwd(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc), ctypes.byref(bd),
-                    ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc), ctypes.byref(dvc),
-                    ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0), dt,
-                    ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0),
-                    ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
-                    ctypes.c_void_p(stream))
+    order_temporaries([dq, dk, dv, dtable, workspace])
+    bopt = None
+    if out is not None or lse is not None:
+        if out is None or lse is None:
+            raise ValueError("out and lse are given together")
+        _check_lse(lse, q)
+        foc = _tensor_c(out, lay)
+        bo = BwdOptionsC()
+        bo.out, bo.lse = ctypes.addressof(foc), lse.data_ptr()
+        bopt = ctypes.byref(bo)
+        if side:
+            out.record_stream(s_obj)
+            lse.record_stream(s_obj)
+    st = h.attn_bwd_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc), ctypes.byref(bd),
+                        ctypes.byref(md), ctypes.byref(dqc), ctypes.byref(dkc), ctypes.byref(dvc),
+                        ctypes.c_void_p(dtable.data_ptr() if dtable is not None else 0), dt, bopt,
+                        ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0),
+                        ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+                        ctypes.c_void_p(stream))
     if st != ATTN_OK:
         raise AttnError(st, h.attn_strerror(st).decode())
     del keep

@@ -252,6 +252,19 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
   if (overlaps(o, es, q, ies) || overlaps(o, es, k, ies) || overlaps(o, es, v, ies)) return ATTN_E_ALIAS;
 
   if (opt) a->win_heads = opt->window_heads;
+  if (opt && opt->lse) {
+    // Per-row log-sum-exp: [B, H, N] fp32 (N: the tokens of q's layout).
+    if (dtype == ATTN_F32) return ATTN_E_UNSUPPORTED;
+    if ((uintptr_t)opt->lse % 4) return ATTN_E_LAYOUT;
+    attn_tensor_t lt{};
+    lt.data = opt->lse;
+    lt.dims[0] = q->dims[0]; lt.dims[1] = q->dims[1]; lt.dims[2] = q->dims[2]; lt.dims[3] = 1;
+    lt.strides[2] = 1; lt.strides[1] = q->dims[2]; lt.strides[0] = q->dims[1] * q->dims[2];
+    if (overlaps(&lt, 4, o, es) || overlaps(&lt, 4, q, ies) || overlaps(&lt, 4, k, ies) ||
+        overlaps(&lt, 4, v, ies))
+      return ATTN_E_ALIAS;
+    a->lse = opt->lse;
+  }
 
   // The kernel the call takes must fit one CU's LDS (and the grid the
   // launch limit); a requested form must exist for the call.
@@ -261,7 +274,7 @@ int validate(const void* qv, const void* kv, const void* vv, const void* biasv,
 
 int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov, const void* biasv,
                  const void* maskv, const void* dqv, const void* dkv, const void* dvv, float* dtable,
-                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes) {
+                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes, const void* optv) {
   if (!ba || !ws_bytes) return ATTN_E_NULL;
   memset(ba, 0, sizeof(*ba));
   *ws_bytes = 0;
@@ -316,6 +329,29 @@ int validate_bwd(const void* qv, const void* kv, const void* vv, const void* dov
                                                    : bwd_rel_rows(ba->a);
     ba->dtable = dtable;
   }
+  // The forward's O and log-sum-exp (attn_bwd_opt): O shaped and laid out
+  // like dout, lse [B, H, Nq] fp32; neither may overlap a gradient.
+  const attn_bwd_options_t* opt = (const attn_bwd_options_t*)optv;
+  if (opt && (opt->out || opt->lse)) {
+    if (!opt->out || !opt->lse) return ATTN_E_NULL;
+    const attn_tensor_t* fo = opt->out;
+    if ((st = check_tensor(fo, es)) != ATTN_OK) return st;
+    for (int i = 0; i < 4; ++i)
+      if (fo->dims[i] != dout->dims[i]) return ATTN_E_SHAPE;
+    if (fo->layout != dout->layout) return ATTN_E_LAYOUT;
+    if ((fo->dims[2] - 1) * fo->strides[2] + fo->dims[3] >= (int64_t(1) << (ba->a.image ? 29 : 31)))
+      return ATTN_E_UNSUPPORTED;
+    if ((uintptr_t)opt->lse % 4) return ATTN_E_LAYOUT;
+    attn_tensor_t lt{};
+    lt.data = (void*)opt->lse;
+    lt.dims[0] = q->dims[0]; lt.dims[1] = q->dims[1]; lt.dims[2] = q->dims[2]; lt.dims[3] = 1;
+    lt.strides[2] = 1; lt.strides[1] = q->dims[2]; lt.strides[0] = q->dims[1] * q->dims[2];
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(outs[i], fo, es) || overlaps(outs[i], es, &lt, 4)) return ATTN_E_ALIAS;
+    ba->fo = fo->data;
+    ba->fo_sb = fo->strides[0]; ba->fo_sh = fo->strides[1]; ba->fo_sn = fo->strides[2];
+    ba->lse_in = opt->lse;
+  }
   *ws_bytes = bwd_workspace_bytes(ba->a, plan.kernel);
   return ATTN_OK;
 }
@@ -357,9 +393,26 @@ int attn_bwd_check(const attn_tensor_t* q, const attn_tensor_t* k, const attn_te
                    size_t workspace_bytes) {
   attn::AttnBwdArgs ba;
   size_t need = 0;
-  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need);
+  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need,
+                              nullptr);
   if (st != ATTN_OK) return st;
   return attn::check_workspace(workspace, workspace_bytes, need);
+}
+
+int attn_bwd_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                 const attn_tensor_t* dout, const attn_bias_desc_t* bias_desc,
+                 const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
+                 const attn_tensor_t* dv, float* dtable, int32_t dtype,
+                 const attn_bwd_options_t* options, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  attn::AttnBwdArgs ba;
+  size_t need = 0;
+  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need,
+                              options);
+  if (st != ATTN_OK) return st;
+  if ((st = attn::check_workspace(workspace, workspace_bytes, need)) != ATTN_OK) return st;
+  ba.ws = (float*)workspace;
+  return attn::launch_bwd(ba, stream);
 }
 
 int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
@@ -367,13 +420,8 @@ int attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t
              const attn_mask_desc_t* mask_desc, const attn_tensor_t* dq, const attn_tensor_t* dk,
              const attn_tensor_t* dv, float* dtable, int32_t dtype, void* workspace,
              size_t workspace_bytes, void* stream) {
-  attn::AttnBwdArgs ba;
-  size_t need = 0;
-  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need);
-  if (st != ATTN_OK) return st;
-  if ((st = attn::check_workspace(workspace, workspace_bytes, need)) != ATTN_OK) return st;
-  ba.ws = (float*)workspace;
-  return attn::launch_bwd(ba, stream);
+  return attn_bwd_opt(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, nullptr, workspace,
+                      workspace_bytes, stream);
 }
 
 int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
@@ -419,6 +467,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return (1 << 16) | 4; }
+int attn_version(void) { return (1 << 16) | 5; }
 
 }  // extern "C"

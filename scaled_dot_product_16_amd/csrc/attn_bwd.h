@@ -578,14 +578,34 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   // Pass 1 state (per lane: partial sums over its keys, against the row
   // maximum m shared by the four lane groups).
   float m = -INFINITY, l = 0.f, t = 0.f, L = 0.f, Dq = 0.f;
+  // With the forward's O and log-sum-exp (attn_bwd_opt) the first pass is
+  // not needed: L from lse (natural log -> log2), D = dO_i . O_i.
+  const bool stats = ba.lse_in != nullptr;
+  if (stats) {
+    L = ba.lse_in[(int64_t)(b * a.H + h) * Nq + qi] * kLog2e;
+    const uint16_t* fop = (const uint16_t*)ba.fo + (int64_t)b * ba.fo_sb + (int64_t)h * ba.fo_sh +
+                          (int64_t)qi * ba.fo_sn;
+    float part = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      if (d0 < D) {
+        const u32x4 ov = *(const u32x4*)(fop + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = E::dot2(df[dc][e], ov[e], part);
+      }
+    }
+    Dq = sum_across_groups(part);
+  }
   f32x4 acc[CBD];
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_it = 2 * ntiles;
-  for (int it = 0; it < n_it; ++it) {
+  const int it0 = stats ? ntiles : 0;  // tile 0 of the pass it starts with is in stage 0
+  for (int it = it0; it < n_it; ++it) {
     const bool second = it >= ntiles;
     const int tile = second ? it - ntiles : it;
-    const int st = it & 1;
+    const int st = (it - it0) & 1;
     const bool more = it + 1 < n_it;
     if (more) {  // the next tile's loads, in flight during this tile
       const int nt = it + 1 >= ntiles ? it + 1 - ntiles : it + 1;

@@ -72,6 +72,7 @@ struct AttnArgs {
   int32_t win_heads; // requested heads per workgroup of the window path (0: library's choice)
   int32_t f8;        // q, k, v are E4M3 codes (their q and k scales are folded into `scale`)
   float v_descale;   // E4M3 inputs: the scale of v, applied with the row-sum division
+  float* lse;        // per-row log-sum-exp output (natural log), or null
 };
 
 // A validated backward call: the forward call (its `o` is the output
@@ -84,9 +85,13 @@ struct AttnBwdArgs {
   int64_t dq_sb, dq_sh, dq_sn;
   int64_t dk_sb, dk_sh, dk_sn;
   int64_t dv_sb, dv_sh, dv_sn;
-  float* dtable;  // [n_tab, H] (TABLE bias) or null
-  float* ws;      // workspace: per-window table gradients [H][n_tab][B], or rows' L and D
-  int32_t n_tab;  // table rows (TABLE bias), else 0
+  float* dtable;  // [n_tab, H] (TABLE bias), [n_tab, D] (RELPOS: [dRh; dRw]) or null
+  float* ws;      // workspace: per-window table gradients [H][n_tab][B], or the tiled path's
+  int32_t n_tab;  // table rows (TABLE bias, RELPOS), else 0
+  // The forward's output O and per-row log-sum-exp (attn_bwd_opt), or null.
+  const void* fo;
+  int64_t fo_sb, fo_sh, fo_sn;
+  const float* lse_in;
 };
 
 // Host-side validation shared by attn_check and attn_fwd.  Returns an ATTN_*
@@ -102,7 +107,7 @@ int launch(const AttnArgs& a, void* stream);
 // call needs) on success.
 int validate_bwd(const void* q, const void* k, const void* v, const void* dout, const void* bias_desc,
                  const void* mask_desc, const void* dq, const void* dk, const void* dv, float* dtable,
-                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes);
+                 int32_t dtype, AttnBwdArgs* ba, size_t* ws_bytes, const void* bwd_options);
 
 // Queue the backward kernels of a validated call.
 int launch_bwd(const AttnBwdArgs& ba, void* stream);

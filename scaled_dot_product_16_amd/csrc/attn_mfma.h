@@ -880,6 +880,18 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // Epilogue: normalise by the row sum (row D of O^T, held by lane group
   // (D%16)/4) and store O (lane holds O[q][cb*16 + g*4 .. +3]).
   uint16_t* obase = (uint16_t*)a.o + tok_base(a, a.o_sb, a.o_sh, b, h);
+  // Row log-sum-exp (natural log) of query qi: m is the row's reference in
+  // log2 units, lsum the row sum against it; one lane group writes it.
+  auto write_lse = [&](int qb, float lsum, int qi) {
+    if (a.lse && g == 0 && qi < a.Nq) {
+      const uint32_t row = tok_row(a, 1, b, qi);
+      if (row != kPadTok) {
+        const int64_t ntok = a.image ? (int64_t)a.img_h * a.img_w : a.Nq;
+        const int img = a.image ? fdiv(b, a.fd_nw) : b;
+        a.lse[((int64_t)img * a.H + h) * ntok + row] = (m[qb] + __builtin_amdgcn_logf(lsum)) * kLn2;
+      }
+    }
+  };
   constexpr int LB = D / 16, LG = (D % 16) / 4, LR = D % 4;
 #ifndef ATTN_STAGE_O
 #define ATTN_STAGE_O 1
@@ -900,6 +912,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         else lsum = sum_across_groups(l[qb]);
         const float inv = (F8 ? a.v_descale : 1.f) / lsum;
         const int r = qb * 16 + (kLean ? lane_id_here() & 15 : l16);
+        write_lse(qb, lsum, q0 + wq0 + r);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const int c0 = cb * 16 + g * 4;
@@ -929,6 +942,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     else lsum = sum_across_groups(l[qb]);
     const float inv = (F8 ? a.v_descale : 1.f) / lsum;
     const int qi = q0 + wq0 + qb * 16 + (kLean ? lane_id_here() & 15 : l16);
+    write_lse(qb, lsum, qi);
     const uint32_t off = qi < a.Nq ? tok_row(a, a.o_sn, b, qi) : kPadTok;
     if (off != kPadTok) {  // rows past Nq and padding tokens are not stored
 #pragma unroll

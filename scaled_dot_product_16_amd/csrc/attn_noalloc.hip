@@ -55,7 +55,8 @@ ATTN_API int attn_bwd_noalloc(const attn_tensor_t* q, const attn_tensor_t* k, co
                               int32_t dtype, void* stream) {
   attn::AttnBwdArgs ba;
   size_t need = 0;
-  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need);
+  int st = attn::validate_bwd(q, k, v, dout, bias_desc, mask_desc, dq, dk, dv, dtable, dtype, &ba, &need,
+                              nullptr);
   if (st != ATTN_OK) return st;
   if (need > attn::kScratchBytes) return ATTN_E_UNSUPPORTED;  // beyond the fixed array
   void* ws = nullptr;

@@ -287,6 +287,12 @@ inline Plan plan_half(const AttnArgs& a) {
     p.kernel = -1;
     return p;
   }
+  // The per-row log-sum-exp output is written by the one-head window form
+  // and the tiled forms.
+  if (a.lse && a.win_heads > 1) {
+    p.kernel = -1;
+    return p;
+  }
   if (a.bias_kind != ATTN_BIAS_RELPOS && a.Nq <= 64 && a.Nk <= 64) {
     p.nw = kWinWaves;
     // Heads per workgroup: one unless the caller asks for more (one head

@@ -373,8 +373,16 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
       }
   }
 
-  float inv = F32 ? 1.f / sum_across_groups(ps) : __builtin_amdgcn_rcpf(sum_across_groups(ps));
+  const float tot = sum_across_groups(ps);
+  float inv = F32 ? 1.f / tot : __builtin_amdgcn_rcpf(tot);
   if constexpr (F8) inv *= a.v_descale;
+  if constexpr (!F32) {
+    // Row log-sum-exp (natural log): mx is the row maximum in log2 units.
+    if (a.lse && g == 0 && wave * 16 + l16 < N && !q_pad) {
+      const int ntok = a.image ? a.img_h * a.img_w : N;
+      a.lse[((int64_t)bimg * H + h) * ntok + q_pix] = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
+    }
+  }
   if (wave * 16 + l16 < N && !q_pad) {
     // Query row wave*16 + l16 is q_tok here, so its pixel is q_pix.
     const uint32_t off = q_pix * (uint32_t)a.o_sn;

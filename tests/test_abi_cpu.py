@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_check", "attn_strerror", "attn_version",
-                          "attn_fwd_opt", "attn_check_opt", "attn_bwd", "attn_bwd_check",
+                          "attn_fwd_opt", "attn_check_opt", "attn_bwd", "attn_bwd_opt", "attn_bwd_check",
                           "attn_bwd_workspace_size", "attn_bwd_noalloc"}
     for n in names:
         assert hasattr(lib, n)
@@ -45,15 +45,16 @@ def test_struct_layout_matches_header(lib):
     assert ctypes.sizeof(B.MaskDescC) == 8 + 8 + 8 + 16 + 24 + 4 + 4
     assert ctypes.sizeof(B.OptionsC) == 32
     assert [B.OptionsC.__dict__[f].offset for f in ("window_heads", "qkv_format", "q_descale",
-                                                   "k_descale", "v_descale", "reserved")] == \
-        [0, 4, 8, 12, 16, 20]
+                                                   "k_descale", "v_descale", "reserved", "lse")] == \
+        [0, 4, 8, 12, 16, 20, 24]
+    assert ctypes.sizeof(B.BwdOptionsC) == 32
 
 
 def test_strerror_and_version(lib):
     for st in range(8):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(99) == b"unknown status"
-    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 4
+    assert lib.attn_version() >> 16 == 1 and lib.attn_version() & 0xFFFF >= 5
 
 
 def t(*shape, dtype=torch.float16):
@@ -439,3 +440,67 @@ def test_e4m3_inputs_validation(lib):
     assert B.check(qa, qs, qs.clone(), out=oa, qkv_descale=sc) == 5
     ob = raw.view(torch.float16)[2 * 8 * 4096 * 40 // 2:].view(2, 8, 4096, 40)  # starts past q's bytes
     assert B.check(qa, qs, qs.clone(), out=ob, qkv_descale=sc) == 0
+
+
+def test_lse_output_validation(lib):
+    # The per-row log-sum-exp output: fp32 [B, H, N], 4-byte aligned, no
+    # overlap; half precision and the one-head window form only.
+    q = t(2, 3, 300, 64)
+    lse = torch.zeros(2, 3, 300)
+    assert B.check(q, q.clone(), q.clone(), lse=lse) == 0
+    qw = t(4, 3, 49, 32)
+    lw = torch.zeros(4, 3, 49)
+    assert B.check(qw, qw.clone(), qw.clone(), lse=lw) == 0
+    assert B.check(qw, qw.clone(), qw.clone(), lse=lw, window_heads=3) == 4
+    qf = t(2, 3, 300, 64, dtype=torch.float32)
+    assert B.check(qf, qf.clone(), qf.clone(), lse=lse) == 4
+    # Image layout: [images, H, img_h*img_w].
+    qi = t(2, 3, 56 * 56, 32)
+    tab = B.TableBias(t(169, 3), (7, 7))
+    geom = B.Window(56, 56, 7, 7, 3, 3)
+    assert B.check(qi, qi.clone(), qi.clone(), bias=tab, mask=B.ShiftMask(geom), layout="image",
+                   lse=torch.zeros(2, 3, 56 * 56)) == 0
+    # Misaligned and overlapping outputs, through the C entry point.
+    raw = torch.zeros(2 * 3 * 300 + 4)
+    o = B.OptionsC()
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(q, q.clone(), q.clone(), t(2, 3, 300, 64), None, None,
+                                                 "batched", None)
+    def st(ptr):
+        o.lse = ptr
+        return lib.attn_check_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(bd),
+                                  ctypes.byref(md), ctypes.byref(oc), dt, ctypes.byref(o))
+    assert st(raw.data_ptr()) == 0
+    assert st(raw.data_ptr() + 2) == 3
+    assert st(q.data_ptr()) == 5          # over q
+    del keep
+
+
+def test_backward_options_validation(lib):
+    # attn_bwd_opt: out and lse together (one alone: E_NULL), out shaped like
+    # dout, lse 4-byte aligned, neither overlapping a gradient.  Only calls
+    # that validation refuses are made here (they return before any HIP call).
+    h = B.lib()
+    ins = [t(1, 2, 300, 64) for _ in range(4)]
+    grads = [t(1, 2, 300, 64) for _ in range(3)]
+    fo, lse = t(1, 2, 300, 64), torch.zeros(1, 2, 300 + 4)
+    qc, kc, vc, bd, md, oc, dt, keep = B._marshal(*ins, None, None, "batched", None)
+    T = lambda x: B._tensor_c(x, 0)
+    d1, d2, d3 = (T(x) for x in grads)
+    ws = torch.zeros(2 * 2 * 300)
+
+    def st(out_t, lse_ptr):
+        bo = B.BwdOptionsC()
+        foc = T(out_t) if out_t is not None else None
+        bo.out = ctypes.addressof(foc) if foc is not None else None
+        bo.lse = lse_ptr
+        return h.attn_bwd_opt(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(oc),
+                              ctypes.byref(bd), ctypes.byref(md), ctypes.byref(d1), ctypes.byref(d2),
+                              ctypes.byref(d3), None, dt, ctypes.byref(bo), ctypes.c_void_p(ws.data_ptr()),
+                              ws.numel() * 4, None)
+    assert st(fo, None) == 1                          # lse missing
+    assert st(None, lse.data_ptr()) == 1              # out missing
+    assert st(t(1, 2, 299, 64), lse.data_ptr()) == 2  # out not shaped like dout
+    assert st(fo, lse.data_ptr() + 2) == 3            # lse misaligned
+    assert st(grads[0], lse.data_ptr()) == 5          # out is dq
+    assert st(fo, grads[1].data_ptr()) == 5           # lse inside dk
+    del keep

@@ -76,3 +76,32 @@ def test_side_stream_with_noncontiguous_mask():
     assert torch.equal(out, ref)
     err = check_full(w, inp, out, name="side stream, strided additive mask")
     say(f"  max abs err {err:.3e} (tol {TOL[w.dtype]:.0e})")
+
+
+@pytest.mark.parametrize("raw_handle", [False, True])
+def test_backward_side_stream_with_noncontiguous_table(raw_handle):
+    # attn_bwd on a side stream: the contiguous table copy, the gradient
+    # outputs and the workspace made by the binding on the current stream
+    # are ordered before the kernels and kept alive until they have run.
+    w = W.custom(W.F16, B=64, H=3, Nq=49, Nk=49, d=32, bias="table", grid=(7, 7), cfg_id=642)
+    say(f"[streams] backward, table bias as a transposed view, side stream (raw handle: {raw_handle})")
+    inp = W.make_inputs(w, seed=3, std_table=0.5)
+    inp["dout"] = W.to_dtype(W.normal(w.q_shape, w.cfg_id, 7, 1.0, 3), w.dtype)
+    dev = to_device(inp)
+    tab = dev["table"].t().contiguous().t()
+    ref = Bd.bwd(dev["q"], dev["k"], dev["v"], dev["dout"], bias=Bd.TableBias(tab, w.grid))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        torch.cuda._sleep(2_000_000)
+        tab = dev["table"].t().contiguous().t()
+        stream = side.cuda_stream if raw_handle else side
+        outs.append(Bd.bwd(dev["q"], dev["k"], dev["v"], dev["dout"], bias=Bd.TableBias(tab, w.grid),
+                           stream=stream))
+        del tab
+        torch.empty(1 << 20, dtype=torch.float16, device="cuda").fill_(7.0)  # would reuse freed memory
+    torch.cuda.synchronize()
+    for o in outs:
+        for x, y in zip(o, ref):
+            assert torch.equal(x, y)
