@@ -170,10 +170,14 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
       // (a padding token of the image layout is a zero query)
-      if constexpr (F8)
-        qf[qb][dc] = d0 < D && off != kPadTok ? widen_e4m3<E>(*(const u32x2*)(qbase + off + d0))
-                                              : u32x4{0, 0, 0, 0};
-      else
+      if constexpr (F8) {
+        // Loaded from an address that is always valid and then selected, so
+        // the loads of all fragments are in flight together (a load inside
+        // the condition would be waited for before its conversion).
+        const bool ok = d0 < D && off != kPadTok;
+        const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
+        qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
+      } else
         qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
     }
   }

@@ -180,10 +180,13 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_fwd_win(AttnArgs a) {
 #pragma unroll
     for (int dc = 0; dc < KCH; ++dc) {
       const int d0 = dc * 32 + g * 8;
-      if constexpr (F8)
-        qf[dc] = d0 < D && !q_pad ? widen_e4m3<E>(__builtin_nontemporal_load((const u32x2*)(qp + q_off + d0)))
-                                  : u32x4{0, 0, 0, 0};
-      else
+      if constexpr (F8) {
+        // Unconditional load (q_off is a valid row, d0 < D here or clamped),
+        // then a select: the load is not waited for inside a branch.
+        const bool ok = d0 < D && !q_pad;
+        const u32x4 wq = widen_e4m3<E>(__builtin_nontemporal_load((const u32x2*)(qp + q_off + (ok ? d0 : 0))));
+        qf[dc] = ok ? wq : u32x4{0, 0, 0, 0};
+      } else
         qf[dc] = d0 < D && !q_pad ? __builtin_nontemporal_load((const u32x4*)(qp + (size_t)(q_off + d0) * 2))
                                   : u32x4{0, 0, 0, 0};
     }
