@@ -395,6 +395,14 @@ struct BwdTileCfg {
   static constexpr int TILE = 64 * ROW;  // elements of one staged tile
 };
 
+// Wait for every vector-memory load this wave has issued (s_waitcnt with
+// vmcnt 0, expcnt and lgkmcnt left at their maxima).  Placed before a key
+// loop whose operands include fragments loaded in the prologue: the
+// compiler's wait analysis cannot see at the loop head that those loads are
+// done, and would otherwise wait in every iteration for the next tile's
+// prefetch as well, taking the overlap away.
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // The CPT 16-byte chunks this thread moves of rows [r0, r0 + 64) of a [N, D]
 // slice (rows clamped to N-1): global -> registers, registers -> LDS tile.
 template <int D>
@@ -602,6 +610,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_it = 2 * ntiles;
   const int it0 = stats ? ntiles : 0;  // tile 0 of the pass it starts with is in stage 0
+  wait_all_vmem();
   for (int it = it0; it < n_it; ++it) {
     const bool second = it >= ntiles;
     const int tile = second ? it - ntiles : it;
@@ -927,6 +936,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   f32x4 dk[CBD], dv[CBD];
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  wait_all_vmem();
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
     const bool more = t + 1 < ntiles;
