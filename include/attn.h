@@ -319,7 +319,7 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
  *  sequences in the batched layout without a mask and with no bias (SD-
  *  style self- and cross-attention) or the RELPOS bias on equal query and
  *  key grids with tables of 2g-1 rows (SAM's windowed and global layers;
- *  grid width 64, or gh + gw <= 84): a row kernel (log-sum-exp, D, dQ and
+ *  grid width 64, or gh + gw <= 84, 83 at d = 80): a row kernel (log-sum-exp, D, dQ and
  *  the relative-position terms) and a column kernel (dK, dV).  Other calls
  *  (fp32, key grids or resized tables, other biases or masks on long
  *  sequences, the image layout beyond 64 tokens) return

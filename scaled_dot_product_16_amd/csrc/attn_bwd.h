@@ -388,7 +388,7 @@ struct BwdTileCfg {
   static constexpr int KCH = (D + 31) / 32;
   static constexpr int DK = KCH * 32;
   static constexpr int CBD = (D + 15) / 16;
-  static constexpr int ROW = DK + 8;
+  static constexpr int ROW = DK + kBwdRowPad;
   static constexpr int RCH = D / 8;
   static constexpr int NCH = 64 * RCH;
   static constexpr int CPT = (NCH + NT - 1) / NT;

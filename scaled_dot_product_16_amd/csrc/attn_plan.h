@@ -217,7 +217,8 @@ constexpr size_t win_pack_lds_bytes(const AttnArgs& a, size_t head_bytes, int hg
 // Window backward kernel (attn_bwd_win): Q, K, V and dO tiles of 64 rows
 // (head dim padded to the 32-wide contraction), P^T and dS^T in the element
 // type (64 keys x 64 queries, rows padded by 8), dS^T in fp32 for the table
-// gradient (rows of 65), then the per-key lookup parts and the table.
+// gradient (rows of 65), then the per-key lookup parts and the table.  (A
+// pad of 16, which the tiled backward takes, measured 2 % slower here.)
 template <int D>
 struct WinBwdCfg {
   static constexpr int NT = kWinWaves * 64;
@@ -395,9 +396,18 @@ inline int make_plan(const AttnArgs& a, Plan* p) {
 // Tiled backward (attn_bwd_rows / attn_bwd_cols) geometry
 // ---------------------------------------------------------------------------
 
+// The staged tiles are read both ways: 16-byte row reads for S and dP, and
+// transposing reads for dQ, dK, dV.  Rows padded by 16 elements past the
+// 32-multiple contraction width have a stride of 8 or 24 dwords modulo 32,
+// which keeps the transposing reads' 4 rows on distinct banks; a pad of 8
+// puts them two to a bank (measured 7 % slower on SD self-attention and SAM
+// global backward).
+constexpr int kBwdRowPad = 16;
+
 // Relative-position forms of the tiled backward: none; general grids (the
 // row kernel keeps per-lane private sums of dRelH/dRelW in LDS, 1280 bytes
-// per column of gh + gw, so gh + gw <= kBwdRelMaxCols); 64-wide grids
+// per column of gh + gw, so gh + gw <= kBwdRelMaxCols, and at d = 80, where
+// the staged tiles are larger, gh + gw <= 83); 64-wide grids
 // (a 64-key tile is one grid row: dRelH is a row sum per tile, dRelW and
 // rel_w stay in registers per key slot).
 constexpr int kBwdRelNone = 0, kBwdRelGeneral = 1, kBwdRelRow64 = 2;
@@ -444,7 +454,7 @@ constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
 constexpr int kBwdARow = 72;
 template <int D>
 constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
-  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  constexpr int ROW = (D + 31) / 32 * 32 + kBwdRowPad;
   size_t s = (size_t)4 * 64 * ROW * 2;
   if (a.bias_kind == ATTN_BIAS_RELPOS) {
     const size_t rows = (size_t)bwd_rel_rows(a);
@@ -458,7 +468,7 @@ constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
 }
 template <int D>
 constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
-  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  constexpr int ROW = (D + 31) / 32 * 32 + kBwdRowPad;
   const int mode = bwd_rel_mode(a);
   if (mode == kBwdRelNone) return 0;
   const size_t g = (size_t)(a.gh + a.gw);
@@ -500,7 +510,7 @@ inline Plan plan_bwd_half(const AttnArgs& a) {
     p.kernel = -1;
     return p;
   }
-  constexpr int ROW = (D + 31) / 32 * 32 + 8;
+  constexpr int ROW = (D + 31) / 32 * 32 + kBwdRowPad;
   p.kernel = kKernMfma;
   p.rmode = bwd_rel_mode(a);
   p.bm = 64;

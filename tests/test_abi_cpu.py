@@ -370,6 +370,16 @@ def test_backward_validation(lib):
     assert bwd_status(q1600, q1600, B.RelposBias(t(79, 32), t(79, 32), (40, 40))) == 0   # gh + gw = 80
     q4096 = t(1, 1, 4096, 64)
     assert bwd_status(q4096, q4096, B.RelposBias(t(127, 64), t(127, 64), (64, 64))) == 0  # 64-wide form
+    # The general form's LDS bound: gh + gw = 84 fits up to d = 64; at d = 80
+    # the larger staged tiles leave room for 83.
+    q42 = t(1, 1, 42 * 42, 64)
+    assert bwd_status(q42, q42, B.RelposBias(t(83, 64), t(83, 64), (42, 42))) == 0
+    q42 = t(1, 1, 42 * 42, 80)
+    assert bwd_status(q42, q42, B.RelposBias(t(83, 80), t(83, 80), (42, 42))) == 4
+    q4241 = t(1, 1, 42 * 41, 80)
+    assert bwd_status(q4241, q4241, B.RelposBias(t(83, 80), t(81, 80), (42, 41))) == 0
+    q43 = t(1, 1, 43 * 42, 32)
+    assert bwd_status(q43, q43, B.RelposBias(t(85, 32), t(83, 32), (43, 42))) == 4
     qi = t(1, 2, 64 * 64, 64)
     img = B.Window(64, 64, 14, 14, 0, 0)
     assert bwd_status(qi, qi, B.RelposBias(t(27, 64), t(27, 64), (14, 14)), layout="image", window=img) == 4
