@@ -417,6 +417,37 @@ __device__ __forceinline__ void load_rows_regs(u32x4* reg, const uint16_t* src, 
   }
 }
 
+// Byte offsets, from a tile's first row, of the CPT 16-byte chunks this
+// thread moves of a 64-row tile with row stride sn (elements).  Offsets that
+// do not fit 32 bits, and chunks past the tile, point past every buffer
+// range (they read zero).
+template <int D>
+__device__ __forceinline__ void tile_chunk_offsets(uint32_t* off, int64_t sn, int tid) {
+  using C = BwdTileCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::CPT; ++c) {
+    const int ch = tid + c * C::NT;
+    const int64_t o = 2 * ((int64_t)(ch / C::RCH) * sn + (ch % C::RCH) * 8);
+    off[c] = ch < C::NCH && o < 0xFFFFFFF0ll ? (uint32_t)o : 0xFFFFFFF0u;
+  }
+}
+
+// Rows [r0, r0 + 64) of an [n, D] slice at src (r0 < n) into registers
+// through a raw buffer resource that ends with row n-1: rows past the slice
+// read as zero.  The resource base is uniform, so the per-tile address work
+// is scalar; the per-chunk offsets come from tile_chunk_offsets.
+template <int D>
+__device__ __forceinline__ void load_tile_regs(u32x4* reg, const uint16_t* src, int64_t sn, int r0, int n,
+                                               const uint32_t* off) {
+  using C = BwdTileCfg<D>;
+  const int64_t span = 2 * ((int64_t)(n - 1 - r0) * sn + D);
+  const auto rs = buffer_rsrc(src + (int64_t)r0 * sn, span < 0xFFFFFFF0ll ? (uint32_t)span : 0xFFFFFFF0u);
+#pragma unroll
+  for (int c = 0; c < C::CPT; ++c) {
+    reg[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], 0, 0);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void store_rows_regs(uint16_t* tile, const u32x4* reg, int tid) {
   using C = BwdTileCfg<D>;
@@ -491,8 +522,11 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   const uint16_t* op = (const uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;  // dO
   const int ntiles = (Nk + 63) / 64;
   u32x4 kreg[C::CPT], vreg[C::CPT];
-  load_rows_regs<D>(kreg, kp, a.k_sn, 0, Nk, tid);
-  load_rows_regs<D>(vreg, vp, a.v_sn, 0, Nk, tid);
+  uint32_t koff[C::CPT], voff[C::CPT];
+  tile_chunk_offsets<D>(koff, a.k_sn, tid);
+  tile_chunk_offsets<D>(voff, a.v_sn, tid);
+  load_tile_regs<D>(kreg, kp, a.k_sn, 0, Nk, koff);
+  load_tile_regs<D>(vreg, vp, a.v_sn, 0, Nk, voff);
   u32x4 qf[KCH], df[KCH];
 #pragma unroll
   for (int dc = 0; dc < KCH; ++dc) {
@@ -503,10 +537,10 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 
   // Relative position: rel_h / rel_w of this workgroup's queries.
   const int gh = a.gh, gw = a.gw, G = gh + gw;
-  const int RS = RP == kBwdRelGeneral ? G : 64;  // row length of `rel` (floats)
+  constexpr int S = kBwdRelS;  // 64-wide form: [grid position][S] arrays
   const size_t stage_bytes = bwd_stage_bytes<D>(a);
-  float* rel = (float*)(lds + stage_bytes);  // general: [64][G]; row form: rel_h [64][64]
-  float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - (RP == kBwdRelGeneral ? 256 * G * 4 : 64 * 64 * 4)) / 4;
+  float* rel = (float*)(lds + stage_bytes);  // general: [64][G]; row form: rel_h^T [64][S]
+  float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - bwd_rows_acc_bytes(a)) / 4;
   const BwdWs wl = bwd_ws_layout(a);
   const int64_t bh = (int64_t)b * a.H + h;
   float* ws_rel = ba.ws + wl.rel + bh * Nq * G;  // [G][Nq] of this (batch item, head)
@@ -544,7 +578,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       for (int i = 0; i < 4; ++i) {  // lane (l16, g) holds rel_h[qloc][16mb + 4g + i]
         const int kh2 = mb * 16 + g * 4 + i;
         if (kh2 < gh) {
-          rel[qloc * 64 + kh2] = acc_h[i];
+          rel[kh2 * S + qloc] = acc_h[i];
           if (qrow < Nq) ws_rel[(int64_t)kh2 * Nq + qrow] = acc_h[i];
         }
       }
@@ -568,11 +602,12 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kw = (i >> 2) * 16 + g * 4 + (i & 3);
-      wreg[i] = gwl[(qloc - kw + 63) * 64 + qloc];
-      if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = wreg[i];
+      const float w = gwl[(qloc - kw + 63) * 64 + qloc];
+      if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = w;
+      wreg[i] = w * kLog2e;  // log2 units in the key loop
       wacc[i] = 0.f;
     }
-    for (int e = tid; e < 64 * 64; e += 256) dacc[e] = 0.f;
+    for (int e = tid; e < 64 * S; e += 256) dacc[e] = 0.f;
     __syncthreads();  // the stages are written below
   }
 
@@ -605,28 +640,37 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     }
     Dq = sum_across_groups(part);
   }
+  // Second-pass forms: the logits enter as scale*log2(e)*s + bias - L (yoff
+  // = -L; 0 in the first pass), and dP accumulates onto -D (dinit), so that
+  // P = exp2(y) and dS = P * dP take no further subtraction.
+  float yoff = stats ? -L : 0.f;
+  f32x4 dinit = stats ? f32x4{-Dq, -Dq, -Dq, -Dq} : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc[CBD];
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_it = 2 * ntiles;
   const int it0 = stats ? ntiles : 0;  // tile 0 of the pass it starts with is in stage 0
-  wait_all_vmem();
-  for (int it = it0; it < n_it; ++it) {
-    const bool second = it >= ntiles;
+  // One step of the key loop: iteration it of the two passes over the key
+  // tiles (it < ntiles: statistics; it >= ntiles: gradients).  Each pass
+  // runs as a loop of its own, so that the compiler keeps each pass's
+  // state in place; the next tile's loads cross the pass boundary.
+  auto step = [&](int it, auto pass) {
+    constexpr bool second = decltype(pass)::value;
     const int tile = second ? it - ntiles : it;
     const int st = (it - it0) & 1;
     const bool more = it + 1 < n_it;
     if (more) {  // the next tile's loads, in flight during this tile
       const int nt = it + 1 >= ntiles ? it + 1 - ntiles : it + 1;
-      load_rows_regs<D>(kreg, kp, a.k_sn, nt * 64, Nk, tid);
-      load_rows_regs<D>(vreg, vp, a.v_sn, nt * 64, Nk, tid);
+      load_tile_regs<D>(kreg, kp, a.k_sn, nt * 64, Nk, koff);
+      load_tile_regs<D>(vreg, vp, a.v_sn, nt * 64, Nk, voff);
     }
     const uint16_t* Kt = Ks + st * TILE;
     const uint16_t* Vt = Vs + st * TILE;
     f32x4 s[4], dp[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = dinit;
 #pragma unroll
       for (int dc = 0; dc < KCH; ++dc) {
         s[kb] = E::mfma(*(const u32x4*)&Kt[(kb * 16 + l16) * ROW + dc * 32 + g * 8], qf[dc], s[kb]);
@@ -635,29 +679,33 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     }
     float y[16];
     int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
-    float bias_row = 0.f;  // 64-wide form: rel_h of this tile's grid row
-    if constexpr (RP == kBwdRelRow64) bias_row = rel[qloc * 64 + tile];
+    // The 64-wide form: rel_h of this tile's grid row, with yoff folded in.
+    float yrow = yoff;
+    if constexpr (RP == kBwdRelRow64) yrow = fmaf(rel[tile * S + qloc], kLog2e, yoff);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
+      const float sv = s[i >> 2][i & 3];
       if constexpr (RP == kBwdRelNone) {
-        y[i] = key < Nk ? s[i >> 2][i & 3] * c2 : -INFINITY;
+        y[i] = fmaf(sv, c2, yoff);
+      } else if constexpr (RP == kBwdRelGeneral) {
+        // Keys past Nk read the last key's entries (masked below).
+        const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
+        const int kc = min(key, Nk - 1);
+        kh_i[i] = fdiv(kc, a.fd_gw);
+        kw_i[i] = kc - kh_i[i] * gw;
+        const float bias = rel[qloc * G + kh_i[i]] + rel[qloc * G + gh + kw_i[i]];
+        y[i] = fmaf(bias, kLog2e, fmaf(sv, c2, yoff));
       } else {
-        // The bias is read for every slot (keys past Nk read the last key's
-        // entries) and those keys get -inf added: no branch around the reads.
-        float bias;
-        if constexpr (RP == kBwdRelGeneral) {
-          const int kc = min(key, Nk - 1);
-          kh_i[i] = fdiv(kc, a.fd_gw);
-          kw_i[i] = kc - kh_i[i] * gw;
-          bias = rel[qloc * RS + kh_i[i]] + rel[qloc * RS + gh + kw_i[i]];
-        } else {
-          bias = bias_row + wreg[i];
-        }
-        y[i] = fmaf(bias, kLog2e, s[i >> 2][i & 3] * c2) + (key < Nk ? 0.f : -INFINITY);
+        y[i] = fmaf(sv, c2, yrow) + wreg[i];
       }
     }
-    if (!second) {
+    // Keys past Nk only occur in the last tile (a uniform branch).
+    if (tile * 64 + 64 > Nk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3) >= Nk) y[i] = -INFINITY;
+    }
+    if constexpr (!second) {
       float mx = y[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
@@ -677,11 +725,13 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         const float lt = sum_across_groups(l);
         L = m + __builtin_amdgcn_logf(lt);  // log2 of the row sum
         Dq = sum_across_groups(t) / lt;
+        yoff = -L;
+        dinit = f32x4{-Dq, -Dq, -Dq, -Dq};
       }
     } else {
       float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i] - L) * (dp[i >> 2][i & 3] - Dq);
+      for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i]) * dp[i >> 2][i & 3];
       if constexpr (RP == kBwdRelGeneral) {
         // Private sums of this lane (keys past Nk have dS = 0).
         float* my = dacc + tid * G;
@@ -698,7 +748,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
           wacc[i] += ds[i];
         }
         rs = sum_across_groups(rs);
-        if (g == 0) dacc[qloc * 64 + tile] = rs;
+        if (g == 0) dacc[tile * S + qloc] = rs;
       }
       u32x4 sf[2];
 #pragma unroll
@@ -722,17 +772,20 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       store_rows_regs<D>(Vs + (st ^ 1) * TILE, vreg, tid);
     }
     __syncthreads();
-  }
+  };
+  wait_all_vmem();
+  for (int it = it0; it < ntiles; ++it) step(it, std::false_type{});
+  for (int it = ntiles; it < n_it; ++it) step(it, std::true_type{});
   float* wsL = ba.ws + (int64_t)(b * a.H + h) * Nq;
   float* wsD = wsL + (int64_t)a.B * a.H * Nq;
   f32x4 bq[CBD];  // bias path of dQ (already in final units)
 #pragma unroll
   for (int cb = 0; cb < CBD; ++cb) bq[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (RP != kBwdRelNone) {
-    const int RH = 2 * gh - 1, RT = RH + 2 * gw - 1;
+    const int RH = 2 * gh - 1, RW = 2 * gw - 1, RT = RH + RW;
     // dRel of this workgroup's queries: general grids sum the four lane
-    // groups' private rows into `rel` [64][G]; the row form has dRelH in
-    // `dacc` [64][64] and writes dRelW from registers into `rel` [64][64].
+    // groups' private rows into `rel` [64][G]; the row form has dRelH^T in
+    // `dacc` [64][S] and writes dRelW^T from registers into `rel` [64][S].
     if constexpr (RP == kBwdRelGeneral) {
       for (int e = tid; e < 64 * G; e += 256) {
         const int ql = e / G, x = e - ql * G;
@@ -742,39 +795,17 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rel[qloc * 64 + (i >> 2) * 16 + g * 4 + (i & 3)] = wacc[i];
+      for (int i = 0; i < 16; ++i) rel[((i >> 2) * 16 + g * 4 + (i & 3)) * S + qloc] = wacc[i];
     }
-    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : dacc[ql * 64 + x]; };
-    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : rel[ql * 64 + x]; };
-    // The stacked tables [Rh; Rw] into the free K/V stages.
-    uint16_t* Rs = (uint16_t*)lds;
-    for (int e = tid * 8; e < RT * D; e += 256 * 8)
-      *(u32x4*)&Rs[e] = e < RH * D ? *(const u32x4*)(rhp + e) : *(const u32x4*)(rwp + (e - RH * D));
+    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : dacc[x * S + ql]; };
+    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : rel[x * S + ql]; };
     __syncthreads();
-    {
-      const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * gw;
-      const int c0 = g * 4;  // this lane's columns: cb*16 + c0 .. +3
-      auto add_rows = [&](float w, int row) {
-        const uint16_t* rr = Rs + row * D + c0;
-#pragma unroll
-        for (int cb = 0; cb < CBD; ++cb) {
-          if (cb * 16 + c0 < D) {
-            const u32x2 r2 = *(const u32x2*)(rr + cb * 16);
-            bq[cb][0] = fmaf(w, E::to_f((uint16_t)(r2[0] & 0xFFFF)), bq[cb][0]);
-            bq[cb][1] = fmaf(w, E::to_f((uint16_t)(r2[0] >> 16)), bq[cb][1]);
-            bq[cb][2] = fmaf(w, E::to_f((uint16_t)(r2[1] & 0xFFFF)), bq[cb][2]);
-            bq[cb][3] = fmaf(w, E::to_f((uint16_t)(r2[1] >> 16)), bq[cb][3]);
-          }
-        }
-      };
-      for (int x = 0; x < gh; ++x) add_rows(d_relh(qloc, x), qh - x + gh - 1);
-      for (int x = 0; x < gw; ++x) add_rows(d_relw(qloc, x), RH + qw - x + gw - 1);
-    }
-    __syncthreads();  // the stages are rewritten below
-    // Coefficients A[r][i] (E, rows padded to a multiple of 16 with zeros).
-    const int RB = (RT + 15) / 16;
-    uint16_t* Am = (uint16_t*)lds;  // [RB*16][kBwdARow]
-    for (int e = tid; e < RB * 16 * 64; e += 256) {
+    // Coefficients A[r][i] (element type) in the free K/V stages: the weight
+    // of table row r (Rh rows, then Rw rows) in query i's bias; zero for
+    // rows RT .. AR-1 and queries past Nq.
+    const int AR = bwd_rel_arows(a);
+    uint16_t* Am = (uint16_t*)lds;  // [AR][kBwdARow]
+    for (int e = tid; e < AR * 64; e += 256) {
       const int r = e >> 6, ql = e & 63, qr = qt * 64 + ql;
       float v = 0.f;
       if (r < RT && qr < Nq) {
@@ -789,7 +820,38 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
       Am[r * kBwdARow + ql] = (uint16_t)(E::pack2(v, 0.f) & 0xFFFF);
     }
-    __syncthreads();  // `rel` and `dacc` are free: the Q tile goes there
+    __syncthreads();  // `rel` and `dacc` are free: the tables, then the Q tile go there
+    // Bias path of dQ on the matrix cores, one table at a time:
+    //   dQ_bias^T[c][i] = sum_r T^T[c][r] A[r0 + r][i]  (T = Rh, r0 = 0; T = Rw, r0 = RH).
+    // Both operands by transposing reads (the table staged with rows padded
+    // to 32 by zeros, A as it stands), so their K orders agree; the result
+    // has the layout of the dQ accumulators.
+    {
+      constexpr int TR = bwd_rel_tab_row<D>();
+      uint16_t* Tb = (uint16_t*)rel;
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        const int nr = half ? RW : RH, r0 = half ? RH : 0, nrp = bwd_up32(nr);
+        const uint16_t* src = half ? rwp : rhp;
+        for (int e = tid * 8; e < nrp * TR; e += 256 * 8) {
+          const int row = e / TR, col = e - row * TR;
+          *(u32x4*)&Tb[e] = row < nr && col < D ? *(const u32x4*)(src + row * D + col) : u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+        for (int kc = 0; kc < nrp / 32; ++kc) {
+          const uint16_t* aptr = Am + (r0 + kc * 32 + vt_row) * kBwdARow + wave * 16 + vt_col;
+          const u32x2 blo = lds_read_tr16(aptr), bhi = lds_read_tr16(aptr + 16 * kBwdARow);
+#pragma unroll
+          for (int cb = 0; cb < CBD; ++cb) {
+            const uint16_t* tptr = Tb + (kc * 32 + vt_row) * TR + cb * 16 + vt_col;
+            const u32x2 tlo = lds_read_tr16(tptr), thi = lds_read_tr16(tptr + 16 * TR);
+            bq[cb] = E::mfma(u32x4{tlo[0], tlo[1], thi[0], thi[1]}, u32x4{blo[0], blo[1], bhi[0], bhi[1]}, bq[cb]);
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const int RB = (RT + 15) / 16;
     uint16_t* Qs = (uint16_t*)rel;
     {
       u32x4 qreg[C::CPT];
@@ -884,32 +946,42 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   constexpr int RC = RP == kBwdRelNone ? 1 : RP == kBwdRelRow64 ? 17 : (kBwdRelMaxCols * 64 + 255) / 256;
   float rreg[RC];
   u32x4 qreg[C::CPT], oreg[C::CPT];
-  float lreg = INFINITY, dreg = 0.f;  // rows past Nq: P = 0
+  uint32_t qoff[C::CPT], ooff[C::CPT];
+  tile_chunk_offsets<D>(qoff, a.q_sn, tid);
+  tile_chunk_offsets<D>(ooff, a.o_sn, tid);
+  float lreg = 0.f, dreg = 0.f;
+  // Query rows past Nq read as zero (Q, dO, their D); their L is set to
+  // +inf when staged, so that P = 0 for them whatever their bias.
   auto load_tile = [&](int t) {
-    load_rows_regs<D>(qreg, qp, a.q_sn, t * 64, Nq, tid);
-    load_rows_regs<D>(oreg, op, a.o_sn, t * 64, Nq, tid);
+    load_tile_regs<D>(qreg, qp, a.q_sn, t * 64, Nq, qoff);
+    load_tile_regs<D>(oreg, op, a.o_sn, t * 64, Nq, ooff);
     if (tid < 64) {
-      const int q = t * 64 + tid;
-      lreg = q < Nq ? wsL[q] : INFINITY;
-      dreg = q < Nq ? wsD[q] : 0.f;
+      const uint32_t nb = (uint32_t)(Nq - t * 64) * 4;
+      lreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(wsL + t * 64, nb), tid * 4, 0, 0));
+      dreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(wsD + t * 64, nb), tid * 4, 0, 0));
     }
     if constexpr (RP != kBwdRelNone) {
+      // [G][Nq] floats of this (batch item, head): at most 128 x 4096.
+      const auto rr = buffer_rsrc(ws_rel, (uint32_t)(G * Nq) * 4);
 #pragma unroll
       for (int c = 0; c < RC; ++c) {
         const int e = tid + c * 256, x = e >> 6, q = t * 64 + (e & 63);
         // Column x of the stage: rel_h / rel_w column (the 64-wide form
-        // stages column kt of rel_h, then the 64 rel_w columns).
+        // stages column kt of rel_h, then the 64 rel_w columns).  Rows past
+        // Nq read another column's finite entries or zero; their P is 0.
         const int col = RP == kBwdRelGeneral ? x : (x == 0 ? kt : gh + x - 1);
-        rreg[c] = e < 64 * NC && q < Nq ? ws_rel[(int64_t)col * Nq + q] : 0.f;
+        if (e < 64 * NC) rreg[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(col * Nq + q) * 4, 0, 0));
       }
     }
   };
-  auto store_tile = [&](int st) {
+  // L and D are staged negated: the exponent is scale*log2(e)*s + bias - L
+  // with one FMA, and dP accumulates onto -D.
+  auto store_tile = [&](int st, int t) {
     store_rows_regs<D>(Qs + st * TILE, qreg, tid);
     store_rows_regs<D>(Os + st * TILE, oreg, tid);
     if (tid < 64) {
-      Ls[st * 64 + tid] = lreg;
-      Ds[st * 64 + tid] = dreg;
+      Ls[st * 64 + tid] = t * 64 + tid < Nq ? -lreg : -INFINITY;
+      Ds[st * 64 + tid] = -dreg;
     }
     if constexpr (RP != kBwdRelNone) {
 #pragma unroll
@@ -929,7 +1001,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     vf[dc] = d0 < D ? *(const u32x4*)(vp + (int64_t)ki * a.v_sn + d0) : u32x4{0, 0, 0, 0};
   }
   zero_pad_cols<D>(Qs, 4, tid);  // both stages of Q and dO
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
   const float c2 = a.scale * kLog2e;
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
@@ -945,12 +1017,13 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     const uint16_t* Ot = Os + st * TILE;
     const float* Lt = Ls + st * 64;
     const float* Dt = Ds + st * 64;
-    // S = Q K^T and dP = dO V^T: rows are queries qb*16 + g*4 + r, the
+    // S = Q K^T and dP = dO V^T - D: rows are queries qb*16 + g*4 + r, the
     // column is this lane's key.
     f32x4 s[4], dp[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      s[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[qb] = *(const f32x4*)&Dt[qb * 16 + g * 4];
 #pragma unroll
       for (int dc = 0; dc < KCH; ++dc) {
         s[qb] = E::mfma(*(const u32x4*)&Qt[(qb * 16 + l16) * ROW + dc * 32 + g * 8], kf[dc], s[qb]);
@@ -960,18 +1033,17 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     float p[16], ds[16];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 Lq = *(const f32x4*)&Lt[qb * 16 + g * 4];
-      const f32x4 Dv = *(const f32x4*)&Dt[qb * 16 + g * 4];
+      const f32x4 nL = *(const f32x4*)&Lt[qb * 16 + g * 4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float y = s[qb][r] * c2;
+        float y = fmaf(s[qb][r], c2, nL[r]);
         if constexpr (RP != kBwdRelNone) {
           const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4 + r;
           y = fmaf(rs[xh * 64] + rs[xw * 64], kLog2e, y);
         }
-        const float pv = __builtin_amdgcn_exp2f(y - Lq[r]);
+        const float pv = __builtin_amdgcn_exp2f(y);
         p[qb * 4 + r] = pv;
-        ds[qb * 4 + r] = pv * (dp[qb][r] - Dv[r]);
+        ds[qb * 4 + r] = pv * dp[qb][r];
       }
     }
     u32x4 pf[2], sf[2];
@@ -994,7 +1066,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         dv[cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pf[kc], dv[cb]);
         dk[cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kc], dk[cb]);
       }
-    if (more) store_tile(st ^ 1);  // stage st^1 was last read before the previous barrier
+    if (more) store_tile(st ^ 1, t + 1);  // stage st^1 was last read before the previous barrier
     __syncthreads();
   }
   if (krow < Nk) {
@@ -1016,16 +1088,29 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 // workgroups p of part[p][o] (o = r*D + c over the stacked [Rh; Rw] rows).
 // One workgroup of 16 waves per 64 outputs: wave w adds p = w, w+16, ... in
 // order, then the 16 partial sums are added in a fixed order (bitwise
-// deterministic).  (A template only so that every compiled instance may
-// carry its copy.)
+// deterministic).  The loads of 8 parts are issued together before they are
+// added (in the same order), so each wave keeps 8 in flight instead of
+// waiting for one at a time.  (A template only so that every compiled
+// instance may carry its copy.)
 template <int>
 __global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* out, int n_out, int n_part) {
   __shared__ float red[16][64];
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, w = tid >> 6;
   const int o = __builtin_amdgcn_workgroup_id_x() * 64 + lane;
   float acc = 0.f;
-  if (o < n_out)
-    for (int p = w; p < n_part; p += 16) acc += part[(size_t)p * n_out + o];
+  if (o < n_out) {
+    const float* src = part + o;
+    const size_t step = (size_t)16 * n_out;
+    int p = w;
+    for (; p + 7 * 16 < n_part; p += 8 * 16) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = src[(size_t)p * n_out + j * step];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+    for (; p < n_part; p += 16) acc += src[(size_t)p * n_out];
+  }
   red[w][lane] = acc;
   __syncthreads();
   if (w == 0 && o < n_out) {

@@ -446,25 +446,50 @@ constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
   return w;
 }
 
-// LDS of the row kernel: the K/V stages, also used after the key loop for
-// the stacked tables [Rh; Rw] (elements) and the coefficient matrix of the
-// table-gradient product ([16*ceil(rows/16)][kBwdARow] elements); then the
-// relative-position region: rel_h/rel_w (later dRel and the Q tile) and the
-// dRel sums.
-constexpr int kBwdARow = 72;
+// LDS of the row kernel: the K/V stages, used after the key loop for the
+// coefficient matrix A of the table-gradient products ([bwd_rel_arows][
+// kBwdARow] elements; a row stride of 40 dwords keeps the transposing reads
+// of A on distinct banks); then the relative-position region: rel_h/rel_w
+// (later dRel, one staged table, the Q tile) and the dRel sums.  The 64-wide
+// form keeps rel_h / dRelH / dRelW as [64 grid positions][kBwdRelS] floats,
+// position-major, so that a wave's 16 queries touch consecutive words.
+constexpr int kBwdARow = 80;
+constexpr int kBwdRelS = 68;
+constexpr int bwd_up32(int n) { return (n + 31) / 32 * 32; }
+// Rows of A: each table's rows padded to 32 for the dQ products (Rh rows
+// from 0, Rw rows from 2gh-1) and all rows padded to 16 for the partial.
+constexpr int bwd_rel_arows(const AttnArgs& a) {
+  const int rh = 2 * a.gh - 1, rw = 2 * a.gw - 1;
+  const int x = bwd_up32(rh) > rh + bwd_up32(rw) ? bwd_up32(rh) : rh + bwd_up32(rw);
+  const int y = (rh + rw + 15) / 16 * 16;
+  return x > y ? x : y;
+}
+// One table staged for the dQ products: rows padded to 32, row stride
+// bwd_rel_tab_row elements (CBD*16 columns plus the transposing-read pad).
+template <int D>
+constexpr int bwd_rel_tab_row() {
+  return (D + 15) / 16 * 16 + v_row_pad((D + 15) / 16 * 16);
+}
+template <int D>
+constexpr size_t bwd_rel_tab_bytes(const AttnArgs& a) {
+  const int rh = bwd_up32(2 * a.gh - 1), rw = bwd_up32(2 * a.gw - 1);
+  return (size_t)(rh > rw ? rh : rw) * bwd_rel_tab_row<D>() * 2;
+}
 template <int D>
 constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
   constexpr int ROW = (D + 31) / 32 * 32 + kBwdRowPad;
   size_t s = (size_t)4 * 64 * ROW * 2;
   if (a.bias_kind == ATTN_BIAS_RELPOS) {
-    const size_t rows = (size_t)bwd_rel_rows(a);
-    const size_t am = (rows + 15) / 16 * 16 * kBwdARow * 2, tb = rows * D * 2;
+    const size_t am = (size_t)bwd_rel_arows(a) * kBwdARow * 2;
     s = s > am ? s : am;
-    s = s > tb ? s : tb;
     // 64-wide form: the prologue's G_w[128][64] floats.
     if (bwd_rel_mode(a) == kBwdRelRow64 && s < (size_t)128 * 64 * 4) s = (size_t)128 * 64 * 4;
   }
   return (s + 15) / 16 * 16;
+}
+// Bytes of the dRel sums at the end of the relative-position region.
+constexpr size_t bwd_rows_acc_bytes(const AttnArgs& a) {
+  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * (a.gh + a.gw) * 4 : (size_t)64 * kBwdRelS * 4;
 }
 template <int D>
 constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
@@ -472,11 +497,12 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
   const int mode = bwd_rel_mode(a);
   if (mode == kBwdRelNone) return 0;
   const size_t g = (size_t)(a.gh + a.gw);
-  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : (size_t)64 * 64 * 4;
+  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : (size_t)64 * kBwdRelS * 4;
   const size_t qt = (size_t)64 * ROW * 2;
   rel = (rel > qt ? rel : qt);
+  const size_t acc = bwd_rows_acc_bytes(a), tab = bwd_rel_tab_bytes<D>(a);
+  if (rel + acc < tab) rel = tab - acc;
   rel = (rel + 15) / 16 * 16;
-  const size_t acc = mode == kBwdRelGeneral ? 256 * g * 4 : (size_t)64 * 64 * 4;
   return rel + acc;
 }
 // Columns of rel_h / rel_w the column kernel stages per query: all of them
