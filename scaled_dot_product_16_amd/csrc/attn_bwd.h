@@ -471,20 +471,6 @@ __device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int ti
   }
 }
 
-// Dot product of two rows of D elements of E (16-byte aligned), in fp32,
-// two elements per instruction.
-template <class E, int D>
-__device__ __forceinline__ float dot_rows(const uint16_t* x, const uint16_t* y) {
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const u32x4 xv = *(const u32x4*)(x + c), yv = *(const u32x4*)(y + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s = E::dot2(xv[e], yv[e], s);
-  }
-  return s;
-}
-
 // RP: relative-position form (kBwdRelNone / kBwdRelGeneral / kBwdRelRow64).
 // With the relative position (equal gh x gw grids, tables of 2g-1 rows) the
 // bias of query i and key j = (kh, kw) is rel_h[i][kh] + rel_w[i][kw],
@@ -543,21 +529,44 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - bwd_rows_acc_bytes(a)) / 4;
   const BwdWs wl = bwd_ws_layout(a);
   const int64_t bh = (int64_t)b * a.H + h;
-  float* ws_rel = ba.ws + wl.rel + bh * Nq * G;  // [G][Nq] of this (batch item, head)
+  // [G][Nq] of this (batch item, head), in log2 units (the column kernel's form).
+  float* ws_rel = ba.ws + wl.rel + bh * Nq * G;
   const uint16_t* rhp = (const uint16_t*)a.rh;
   const uint16_t* rwp = (const uint16_t*)a.rw;
   float wreg[RP == kBwdRelRow64 ? 16 : 1], wacc[RP == kBwdRelRow64 ? 16 : 1];
+  const int GP = G | 1;  // general form: private rows of an odd stride (distinct banks per lane)
   if constexpr (RP == kBwdRelGeneral) {
-    for (int e = tid; e < 64 * G; e += 256) {
-      const int ql = e / G, x = e - ql * G;
-      const int qr = min(qt * 64 + ql, Nq - 1);
-      const int qh = fdiv(qr, a.fd_gw), qw = qr - qh * gw;
-      const uint16_t* trow = x < gh ? rhp + (int64_t)(qh - x + gh - 1) * D : rwp + (int64_t)(qw - (x - gh) + gw - 1) * D;
-      const float val = dot_rows<E, D>(qp + (int64_t)qr * a.q_sn, trow);
-      rel[e] = val;
-      if (qt * 64 + ql < Nq) ws_rel[(int64_t)x * Nq + qt * 64 + ql] = val;
+    // rel_h[q][x] = Rh[qh - x + gh - 1] . q (rel_w likewise) from the
+    // products G[m][q] = T[m] . q of every table row m with the wave's 16
+    // queries on the matrix cores (query fragments as the B operand).  Lane
+    // (query, g) then holds rows m = 16mb + 4g + i and keeps those its query
+    // uses: each (query, x) comes from exactly one row.
+    const int qh = fdiv(qi, a.fd_gw), qw = qi - qh * gw;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int nr = half ? 2 * gw - 1 : 2 * gh - 1, ng = half ? gw : gh, q0 = half ? qw : qh;
+      const uint16_t* tp = half ? rwp : rhp;
+      for (int mb = 0; mb < (nr + 15) / 16; ++mb) {
+        const int m = min(mb * 16 + l16, nr - 1);
+        f32x4 acc_t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) {
+          const int d0 = dc * 32 + g * 8;
+          const u32x4 t = *(const u32x4*)(tp + (int64_t)m * D + (d0 < D ? d0 : 0));
+          acc_t = E::mfma(d0 < D ? t : u32x4{0, 0, 0, 0}, qf[dc], acc_t);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mm = mb * 16 + g * 4 + i, x = q0 - mm + ng - 1;
+          if (mm < nr && x >= 0 && x < ng) {
+            const int col = half ? gh + x : x;
+            rel[qloc * G + col] = acc_t[i];
+            if (qrow < Nq) ws_rel[(int64_t)col * Nq + qrow] = acc_t[i] * kLog2e;
+          }
+        }
+      }
     }
-    for (int e = tid; e < 256 * G; e += 256) dacc[e] = 0.f;
+    for (int e = tid; e < 256 * GP; e += 256) dacc[e] = 0.f;
   } else if constexpr (RP == kBwdRelRow64) {
     // gw = 64: the workgroup's 64 queries are grid row qt, and a 64-key tile
     // is one grid row.  rel_h^T[kh][q] = Rh[qt + gh - 1 - kh] . q and
@@ -579,7 +588,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         const int kh2 = mb * 16 + g * 4 + i;
         if (kh2 < gh) {
           rel[kh2 * S + qloc] = acc_h[i];
-          if (qrow < Nq) ws_rel[(int64_t)kh2 * Nq + qrow] = acc_h[i];
+          if (qrow < Nq) ws_rel[(int64_t)kh2 * Nq + qrow] = acc_h[i] * kLog2e;
         }
       }
     }
@@ -602,9 +611,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kw = (i >> 2) * 16 + g * 4 + (i & 3);
-      const float w = gwl[(qloc - kw + 63) * 64 + qloc];
-      if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = w;
-      wreg[i] = w * kLog2e;  // log2 units in the key loop
+      wreg[i] = gwl[(qloc - kw + 63) * 64 + qloc] * kLog2e;  // log2 units
+      if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = wreg[i];
       wacc[i] = 0.f;
     }
     for (int e = tid; e < 64 * S; e += 256) dacc[e] = 0.f;
@@ -734,7 +742,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i]) * dp[i >> 2][i & 3];
       if constexpr (RP == kBwdRelGeneral) {
         // Private sums of this lane (keys past Nk have dS = 0).
-        float* my = dacc + tid * G;
+        float* my = dacc + tid * GP;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           my[kh_i[i]] += ds[i];
@@ -790,8 +798,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       for (int e = tid; e < 64 * G; e += 256) {
         const int ql = e / G, x = e - ql * G;
         const int base = (ql >> 4) * 64 + (ql & 15);
-        rel[e] = ((dacc[base * G + x] + dacc[(base + 16) * G + x]) + dacc[(base + 32) * G + x]) +
-                 dacc[(base + 48) * G + x];
+        rel[e] = ((dacc[base * GP + x] + dacc[(base + 16) * GP + x]) + dacc[(base + 32) * GP + x]) +
+                 dacc[(base + 48) * GP + x];
       }
     } else {
 #pragma unroll
@@ -902,9 +910,10 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 }
 
 // RP: as for the row kernel; the bias of (query i, this lane's key) comes
-// from the rel_h / rel_w rows the row kernel stored, staged per query tile
-// ([columns][64] floats: all gh + gw columns, or the key tile's grid row
-// and the 64 columns of the 64-wide form).
+// from the rel_h / rel_w rows the row kernel stored: for general grids all
+// gh + gw columns staged per query tile in log2 units ([columns][64]
+// floats); in the 64-wide form the key tile's rel_h column joins the staged
+// log-sum-exp and each lane reads its own rel_w column.
 template <class E, int D, int RP = kBwdRelNone>
 __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   using C = BwdTileCfg<D>;
@@ -937,19 +946,33 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   const int NC = bwd_cols_rel_cols(a);
   float* Rst = Ds + 2 * 64;  // [2][NC][64]
   const float* ws_rel = ba.ws + bwd_ws_layout(a).rel + ((int64_t)b * a.H + h) * Nq * G;
+  // Columns of this lane's key: rel_h column kh and rel_w column gh + kw.
+  // General grids stage all columns per query tile (each is shared by the
+  // keys of one grid row or column).  The 64-wide form folds the tile's
+  // rel_h column (grid row kt) into the staged L and reads the lane's own
+  // rel_w column straight from the workspace (one consumer per entry).
   int xh = 0, xw = 0;
   if constexpr (RP != kBwdRelNone) {
     const int kh = fdiv(ki, a.fd_gw), kw = ki - kh * a.gw;
-    xh = RP == kBwdRelGeneral ? kh : 0;
-    xw = RP == kBwdRelGeneral ? gh + kw : 1 + kw;
+    xh = kh;
+    xw = gh + kw;
   }
-  constexpr int RC = RP == kBwdRelNone ? 1 : RP == kBwdRelRow64 ? 17 : (kBwdRelMaxCols * 64 + 255) / 256;
+  constexpr int RC = RP == kBwdRelGeneral ? (kBwdRelMaxCols * 64 + 255) / 256 : 1;
+  f32x4 wv[RP == kBwdRelRow64 ? 4 : 1];  // 64-wide form: rel_w column xw, a tile's 64 queries
+  auto load_w = [&](int t) {
+    if constexpr (RP == kBwdRelRow64) {
+      // Nq = 64 gh: whole tiles; 16-byte aligned in the workspace.
+      const float* col = ws_rel + (int64_t)xw * Nq + t * 64 + g * 4;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) wv[qb] = *(const f32x4*)(col + qb * 16);
+    }
+  };
   float rreg[RC];
   u32x4 qreg[C::CPT], oreg[C::CPT];
   uint32_t qoff[C::CPT], ooff[C::CPT];
   tile_chunk_offsets<D>(qoff, a.q_sn, tid);
   tile_chunk_offsets<D>(ooff, a.o_sn, tid);
-  float lreg = 0.f, dreg = 0.f;
+  float lreg = 0.f, dreg = 0.f, hreg = 0.f;
   // Query rows past Nq read as zero (Q, dO, their D); their L is set to
   // +inf when staged, so that P = 0 for them whatever their bias.
   auto load_tile = [&](int t) {
@@ -959,31 +982,33 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
       const uint32_t nb = (uint32_t)(Nq - t * 64) * 4;
       lreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(wsL + t * 64, nb), tid * 4, 0, 0));
       dreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(wsD + t * 64, nb), tid * 4, 0, 0));
+      if constexpr (RP == kBwdRelRow64)
+        hreg = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ws_rel + (int64_t)kt * Nq + t * 64, nb), tid * 4, 0, 0));
     }
-    if constexpr (RP != kBwdRelNone) {
-      // [G][Nq] floats of this (batch item, head): at most 128 x 4096.
+    if constexpr (RP == kBwdRelGeneral) {
+      // [G][Nq] floats of this (batch item, head): at most 84 x 1764.
       const auto rr = buffer_rsrc(ws_rel, (uint32_t)(G * Nq) * 4);
 #pragma unroll
       for (int c = 0; c < RC; ++c) {
+        // Column x of the stage is rel_h / rel_w column x.  Rows past Nq
+        // read another column's finite entries or zero; their P is 0.
         const int e = tid + c * 256, x = e >> 6, q = t * 64 + (e & 63);
-        // Column x of the stage: rel_h / rel_w column (the 64-wide form
-        // stages column kt of rel_h, then the 64 rel_w columns).  Rows past
-        // Nq read another column's finite entries or zero; their P is 0.
-        const int col = RP == kBwdRelGeneral ? x : (x == 0 ? kt : gh + x - 1);
-        if (e < 64 * NC) rreg[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(col * Nq + q) * 4, 0, 0));
+        if (e < 64 * NC) rreg[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(x * Nq + q) * 4, 0, 0));
       }
     }
   };
   // L and D are staged negated: the exponent is scale*log2(e)*s + bias - L
-  // with one FMA, and dP accumulates onto -D.
+  // with one FMA, and dP accumulates onto -D.  The bias terms come in log2
+  // units; the 64-wide form's rel_h term is part of the staged -L.
   auto store_tile = [&](int st, int t) {
     store_rows_regs<D>(Qs + st * TILE, qreg, tid);
     store_rows_regs<D>(Os + st * TILE, oreg, tid);
     if (tid < 64) {
-      Ls[st * 64 + tid] = t * 64 + tid < Nq ? -lreg : -INFINITY;
+      Ls[st * 64 + tid] = t * 64 + tid < Nq ? hreg - lreg : -INFINITY;
       Ds[st * 64 + tid] = -dreg;
     }
-    if constexpr (RP != kBwdRelNone) {
+    if constexpr (RP == kBwdRelGeneral) {
 #pragma unroll
       for (int c = 0; c < RC; ++c) {
         const int e = tid + c * 256;
@@ -992,6 +1017,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     }
   };
   load_tile(0);
+  load_w(0);
   // K and V rows of this lane's key as B operands (lane = key column).
   u32x4 kf[KCH], vf[KCH];
 #pragma unroll
@@ -1034,18 +1060,23 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const f32x4 nL = *(const f32x4*)&Lt[qb * 16 + g * 4];
+      f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (RP == kBwdRelGeneral) {
+        const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4;
+        bias = *(const f32x4*)(rs + xh * 64) + *(const f32x4*)(rs + xw * 64);
+      } else if constexpr (RP == kBwdRelRow64) {
+        bias = wv[qb];
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float y = fmaf(s[qb][r], c2, nL[r]);
-        if constexpr (RP != kBwdRelNone) {
-          const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4 + r;
-          y = fmaf(rs[xh * 64] + rs[xw * 64], kLog2e, y);
-        }
+        if constexpr (RP != kBwdRelNone) y += bias[r];
         const float pv = __builtin_amdgcn_exp2f(y);
         p[qb * 4 + r] = pv;
         ds[qb * 4 + r] = pv * dp[qb][r];
       }
     }
+    if (more) load_w(t + 1);  // the values of this tile are used: the next tile's, in flight from here
     u32x4 pf[2], sf[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {

@@ -489,7 +489,7 @@ constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
 }
 // Bytes of the dRel sums at the end of the relative-position region.
 constexpr size_t bwd_rows_acc_bytes(const AttnArgs& a) {
-  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * (a.gh + a.gw) * 4 : (size_t)64 * kBwdRelS * 4;
+  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * ((a.gh + a.gw) | 1) * 4 : (size_t)64 * kBwdRelS * 4;
 }
 template <int D>
 constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
@@ -505,11 +505,12 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
   rel = (rel + 15) / 16 * 16;
   return rel + acc;
 }
-// Columns of rel_h / rel_w the column kernel stages per query: all of them
-// (general grids), or the key tile's grid row and the 64 columns.
+// Columns of rel_h / rel_w the column kernel stages per query tile: all of
+// them for general grids; none in the 64-wide form (the key tile's rel_h
+// column joins the staged log-sum-exp, and each lane reads its own rel_w
+// column from the workspace).
 constexpr int bwd_cols_rel_cols(const AttnArgs& a) {
-  const int mode = bwd_rel_mode(a);
-  return mode == kBwdRelNone ? 0 : mode == kBwdRelGeneral ? a.gh + a.gw : 1 + a.gw;
+  return bwd_rel_mode(a) == kBwdRelGeneral ? a.gh + a.gw : 0;
 }
 
 // The backward of a validated call (half precision): window units (at most
