@@ -914,8 +914,13 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 // gh + gw columns staged per query tile in log2 units ([columns][64]
 // floats); in the 64-wide form the key tile's rel_h column joins the staged
 // log-sum-exp and each lane reads its own rel_w column.
-template <class E, int D, int RP = kBwdRelNone>
+//
+// KB: 16-key blocks per wave (a workgroup covers 64 KB keys).  With KB = 2
+// every fragment read from the staged Q / dO tiles feeds two products, which
+// halves the LDS reads per matrix instruction (no relative position).
+template <class E, int D, int RP = kBwdRelNone, int KB = 1>
 __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
+  static_assert(KB == 1 || (KB == 2 && RP == kBwdRelNone), "two key blocks per wave: no relative position");
   using C = BwdTileCfg<D>;
   constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
   const AttnArgs& a = ba.a;
@@ -932,8 +937,8 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   const int kt = bid - kt_div * a.n_qtiles;
   const int b = fdiv(kt_div, a.fd_h), h = kt_div - b * a.H;
   const int Nq = a.Nq, Nk = a.Nk;
-  const int krow = kt * 64 + wave * 16 + l16;
-  const int ki = min(krow, Nk - 1);
+  const int krow0 = kt * 64 * KB + wave * 16 * KB + l16;  // key of block kb: krow0 + 16 kb
+  const int ki = min(krow0, Nk - 1);
   const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
@@ -1018,22 +1023,28 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
   };
   load_tile(0);
   load_w(0);
-  // K and V rows of this lane's key as B operands (lane = key column).
-  u32x4 kf[KCH], vf[KCH];
+  // K and V rows of this lane's keys as B operands (lane = key column).
+  u32x4 kf[KB][KCH], vf[KB][KCH];
 #pragma unroll
-  for (int dc = 0; dc < KCH; ++dc) {
-    const int d0 = dc * 32 + g * 8;
-    kf[dc] = d0 < D ? *(const u32x4*)(kp + (int64_t)ki * a.k_sn + d0) : u32x4{0, 0, 0, 0};
-    vf[dc] = d0 < D ? *(const u32x4*)(vp + (int64_t)ki * a.v_sn + d0) : u32x4{0, 0, 0, 0};
+  for (int kb = 0; kb < KB; ++kb) {
+    const int kr = min(krow0 + 16 * kb, Nk - 1);
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      kf[kb][dc] = d0 < D ? *(const u32x4*)(kp + (int64_t)kr * a.k_sn + d0) : u32x4{0, 0, 0, 0};
+      vf[kb][dc] = d0 < D ? *(const u32x4*)(vp + (int64_t)kr * a.v_sn + d0) : u32x4{0, 0, 0, 0};
+    }
   }
   zero_pad_cols<D>(Qs, 4, tid);  // both stages of Q and dO
   store_tile(0, 0);
   __syncthreads();
   const float c2 = a.scale * kLog2e;
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
-  f32x4 dk[CBD], dv[CBD];
+  f32x4 dk[KB][CBD], dv[KB][CBD];
 #pragma unroll
-  for (int cb = 0; cb < CBD; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) dk[kb][cb] = dv[kb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   wait_all_vmem();
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
@@ -1044,47 +1055,59 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     const float* Lt = Ls + st * 64;
     const float* Dt = Ds + st * 64;
     // S = Q K^T and dP = dO V^T - D: rows are queries qb*16 + g*4 + r, the
-    // column is this lane's key.
-    f32x4 s[4], dp[4];
+    // column is this lane's key of block kb.
+    f32x4 s[KB][4], dp[KB][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[qb] = *(const f32x4*)&Dt[qb * 16 + g * 4];
+      const f32x4 nD = *(const f32x4*)&Dt[qb * 16 + g * 4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[kb][qb] = nD;
+      }
 #pragma unroll
       for (int dc = 0; dc < KCH; ++dc) {
-        s[qb] = E::mfma(*(const u32x4*)&Qt[(qb * 16 + l16) * ROW + dc * 32 + g * 8], kf[dc], s[qb]);
-        dp[qb] = E::mfma(*(const u32x4*)&Ot[(qb * 16 + l16) * ROW + dc * 32 + g * 8], vf[dc], dp[qb]);
+        const u32x4 qa = *(const u32x4*)&Qt[(qb * 16 + l16) * ROW + dc * 32 + g * 8];
+        const u32x4 oa = *(const u32x4*)&Ot[(qb * 16 + l16) * ROW + dc * 32 + g * 8];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb][qb] = E::mfma(qa, kf[kb][dc], s[kb][qb]);
+          dp[kb][qb] = E::mfma(oa, vf[kb][dc], dp[kb][qb]);
+        }
       }
     }
-    float p[16], ds[16];
+    u32x4 pf[KB][2], sf[KB][2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 nL = *(const f32x4*)&Lt[qb * 16 + g * 4];
-      f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (RP == kBwdRelGeneral) {
-        const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4;
-        bias = *(const f32x4*)(rs + xh * 64) + *(const f32x4*)(rs + xw * 64);
-      } else if constexpr (RP == kBwdRelRow64) {
-        bias = wv[qb];
+    for (int kb = 0; kb < KB; ++kb) {
+      float p[16], ds[16];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const f32x4 nL = *(const f32x4*)&Lt[qb * 16 + g * 4];
+        f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (RP == kBwdRelGeneral) {
+          const float* rs = Rst + st * 64 * NC + qb * 16 + g * 4;
+          bias = *(const f32x4*)(rs + xh * 64) + *(const f32x4*)(rs + xw * 64);
+        } else if constexpr (RP == kBwdRelRow64) {
+          bias = wv[qb];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float y = fmaf(s[kb][qb][r], c2, nL[r]);
+          if constexpr (RP != kBwdRelNone) y += bias[r];
+          const float pv = __builtin_amdgcn_exp2f(y);
+          p[qb * 4 + r] = pv;
+          ds[qb * 4 + r] = pv * dp[kb][qb][r];
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float y = fmaf(s[qb][r], c2, nL[r]);
-        if constexpr (RP != kBwdRelNone) y += bias[r];
-        const float pv = __builtin_amdgcn_exp2f(y);
-        p[qb * 4 + r] = pv;
-        ds[qb * 4 + r] = pv * dp[qb][r];
+      for (int kc = 0; kc < 2; ++kc) {
+        pf[kb][kc] = u32x4{E::pack2(p[kc * 8 + 0], p[kc * 8 + 1]), E::pack2(p[kc * 8 + 2], p[kc * 8 + 3]),
+                           E::pack2(p[kc * 8 + 4], p[kc * 8 + 5]), E::pack2(p[kc * 8 + 6], p[kc * 8 + 7])};
+        sf[kb][kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                           E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
       }
     }
     if (more) load_w(t + 1);  // the values of this tile are used: the next tile's, in flight from here
-    u32x4 pf[2], sf[2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      pf[kc] = u32x4{E::pack2(p[kc * 8 + 0], p[kc * 8 + 1]), E::pack2(p[kc * 8 + 2], p[kc * 8 + 3]),
-                     E::pack2(p[kc * 8 + 4], p[kc * 8 + 5]), E::pack2(p[kc * 8 + 6], p[kc * 8 + 7])};
-      sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
-                     E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
-    }
     // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the tiles).
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -1094,22 +1117,29 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         const uint16_t* qptr = Qt + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
         const u32x2 ol = lds_read_tr16(optr), oh = lds_read_tr16(optr + 16 * ROW);
         const u32x2 ql = lds_read_tr16(qptr), qh = lds_read_tr16(qptr + 16 * ROW);
-        dv[cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pf[kc], dv[cb]);
-        dk[cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kc], dk[cb]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          dv[kb][cb] = E::mfma(u32x4{ol[0], ol[1], oh[0], oh[1]}, pf[kb][kc], dv[kb][cb]);
+          dk[kb][cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kb][kc], dk[kb][cb]);
+        }
       }
     if (more) store_tile(st ^ 1, t + 1);  // stage st^1 was last read before the previous barrier
     __syncthreads();
   }
-  if (krow < Nk) {
-    uint16_t* dkp = (uint16_t*)ba.dk + (int64_t)b * ba.dk_sb + (int64_t)h * ba.dk_sh + (int64_t)krow * ba.dk_sn;
-    uint16_t* dvp = (uint16_t*)ba.dv + (int64_t)b * ba.dv_sb + (int64_t)h * ba.dv_sh + (int64_t)krow * ba.dv_sn;
 #pragma unroll
-    for (int cb = 0; cb < CBD; ++cb) {
-      const int c0 = cb * 16 + g * 4;
-      if (c0 < D) {
-        const f32x4 k4 = dk[cb] * a.scale, v4 = dv[cb];
-        *(u32x2*)(dkp + c0) = u32x2{E::pack2(k4[0], k4[1]), E::pack2(k4[2], k4[3])};
-        *(u32x2*)(dvp + c0) = u32x2{E::pack2(v4[0], v4[1]), E::pack2(v4[2], v4[3])};
+  for (int kb = 0; kb < KB; ++kb) {
+    const int krow = krow0 + 16 * kb;
+    if (krow < Nk) {
+      uint16_t* dkp = (uint16_t*)ba.dk + (int64_t)b * ba.dk_sb + (int64_t)h * ba.dk_sh + (int64_t)krow * ba.dk_sn;
+      uint16_t* dvp = (uint16_t*)ba.dv + (int64_t)b * ba.dv_sb + (int64_t)h * ba.dv_sh + (int64_t)krow * ba.dv_sn;
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 k4 = dk[kb][cb] * a.scale, v4 = dv[kb][cb];
+          *(u32x2*)(dkp + c0) = u32x2{E::pack2(k4[0], k4[1]), E::pack2(k4[2], k4[3])};
+          *(u32x2*)(dvp + c0) = u32x2{E::pack2(v4[0], v4[1]), E::pack2(v4[2], v4[3])};
+        }
       }
     }
   }

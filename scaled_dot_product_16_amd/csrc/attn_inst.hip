@@ -199,8 +199,11 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
   ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   const int n_row_wg = ba.a.n_blocks;
+  // Two 16-key blocks per column-kernel wave where no bias term is staged
+  // (up to d = 64: at d = 80 the accumulators exceed 256 registers).
+  constexpr int KB = RP == kBwdRelNone && D <= 64 ? 2 : 1;
   auto rows = attn_bwd_rows<Elem, D, RP>;
-  auto cols = attn_bwd_cols<Elem, D, RP>;
+  auto cols = attn_bwd_cols<Elem, D, RP, KB>;
   if (p.lds > 32 * 1024 &&
       (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
            hipSuccess ||
@@ -209,7 +212,7 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
     return ATTN_E_LAUNCH;
   hipLaunchKernelGGL(rows, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
   if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
-  ba.a.n_qtiles = (ba.a.Nk + 63) / 64;  // key tiles for the column kernel
+  ba.a.n_qtiles = (ba.a.Nk + 64 * KB - 1) / (64 * KB);  // key tiles (64 KB keys) of the column kernel
   ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   hipLaunchKernelGGL(cols, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
