@@ -483,8 +483,13 @@ __device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int ti
 // and writes this workgroup's part of the table gradients,
 //   [dRh; dRw][r][c] = sum_i A[r][i] Q[i][c]  with  A[r][i] = dRelH[i][qh_i + gh - 1 - r]
 // (Rh rows; Rw rows likewise), as one small MFMA product Q^T A^T.
-template <class E, int D, int RP = kBwdRelNone>
+//
+// QB: 16-query blocks per wave (a workgroup covers 64 QB queries).  With
+// QB = 2 every fragment read from the staged K / V tiles feeds two
+// products (no relative position).
+template <class E, int D, int RP = kBwdRelNone, int QB = 1>
 __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
+  static_assert(QB == 1 || (QB == 2 && RP == kBwdRelNone), "two query blocks per wave: no relative position");
   using C = BwdTileCfg<D>;
   constexpr int KCH = C::KCH, CBD = C::CBD, ROW = C::ROW, TILE = C::TILE;
   const AttnArgs& a = ba.a;
@@ -499,8 +504,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   const int qt = bid - qt_div * a.n_qtiles;
   const int b = fdiv(qt_div, a.fd_h), h = qt_div - b * a.H;
   const int Nq = a.Nq, Nk = a.Nk;
-  const int qloc = wave * 16 + l16;
-  const int qrow = qt * 64 + qloc;
+  const int qloc = wave * 16 * QB + l16;  // query of block j: qloc + 16 j
+  const int qrow = qt * 64 * QB + qloc;
   const int qi = min(qrow, Nq - 1);
   const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
@@ -513,12 +518,16 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   tile_chunk_offsets<D>(voff, a.v_sn, tid);
   load_tile_regs<D>(kreg, kp, a.k_sn, 0, Nk, koff);
   load_tile_regs<D>(vreg, vp, a.v_sn, 0, Nk, voff);
-  u32x4 qf[KCH], df[KCH];
+  u32x4 qf[QB][KCH], df[QB][KCH];
 #pragma unroll
-  for (int dc = 0; dc < KCH; ++dc) {
-    const int d0 = dc * 32 + g * 8;
-    qf[dc] = d0 < D ? *(const u32x4*)(qp + (int64_t)qi * a.q_sn + d0) : u32x4{0, 0, 0, 0};
-    df[dc] = d0 < D ? *(const u32x4*)(op + (int64_t)qi * a.o_sn + d0) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < QB; ++j) {
+    const int qj = min(qrow + 16 * j, Nq - 1);
+#pragma unroll
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      qf[j][dc] = d0 < D ? *(const u32x4*)(qp + (int64_t)qj * a.q_sn + d0) : u32x4{0, 0, 0, 0};
+      df[j][dc] = d0 < D ? *(const u32x4*)(op + (int64_t)qj * a.o_sn + d0) : u32x4{0, 0, 0, 0};
+    }
   }
 
   // Relative position: rel_h / rel_w of this workgroup's queries.
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         for (int dc = 0; dc < KCH; ++dc) {
           const int d0 = dc * 32 + g * 8;
           const u32x4 t = *(const u32x4*)(tp + (int64_t)m * D + (d0 < D ? d0 : 0));
-          acc_t = E::mfma(d0 < D ? t : u32x4{0, 0, 0, 0}, qf[dc], acc_t);
+          acc_t = E::mfma(d0 < D ? t : u32x4{0, 0, 0, 0}, qf[0][dc], acc_t);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -581,7 +590,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         const int d0 = dc * 32 + g * 8;
         const u32x4 af = kh < gh && d0 < D ? *(const u32x4*)(rhp + (int64_t)(qt + gh - 1 - kh) * D + d0)
                                            : u32x4{0, 0, 0, 0};
-        acc_h = E::mfma(af, qf[dc], acc_h);
+        acc_h = E::mfma(af, qf[0][dc], acc_h);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {  // lane (l16, g) holds rel_h[qloc][16mb + 4g + i]
@@ -601,7 +610,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       for (int dc = 0; dc < KCH; ++dc) {
         const int d0 = dc * 32 + g * 8;
         const u32x4 af = m < 127 && d0 < D ? *(const u32x4*)(rwp + (int64_t)m * D + d0) : u32x4{0, 0, 0, 0};
-        acc_w = E::mfma(af, qf[dc], acc_w);
+        acc_w = E::mfma(af, qf[0][dc], acc_w);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) gwl[(mb * 16 + g * 4 + i) * 64 + qloc] = acc_w[i];
@@ -626,36 +635,43 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 
   const float c2 = a.scale * kLog2e;
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
-  // Pass 1 state (per lane: partial sums over its keys, against the row
-  // maximum m shared by the four lane groups).
-  float m = -INFINITY, l = 0.f, t = 0.f, L = 0.f, Dq = 0.f;
+  // Pass 1 state of each query block (per lane: partial sums over its
+  // keys, against the row maximum m shared by the four lane groups).
+  float m[QB], l[QB], t[QB], L[QB], Dq[QB];
   // With the forward's O and log-sum-exp (attn_bwd_opt) the first pass is
   // not needed: L from lse (natural log -> log2), D = dO_i . O_i.
   const bool stats = ba.lse_in != nullptr;
-  if (stats) {
-    L = ba.lse_in[(int64_t)(b * a.H + h) * Nq + qi] * kLog2e;
-    const uint16_t* fop = (const uint16_t*)ba.fo + (int64_t)b * ba.fo_sb + (int64_t)h * ba.fo_sh +
-                          (int64_t)qi * ba.fo_sn;
-    float part = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
-      const int d0 = dc * 32 + g * 8;
-      if (d0 < D) {
-        const u32x4 ov = *(const u32x4*)(fop + d0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part = E::dot2(df[dc][e], ov[e], part);
-      }
-    }
-    Dq = sum_across_groups(part);
-  }
   // Second-pass forms: the logits enter as scale*log2(e)*s + bias - L (yoff
   // = -L; 0 in the first pass), and dP accumulates onto -D (dinit), so that
   // P = exp2(y) and dS = P * dP take no further subtraction.
-  float yoff = stats ? -L : 0.f;
-  f32x4 dinit = stats ? f32x4{-Dq, -Dq, -Dq, -Dq} : f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[CBD];
+  float yoff[QB];
+  f32x4 dinit[QB], acc[QB][CBD];
 #pragma unroll
-  for (int cb = 0; cb < CBD; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < QB; ++j) {
+    m[j] = -INFINITY;
+    l[j] = t[j] = L[j] = Dq[j] = 0.f;
+    if (stats) {
+      const int qj = min(qrow + 16 * j, Nq - 1);
+      L[j] = ba.lse_in[(int64_t)(b * a.H + h) * Nq + qj] * kLog2e;
+      const uint16_t* fop = (const uint16_t*)ba.fo + (int64_t)b * ba.fo_sb + (int64_t)h * ba.fo_sh +
+                            (int64_t)qj * ba.fo_sn;
+      float part = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < KCH; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        if (d0 < D) {
+          const u32x4 ov = *(const u32x4*)(fop + d0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = E::dot2(df[j][dc][e], ov[e], part);
+        }
+      }
+      Dq[j] = sum_across_groups(part);
+    }
+    yoff[j] = stats ? -L[j] : 0.f;
+    dinit[j] = stats ? f32x4{-Dq[j], -Dq[j], -Dq[j], -Dq[j]} : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < CBD; ++cb) acc[j][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const int n_it = 2 * ntiles;
   const int it0 = stats ? ntiles : 0;  // tile 0 of the pass it starts with is in stage 0
   // One step of the key loop: iteration it of the two passes over the key
@@ -674,95 +690,108 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     }
     const uint16_t* Kt = Ks + st * TILE;
     const uint16_t* Vt = Vs + st * TILE;
-    f32x4 s[4], dp[4];
+    f32x4 s[QB][4], dp[QB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[kb] = dinit;
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        s[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[j][kb] = dinit[j];
+      }
 #pragma unroll
       for (int dc = 0; dc < KCH; ++dc) {
-        s[kb] = E::mfma(*(const u32x4*)&Kt[(kb * 16 + l16) * ROW + dc * 32 + g * 8], qf[dc], s[kb]);
-        dp[kb] = E::mfma(*(const u32x4*)&Vt[(kb * 16 + l16) * ROW + dc * 32 + g * 8], df[dc], dp[kb]);
+        const u32x4 ka = *(const u32x4*)&Kt[(kb * 16 + l16) * ROW + dc * 32 + g * 8];
+        const u32x4 va = *(const u32x4*)&Vt[(kb * 16 + l16) * ROW + dc * 32 + g * 8];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          s[j][kb] = E::mfma(ka, qf[j][dc], s[j][kb]);
+          dp[j][kb] = E::mfma(va, df[j][dc], dp[j][kb]);
+        }
       }
     }
-    float y[16];
-    int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
-    // The 64-wide form: rel_h of this tile's grid row, with yoff folded in.
-    float yrow = yoff;
-    if constexpr (RP == kBwdRelRow64) yrow = fmaf(rel[tile * S + qloc], kLog2e, yoff);
+    u32x4 sf[QB][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float sv = s[i >> 2][i & 3];
-      if constexpr (RP == kBwdRelNone) {
-        y[i] = fmaf(sv, c2, yoff);
-      } else if constexpr (RP == kBwdRelGeneral) {
-        // Keys past Nk read the last key's entries (masked below).
-        const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
-        const int kc = min(key, Nk - 1);
-        kh_i[i] = fdiv(kc, a.fd_gw);
-        kw_i[i] = kc - kh_i[i] * gw;
-        const float bias = rel[qloc * G + kh_i[i]] + rel[qloc * G + gh + kw_i[i]];
-        y[i] = fmaf(bias, kLog2e, fmaf(sv, c2, yoff));
-      } else {
-        y[i] = fmaf(sv, c2, yrow) + wreg[i];
-      }
-    }
-    // Keys past Nk only occur in the last tile (a uniform branch).
-    if (tile * 64 + 64 > Nk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3) >= Nk) y[i] = -INFINITY;
-    }
-    if constexpr (!second) {
-      float mx = y[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
-      const float mn = fmaxf(m, max_across_groups(mx));
-      float ps = 0.f, pd = 0.f;
+    for (int j = 0; j < QB; ++j) {
+      float y[16];
+      int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
+      // The 64-wide form: rel_h of this tile's grid row, with yoff folded in.
+      float yrow = yoff[j];
+      if constexpr (RP == kBwdRelRow64) yrow = fmaf(rel[tile * S + qloc], kLog2e, yoff[j]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(y[i] - mn);
-        ps += e;
-        pd = fmaf(e, dp[i >> 2][i & 3], pd);
+        const float sv = s[j][i >> 2][i & 3];
+        if constexpr (RP == kBwdRelNone) {
+          y[i] = fmaf(sv, c2, yoff[j]);
+        } else if constexpr (RP == kBwdRelGeneral) {
+          // Keys past Nk read the last key's entries (masked below).
+          const int key = tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3);
+          const int kc = min(key, Nk - 1);
+          kh_i[i] = fdiv(kc, a.fd_gw);
+          kw_i[i] = kc - kh_i[i] * gw;
+          const float bias = rel[qloc * G + kh_i[i]] + rel[qloc * G + gh + kw_i[i]];
+          y[i] = fmaf(bias, kLog2e, fmaf(sv, c2, yoff[j]));
+        } else {
+          y[i] = fmaf(sv, c2, yrow) + wreg[i];
+        }
       }
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile
-      l = fmaf(l, alpha, ps);
-      t = fmaf(t, alpha, pd);
-      m = mn;
-      if (it == ntiles - 1) {
-        const float lt = sum_across_groups(l);
-        L = m + __builtin_amdgcn_logf(lt);  // log2 of the row sum
-        Dq = sum_across_groups(t) / lt;
-        yoff = -L;
-        dinit = f32x4{-Dq, -Dq, -Dq, -Dq};
-      }
-    } else {
-      float ds[16];
+      // Keys past Nk only occur in the last tile (a uniform branch).
+      if (tile * 64 + 64 > Nk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i]) * dp[i >> 2][i & 3];
-      if constexpr (RP == kBwdRelGeneral) {
-        // Private sums of this lane (keys past Nk have dS = 0).
-        float* my = dacc + tid * GP;
+        for (int i = 0; i < 16; ++i)
+          if (tile * 64 + (i >> 2) * 16 + g * 4 + (i & 3) >= Nk) y[i] = -INFINITY;
+      }
+      if constexpr (!second) {
+        float mx = y[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
+        const float mn = fmaxf(m[j], max_across_groups(mx));
+        float ps = 0.f, pd = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          my[kh_i[i]] += ds[i];
-          my[gh + kw_i[i]] += ds[i];
+          const float e = __builtin_amdgcn_exp2f(y[i] - mn);
+          ps += e;
+          pd = fmaf(e, dp[j][i >> 2][i & 3], pd);
         }
-      } else if constexpr (RP == kBwdRelRow64) {
-        float rs = 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - mn);  // 0 on the first tile
+        l[j] = fmaf(l[j], alpha, ps);
+        t[j] = fmaf(t[j], alpha, pd);
+        m[j] = mn;
+        if (it == ntiles - 1) {
+          const float lt = sum_across_groups(l[j]);
+          L[j] = m[j] + __builtin_amdgcn_logf(lt);  // log2 of the row sum
+          Dq[j] = sum_across_groups(t[j]) / lt;
+          yoff[j] = -L[j];
+          dinit[j] = f32x4{-Dq[j], -Dq[j], -Dq[j], -Dq[j]};
+        }
+      } else {
+        float ds[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          rs += ds[i];
-          wacc[i] += ds[i];
+        for (int i = 0; i < 16; ++i) ds[i] = __builtin_amdgcn_exp2f(y[i]) * dp[j][i >> 2][i & 3];
+        if constexpr (RP == kBwdRelGeneral) {
+          // Private sums of this lane (keys past Nk have dS = 0).
+          float* my = dacc + tid * GP;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            my[kh_i[i]] += ds[i];
+            my[gh + kw_i[i]] += ds[i];
+          }
+        } else if constexpr (RP == kBwdRelRow64) {
+          float rs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            rs += ds[i];
+            wacc[i] += ds[i];
+          }
+          rs = sum_across_groups(rs);
+          if (g == 0) dacc[tile * S + qloc] = rs;
         }
-        rs = sum_across_groups(rs);
-        if (g == 0) dacc[tile * S + qloc] = rs;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          sf[j][kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
+                            E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
       }
-      u32x4 sf[2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        sf[kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
-                       E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+    }
+    if constexpr (second) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -770,7 +799,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
           const uint16_t* ptr = Kt + (kc * 32 + vt_row) * ROW + cb * 16 + vt_col;
           const u32x2 lo = lds_read_tr16(ptr);
           const u32x2 hi = lds_read_tr16(ptr + 16 * ROW);
-          acc[cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[kc], acc[cb]);
+#pragma unroll
+          for (int j = 0; j < QB; ++j) acc[j][cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[j][kc], acc[j][cb]);
         }
     }
     if (more) {
@@ -892,18 +922,22 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
     }
   }
-  if (qrow < Nq) {
-    if (g == 0) {
-      wsL[qrow] = L;
-      wsD[qrow] = Dq;
-    }
-    uint16_t* dq = (uint16_t*)ba.dq + (int64_t)b * ba.dq_sb + (int64_t)h * ba.dq_sh + (int64_t)qrow * ba.dq_sn;
 #pragma unroll
-    for (int cb = 0; cb < CBD; ++cb) {
-      const int c0 = cb * 16 + g * 4;
-      if (c0 < D) {
-        const f32x4 v = acc[cb] * a.scale + bq[cb];
-        *(u32x2*)(dq + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+  for (int j = 0; j < QB; ++j) {
+    const int qr = qrow + 16 * j;
+    if (qr < Nq) {
+      if (g == 0) {
+        wsL[qr] = L[j];
+        wsD[qr] = Dq[j];
+      }
+      uint16_t* dq = (uint16_t*)ba.dq + (int64_t)b * ba.dq_sb + (int64_t)h * ba.dq_sh + (int64_t)qr * ba.dq_sn;
+#pragma unroll
+      for (int cb = 0; cb < CBD; ++cb) {
+        const int c0 = cb * 16 + g * 4;
+        if (c0 < D) {
+          const f32x4 v = acc[j][cb] * a.scale + (j == 0 ? bq[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+          *(u32x2*)(dq + c0) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+        }
       }
     }
   }

@@ -195,14 +195,15 @@ template <int RP>
 static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
   constexpr int D = INST_D;
   AttnBwdArgs ba = ba0;
-  ba.a.n_qtiles = (ba.a.Nq + 63) / 64;
+  // Two 16-query (16-key) blocks per row (column) kernel wave where no bias
+  // term is staged (up to d = 64: at d = 80 the accumulators exceed 256
+  // registers).
+  constexpr int KB = RP == kBwdRelNone && D <= 64 ? 2 : 1;
+  ba.a.n_qtiles = (ba.a.Nq + 64 * KB - 1) / (64 * KB);  // query tiles (64 KB queries) of the row kernel
   ba.a.fd_qt = make_fastdiv(ba.a.n_qtiles);
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   const int n_row_wg = ba.a.n_blocks;
-  // Two 16-key blocks per column-kernel wave where no bias term is staged
-  // (up to d = 64: at d = 80 the accumulators exceed 256 registers).
-  constexpr int KB = RP == kBwdRelNone && D <= 64 ? 2 : 1;
-  auto rows = attn_bwd_rows<Elem, D, RP>;
+  auto rows = attn_bwd_rows<Elem, D, RP, KB>;
   auto cols = attn_bwd_cols<Elem, D, RP, KB>;
   if (p.lds > 32 * 1024 &&
       (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
