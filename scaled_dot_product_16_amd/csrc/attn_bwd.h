@@ -478,11 +478,13 @@ __device__ __forceinline__ void zero_pad_cols(uint16_t* tiles, int ntile, int ti
 // kernel computes these rows for its 64 queries (and stores them for the
 // column kernel), adds the bias to every score, and in its second pass also
 // gathers dRelH[i][kh] = sum over kw of dS and dRelW[i][kw] = sum over kh.
-// After the key loop it adds the bias path to dQ,
-//   dQ_i += sum_kh dRelH[i][kh] Rh[..] + sum_kw dRelW[i][kw] Rw[..],
+// After the key loop it builds the banded coefficient matrix
+//   A[r][i] = dRelH[i][qh_i + gh - 1 - r]  (Rh rows r; Rw rows likewise),
+// adds the bias path to dQ,
+//   dQ_i += sum_kh dRelH[i][kh] Rh[..] + sum_kw dRelW[i][kw] Rw[..] = sum_r A[r][i] [Rh; Rw][r],
 // and writes this workgroup's part of the table gradients,
-//   [dRh; dRw][r][c] = sum_i A[r][i] Q[i][c]  with  A[r][i] = dRelH[i][qh_i + gh - 1 - r]
-// (Rh rows; Rw rows likewise), as one small MFMA product Q^T A^T.
+//   [dRh; dRw][r][c] = sum_i A[r][i] Q[i][c],
+// both as small MFMA products over A.
 //
 // QB: 16-query blocks per wave (a workgroup covers 64 QB queries).  With
 // QB = 2 every fragment read from the staged K / V tiles feeds two
