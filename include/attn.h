@@ -309,9 +309,10 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
  *    order by a second kernel), else 0.  Longer sequences: 2 * B * H * Nq * 4
  *    bytes (each query row's log-sum-exp and sum_j P_ij dP_ij); with RELPOS
  *    also each query's rel_h / rel_w rows (B * H * Nq * (gh + gw) floats)
- *    and one partial [dRh; dRw] per 64 query rows (B * H * ceil(Nq / 64) *
- *    ((2gh-1) + (2gw-1)) * d floats), summed in a fixed order.
- *    Bitwise-deterministic, no atomics.
+ *    and one partial [dRh; dRw] per 64 query rows (B * H * ceil(Nq / 64)
+ *    slots of ((2gh-1) + (2gw-1)) * d floats, at least (gh + 64) * 64 when
+ *    gw = 64), summed in a fixed order; these two regions start on multiples
+ *    of 4 floats.  Bitwise-deterministic, no atomics.
  *
  *  Built: half precision (F16/BF16).  Units of at most 64 queries and keys
  *  (the window path: Swin windows in either layout, with shift and padding

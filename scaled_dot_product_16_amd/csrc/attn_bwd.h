@@ -534,11 +534,15 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 
   // Relative position: rel_h / rel_w of this workgroup's queries.
   const int gh = a.gh, gw = a.gw, G = gh + gw;
-  constexpr int S = kBwdRelS;  // 64-wide form: [grid position][S] arrays
   const size_t stage_bytes = bwd_stage_bytes<D>(a);
-  float* rel = (float*)(lds + stage_bytes);  // general: [64][G]; row form: rel_h^T [64][S]
+  // General grids: rel_h/rel_w [64][G] (then dRel); after the key loop,
+  // table slices and the Q tile.
+  float* rel = (float*)(lds + stage_bytes);
   float* dacc = rel + (bwd_rows_rel_bytes<D>(a) - bwd_rows_acc_bytes(a)) / 4;
   const BwdWs wl = bwd_ws_layout(a);
+  // This workgroup's partial slot; the 64-wide form first keeps dRelH^T
+  // [gh][64] and dRelW^T [64][64] there (grid position major).
+  float* pslot = ba.ws + wl.part + (int64_t)bid * wl.pstride;
   const int64_t bh = (int64_t)b * a.H + h;
   // [G][Nq] of this (batch item, head), in log2 units (the column kernel's form).
   float* ws_rel = ba.ws + wl.rel + bh * Nq * G;
@@ -598,7 +602,6 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       for (int i = 0; i < 4; ++i) {  // lane (l16, g) holds rel_h[qloc][16mb + 4g + i]
         const int kh2 = mb * 16 + g * 4 + i;
         if (kh2 < gh) {
-          rel[kh2 * S + qloc] = acc_h[i];
           if (qrow < Nq) ws_rel[(int64_t)kh2 * Nq + qrow] = acc_h[i] * kLog2e;
         }
       }
@@ -626,7 +629,6 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       if (qrow < Nq) ws_rel[(int64_t)(gh + kw) * Nq + qrow] = wreg[i];
       wacc[i] = 0.f;
     }
-    for (int e = tid; e < 64 * S; e += 256) dacc[e] = 0.f;
     __syncthreads();  // the stages are written below
   }
 
@@ -680,6 +682,11 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   // tiles (it < ntiles: statistics; it >= ntiles: gradients).  Each pass
   // runs as a loop of its own, so that the compiler keeps each pass's
   // state in place; the next tile's loads cross the pass boundary.
+  // 64-wide form: rel_h of this query and the current tile's grid row, in
+  // log2 units, from the workspace (written in the prologue, before the
+  // barriers above); the next tile's value is loaded one tile ahead.
+  float hcur = 0.f, hnext = 0.f;
+  if constexpr (RP == kBwdRelRow64) hcur = ws_rel[qi];
   auto step = [&](int it, auto pass) {
     constexpr bool second = decltype(pass)::value;
     const int tile = second ? it - ntiles : it;
@@ -689,6 +696,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       const int nt = it + 1 >= ntiles ? it + 1 - ntiles : it + 1;
       load_tile_regs<D>(kreg, kp, a.k_sn, nt * 64, Nk, koff);
       load_tile_regs<D>(vreg, vp, a.v_sn, nt * 64, Nk, voff);
+      if constexpr (RP == kBwdRelRow64) hnext = ws_rel[(int64_t)nt * Nq + qi];
     }
     const uint16_t* Kt = Ks + st * TILE;
     const uint16_t* Vt = Vs + st * TILE;
@@ -718,7 +726,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       int kh_i[RP == kBwdRelGeneral ? 16 : 1], kw_i[RP == kBwdRelGeneral ? 16 : 1];
       // The 64-wide form: rel_h of this tile's grid row, with yoff folded in.
       float yrow = yoff[j];
-      if constexpr (RP == kBwdRelRow64) yrow = fmaf(rel[tile * S + qloc], kLog2e, yoff[j]);
+      if constexpr (RP == kBwdRelRow64) yrow = hcur + yoff[j];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float sv = s[j][i >> 2][i & 3];
@@ -785,7 +793,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
             wacc[i] += ds[i];
           }
           rs = sum_across_groups(rs);
-          if (g == 0) dacc[tile * S + qloc] = rs;
+          if (g == 0) pslot[tile * 64 + qloc] = rs;
         }
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
@@ -810,6 +818,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       // that ended it; this tile's reads of stage st end at the barrier below.
       store_rows_regs<D>(Ks + (st ^ 1) * TILE, kreg, tid);
       store_rows_regs<D>(Vs + (st ^ 1) * TILE, vreg, tid);
+      if constexpr (RP == kBwdRelRow64) hcur = hnext;
     }
     __syncthreads();
   };
@@ -825,7 +834,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     const int RH = 2 * gh - 1, RW = 2 * gw - 1, RT = RH + RW;
     // dRel of this workgroup's queries: general grids sum the four lane
     // groups' private rows into `rel` [64][G]; the row form has dRelH^T in
-    // `dacc` [64][S] and writes dRelW^T from registers into `rel` [64][S].
+    // its partial slot and adds dRelW^T from registers.
     if constexpr (RP == kBwdRelGeneral) {
       for (int e = tid; e < 64 * G; e += 256) {
         const int ql = e / G, x = e - ql * G;
@@ -835,10 +844,10 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rel[((i >> 2) * 16 + g * 4 + (i & 3)) * S + qloc] = wacc[i];
+      for (int i = 0; i < 16; ++i) pslot[(gh + (i >> 2) * 16 + g * 4 + (i & 3)) * 64 + qloc] = wacc[i];
     }
-    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : dacc[x * S + ql]; };
-    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : rel[x * S + ql]; };
+    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : pslot[x * 64 + ql]; };
+    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : pslot[(gh + x) * 64 + ql]; };
     __syncthreads();
     // Coefficients A[r][i] (element type) in the free K/V stages: the weight
     // of table row r (Rh rows, then Rw rows) in query i's bias; zero for
@@ -860,35 +869,40 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
       Am[r * kBwdARow + ql] = (uint16_t)(E::pack2(v, 0.f) & 0xFFFF);
     }
-    __syncthreads();  // `rel` and `dacc` are free: the tables, then the Q tile go there
-    // Bias path of dQ on the matrix cores, one table at a time:
+    __syncthreads();  // `rel`, `dacc` and the slot's dRel are free: table slices, then the Q tile go there
+    // Bias path of dQ on the matrix cores, one table slice at a time:
     //   dQ_bias^T[c][i] = sum_r T^T[c][r] A[r0 + r][i]  (T = Rh, r0 = 0; T = Rw, r0 = RH).
-    // Both operands by transposing reads (the table staged with rows padded
+    // Both operands by transposing reads (the slice staged with rows padded
     // to 32 by zeros, A as it stands), so their K orders agree; the result
     // has the layout of the dQ accumulators.
     {
       constexpr int TR = bwd_rel_tab_row<D>();
+      const int TS = bwd_rel_tab_rows(a);
       uint16_t* Tb = (uint16_t*)rel;
 #pragma unroll 1
       for (int half = 0; half < 2; ++half) {
-        const int nr = half ? RW : RH, r0 = half ? RH : 0, nrp = bwd_up32(nr);
+        const int nr = half ? RW : RH, r0 = half ? RH : 0;
         const uint16_t* src = half ? rwp : rhp;
-        for (int e = tid * 8; e < nrp * TR; e += 256 * 8) {
-          const int row = e / TR, col = e - row * TR;
-          *(u32x4*)&Tb[e] = row < nr && col < D ? *(const u32x4*)(src + row * D + col) : u32x4{0, 0, 0, 0};
-        }
-        __syncthreads();
-        for (int kc = 0; kc < nrp / 32; ++kc) {
-          const uint16_t* aptr = Am + (r0 + kc * 32 + vt_row) * kBwdARow + wave * 16 + vt_col;
-          const u32x2 blo = lds_read_tr16(aptr), bhi = lds_read_tr16(aptr + 16 * kBwdARow);
-#pragma unroll
-          for (int cb = 0; cb < CBD; ++cb) {
-            const uint16_t* tptr = Tb + (kc * 32 + vt_row) * TR + cb * 16 + vt_col;
-            const u32x2 tlo = lds_read_tr16(tptr), thi = lds_read_tr16(tptr + 16 * TR);
-            bq[cb] = E::mfma(u32x4{tlo[0], tlo[1], thi[0], thi[1]}, u32x4{blo[0], blo[1], bhi[0], bhi[1]}, bq[cb]);
+#pragma unroll 1
+        for (int s0 = 0; s0 < nr; s0 += TS) {
+          const int ns = min(TS, nr - s0), nrp = bwd_up32(ns);
+          for (int e = tid * 8; e < nrp * TR; e += 256 * 8) {
+            const int row = e / TR, col = e - row * TR;
+            *(u32x4*)&Tb[e] = row < ns && col < D ? *(const u32x4*)(src + (s0 + row) * D + col) : u32x4{0, 0, 0, 0};
           }
+          __syncthreads();
+          for (int kc = 0; kc < nrp / 32; ++kc) {
+            const uint16_t* aptr = Am + (r0 + s0 + kc * 32 + vt_row) * kBwdARow + wave * 16 + vt_col;
+            const u32x2 blo = lds_read_tr16(aptr), bhi = lds_read_tr16(aptr + 16 * kBwdARow);
+#pragma unroll
+            for (int cb = 0; cb < CBD; ++cb) {
+              const uint16_t* tptr = Tb + (kc * 32 + vt_row) * TR + cb * 16 + vt_col;
+              const u32x2 tlo = lds_read_tr16(tptr), thi = lds_read_tr16(tptr + 16 * TR);
+              bq[cb] = E::mfma(u32x4{tlo[0], tlo[1], thi[0], thi[1]}, u32x4{blo[0], blo[1], bhi[0], bhi[1]}, bq[cb]);
+            }
+          }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
     const int RB = (RT + 15) / 16;
@@ -903,7 +917,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     // part^T[c][r] = sum_i Q[i][c] A[r][i]: A operand Q^T by transposing
     // reads of the Q tile, B operand A^T (lane = table row r), both in the
     // query order the transposing reads produce.
-    float* part = ba.ws + wl.part + (int64_t)bid * RT * D;
+    float* part = pslot;
     for (int rb = wave; rb < RB; rb += 4) {
 #pragma unroll
       for (int cb = 0; cb < CBD; ++cb) {
@@ -1182,7 +1196,8 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 }
 
 // Relative-position table gradients: out[o] = sum over the row-kernel
-// workgroups p of part[p][o] (o = r*D + c over the stacked [Rh; Rw] rows).
+// workgroups p of part[p * stride + o] (o = r*D + c over the stacked
+// [Rh; Rw] rows).
 // One workgroup of 16 waves per 64 outputs: wave w adds p = w, w+16, ... in
 // order, then the 16 partial sums are added in a fixed order (bitwise
 // deterministic).  The loads of 8 parts are issued together before they are
@@ -1190,23 +1205,24 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 // waiting for one at a time.  (A template only so that every compiled
 // instance may carry its copy.)
 template <int>
-__global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* out, int n_out, int n_part) {
+__global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* out, int n_out, int n_part,
+                                                              int64_t stride) {
   __shared__ float red[16][64];
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, w = tid >> 6;
   const int o = __builtin_amdgcn_workgroup_id_x() * 64 + lane;
   float acc = 0.f;
   if (o < n_out) {
     const float* src = part + o;
-    const size_t step = (size_t)16 * n_out;
+    const size_t step = (size_t)16 * stride;
     int p = w;
     for (; p + 7 * 16 < n_part; p += 8 * 16) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = src[(size_t)p * n_out + j * step];
+      for (int j = 0; j < 8; ++j) v[j] = src[(size_t)p * stride + j * step];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc += v[j];
     }
-    for (; p < n_part; p += 16) acc += src[(size_t)p * n_out];
+    for (; p < n_part; p += 16) acc += src[(size_t)p * stride];
   }
   red[w][lane] = acc;
   __syncthreads();

@@ -222,8 +222,9 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
     // [dRh; dRw] = fixed-order sum of the row kernel's per-workgroup parts.
     const int n_out = bwd_rel_rows(ba.a) * D;
     auto red = attn_bwd_part_reduce<0>;
-    hipLaunchKernelGGL(red, dim3((unsigned)((n_out + 63) / 64)), dim3(1024), 0, s,
-                       (const float*)(ba.ws + bwd_ws_layout(ba.a).part), ba.dtable, n_out, n_row_wg);
+    const BwdWs wl = bwd_ws_layout(ba.a);
+    hipLaunchKernelGGL(red, dim3((unsigned)((n_out + 63) / 64)), dim3(1024), 0, s, (const float*)(ba.ws + wl.part),
+                       ba.dtable, n_out, n_row_wg, (int64_t)wl.pstride);
     if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
   }
   return ATTN_OK;

@@ -427,18 +427,27 @@ constexpr int bwd_rel_rows(const AttnArgs& a) { return 2 * a.gh - 1 + 2 * a.gw -
 // query ([B*H*Nq][gh + gw], written by the row kernel, read by the column
 // kernel) and one partial [Rh; Rw] gradient per row-kernel workgroup
 // ([B*H*ceil(Nq/64)][rows][D], summed in a fixed order afterwards).
+// Per-workgroup slot of the partial table gradients (floats): the [dRh; dRw]
+// part, and in the 64-wide form first the workgroup's dRelH^T and dRelW^T
+// ([gh + 64][64] floats, read back after the key loop).
+constexpr size_t bwd_part_stride(const AttnArgs& a) {
+  const size_t part = (size_t)bwd_rel_rows(a) * (size_t)a.D;
+  const size_t drel = bwd_rel_mode(a) == kBwdRelRow64 ? (size_t)(a.gh + 64) * 64 : 0;
+  return part > drel ? part : drel;
+}
 struct BwdWs {
-  size_t L, D, rel, part, total;
+  size_t L, D, rel, part, pstride, total;
 };
 constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
   const size_t n = (size_t)a.B * a.H * a.Nq;
-  BwdWs w{0, n, 0, 0, 0};
+  BwdWs w{0, n, 0, 0, 0, 0};
   size_t off = (2 * n + 3) / 4 * 4;
   w.rel = off;
   if (a.bias_kind == ATTN_BIAS_RELPOS) {
     off = (off + n * (size_t)(a.gh + a.gw) + 3) / 4 * 4;
     w.part = off;
-    off += (size_t)a.B * a.H * (size_t)((a.Nq + 63) / 64) * (size_t)bwd_rel_rows(a) * (size_t)a.D;
+    w.pstride = bwd_part_stride(a);
+    off += (size_t)a.B * a.H * (size_t)((a.Nq + 63) / 64) * w.pstride;
   } else {
     w.part = off;
   }
@@ -449,12 +458,13 @@ constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
 // LDS of the row kernel: the K/V stages, used after the key loop for the
 // coefficient matrix A of the table-gradient products ([bwd_rel_arows][
 // kBwdARow] elements; a row stride of 40 dwords keeps the transposing reads
-// of A on distinct banks); then the relative-position region: rel_h/rel_w
-// (later dRel, one staged table, the Q tile) and the dRel sums.  The 64-wide
-// form keeps rel_h / dRelH / dRelW as [64 grid positions][kBwdRelS] floats,
-// position-major, so that a wave's 16 queries touch consecutive words.
+// of A on distinct banks); then the relative-position region.  General
+// grids: rel_h/rel_w (later dRel, one staged table, the Q tile) and the
+// per-lane dRel sums.  The 64-wide form keeps rel_h in the workspace and
+// dRelH / dRelW in the workgroup's partial slot, so its region only holds a
+// 64-row slice of a table, then the Q tile: 51 KB at d <= 64, three
+// workgroups per CU.
 constexpr int kBwdARow = 80;
-constexpr int kBwdRelS = 68;
 constexpr int bwd_up32(int n) { return (n + 31) / 32 * 32; }
 // Rows of A: each table's rows padded to 32 for the dQ products (Rh rows
 // from 0, Rw rows from 2gh-1) and all rows padded to 16 for the partial.
@@ -464,16 +474,22 @@ constexpr int bwd_rel_arows(const AttnArgs& a) {
   const int y = (rh + rw + 15) / 16 * 16;
   return x > y ? x : y;
 }
-// One table staged for the dQ products: rows padded to 32, row stride
-// bwd_rel_tab_row elements (CBD*16 columns plus the transposing-read pad).
+// Rows of one staged table slice for the dQ products: a whole table
+// padded to 32 rows (general grids), or 64 rows at a time (64-wide form).
+constexpr int bwd_rel_tab_rows(const AttnArgs& a) {
+  if (bwd_rel_mode(a) == kBwdRelRow64) return 64;
+  const int rh = bwd_up32(2 * a.gh - 1), rw = bwd_up32(2 * a.gw - 1);
+  return rh > rw ? rh : rw;
+}
+// Row stride of a staged table slice (elements): CBD*16 columns plus the
+// transposing-read pad.
 template <int D>
 constexpr int bwd_rel_tab_row() {
   return (D + 15) / 16 * 16 + v_row_pad((D + 15) / 16 * 16);
 }
 template <int D>
 constexpr size_t bwd_rel_tab_bytes(const AttnArgs& a) {
-  const int rh = bwd_up32(2 * a.gh - 1), rw = bwd_up32(2 * a.gw - 1);
-  return (size_t)(rh > rw ? rh : rw) * bwd_rel_tab_row<D>() * 2;
+  return (size_t)bwd_rel_tab_rows(a) * bwd_rel_tab_row<D>() * 2;
 }
 template <int D>
 constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
@@ -487,9 +503,10 @@ constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
   }
   return (s + 15) / 16 * 16;
 }
-// Bytes of the dRel sums at the end of the relative-position region.
+// Bytes of the per-lane dRel sums at the end of the relative-position
+// region (general grids).
 constexpr size_t bwd_rows_acc_bytes(const AttnArgs& a) {
-  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * ((a.gh + a.gw) | 1) * 4 : (size_t)64 * kBwdRelS * 4;
+  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * ((a.gh + a.gw) | 1) * 4 : 0;
 }
 template <int D>
 constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
@@ -497,7 +514,7 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
   const int mode = bwd_rel_mode(a);
   if (mode == kBwdRelNone) return 0;
   const size_t g = (size_t)(a.gh + a.gw);
-  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : (size_t)64 * kBwdRelS * 4;
+  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : 0;
   const size_t qt = (size_t)64 * ROW * 2;
   rel = (rel > qt ? rel : qt);
   const size_t acc = bwd_rows_acc_bytes(a), tab = bwd_rel_tab_bytes<D>(a);
