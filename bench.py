@@ -56,9 +56,9 @@ BACKWARD = ["C2b", "C3b", "C4b", "C5sb"]
 TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 2e-2}
 
 
-# Sources that only hold the backward kernels and their entry points; the
-# forward kernels' counter records do not depend on them.
-BACKWARD_ONLY_SOURCES = ("attn_bwd.h", "attn_noalloc.hip")
+# Sources that only hold the backward kernels, their plan, launchers and
+# entry points; the forward kernels' counter records do not depend on them.
+BACKWARD_ONLY_SOURCES = ("attn_bwd.h", "attn_bwd_launch.h", "attn_plan_bwd.h", "attn_noalloc.hip")
 
 
 def kernel_source_hash() -> str:
