@@ -1197,32 +1197,36 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 
 // Relative-position table gradients: out[o] = sum over the row-kernel
 // workgroups p of part[p * stride + o] (o = r*D + c over the stacked
-// [Rh; Rw] rows).
-// One workgroup of 16 waves per 64 outputs: wave w adds p = w, w+16, ... in
-// order, then the 16 partial sums are added in a fixed order (bitwise
-// deterministic).  The loads of 8 parts are issued together before they are
-// added (in the same order), so each wave keeps 8 in flight instead of
-// waiting for one at a time.  (A template only so that every compiled
-// instance may carry its copy.)
+// [Rh; Rw] rows), in two fixed-order stages (bitwise deterministic):
+// attn_bwd_part_reduce sums slice s of the parts, p in [s*P/S, (s+1)*P/S),
+// into sums[s][o] (out itself when S = 1), and attn_bwd_part_final adds the
+// S slices in order.  Slicing lets small tables still fill the chip.
+// Within a slice, one workgroup of 16 waves per 64 outputs: wave w adds
+// p = w, w+16, ... in order, then the 16 partial sums are added in a fixed
+// order.  The loads of 8 parts are issued together before they are added
+// (in the same order), so each wave keeps 8 in flight.  (Templates only so
+// that every compiled instance may carry its copy.)
 template <int>
-__global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* out, int n_out, int n_part,
-                                                              int64_t stride) {
+__global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, float* sums, int n_out, int n_part,
+                                                              int64_t stride, int S) {
   __shared__ float red[16][64];
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, w = tid >> 6;
   const int o = __builtin_amdgcn_workgroup_id_x() * 64 + lane;
+  const int sl = __builtin_amdgcn_workgroup_id_y();  // slice, < S
+  const int p0 = (int)((int64_t)n_part * sl / S), p1 = (int)((int64_t)n_part * (sl + 1) / S);
   float acc = 0.f;
   if (o < n_out) {
     const float* src = part + o;
     const size_t step = (size_t)16 * stride;
-    int p = w;
-    for (; p + 7 * 16 < n_part; p += 8 * 16) {
+    int p = p0 + w;
+    for (; p + 7 * 16 < p1; p += 8 * 16) {
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = src[(size_t)p * stride + j * step];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc += v[j];
     }
-    for (; p < n_part; p += 16) acc += src[(size_t)p * stride];
+    for (; p < p1; p += 16) acc += src[(size_t)p * stride];
   }
   red[w][lane] = acc;
   __syncthreads();
@@ -1230,6 +1234,16 @@ __global__ __launch_bounds__(1024) void attn_bwd_part_reduce(const float* part, 
     float t = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) t += red[j][lane];
+    sums[(int64_t)sl * n_out + o] = t;
+  }
+}
+
+template <int>
+__global__ __launch_bounds__(256) void attn_bwd_part_final(const float* sums, float* out, int n_out, int S) {
+  const int o = __builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
+  if (o < n_out) {
+    float t = 0.f;
+    for (int s = 0; s < S; ++s) t += sums[(int64_t)s * n_out + o];
     out[o] = t;
   }
 }

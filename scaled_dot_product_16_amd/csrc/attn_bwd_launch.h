@@ -70,13 +70,28 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
   hipLaunchKernelGGL(cols, dim3((unsigned)ba.a.n_blocks), dim3(256), p.lds, s, ba);
   if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
   if constexpr (RP != kBwdRelNone) {
-    // [dRh; dRw] = fixed-order sum of the row kernel's per-workgroup parts.
+    // [dRh; dRw] = fixed-order sum of the row kernel's per-workgroup parts,
+    // in S slices when the table alone would leave the chip idle; the slice
+    // sums go to the workspace's L and D rows (dead once the column kernel
+    // is done), which must hold S * n_out floats.
     const int n_out = bwd_rel_rows(ba.a) * D;
-    auto red = attn_bwd_part_reduce<0>;
+    const int chunks = (n_out + 63) / 64;
+    const int64_t room = 2 * (int64_t)ba.a.B * ba.a.H * ba.a.Nq / n_out;
+    int S = (512 + chunks - 1) / chunks;
+    S = (int)(S < 16 ? S : 16);
+    S = (int)(S < room ? S : room);
+    S = S < n_row_wg ? S : n_row_wg;
+    S = S > 1 ? S : 1;
     const BwdWs wl = bwd_ws_layout(ba.a);
-    hipLaunchKernelGGL(red, dim3((unsigned)((n_out + 63) / 64)), dim3(1024), 0, s, (const float*)(ba.ws + wl.part),
-                       ba.dtable, n_out, n_row_wg, (int64_t)wl.pstride);
+    float* sums = S > 1 ? ba.ws + wl.L : ba.dtable;
+    hipLaunchKernelGGL(attn_bwd_part_reduce<0>, dim3((unsigned)chunks, (unsigned)S), dim3(1024), 0, s,
+                       (const float*)(ba.ws + wl.part), sums, n_out, n_row_wg, (int64_t)wl.pstride, S);
     if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+    if (S > 1) {
+      hipLaunchKernelGGL(attn_bwd_part_final<0>, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s,
+                         (const float*)sums, ba.dtable, n_out, S);
+      if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+    }
   }
   return ATTN_OK;
 }
