@@ -352,6 +352,24 @@ def test_backward_validation(lib):
     assert h.attn_bwd_check(*args3(ctypes.c_void_p(dr.data_ptr()), need3.value)) == 0
     assert h.attn_bwd_check(*args3(None, need3.value)) == 1              # no [dRh; dRw] output
     assert h.attn_bwd_check(*args3(ctypes.c_void_p(dr.data_ptr()), need3.value - 4)) == 2
+    # 64-wide grids: each partial slot holds at least (gh + 64) * 64 floats
+    # (the workgroup's dRelH and dRelW before its partial).  A 4x64 grid at
+    # d = 32: slots of max((7 + 127) * 32, 68 * 64) = 4352 floats.
+    def ws_need(qq, bias):
+        m = B._marshal(qq, qq.clone(), qq.clone(), qq.clone(), bias, None, "batched", None)
+        n = ctypes.c_size_t(0)
+        assert h.attn_bwd_workspace_size(ctypes.byref(m[0]), ctypes.byref(m[1]), ctypes.byref(m[2]),
+                                         ctypes.byref(m[5]), ctypes.byref(m[3]), ctypes.byref(m[4]), m[6],
+                                         ctypes.byref(n)) == 0
+        return n.value
+    q4 = t(2, 3, 4 * 64, 32)
+    n4 = 2 * 3 * 4 * 64
+    assert ws_need(q4, B.RelposBias(t(7, 32), t(127, 32), (4, 64))) == \
+        4 * (up4(up4(2 * n4) + n4 * 68) + 2 * 3 * 4 * 4352)
+    q8 = t(1, 2, 8 * 64, 64)       # d = 64: the [dRh; dRw] part is the larger
+    n8 = 1 * 2 * 8 * 64
+    assert ws_need(q8, B.RelposBias(t(15, 64), t(127, 64), (8, 64))) == \
+        4 * (up4(up4(2 * n8) + n8 * 72) + 1 * 2 * 8 * (15 + 127) * 64)
     # Not built: keys on their own grid, resized tables, a mask, the image
     # layout beyond windows, and general grids with gh + gw > 84.
     def bwd_status(qq, kk, bias, mask=None, layout="batched", window=None):
