@@ -506,6 +506,12 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // Transposing V reads: this lane addresses key row (l16 / 4) of its group's
   // 4-key slice and channel block 4 * (l16 % 4).
   const int vt_row = g * 4 + (l16 >> 2), vt_col = 4 * (l16 & 3);
+  // When D is a multiple of 16, the last 16-row block of V^T holds only the
+  // ones row (row D) and zeros: its fragment is a constant (one in every
+  // element of the lanes of row 0), taken from registers instead of LDS.
+  constexpr bool kOnesBlock = C::ONES && D % 16 == 0;
+  const uint32_t one2 = l16 == 0 ? (uint32_t)E::one_bits() * 0x10001u : 0u;
+  const u32x4 ones_frag = u32x4{one2, one2, one2, one2};
   // S^T = K Q^T for one key tile.  All K fragments are read first, so the
   // LDS latency is paid once per tile.  The first product of each chain
   // takes its addend directly: zero, or the row-form relative-position term.
@@ -586,6 +592,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         if (kc >= nkc) continue;
+        if (kOnesBlock && cb == CB - 1) {
+          vf[kc][cb] = ones_frag;
+          continue;
+        }
         const uint16_t* vp = Vt + (kc * 32 + vr) * VROW + cb * 16 + vc;
         const u32x2 lo = lds_read_tr16(vp);
         const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
@@ -776,6 +786,10 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
       u32x4 vf[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
+        if (kOnesBlock && cb == CB - 1) {
+          vf[cb] = ones_frag;
+          continue;
+        }
         const uint16_t* vp = Vt + (kc * 32 + vt_row) * VROW + cb * 16 + vt_col;
         const u32x2 lo = lds_read_tr16(vp);
         const u32x2 hi = lds_read_tr16(vp + 16 * VROW);
