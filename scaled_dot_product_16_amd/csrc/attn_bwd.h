@@ -550,7 +550,15 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
   const uint16_t* rwp = (const uint16_t*)a.rw;
   float wreg[RP == kBwdRelRow64 ? 16 : 1], wacc[RP == kBwdRelRow64 ? 16 : 1];
   const int GP = G | 1;  // general form: private rows of an odd stride (distinct banks per lane)
-  if constexpr (RP == kBwdRelGeneral) {
+  // Small general grids: the one-hot key table [padded keys][kBwdAugRow]
+  // where the general form keeps its private sums; the wave's B fragments of
+  // rel_h / rel_w (columns g*8 .. g*8+7 of its query, divided by the scale,
+  // as the element-type sum hi + lo, so the bias keeps about 16 bits), and
+  // the dRel^T accumulators (rows x = 16 xb + 4g + i).
+  uint16_t* Etab = (uint16_t*)dacc;
+  u32x4 relq = u32x4{0, 0, 0, 0}, relq_lo = u32x4{0, 0, 0, 0};
+  f32x4 drel[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if constexpr (RP == kBwdRelGeneral || RP == kBwdRelAug) {
     // rel_h[q][x] = Rh[qh - x + gh - 1] . q (rel_w likewise) from the
     // products G[m][q] = T[m] . q of every table row m with the wave's 16
     // queries on the matrix cores (query fragments as the B operand).  Lane
@@ -581,7 +589,33 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         }
       }
     }
-    for (int e = tid; e < 256 * GP; e += 256) dacc[e] = 0.f;
+    if constexpr (RP == kBwdRelGeneral) {
+      for (int e = tid; e < 256 * GP; e += 256) dacc[e] = 0.f;
+    } else {
+      const int erows = (Nk + 63) / 64 * 64;
+      for (int e = tid * 8; e < erows * kBwdAugRow; e += 256 * 8) *(u32x4*)&Etab[e] = u32x4{0, 0, 0, 0};
+      __syncthreads();  // the table is zero, and rel holds every column of the wave's queries
+      for (int key = tid; key < Nk; key += 256) {
+        const int kh = fdiv(key, a.fd_gw), kw = key - kh * gw;
+        Etab[key * kBwdAugRow + kh] = E::one_bits();
+        Etab[key * kBwdAugRow + gh + kw] = E::one_bits();
+      }
+      const float inv_scale = 1.f / a.scale;
+      float ext[8], rem[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int x = g * 8 + e;
+        ext[e] = x < G ? rel[qloc * G + x] * inv_scale : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        relq[e] = E::pack2(ext[2 * e], ext[2 * e + 1]);
+        rem[2 * e] = ext[2 * e] - E::to_f((uint16_t)(relq[e] & 0xFFFFu));
+        rem[2 * e + 1] = ext[2 * e + 1] - E::to_f((uint16_t)(relq[e] >> 16));
+      }
+      relq_lo = u32x4{E::pack2(rem[0], rem[1]), E::pack2(rem[2], rem[3]), E::pack2(rem[4], rem[5]),
+                      E::pack2(rem[6], rem[7])};
+    }
   } else if constexpr (RP == kBwdRelRow64) {
     // gw = 64: the workgroup's 64 queries are grid row qt, and a 64-key tile
     // is one grid row.  rel_h^T[kh][q] = Rh[qt + gh - 1 - kh] . q and
@@ -718,6 +752,13 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
           dp[j][kb] = E::mfma(va, df[j][dc], dp[j][kb]);
         }
       }
+      if constexpr (RP == kBwdRelAug) {
+        // + rel_h[q][kh] / scale + rel_w[q][kw] / scale: the key rows of the
+        // one-hot table against the query's packed rel columns.
+        const u32x4 ea = *(const u32x4*)&Etab[(tile * 64 + kb * 16 + l16) * kBwdAugRow + g * 8];
+        s[0][kb] = E::mfma(ea, relq, s[0][kb]);
+        s[0][kb] = E::mfma(ea, relq_lo, s[0][kb]);
+      }
     }
     u32x4 sf[QB][2];
 #pragma unroll
@@ -730,7 +771,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float sv = s[j][i >> 2][i & 3];
-        if constexpr (RP == kBwdRelNone) {
+        if constexpr (RP == kBwdRelNone || RP == kBwdRelAug) {
           y[i] = fmaf(sv, c2, yoff[j]);
         } else if constexpr (RP == kBwdRelGeneral) {
           // Keys past Nk read the last key's entries (masked below).
@@ -799,6 +840,19 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         for (int kc = 0; kc < 2; ++kc)
           sf[j][kc] = u32x4{E::pack2(ds[kc * 8 + 0], ds[kc * 8 + 1]), E::pack2(ds[kc * 8 + 2], ds[kc * 8 + 3]),
                             E::pack2(ds[kc * 8 + 4], ds[kc * 8 + 5]), E::pack2(ds[kc * 8 + 6], ds[kc * 8 + 7])};
+        if constexpr (RP == kBwdRelAug) {
+          // dRel^T[x][q] += sum_key E[key][x] dS[q][key]: the table by
+          // transposing reads (key order as in sf), like K^T for dQ.
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int xb = 0; xb < 2; ++xb) {
+              const uint16_t* ep = Etab + (tile * 64 + kc * 32 + vt_row) * kBwdAugRow + xb * 16 + vt_col;
+              const u32x2 lo = lds_read_tr16(ep);
+              const u32x2 hi = lds_read_tr16(ep + 16 * kBwdAugRow);
+              drel[xb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[j][kc], drel[xb]);
+            }
+        }
       }
     }
     if constexpr (second) {
@@ -835,7 +889,16 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     // dRel of this workgroup's queries: general grids sum the four lane
     // groups' private rows into `rel` [64][G]; the row form has dRelH^T in
     // its partial slot and adds dRelW^T from registers.
-    if constexpr (RP == kBwdRelGeneral) {
+    if constexpr (RP == kBwdRelAug) {
+      // Each wave's own queries (rel is not read after the prologue).
+#pragma unroll
+      for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int x = xb * 16 + g * 4 + i;
+          if (x < G) rel[qloc * G + x] = drel[xb][i];
+        }
+    } else if constexpr (RP == kBwdRelGeneral) {
       for (int e = tid; e < 64 * G; e += 256) {
         const int ql = e / G, x = e - ql * G;
         const int base = (ql >> 4) * 64 + (ql & 15);
@@ -846,8 +909,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) pslot[(gh + (i >> 2) * 16 + g * 4 + (i & 3)) * 64 + qloc] = wacc[i];
     }
-    auto d_relh = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + x] : pslot[x * 64 + ql]; };
-    auto d_relw = [&](int ql, int x) { return RP == kBwdRelGeneral ? rel[ql * G + gh + x] : pslot[(gh + x) * 64 + ql]; };
+    auto d_relh = [&](int ql, int x) { return RP != kBwdRelRow64 ? rel[ql * G + x] : pslot[x * 64 + ql]; };
+    auto d_relw = [&](int ql, int x) { return RP != kBwdRelRow64 ? rel[ql * G + gh + x] : pslot[(gh + x) * 64 + ql]; };
     __syncthreads();
     // Coefficients A[r][i] (element type) in the free K/V stages: the weight
     // of table row r (Rh rows, then Rw rows) in query i's bias; zero for

@@ -55,7 +55,7 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   const int n_row_wg = ba.a.n_blocks;
   auto rows = attn_bwd_rows<Elem, D, RP, KB>;
-  auto cols = attn_bwd_cols<Elem, D, RP, KB>;
+  auto cols = attn_bwd_cols<Elem, D, RP == kBwdRelAug ? kBwdRelGeneral : RP, KB>;
   if (p.lds > 32 * 1024 &&
       (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
            hipSuccess ||
@@ -101,6 +101,7 @@ static int launch_bwd_tiled(const AttnBwdArgs& ba, const Plan& p, hipStream_t s)
     case kBwdRelNone: return launch_bwd_tiled_rp<kBwdRelNone>(ba, p, s);
     case kBwdRelGeneral: return launch_bwd_tiled_rp<kBwdRelGeneral>(ba, p, s);
     case kBwdRelRow64: return launch_bwd_tiled_rp<kBwdRelRow64>(ba, p, s);
+    case kBwdRelAug: return launch_bwd_tiled_rp<kBwdRelAug>(ba, p, s);
     default: return ATTN_E_UNSUPPORTED;
   }
 }

@@ -51,15 +51,27 @@ constexpr int kBwdRowPad = 16;
 // per column of gh + gw, so gh + gw <= kBwdRelMaxCols, and at d = 80, where
 // the staged tiles are larger, gh + gw <= 83); 64-wide grids
 // (a 64-key tile is one grid row: dRelH is a row sum per tile, dRelW and
-// rel_w stay in registers per key slot).
-constexpr int kBwdRelNone = 0, kBwdRelGeneral = 1, kBwdRelRow64 = 2;
+// rel_w stay in registers per key slot); small general grids (gh + gw <=
+// 32, at most 256 keys: the row kernel adds the bias and gathers dRelH /
+// dRelW on the matrix cores through a one-hot table of the keys' grid
+// positions, E[key][x] = 1 for x = kh and x = gh + kw; its column kernel is
+// the general form's).
+constexpr int kBwdRelNone = 0, kBwdRelGeneral = 1, kBwdRelRow64 = 2, kBwdRelAug = 3;
 constexpr int kBwdRelMaxCols = 84;
+constexpr int kBwdAugMaxCols = 32, kBwdAugMaxKeys = 256;
+// Row stride (elements) of the one-hot key table: 32 columns plus the pad
+// that keeps its transposing reads on distinct banks.
+constexpr int kBwdAugRow = 32 + kBwdRowPad;
 
 constexpr int bwd_rel_mode(const AttnArgs& a) {
   return a.bias_kind != ATTN_BIAS_RELPOS ? kBwdRelNone
          : (a.gw == 64 && a.gh <= 64)     ? kBwdRelRow64
-                                          : kBwdRelGeneral;
+         : (a.gh + a.gw <= kBwdAugMaxCols && a.Nk <= kBwdAugMaxKeys) ? kBwdRelAug
+                                                                       : kBwdRelGeneral;
 }
+// General grids in either form: rel_h / rel_w rows of the workgroup's
+// queries in LDS, and all columns staged by the column kernel.
+constexpr bool bwd_rel_general(int mode) { return mode == kBwdRelGeneral || mode == kBwdRelAug; }
 
 // Rows of the stacked table [Rh; Rw] (equal grids, tables of the needed length).
 constexpr int bwd_rel_rows(const AttnArgs& a) { return 2 * a.gh - 1 + 2 * a.gw - 1; }
@@ -145,10 +157,14 @@ constexpr size_t bwd_stage_bytes(const AttnArgs& a) {
   }
   return (s + 15) / 16 * 16;
 }
-// Bytes of the per-lane dRel sums at the end of the relative-position
-// region (general grids).
+// Bytes at the end of the relative-position region that only the key loop
+// uses: the per-lane dRel sums (general grids) or the one-hot key table
+// (small general grids, one row per key of the padded tiles).
 constexpr size_t bwd_rows_acc_bytes(const AttnArgs& a) {
-  return bwd_rel_mode(a) == kBwdRelGeneral ? (size_t)256 * ((a.gh + a.gw) | 1) * 4 : 0;
+  const int mode = bwd_rel_mode(a);
+  if (mode == kBwdRelGeneral) return (size_t)256 * ((a.gh + a.gw) | 1) * 4;
+  if (mode == kBwdRelAug) return (size_t)((a.Nk + 63) / 64 * 64) * kBwdAugRow * 2;
+  return 0;
 }
 template <int D>
 constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
@@ -156,7 +172,7 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
   const int mode = bwd_rel_mode(a);
   if (mode == kBwdRelNone) return 0;
   const size_t g = (size_t)(a.gh + a.gw);
-  size_t rel = mode == kBwdRelGeneral ? 64 * g * 4 : 0;
+  size_t rel = bwd_rel_general(mode) ? 64 * g * 4 : 0;
   const size_t qt = (size_t)64 * ROW * 2;
   rel = (rel > qt ? rel : qt);
   const size_t acc = bwd_rows_acc_bytes(a), tab = bwd_rel_tab_bytes<D>(a);
@@ -169,7 +185,7 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
 // column joins the staged log-sum-exp, and each lane reads its own rel_w
 // column from the workspace).
 constexpr int bwd_cols_rel_cols(const AttnArgs& a) {
-  return bwd_rel_mode(a) == kBwdRelGeneral ? a.gh + a.gw : 0;
+  return bwd_rel_general(bwd_rel_mode(a)) ? a.gh + a.gw : 0;
 }
 
 // The backward of a validated call (half precision): window units (at most

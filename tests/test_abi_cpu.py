@@ -398,6 +398,10 @@ def test_backward_validation(lib):
     assert bwd_status(q4241, q4241, B.RelposBias(t(83, 80), t(81, 80), (42, 41))) == 0
     q43 = t(1, 1, 43 * 42, 32)
     assert bwd_status(q43, q43, B.RelposBias(t(85, 32), t(83, 32), (43, 42))) == 4
+    # Small general grids (gh + gw <= 32, at most 256 keys) take the one-hot
+    # key table's form: its largest case fits at d = 80 too.
+    q256 = t(1, 1, 16 * 16, 80)
+    assert bwd_status(q256, q256, B.RelposBias(t(31, 80), t(31, 80), (16, 16))) == 0
     qi = t(1, 2, 64 * 64, 64)
     img = B.Window(64, 64, 14, 14, 0, 0)
     assert bwd_status(qi, qi, B.RelposBias(t(27, 64), t(27, 64), (14, 14)), layout="image", window=img) == 4

@@ -196,7 +196,11 @@ def test_backward_unsupported_calls():
 
 
 # Relative-position backward (tiled path): equal grids, tables of 2g-1 rows.
-RELPOS_GRIDS = [(2, 3), (7, 7), (14, 14), (8, 12), (5, 16), (30, 30), (1, 64), (3, 64), (16, 64)]
+# gh + gw <= 32 with at most 256 keys: the one-hot table form ((16, 16) and
+# (17, 15) at its limits); (16, 17), (30, 30): the general form; gw = 64:
+# the 64-wide form.
+RELPOS_GRIDS = [(2, 3), (7, 7), (14, 14), (8, 12), (5, 16), (16, 16), (17, 15), (16, 17), (30, 30),
+                (1, 64), (3, 64), (16, 64)]
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
@@ -211,7 +215,7 @@ def test_relpos_backward_grids(dtype, grid):
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 @pytest.mark.parametrize("d", [32, 40, 64, 80])
-@pytest.mark.parametrize("grid", [(14, 14), (4, 64)])
+@pytest.mark.parametrize("grid", [(14, 14), (12, 24), (4, 64)])
 def test_relpos_backward_head_dims(dtype, d, grid):
     n = grid[0] * grid[1]
     w = W.custom(dtype, B=2, H=2, Nq=n, Nk=n, d=d, bias="relpos", grid=grid, cfg_id=870 + d)
