@@ -308,8 +308,10 @@ ATTN_API int attn_check_opt(const attn_tensor_t* q, const attn_tensor_t* k, cons
  *    per-window partial table gradients, summed over windows in a fixed
  *    order by a second kernel), else 0.  Longer sequences: 2 * B * H * Nq * 4
  *    bytes (each query row's log-sum-exp and sum_j P_ij dP_ij); with RELPOS
- *    also each query's rel_h / rel_w rows (B * H * Nq * (gh + gw) floats)
- *    and one partial [dRh; dRw] per 64 query rows (B * H * ceil(Nq / 64)
+ *    also each query's rel_h / rel_w rows (B * H * Nq * (gh + gw) floats;
+ *    B * H * Nq * 32 floats when gh + gw <= 32 and Nk <= 256, a row then
+ *    being 32 columns in the element type, high and low parts) and one
+ *    partial [dRh; dRw] per 64 query rows (B * H * ceil(Nq / 64)
  *    slots of ((2gh-1) + (2gw-1)) * d floats, at least (gh + 64) * 64 when
  *    gw = 64), summed in a fixed order; these two regions start on multiples
  *    of 4 floats.  Bitwise-deterministic, no atomics.

@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
           if (mm < nr && x >= 0 && x < ng) {
             const int col = half ? gh + x : x;
             rel[qloc * G + col] = acc_t[i];
-            if (qrow < Nq) ws_rel[(int64_t)col * Nq + qrow] = acc_t[i] * kLog2e;
+            if (RP == kBwdRelGeneral && qrow < Nq) ws_rel[(int64_t)col * Nq + qrow] = acc_t[i] * kLog2e;
           }
         }
       }
@@ -615,6 +615,12 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
       relq_lo = u32x4{E::pack2(rem[0], rem[1]), E::pack2(rem[2], rem[3]), E::pack2(rem[4], rem[5]),
                       E::pack2(rem[6], rem[7])};
+      // The column kernel's copy: [B*H][Nq][hi 32 | lo 32] elements.
+      if (qrow < Nq) {
+        uint16_t* wq = (uint16_t*)(ba.ws + wl.rel) + (bh * Nq + qrow) * 64 + g * 8;
+        *(u32x4*)wq = relq;
+        *(u32x4*)(wq + 32) = relq_lo;
+      }
     }
   } else if constexpr (RP == kBwdRelRow64) {
     // gw = 64: the workgroup's 64 queries are grid row qt, and a 64-key tile
@@ -1075,6 +1081,22 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     xh = kh;
     xw = gh + kw;
   }
+  // The one-hot table's form: E[key][x] of this lane's key as the B
+  // fragment of the bias product (slots x = g*8 .. g*8+7), and the staged
+  // packed rel rows [2][64][kBwdAugQRow] of the query tile.
+  u32x4 ef = u32x4{0, 0, 0, 0};
+  if constexpr (RP == kBwdRelAug) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = g * 8 + 2 * e;
+      const uint32_t lo = x == xh || x == xw ? E::one_bits() : 0u;
+      const uint32_t hi = x + 1 == xh || x + 1 == xw ? E::one_bits() : 0u;
+      ef[e] = lo | hi << 16;
+    }
+  }
+  uint16_t* Rq = (uint16_t*)Rst;
+  const uint16_t* ws_relq = (const uint16_t*)(ba.ws + bwd_ws_layout(a).rel) + ((int64_t)b * a.H + h) * Nq * 64;
+  u32x4 rqreg[2];
   constexpr int RC = RP == kBwdRelGeneral ? (kBwdRelMaxCols * 64 + 255) / 256 : 1;
   f32x4 wv[RP == kBwdRelRow64 ? 4 : 1];  // 64-wide form: rel_w column xw, a tile's 64 queries
   auto load_w = [&](int t) {
@@ -1104,6 +1126,15 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         hreg = __uint_as_float(
             __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ws_rel + (int64_t)kt * Nq + t * 64, nb), tid * 4, 0, 0));
     }
+    if constexpr (RP == kBwdRelAug) {
+      // 64 rows of 128 bytes; rows past Nq read as zero.
+      const auto rr = buffer_rsrc(ws_relq + (int64_t)t * 64 * 64, (uint32_t)(Nq - t * 64) * 128);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256;
+        rqreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)c * 16, 0, 0);
+      }
+    }
     if constexpr (RP == kBwdRelGeneral) {
       // [G][Nq] floats of this (batch item, head): at most 84 x 1764.
       const auto rr = buffer_rsrc(ws_rel, (uint32_t)(G * Nq) * 4);
@@ -1131,6 +1162,13 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
       for (int c = 0; c < RC; ++c) {
         const int e = tid + c * 256;
         if (e < 64 * NC) Rst[st * 64 * NC + e] = rreg[c];
+      }
+    }
+    if constexpr (RP == kBwdRelAug) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256;  // row c / 8, chunk c % 8
+        *(u32x4*)&Rq[st * 64 * kBwdAugQRow + (c >> 3) * kBwdAugQRow + (c & 7) * 8] = rqreg[i];
       }
     }
   };
@@ -1188,6 +1226,12 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
           dp[kb][qb] = E::mfma(oa, vf[kb][dc], dp[kb][qb]);
         }
       }
+      if constexpr (RP == kBwdRelAug) {
+        // + (rel_h[q][kh] + rel_w[q][kw]) / scale, high and low parts.
+        const uint16_t* rq = Rq + st * 64 * kBwdAugQRow + (qb * 16 + l16) * kBwdAugQRow + g * 8;
+        s[0][qb] = E::mfma(*(const u32x4*)rq, ef, s[0][qb]);
+        s[0][qb] = E::mfma(*(const u32x4*)(rq + 32), ef, s[0][qb]);
+      }
     }
     u32x4 pf[KB][2], sf[KB][2];
 #pragma unroll
@@ -1206,7 +1250,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float y = fmaf(s[kb][qb][r], c2, nL[r]);
-          if constexpr (RP != kBwdRelNone) y += bias[r];
+          if constexpr (RP == kBwdRelGeneral || RP == kBwdRelRow64) y += bias[r];
           const float pv = __builtin_amdgcn_exp2f(y);
           p[qb * 4 + r] = pv;
           ds[qb * 4 + r] = pv * dp[kb][qb][r];

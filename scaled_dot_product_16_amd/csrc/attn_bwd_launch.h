@@ -55,7 +55,7 @@ static int launch_bwd_tiled_rp(const AttnBwdArgs& ba0, const Plan& p, hipStream_
   ba.a.n_blocks = ba.a.n_qtiles * ba.a.H * ba.a.B;
   const int n_row_wg = ba.a.n_blocks;
   auto rows = attn_bwd_rows<Elem, D, RP, KB>;
-  auto cols = attn_bwd_cols<Elem, D, RP == kBwdRelAug ? kBwdRelGeneral : RP, KB>;
+  auto cols = attn_bwd_cols<Elem, D, RP, KB>;
   if (p.lds > 32 * 1024 &&
       (hipFuncSetAttribute((const void*)rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) !=
            hipSuccess ||

@@ -62,6 +62,11 @@ constexpr int kBwdAugMaxCols = 32, kBwdAugMaxKeys = 256;
 // Row stride (elements) of the one-hot key table: 32 columns plus the pad
 // that keeps its transposing reads on distinct banks.
 constexpr int kBwdAugRow = 32 + kBwdRowPad;
+// Small general grids hand each query's rel_h / rel_w row to the column
+// kernel as 32 columns / scale in the element type, high then low part
+// (64 elements, 128 bytes); the column kernel stages a query tile of them
+// with rows of kBwdAugQRow elements.
+constexpr int kBwdAugQRow = 64 + kBwdRowPad;
 
 constexpr int bwd_rel_mode(const AttnArgs& a) {
   return a.bias_kind != ATTN_BIAS_RELPOS ? kBwdRelNone
@@ -86,9 +91,11 @@ constexpr size_t bwd_part_stride(const AttnArgs& a) {
 }
 // Workspace of the tiled backward, in floats: the rows' L and D (B*H*Nq
 // each), then with the relative position the rel_h / rel_w rows of every
-// query ([B*H][gh + gw][Nq], written by the row kernel, read by the column
-// kernel) and one partial slot per row-kernel workgroup ([B*H*ceil(Nq/64)]
-// slots of pstride floats, summed in a fixed order afterwards).
+// query ([B*H][gh + gw][Nq] floats, or [B*H][Nq][64] elements in the one-
+// hot table's form, 32 floats a query; written by the row kernel, read by
+// the column kernel) and one partial slot per row-kernel workgroup
+// ([B*H*ceil(Nq/64)] slots of pstride floats, summed in a fixed order
+// afterwards).
 struct BwdWs {
   size_t L, D, rel, part, pstride, total;
 };
@@ -98,7 +105,8 @@ constexpr BwdWs bwd_ws_layout(const AttnArgs& a) {
   size_t off = (2 * n + 3) / 4 * 4;
   w.rel = off;
   if (a.bias_kind == ATTN_BIAS_RELPOS) {
-    off = (off + n * (size_t)(a.gh + a.gw) + 3) / 4 * 4;
+    const size_t per_q = bwd_rel_mode(a) == kBwdRelAug ? 32 : (size_t)(a.gh + a.gw);
+    off = (off + n * per_q + 3) / 4 * 4;
     w.part = off;
     w.pstride = bwd_part_stride(a);
     off += (size_t)a.B * a.H * (size_t)((a.Nq + 63) / 64) * w.pstride;
@@ -183,9 +191,15 @@ constexpr size_t bwd_rows_rel_bytes(const AttnArgs& a) {
 // Columns of rel_h / rel_w the column kernel stages per query tile: all of
 // them for general grids; none in the 64-wide form (the key tile's rel_h
 // column joins the staged log-sum-exp, and each lane reads its own rel_w
-// column from the workspace).
+// column from the workspace) or the one-hot table's form (which stages the
+// packed rows instead).
 constexpr int bwd_cols_rel_cols(const AttnArgs& a) {
-  return bwd_rel_general(bwd_rel_mode(a)) ? a.gh + a.gw : 0;
+  return bwd_rel_mode(a) == kBwdRelGeneral ? a.gh + a.gw : 0;
+}
+// Bytes of the column kernel's two stages of relative-position data.
+constexpr size_t bwd_cols_rel_bytes(const AttnArgs& a) {
+  return bwd_rel_mode(a) == kBwdRelAug ? (size_t)2 * 64 * kBwdAugQRow * 2
+                                       : (size_t)2 * 64 * bwd_cols_rel_cols(a) * 4;
 }
 
 // The backward of a validated call (half precision): window units (at most
@@ -222,7 +236,7 @@ inline Plan plan_bwd_half(const AttnArgs& a) {
   // position regions); column kernel: two stages of the Q and dO tiles, of
   // the 64 rows' L and D, and of the staged rel_h / rel_w columns.
   const size_t rows = bwd_stage_bytes<D>(a) + bwd_rows_rel_bytes<D>(a);
-  const size_t cols = (size_t)4 * 64 * ROW * 2 + 4 * 64 * 4 + (size_t)2 * 64 * bwd_cols_rel_cols(a) * 4;
+  const size_t cols = (size_t)4 * 64 * ROW * 2 + 4 * 64 * 4 + bwd_cols_rel_bytes(a);
   p.lds = rows > cols ? rows : cols;
   return p;
 }

@@ -333,9 +333,10 @@ def test_backward_validation(lib):
     assert h.attn_bwd_check(*args2(ctypes.c_void_p(wsl.data_ptr()), 2 * 2 * 100 * 4)) == 0
     # The relative position on a long sequence (10x10 grid, equal key grid,
     # tables of 19 rows): dtable = [dRh; dRw] (19 + 19 rows of d floats) and
-    # a workspace of L, D (2*B*H*Nq), the rel_h / rel_w rows (B*H*Nq*(gh+gw))
-    # and one partial per 64 query rows (B*H*ceil(Nq/64)*(19+19)*d), each
-    # region rounded up to 4 floats.
+    # a workspace of L, D (2*B*H*Nq), the rel_h / rel_w rows (B*H*Nq*32 when
+    # gh + gw <= 32 and Nk <= 256, else B*H*Nq*(gh+gw)) and one partial per
+    # 64 query rows (B*H*ceil(Nq/64)*(19+19)*d), each region rounded up to 4
+    # floats.
     rb = B.RelposBias(t(19, 64), t(19, 64), (10, 10))
     qc3, kc3, vc3, bd3, md3, oc3, dt3, keep3 = B._marshal(*ins, rb, None, "batched", None)
     need3 = ctypes.c_size_t(0)
@@ -343,7 +344,16 @@ def test_backward_validation(lib):
                                      ctypes.byref(oc3), ctypes.byref(bd3), ctypes.byref(md3), dt3,
                                      ctypes.byref(need3)) == 0
     up4 = lambda n: (n + 3) // 4 * 4
-    assert need3.value == 4 * (up4(up4(2 * 2 * 100) + 2 * 100 * 20) + 2 * 2 * 38 * 64)
+    assert need3.value == 4 * (up4(up4(2 * 2 * 100) + 2 * 100 * 32) + 2 * 2 * 38 * 64)
+    rb18 = B.RelposBias(t(35, 64), t(31, 64), (18, 16))     # gh + gw = 34: (gh + gw) floats a query
+    q18 = t(1, 2, 18 * 16, 64)
+    m18 = B._marshal(q18, q18.clone(), q18.clone(), q18.clone(), rb18, None, "batched", None)
+    need18 = ctypes.c_size_t(0)
+    assert h.attn_bwd_workspace_size(ctypes.byref(m18[0]), ctypes.byref(m18[1]), ctypes.byref(m18[2]),
+                                     ctypes.byref(m18[5]), ctypes.byref(m18[3]), ctypes.byref(m18[4]), m18[6],
+                                     ctypes.byref(need18)) == 0
+    assert need18.value == 4 * (up4(up4(2 * 2 * 288) + 2 * 288 * 34) + 2 * 5 * 66 * 64)
+    del m18
     dr = torch.zeros(38, 64)
     wsr = torch.zeros(need3.value // 4)
     args3 = lambda dtab, n: (ctypes.byref(qc3), ctypes.byref(kc3), ctypes.byref(vc3), ctypes.byref(oc3),
