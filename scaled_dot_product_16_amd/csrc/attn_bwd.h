@@ -27,7 +27,7 @@ template <class E, int D, int BIAS, int MASKK>
 __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
   using C = WinBwdCfg<D>;
   constexpr int NT = C::NT, KCH = C::KCH, DK = C::DK, CBD = C::CBD, ROW = C::ROW, PROW = C::PROW,
-                FROW = C::FROW, RCH = C::RCH, NCH = C::NCH, CPT = C::CPT;
+                RCH = C::RCH, NCH = C::NCH, CPT = C::CPT;
   constexpr int TILE = 64 * ROW;
   constexpr bool kTab = BIAS == ATTN_BIAS_TABLE || MASKK == ATTN_MASK_SHIFT_REGIONS;
   const AttnArgs& a = ba.a;
@@ -38,9 +38,12 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
   uint16_t* Os = Qs + TILE;               // dO
   uint16_t* Pt = Os + TILE;               // [64 keys][PROW] P^T, element type
   uint16_t* St = Pt + 64 * PROW;          // [64 keys][PROW] dS^T, element type
-  float* Sf = (float*)(St + 64 * PROW);   // [64 keys][FROW] dS^T, fp32 (table gradient)
-  int* kinfo = (int*)(Sf + 64 * FROW);
+  int* kinfo = (int*)(St + 64 * PROW);
   float* tbl = (float*)(kinfo + 64);      // 9 table copies, log2 units
+  // dS^T in fp32 for the table gradient, [Nk][Nq + 1], written once the K
+  // and V tiles are dead: in their space when it fits, else after the table.
+  float* Sf = win_bwd_sf_in_kv<D>(a) ? (float*)lds
+                                     : (float*)(lds + C::BYTES + (win_uses_table(a) ? 9 * win_tab_entries(a) * 4 : 0));
 
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -238,7 +241,6 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
       const uint32_t pp = E::pack2(p[kb * 4 + r], ds[kb * 4 + r]);
       Pt[key * PROW + qrow] = (uint16_t)(pp & 0xffff);
       St[key * PROW + qrow] = (uint16_t)(pp >> 16);
-      Sf[key * FROW + qrow] = ds[kb * 4 + r];
     }
   // dQ^T = K^T dS^T: dS^T packed as the B operand (the forward's P layout),
   // K^T from transposing reads of the K tile.
@@ -275,7 +277,19 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
       }
     }
   }
-  __syncthreads();  // P^T, dS^T complete
+  __syncthreads();  // P^T, dS^T complete; the K and V tiles are dead
+  const int fs = N + 1;  // row stride of the fp32 dS^T
+  if constexpr (BIAS == ATTN_BIAS_TABLE) {
+    if (qvalid) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb * 16 + g * 4 + r;
+          if (key < Nk) Sf[key * fs + qrow] = ds[kb * 4 + r];
+        }
+    }
+  }
 
   // ---- Per key block: dK = scale * dS^T Q, dV = P^T dO ----------------------
   // Keys 16w .. 16w+15 are the column block; the contraction runs over the
@@ -322,17 +336,30 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
   }
 
   // ---- Table gradient of this unit --------------------------------------
-  // Row r of the table holds offset (dh, dw) = query - key; its gradient is
-  // the sum of dS over the unit's pairs with that offset, summed here in
-  // query order by one thread (fixed order: deterministic).
+  // Row r of the table holds offset (oh, ow) = query - key; its gradient is
+  // the sum of dS over the unit's pairs with that offset.  Two fixed-order
+  // stages (deterministic): M[qh][kh][ow], the sum over qw - kw = ow of the
+  // (query row qh, key row kh) block, for every (qh, kh, ow); then row r,
+  // the sum of M[qh][qh - oh][ow] over qh in order.
   if constexpr (BIAS == ATTN_BIAS_TABLE) {
+    __syncthreads();  // the fp32 dS^T is complete; Q, dO, P^T and dS^T are dead
     const int gh = a.gh, gw = a.gw, tw = 2 * gw - 1;
-    for (int r = tid; r < n_tab; r += NT) {
-      const int oh = r / tw - (gh - 1), ow = r % tw - (gw - 1);
+    float* Mg = (float*)Pt;  // [gh][gh][tw] floats (at most 4096) in the P^T / dS^T space
+    const float inv_tw = __builtin_amdgcn_rcpf((float)tw), inv_gh = __builtin_amdgcn_rcpf((float)gh);
+    for (int t = tid; t < gh * gh * tw; t += NT) {
+      const int blk = div_small(t, inv_tw), owi = t - blk * tw;
+      const int qh = div_small(blk, inv_gh), kh = blk - qh * gh, ow = owi - (gw - 1);
+      // Query (qh, qw), key (kh, qw - ow): Sf[(kh*gw + qw - ow) * fs + qh*gw + qw].
+      const int base = (kh * gw - ow) * fs + qh * gw;
       float acc = 0.f;
-      for (int qh = max(0, oh); qh < min(gh, gh + oh); ++qh)
-        for (int qw = max(0, ow); qw < min(gw, gw + ow); ++qw)
-          acc += Sf[((qh - oh) * gw + (qw - ow)) * FROW + qh * gw + qw];
+      for (int qw = max(0, ow); qw < min(gw, gw + ow); ++qw) acc += Sf[base + qw * (fs + 1)];
+      Mg[t] = acc;
+    }
+    __syncthreads();
+    for (int r = tid; r < n_tab; r += NT) {
+      const int ohi = div_small(r, inv_tw), owi = r - ohi * tw, oh = ohi - (gh - 1);
+      float acc = 0.f;
+      for (int qh = max(0, oh); qh < min(gh, gh + oh); ++qh) acc += Mg[(qh * gh + qh - oh) * tw + owi];
       ba.ws[((int64_t)h * n_tab + r) * a.B + b] = acc;  // [H][n_tab][B]: windows contiguous
     }
   }

@@ -11,9 +11,11 @@ namespace attn {
 
 // Window backward kernel (attn_bwd_win): Q, K, V and dO tiles of 64 rows
 // (head dim padded to the 32-wide contraction), P^T and dS^T in the element
-// type (64 keys x 64 queries, rows padded by 8), dS^T in fp32 for the table
-// gradient (rows of 65), then the per-key lookup parts and the table.  (A
-// pad of 16, which the tiled backward takes, measured 2 % slower here.)
+// type (64 keys x 64 queries, rows padded by 8), the per-key lookup parts
+// and the table.  (A pad of 16, which the tiled backward takes, measured 2 %
+// slower here.)  With a TABLE bias, dS^T is also kept in fp32 for the table
+// gradient ([Nk][Nq + 1] floats): written after the K and V tiles are dead,
+// into their space when it fits there, else after the table.
 template <int D>
 struct WinBwdCfg {
   static constexpr int NT = kWinWaves * 64;
@@ -22,16 +24,24 @@ struct WinBwdCfg {
   static constexpr int CBD = (D + 15) / 16;   // 16-wide blocks of dQ, dK, dV columns
   static constexpr int ROW = DK + 8;
   static constexpr int PROW = 64 + 8;
-  static constexpr int FROW = 64 + 1;
   static constexpr int RCH = D / 8;
   static constexpr int NCH = 64 * RCH;
   static constexpr int CPT = (NCH + NT - 1) / NT;
-  static constexpr size_t BYTES = (size_t)4 * 64 * ROW * 2 + (size_t)2 * 64 * PROW * 2 +
-                                  (size_t)64 * FROW * 4 + 64 * 4;
+  static constexpr size_t KV_BYTES = (size_t)2 * 64 * ROW * 2;  // the K and V tiles
+  static constexpr size_t BYTES = (size_t)4 * 64 * ROW * 2 + (size_t)2 * 64 * PROW * 2 + 64 * 4;
 };
 
-constexpr size_t win_bwd_lds_bytes(const AttnArgs& a, size_t base) {
-  return base + (win_uses_table(a) ? (size_t)9 * win_tab_entries(a) * 4 : 0);
+constexpr size_t win_bwd_sf_bytes(const AttnArgs& a) {
+  return a.bias_kind == ATTN_BIAS_TABLE ? (size_t)a.Nk * (a.Nq + 1) * 4 : 0;
+}
+template <int D>
+constexpr bool win_bwd_sf_in_kv(const AttnArgs& a) {
+  return win_bwd_sf_bytes(a) <= WinBwdCfg<D>::KV_BYTES;
+}
+template <int D>
+constexpr size_t win_bwd_lds_bytes(const AttnArgs& a) {
+  const size_t n = WinBwdCfg<D>::BYTES + (win_uses_table(a) ? (size_t)9 * win_tab_entries(a) * 4 : 0);
+  return n + (win_bwd_sf_in_kv<D>(a) ? 0 : win_bwd_sf_bytes(a));
 }
 
 // ---------------------------------------------------------------------------
@@ -216,7 +226,7 @@ inline Plan plan_bwd_half(const AttnArgs& a) {
   if (a.Nq <= 64 && a.Nk <= 64 && a.bias_kind != ATTN_BIAS_RELPOS) {
     p.kernel = kKernWin;
     p.blocks = (int64_t)a.B * a.H;
-    p.lds = win_bwd_lds_bytes(a, WinBwdCfg<D>::BYTES);
+    p.lds = win_bwd_lds_bytes<D>(a);
     return p;
   }
   const bool rel_ok = a.bias_kind == ATTN_BIAS_RELPOS && a.gh == a.kgh && a.gw == a.kgw &&
