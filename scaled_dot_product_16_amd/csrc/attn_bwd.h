@@ -767,6 +767,9 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
     }
     const uint16_t* Kt = Ks + st * TILE;
     const uint16_t* Vt = Vs + st * TILE;
+    // The blocks of matrix products run at a raised wave priority, so a
+    // wave that reaches them issues ahead of the others' vector work.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 s[QB][4], dp[QB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -793,6 +796,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
         s[0][kb] = E::mfma(ea, relq_lo, s[0][kb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     u32x4 sf[QB][2];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
@@ -889,6 +893,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
       }
     }
     if constexpr (second) {
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -899,6 +904,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rows(AttnBwdArgs ba) {
 #pragma unroll
           for (int j = 0; j < QB; ++j) acc[j][cb] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[j][kc], acc[j][cb]);
         }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (more) {
       // Stage st^1 was last read in the previous tile, before the barrier
@@ -1234,6 +1240,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     const float* Dt = Ds + st * 64;
     // S = Q K^T and dP = dO V^T - D: rows are queries qb*16 + g*4 + r, the
     // column is this lane's key of block kb.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 s[KB][4], dp[KB][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -1260,6 +1267,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
         s[0][qb] = E::mfma(*(const u32x4*)(rq + 32), ef, s[0][qb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     u32x4 pf[KB][2], sf[KB][2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -1293,6 +1301,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     }
     if (more) load_w(t + 1);  // the values of this tile are used: the next tile's, in flight from here
     // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the tiles).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -1307,6 +1316,7 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
           dk[kb][cb] = E::mfma(u32x4{ql[0], ql[1], qh[0], qh[1]}, sf[kb][kc], dk[kb][cb]);
         }
       }
+    __builtin_amdgcn_s_setprio(0);
     if (more) store_tile(st ^ 1, t + 1);  // stage st^1 was last read before the previous barrier
     __syncthreads();
   }
