@@ -1128,7 +1128,8 @@ __global__ __launch_bounds__(256) void attn_bwd_cols(AttnBwdArgs ba) {
     }
   }
   uint16_t* Rq = (uint16_t*)Rst;
-  const uint16_t* ws_relq = (const uint16_t*)(ba.ws + bwd_ws_layout(a).rel) + ((int64_t)b * a.H + h) * Nq * 64;
+  const uint16_t* ws_relq =
+      RP == kBwdRelAug ? (const uint16_t*)(ba.ws + bwd_ws_layout(a).rel) + ((int64_t)b * a.H + h) * Nq * 64 : nullptr;
   u32x4 rqreg[2];
   constexpr int RC = RP == kBwdRelGeneral ? (kBwdRelMaxCols * 64 + 255) / 256 : 1;
   f32x4 wv[RP == kBwdRelRow64 ? 4 : 1];  // 64-wide form: rel_w column xw, a tile's 64 queries
