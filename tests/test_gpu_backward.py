@@ -106,6 +106,11 @@ CASES = [
     ("none", None, "additive", None),
     ("table", (7, 7), "additive", None),
     ("additive", None, "shift", (14, 14, 7, 7, 3, 3)),
+    # Extreme window shapes for the table gradient's two stages: 16 x 4,
+    # 64 x 1 (the largest intermediate, 64 * 64 sums) and 1 x 64.
+    ("table", (16, 4), "none", None),
+    ("table", (64, 1), "none", None),
+    ("table", (1, 64), "none", None),
 ]
 
 
@@ -122,6 +127,17 @@ def test_backward_bias_and_mask(dtype, case):
                  cfg_id=820 + case)
     say(f"[backward] {dtype} {bias} {grid} {mask} {window}")
     inp = with_dense_terms(w, inputs(w, seed=case), n_bias=2, n_mask=3)
+    check_grads(w, inp, run_bwd(w, to_device(inp)))
+
+
+@pytest.mark.parametrize("d", [40, 64, 80])
+def test_backward_table_head_dims(d):
+    # The fp32 dS^T of the table gradient in the dead K / V tiles (which
+    # hold it at every head dim above 32; at d = 32 an 8 x 8 window needs
+    # its own region, covered above).
+    w = W.custom(W.BF16, B=6, H=3, Nq=64, Nk=64, d=d, bias="table", grid=(8, 8), cfg_id=830 + d)
+    say(f"[backward] table bias 8x8, d={d}")
+    inp = inputs(w, seed=d)
     check_grads(w, inp, run_bwd(w, to_device(inp)))
 
 
