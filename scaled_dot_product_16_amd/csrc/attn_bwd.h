@@ -366,26 +366,33 @@ __global__ __launch_bounds__(kWinWaves * 64) void attn_bwd_win(AttnBwdArgs ba) {
 }
 
 // d_table[r, h] = sum over the batch items b (windows) of the per-unit
-// partial sums ws[h][r][b].  One workgroup per (row, head): each thread adds
-// a strided slice of the windows, then a fixed tree in LDS adds the 256
-// partial sums (the same order every run: deterministic).  (A template only
-// so that every compiled instance may carry its copy.)
+// partial sums ws[h][r][b].  One wave per (row, head), four per workgroup:
+// lane l adds windows l, l + 64, ... in order, with the loads of 8 windows
+// issued before they are added, then a fixed butterfly across the wave
+// (shuffles, no barrier) adds the 64 lane sums; lane 0 holds the same sum
+// every run (deterministic).  (A template only so that every compiled
+// instance may carry its copy.)
 template <int kUnused>
 __global__ __launch_bounds__(256) void attn_bwd_table_reduce(const float* ws, float* dtable, int B,
                                                              int H, int n_tab) {
-  __shared__ float part[256];
-  const int i = blockIdx.x;  // i = r * H + h
+  const int lane = __builtin_amdgcn_workitem_id_x() & 63;
+  const int i = __builtin_amdgcn_workgroup_id_x() * 4 + (__builtin_amdgcn_workitem_id_x() >> 6);  // r * H + h
+  if (i >= n_tab * H) return;  // whole waves
   const int r = i / H, h = i - r * H;
   const float* src = ws + ((int64_t)h * n_tab + r) * B;
   float acc = 0.f;
-  for (int b = threadIdx.x; b < B; b += 256) acc += src[b];
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
+  int b = lane;
+  for (; b + 7 * 64 < B; b += 8 * 64) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[b + j * 64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
   }
-  if (threadIdx.x == 0) dtable[i] = part[0];
+  for (; b < B; b += 64) acc += src[b];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) dtable[i] = acc;
 }
 
 // ---------------------------------------------------------------------------

@@ -24,7 +24,7 @@ int launch_bwd_one(const AttnBwdArgs& ba0, const Plan& p, hipStream_t s) {
   if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
   if constexpr (BIAS == ATTN_BIAS_TABLE) {
     const int n = ba.n_tab * ba.a.H;
-    hipLaunchKernelGGL(attn_bwd_table_reduce<0>, dim3((unsigned)n), dim3(256), 0, s, (const float*)ba.ws,
+    hipLaunchKernelGGL(attn_bwd_table_reduce<0>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, (const float*)ba.ws,
                        ba.dtable, ba.a.B, ba.a.H, ba.n_tab);
     if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
   }
