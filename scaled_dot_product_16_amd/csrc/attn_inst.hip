@@ -73,6 +73,11 @@ int launch_mfma(const Plan& p, const AttnArgs& a, hipStream_t s) {
   using C = MfmaCfg<D, NW, kNQB>;
   AttnArgs t = a;
   t.n_qtiles = (a.Nq + C::BM - 1) / C::BM;
+  t.tpw = 1;
+  if (RMODE == kTwoTiles && !a.image && two_tile_persists<D>()) {  // workgroups per unit, each over tpw query tiles
+    t.tpw = p.tpw;
+    t.n_qtiles = (t.n_qtiles + p.tpw - 1) / p.tpw;
+  }
   t.fd_qt = make_fastdiv(t.n_qtiles);
   t.n_blocks = (int)p.blocks;
   constexpr bool kPingPong = NW == 8 && RMODE != kTwoTiles;

@@ -67,6 +67,7 @@ struct AttnArgs {
   // Filled by the launcher.
   int32_t n_qtiles;
   int32_t n_blocks;  // workgroups in the grid
+  int32_t tpw;       // two-tile form, batched layout: consecutive query tiles per workgroup (0: one)
   int32_t n_hgrp;    // head groups per batch item (packed window kernel)
   FastDiv fd_hgrp;
   int32_t win_heads; // requested heads per workgroup of the window path (0: library's choice)

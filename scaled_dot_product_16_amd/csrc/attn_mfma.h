@@ -156,31 +156,38 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   const int qt = bid - qt_div * a.n_qtiles;
   const int b = fdiv(qt_div, a.fd_h);
   const int h = qt_div - b * a.H;
-  const int q0 = qt * BM;
+  // The two-tile form in the batched layout walks tpw consecutive query
+  // tiles per workgroup (q0 advances by BM after each), except at d = 64,
+  // where its output staging would cost a resident workgroup per CU.
+  constexpr bool kPersist = RMODE == kTwoTiles && !IMG && two_tile_persists<D>();
+  int q0 = qt * (kPersist ? max(a.tpw, 1) : 1) * BM;
   const int wq0 = wave * NQB * 16;  // first query row of this wave inside the tile
 
   // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
   u32x4 qf[NQB][KCHT];
   const char* qbase = (const char*)a.q + IES * tok_base(a, a.q_sb, a.q_sh, b, h);
+  auto load_qf = [&](int qs) {  // the fragments of the tile starting at query qs
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
-    const uint32_t off = tok_row(a, a.q_sn, b, qi);
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qi = min(qs + wq0 + qb * 16 + l16, a.Nq - 1);
+      const uint32_t off = tok_row(a, a.q_sn, b, qi);
 #pragma unroll
-    for (int dc = 0; dc < KCH; ++dc) {
-      const int d0 = dc * 32 + g * 8;
-      // (a padding token of the image layout is a zero query)
-      if constexpr (F8) {
-        // Loaded from an address that is always valid and then selected, so
-        // the loads of all fragments are in flight together (a load inside
-        // the condition would be waited for before its conversion).
-        const bool ok = d0 < D && off != kPadTok;
-        const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
-        qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
-      } else
-        qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
+      for (int dc = 0; dc < KCH; ++dc) {
+        const int d0 = dc * 32 + g * 8;
+        // (a padding token of the image layout is a zero query)
+        if constexpr (F8) {
+          // Loaded from an address that is always valid and then selected,
+          // so the loads of all fragments are in flight together (a load
+          // inside the condition would be waited for before its conversion).
+          const bool ok = d0 < D && off != kPadTok;
+          const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
+          qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
+        } else
+          qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
+      }
     }
-  }
+  };
+  load_qf(q0);
 
   // Tile loaders: CPT 16-byte chunks of K and of V per thread, through
   // buffer resources.  Batched layout: the resource of tile t starts at key
@@ -862,11 +869,81 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   store_k_from(1, 1, kreg1);
   store_v_from(1, vreg1);
   __syncthreads();
-  if (q0 + wq0 < a.Nq) {
-    qk(Ks, s_cur);
-    tile(0, std::false_type{});
-    qk(Ks + C::K_ELEMS, s_cur, RFAST ? 4 : min(4, (a.Nk - BN + 15) / 16));
-    tile(1, std::true_type{});
+  if constexpr (kPersist) {
+    // The workgroup's query tiles in turn against the staged K and V: no
+    // workgroup barrier in the loop (each wave stages its own output rows
+    // in a region of its own).
+    const int q_end = min(a.Nq, q0 + max(a.tpw, 1) * BM);
+    uint16_t* obase = (uint16_t*)a.o + tok_base(a, a.o_sb, a.o_sh, b, h);
+    const bool staged = D % 8 == 0 && a.o_sn == D && ((a.o_sb | a.o_sh) & 7) == 0;
+    uint16_t* stage = (uint16_t*)(lds + ((mfma_lds_bytes<D, NW, NQB, RMODE>(a) + 15) & ~(size_t)15)) +
+                      wave * (NQB * 16 * D);
+    constexpr int PLB = D / 16, PLG = (D % 16) / 4, PLR = D % 4;
+    while (true) {
+      const int qn = q0 + BM;
+      const bool more = qn < q_end;  // (a wave with no row below Nq is in the last tile)
+      if (q0 + wq0 < a.Nq) {
+        qk(Ks, s_cur);
+        tile(0, std::false_type{});
+        qk(Ks + C::K_ELEMS, s_cur, min(4, (a.Nk - BN + 15) / 16));
+        if (more) load_qf(qn);  // Q is not read again in this tile: the next tile's rows in flight
+        tile(1, std::true_type{});
+        // Normalise by the row sum and store this tile's rows of the wave.
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float lsum;
+          if constexpr (C::ONES) lsum = __shfl(o[PLB < CB ? PLB : 0][qb][PLR], PLG * 16 + l16);
+          else lsum = sum_across_groups(l[qb]);
+          const float inv = (F8 ? a.v_descale : 1.f) / lsum;
+          const int qi = q0 + wq0 + qb * 16 + l16;
+          if (a.lse && g == 0 && qi < a.Nq)
+            a.lse[((int64_t)b * a.H + h) * a.Nq + qi] = (m[qb] + __builtin_amdgcn_logf(lsum)) * kLn2;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const int c0 = cb * 16 + g * 4;
+            if (c0 < D) {
+              const f32x4 v = o[cb][qb] * inv;
+              const u32x2 packed = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+              if (staged) *(u32x2*)(stage + (qb * 16 + l16) * D + c0) = packed;
+              else if (qi < a.Nq)
+                __builtin_nontemporal_store(packed, (u32x2*)(obase + tok_row(a, a.o_sn, b, qi) + c0));
+            }
+          }
+        }
+        if (staged) {
+          // The wave's NQB*16 rows are one contiguous span: 16-byte chunks.
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int row0 = q0 + wq0;
+          uint16_t* dst = obase + (int64_t)row0 * D;
+          constexpr int NCO = NQB * 16 * D / 8;
+          for (int c = lane; c < NCO; c += 64)
+            if (row0 + c * 8 / D < a.Nq)
+              __builtin_nontemporal_store(*(const u32x4*)(stage + c * 8), (u32x4*)(dst + c * 8));
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+      }
+      if (!more) break;
+      q0 = qn;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  } else {
+    if (q0 + wq0 < a.Nq) {
+      qk(Ks, s_cur);
+      tile(0, std::false_type{});
+      qk(Ks + C::K_ELEMS, s_cur, RFAST ? 4 : min(4, (a.Nk - BN + 15) / 16));
+      tile(1, std::true_type{});
+    }
   }
   } else {
   store_k(0, 0);
@@ -918,7 +995,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // are one contiguous span.  It is staged through LDS (the K/V stages are
   // free by now) and stored as 16-byte chunks, so each streaming store
   // covers whole lines instead of 8-byte pieces of four rows.
-  if constexpr (ATTN_STAGE_O && TWO && !IMG && D % 8 == 0) {
+  if constexpr (ATTN_STAGE_O && TWO && !IMG && !kPersist && D % 8 == 0) {
     if (a.o_sn == D && ((a.o_sb | a.o_sh) & 7) == 0) {
       static_assert((size_t)NW * NQB * 16 * D * 2 <= C::KV_BYTES, "O staging must fit the K/V stages");
       __syncthreads();  // every wave has finished reading K and V

@@ -230,7 +230,8 @@ struct Plan {
   int rmode;      // tiled kernel form (kRel*, kTwoTiles)
   int nw;         // waves per workgroup
   int hg;         // heads per workgroup (packed window kernel)
-  int bm;         // queries per workgroup (tiled kernels)
+  int bm;         // queries per workgroup and tile (tiled kernels)
+  int tpw;        // two-tile form, batched layout: query tiles per workgroup
   int64_t blocks; // workgroups
   size_t lds;     // LDS bytes per workgroup (dynamic plus static)
 };
@@ -241,6 +242,27 @@ template <int D>
 constexpr int two_tile_wpe() { return D <= 40 ? 4 : (D <= 64 ? 3 : 2); }
 template <int D>
 constexpr int two_tile_nw() { return two_tile_wpe<D>() % 2 == 0 ? 8 : 4; }
+// Two-tile form in the batched layout: each workgroup keeps the K and V
+// tiles of its (batch item, head) in LDS and walks tpw consecutive query
+// tiles, the next tile's Q in flight during the current one, so that the
+// grid is about one round of resident workgroups (256 CUs of the chip).
+// Its output is staged through a region of its own (NW * NQB * 16 * D
+// elements) instead of the K/V stages.  Not at d = 64, where that region
+// would leave two resident workgroups per CU instead of three.
+constexpr int kPersistCUs = 256;
+template <int D>
+constexpr int two_tile_tpw(const AttnArgs& a, int bm) {
+  const int64_t per_unit = (a.Nq + bm - 1) / bm;
+  const int64_t total = per_unit * a.H * a.B;
+  const int64_t slots = (int64_t)kPersistCUs * (4 * two_tile_wpe<D>() / two_tile_nw<D>());
+  int64_t t = (total + slots - 1) / slots;
+  if (t > per_unit) t = per_unit;
+  return t < 1 ? 1 : (int)t;
+}
+template <int D>
+constexpr size_t two_tile_stage_bytes() { return (size_t)two_tile_nw<D>() * kNQB * 16 * D * 2; }
+template <int D>
+constexpr bool two_tile_persists() { return D != 64; }
 
 template <int D, int NW>
 constexpr size_t mfma_lds_for(const AttnArgs& a, int rmode) {
@@ -318,8 +340,15 @@ inline Plan plan_half(const AttnArgs& a) {
     p.nw = two_tile_nw<D>();
   }
   p.bm = p.nw * kNQB * 16;
+  p.tpw = 1;
   p.blocks = (int64_t)((a.Nq + p.bm - 1) / p.bm) * a.H * a.B;
   p.lds = p.nw == 8 ? mfma_lds_for<D, 8>(a, p.rmode) : mfma_lds_for<D, 4>(a, p.rmode);
+  if (p.rmode == kTwoTiles && !a.image && two_tile_persists<D>()) {
+    p.tpw = two_tile_tpw<D>(a, p.bm);
+    const int64_t per_unit = (a.Nq + p.bm - 1) / p.bm;
+    p.blocks = (per_unit + p.tpw - 1) / p.tpw * a.H * a.B;
+    p.lds = (p.lds + 15) / 16 * 16 + two_tile_stage_bytes<D>();
+  }
   return p;
 }
 

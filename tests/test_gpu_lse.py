@@ -64,6 +64,7 @@ CASES = [
     ("table form, additive bias and mask", dict(dtype=W.F16, B=3, H=2, Nq=300, Nk=300, d=64, bias="additive",
                                                mask="additive"), 0.02),
     ("two-tile form (cross-attention)", dict(dtype=W.F16, B=2, H=4, Nq=1000, Nk=77, d=40), 0.02),
+    ("two-tile form, three query tiles per workgroup", dict(dtype=W.F16, B=40, H=8, Nq=1000, Nk=77, d=40), 0.02),
     # The contraction form carries the relative-position terms through the
     # matrix cores in the element type (error ~ |bias| * 2^-9 in bf16): its
     # tables are drawn at the workloads' N(0, 0.02^2).

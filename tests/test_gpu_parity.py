@@ -166,6 +166,21 @@ def test_two_key_tiles_dense_terms(dtype, n):
     check_full(w, inp, run_gpu(w, to_device(inp)))
 
 
+@pytest.mark.parametrize("dtype,d", [(W.F16, 32), (W.F16, 40), (W.BF16, 64), (W.BF16, 80)])
+def test_two_tiles_several_query_tiles_per_workgroup(dtype, d):
+    # Cross-attention to 77 keys (the two-tile form, batched layout) with
+    # enough (batch item, head) units that each workgroup walks 3 or 4
+    # consecutive query tiles (K and V kept in LDS, the next tile's Q loaded
+    # during the current one; at d = 64 one tile per workgroup); 1000
+    # queries leave a ragged last tile, and at d = 32, 40 the last workgroup
+    # of a unit holds fewer tiles than the first.
+    w = W.custom(dtype, B=40, H=8, Nq=1000, Nk=77, d=d, cfg_id=700 + d)
+    say(f"[two tiles, several query tiles per workgroup] {dtype} d={d}")
+    inp = W.make_inputs(w, seed=d)
+    res = check_full_pooled(w, inp, run_gpu(w, to_device(inp)), name=f"two tiles, 3-4 query tiles per workgroup d={d}")
+    say(f"  max abs err {res['err']:.3e} over {res['units']} units")
+
+
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16, W.F32])
 @pytest.mark.parametrize("geom", [(14, 14, 7, 7, 3, 3), (16, 32, 4, 8, 2, 5), (12, 12, 6, 6, 0, 0)])
 def test_image_layout(dtype, geom):
