@@ -160,34 +160,31 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
   // tiles per workgroup (q0 advances by BM after each), except at d = 64,
   // where its output staging would cost a resident workgroup per CU.
   constexpr bool kPersist = RMODE == kTwoTiles && !IMG && two_tile_persists<D>();
-  int q0 = qt * (kPersist ? max(a.tpw, 1) : 1) * BM;
+  const int q0 = qt * (kPersist ? max(a.tpw, 1) : 1) * BM;
   const int wq0 = wave * NQB * 16;  // first query row of this wave inside the tile
 
   // Query fragments (B operand of S^T = K Q^T): lane holds Q[q][dc*32 + g*8 .. +7].
   u32x4 qf[NQB][KCHT];
   const char* qbase = (const char*)a.q + IES * tok_base(a, a.q_sb, a.q_sh, b, h);
-  auto load_qf = [&](int qs) {  // the fragments of the tile starting at query qs
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qi = min(qs + wq0 + qb * 16 + l16, a.Nq - 1);
-      const uint32_t off = tok_row(a, a.q_sn, b, qi);
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qi = min(q0 + wq0 + qb * 16 + l16, a.Nq - 1);
+    const uint32_t off = tok_row(a, a.q_sn, b, qi);
 #pragma unroll
-      for (int dc = 0; dc < KCH; ++dc) {
-        const int d0 = dc * 32 + g * 8;
-        // (a padding token of the image layout is a zero query)
-        if constexpr (F8) {
-          // Loaded from an address that is always valid and then selected,
-          // so the loads of all fragments are in flight together (a load
-          // inside the condition would be waited for before its conversion).
-          const bool ok = d0 < D && off != kPadTok;
-          const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
-          qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
-        } else
-          qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
-      }
+    for (int dc = 0; dc < KCH; ++dc) {
+      const int d0 = dc * 32 + g * 8;
+      // (a padding token of the image layout is a zero query)
+      if constexpr (F8) {
+        // Loaded from an address that is always valid and then selected, so
+        // the loads of all fragments are in flight together (a load inside
+        // the condition would be waited for before its conversion).
+        const bool ok = d0 < D && off != kPadTok;
+        const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
+        qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
+      } else
+        qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
     }
-  };
-  load_qf(q0);
+  }
 
   // Tile loaders: CPT 16-byte chunks of K and of V per thread, through
   // buffer resources.  Batched layout: the resource of tile t starts at key
@@ -874,15 +871,38 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
     // workgroup barrier in the loop (each wave stages its own output rows
     // in a region of its own).
     const int q_end = min(a.Nq, q0 + max(a.tpw, 1) * BM);
+    int qc = q0;  // the current tile's first query
     uint16_t* obase = (uint16_t*)a.o + tok_base(a, a.o_sb, a.o_sh, b, h);
     const bool staged = D % 8 == 0 && a.o_sn == D && ((a.o_sb | a.o_sh) & 7) == 0;
     uint16_t* stage = (uint16_t*)(lds + ((mfma_lds_bytes<D, NW, NQB, RMODE>(a) + 15) & ~(size_t)15)) +
                       wave * (NQB * 16 * D);
     constexpr int PLB = D / 16, PLG = (D % 16) / 4, PLR = D % 4;
+    // The Q fragments of the tile starting at query qs, as in the prologue.
+    auto load_qf = [&](int qs) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = min(qs + wq0 + qb * 16 + l16, a.Nq - 1);
+        const uint32_t off = tok_row(a, a.q_sn, b, qi);
+#pragma unroll
+        for (int dc = 0; dc < KCH; ++dc) {
+          const int d0 = dc * 32 + g * 8;
+          // (a padding token of the image layout is a zero query)
+          if constexpr (F8) {
+            // Loaded from an address that is always valid and then selected,
+            // so the loads of all fragments are in flight together (a load
+            // inside the condition would be waited for before its conversion).
+            const bool ok = d0 < D && off != kPadTok;
+            const u32x4 wq = widen_e4m3<E>(*(const u32x2*)(qbase + (ok ? off + d0 : 0)));
+            qf[qb][dc] = ok ? wq : u32x4{0, 0, 0, 0};
+          } else
+            qf[qb][dc] = d0 < D && off != kPadTok ? *(const u32x4*)(qbase + 2 * (off + d0)) : u32x4{0, 0, 0, 0};
+        }
+      }
+    };
     while (true) {
-      const int qn = q0 + BM;
+      const int qn = qc + BM;
       const bool more = qn < q_end;  // (a wave with no row below Nq is in the last tile)
-      if (q0 + wq0 < a.Nq) {
+      if (qc + wq0 < a.Nq) {
         qk(Ks, s_cur);
         tile(0, std::false_type{});
         qk(Ks + C::K_ELEMS, s_cur, min(4, (a.Nk - BN + 15) / 16));
@@ -895,7 +915,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           if constexpr (C::ONES) lsum = __shfl(o[PLB < CB ? PLB : 0][qb][PLR], PLG * 16 + l16);
           else lsum = sum_across_groups(l[qb]);
           const float inv = (F8 ? a.v_descale : 1.f) / lsum;
-          const int qi = q0 + wq0 + qb * 16 + l16;
+          const int qi = qc + wq0 + qb * 16 + l16;
           if (a.lse && g == 0 && qi < a.Nq)
             a.lse[((int64_t)b * a.H + h) * a.Nq + qi] = (m[qb] + __builtin_amdgcn_logf(lsum)) * kLn2;
 #pragma unroll
@@ -915,7 +935,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int row0 = q0 + wq0;
+          const int row0 = qc + wq0;
           uint16_t* dst = obase + (int64_t)row0 * D;
           constexpr int NCO = NQB * 16 * D / 8;
           for (int c = lane; c < NCO; c += 64)
@@ -927,7 +947,7 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
         }
       }
       if (!more) break;
-      q0 = qn;
+      qc = qn;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         m[qb] = -INFINITY;
