@@ -1011,10 +1011,11 @@ __global__ __launch_bounds__(NW * 64) ATTN_WAVES_PER_EU(WPE) void attn_fwd_mfma(
 #ifndef ATTN_STAGE_O
 #define ATTN_STAGE_O 1
 #endif
-  // Two-tile form with rows stored back to back: a wave's NQB*16 output rows
-  // are one contiguous span.  It is staged through LDS (the K/V stages are
-  // free by now) and stored as 16-byte chunks, so each streaming store
-  // covers whole lines instead of 8-byte pieces of four rows.
+  // Two-tile form over one query tile (batched layout at d = 64) with rows
+  // stored back to back: a wave's NQB*16 output rows are one contiguous
+  // span.  It is staged through LDS (the K/V stages are free by now) and
+  // stored as 16-byte chunks, so each streaming store covers whole lines
+  // instead of 8-byte pieces of four rows.
   if constexpr (ATTN_STAGE_O && TWO && !IMG && !kPersist && D % 8 == 0) {
     if (a.o_sn == D && ((a.o_sb | a.o_sh) & 7) == 0) {
       static_assert((size_t)NW * NQB * 16 * D * 2 <= C::KV_BYTES, "O staging must fit the K/V stages");
