@@ -264,6 +264,21 @@ def test_relpos_backward_sam_global(d, heads):
     say(f"  max abs errors {worst}")
 
 
+def test_relpos_backward_one_hot_form_deterministic():
+    # SAM-style 14 x 14 windows take the one-hot key table form (bias and
+    # dRh/dRw gathers as matrix products, a fixed-order partial reduction):
+    # two calls agree bitwise, and the result matches the oracle.
+    w = W.custom(W.BF16, B=6, H=3, Nq=196, Nk=196, d=64, bias="relpos", grid=(14, 14), cfg_id=895)
+    inp = inputs(w, seed=5, std_table=0.5)
+    dev = to_device(inp)
+    a = run_bwd(w, dev)
+    b = run_bwd(w, dev)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[3][0], b[3][0]) and torch.equal(a[3][1], b[3][1])
+    check_grads(w, inp, a)
+
+
 def test_relpos_backward_bias_is_seen_and_deterministic():
     # The table gradients and the bias path into dQ are large next to the
     # tolerance with tables of std 0.5; two calls agree bitwise.
